@@ -73,8 +73,9 @@ static void xpose_u64(uint64_t *out, const uint64_t *in, int64_t batch,
  * ld_in        input row pitch in elements, >= cols.
  * ld_out       output row pitch in elements, >= rows.
  * stride_in    distance between input matrices in elements (ignored when
- *              batch <= 1), >= rows * ld_in.
- * stride_out   distance between output matrices in elements, >= cols * ld_out.
+ *              batch <= 1), >= 0; input matrices may overlap.
+ * stride_out   distance between output matrices in elements (ignored when
+ *              batch <= 1), >= (cols - 1) * ld_out + rows.
  * elem_bytes   1, 2, 4 or 8.
  * Returns 0, or -1 for arguments outside those ranges (nothing is written).
  */
@@ -85,7 +86,9 @@ int oracle_xpose(void *out, const void *in, int64_t batch, int64_t rows,
   if (batch == 0 || rows == 0 || cols == 0) return ORACLE_OK;
   if (!out || !in) return ORACLE_EINVAL;
   if (ld_in < cols || ld_out < rows) return ORACLE_EINVAL;
-  if (batch > 1 && (stride_in < rows * ld_in || stride_out < cols * ld_out))
+  /* Input matrices are only read, so they may overlap (stride_in >= 0);
+   * output matrices must not: each spans (cols-1)*ld_out + rows elements. */
+  if (batch > 1 && (stride_in < 0 || stride_out < (cols - 1) * ld_out + rows))
     return ORACLE_EINVAL;
   switch (elem_bytes) {
     case 1: xpose_u8(out, in, batch, rows, cols, ld_in, ld_out, stride_in, stride_out); break;

@@ -252,3 +252,15 @@ def test_planted_mistakes_are_caught(name):
         except (AssertionError, ValueError, IndexError):
             caught.append(check.__name__)
     assert caught, f"mutant {name} passed every check"
+
+
+def test_overlapping_inputs_allowed_outputs_not():
+    """Input matrices may coincide (they are only read); output matrices may
+    not overlap."""
+    src = wl.random_bits((12 * 9,), 4, seed=40)
+    out = np.zeros(3 * 9 * 12, dtype=np.uint32)
+    oracle.transpose_into(out, src, 3, 12, 9, 9, 12, 0, 9 * 12)
+    one = np.ascontiguousarray(src.reshape(12, 9).T).reshape(-1)
+    assert np.array_equal(out.reshape(3, -1), np.stack([one] * 3))
+    with pytest.raises(ValueError):
+        oracle.transpose_into(out, src, 3, 12, 9, 9, 12, 0, 9 * 12 - 1)
