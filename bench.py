@@ -1,0 +1,318 @@
+"""Throughput of the LDS-tiled transpose on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload KEY] [--table]
+
+One step is one transpose of the whole workload (default: 8192 x 8192 fp32,
+row-major, ld = cols) with the input already resident in HBM.  Prints ONE
+JSON line: effective GB/s = (read + write bytes) / time, with the copy
+yardstick, the LDS-layout ablation, the kernel's roofline fraction measured
+live with HIP events on the launch stream, and the oracle timed on one host
+core.  --table additionally writes a markdown table over every workload to
+stderr.
+
+Timing protocol ("Shared memory and the bank conflict", section "What to
+record": median of repeated runs after a warm-up, the copy measured the same
+way): W untimed launches, then K launches bracketed by device
+synchronisation (the wall-clock value) with an event pair around each
+launch (median / min / p90 / mean per launch).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+METRIC = ("effective GB/s (R+W bytes) and % of HBM peak, 8192x8192 fp32 "
+          "transpose, 1 GPU")
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "lds_tiled_matrix_amd", "csrc",
+                             "xpose_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_8192_f32.md")
+SIGNED = {1: np.int8, 2: np.int16, 4: np.int32, 8: np.int64}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln and ln.startswith("- "):
+                k, v = ln[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(launch, stream, steps, warmup):
+    """W untimed launches, then K timed ones.  Returns (wall_s, per-launch
+    event durations in seconds)."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        starts[k].record(stream)
+        launch()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+    return wall, durs
+
+
+def summarize(durs, nbytes):
+    d = sorted(durs)
+    med = statistics.median(d)
+    p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
+    mean = sum(d) / len(d)
+    return {"median_us": round(med * 1e6, 2), "min_us": round(d[0] * 1e6, 2),
+            "p90_us": round(p90 * 1e6, 2), "mean_us": round(mean * 1e6, 2),
+            "median_GBps": round(nbytes / med / 1e9, 1),
+            "mean_GBps": round(nbytes / mean / 1e9, 1)}
+
+
+def cpu_baseline(w, host_in, max_seconds=12.0, max_runs=6):
+    """The oracle as it stands, pinned to one host core, on the full
+    workload: 1 warm-up, then repeated runs until max_seconds or max_runs;
+    median effective GB/s."""
+    import oracle
+    old = os.sched_getaffinity(0)
+    core = min(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        oracle.transpose(host_in)  # warm-up (also faults the pages in)
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < max_runs and (time.perf_counter() - t_start) < max_seconds:
+            t0 = time.perf_counter()
+            out = oracle.transpose(host_in)
+            times.append(time.perf_counter() - t0)
+    finally:
+        os.sched_setaffinity(0, old)
+    med = statistics.median(times)
+    return out, {
+        "value": round(w.rw_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": (f"full {w.description}; single-threaded C nested loop "
+                   f"pinned to core {core}; 1 warm-up + {len(times)} timed "
+                   f"runs, median {med * 1e3:.1f} ms"),
+    }
+
+
+def host_cpu_name() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_workload(X, w, steps, warmup, stream, layouts=True):
+    """Time the default launch (and each layout) on one workload plus the
+    copy yardstick over the same bytes.  Returns a dict and the device
+    tensors (input, output) so the caller can check parity."""
+    import torch
+    dev = torch.device("cuda", 0)
+    host = wl.make_input(w)
+    if host.dtype.kind == "u" and host.dtype.itemsize > 1:
+        host = host.view(SIGNED[host.dtype.itemsize])
+    x = torch.from_numpy(host).to(dev)
+    out_shape = (w.cols, w.rows) if w.batch == 1 else (w.batch, w.cols, w.rows)
+    y = torch.empty(out_shape, dtype=x.dtype, device=dev)
+    code = X.dtype_code(x.dtype)
+    sh = int(stream.cuda_stream)
+    nbytes = w.rw_bytes
+
+    def launch_with(opts):
+        def go():
+            rc = X.xpose_batched_ex(y.data_ptr(), x.data_ptr(), w.batch,
+                                    w.rows, w.cols, w.cols, w.rows,
+                                    w.rows * w.cols, w.cols * w.rows, code,
+                                    opts, sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+        return go
+
+    # Copy yardstick: same byte count, same buffers (input -> output).
+    def copy_go():
+        rc = X.xpose_copy(y.data_ptr(), x.data_ptr(), nbytes // 2, sh)
+        if rc:
+            raise RuntimeError(X.strerror(rc))
+
+    res = {}
+    with torch.cuda.stream(stream):
+        wall_c, durs_c = time_launches(copy_go, stream, steps, warmup)
+        res["copy"] = summarize(durs_c, nbytes)
+        res["copy"]["wall_GBps"] = round(steps * nbytes / wall_c / 1e9, 1)
+        # hipMemcpyAsync device-to-device, for context.
+        yb, xb = y.view(-1), x.view(-1)
+        wall_m, durs_m = time_launches(lambda: yb.copy_(xb), stream,
+                                       steps, warmup)
+        res["memcpy_d2d"] = summarize(durs_m, nbytes)
+        if layouts:
+            res["ablation"] = {}
+            for lay, name in X.LAYOUT_NAMES.items():
+                _, d = time_launches(launch_with(X.XposeOpts(lay, 0, 0, 0)),
+                                     stream, steps, warmup)
+                res["ablation"][name] = summarize(d, nbytes)
+        # The default launch last, so its output stays in y.
+        wall, durs = time_launches(launch_with(None), stream, steps, warmup)
+    torch.cuda.synchronize()
+    res["wall_s"] = wall
+    res["default"] = summarize(durs, nbytes)
+    res["plan"] = X.plan_for(x, y)
+    return res, host, y
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=wl.HEADLINE, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the oracle CPU baseline and the parity check")
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--table", action="store_true",
+                    help="also measure every workload; markdown table to stderr")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for "
+              f"--gpus {args.gpus}); the transpose has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+    import lds_tiled_matrix_amd as X
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    w = wl.WORKLOADS[args.workload]
+    stream = torch.cuda.Stream()
+    log(f"bench: {w.description}; steps={args.steps} warmup={args.warmup}")
+    res, host, y = bench_workload(X, w, args.steps, args.warmup, stream,
+                                  layouts=not args.no_ablation)
+    nbytes = w.rw_bytes
+    wall = res["wall_s"]
+    value = args.steps * nbytes / wall / 1e9
+    d = res["default"]
+    achieved = nbytes / (d["mean_us"] * 1e-6) / 1e9
+    copy_gbps = res["copy"]["mean_GBps"]
+
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        log("bench: oracle on one host core (CPU baseline + parity)")
+        want, cpu = cpu_baseline(w, host)
+        got = y.cpu().numpy()
+        parity = bool(np.array_equal(got, want))
+        cpu["host_cpu"] = host_cpu_name()
+        if not parity:
+            log("bench: PARITY FAILURE against the oracle")
+
+    plan = res["plan"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.description, "batch": w.batch, "rows": w.rows,
+            "cols": w.cols, "ld_in": w.cols, "ld_out": w.rows,
+            "rw_bytes": nbytes,
+            "layout": X.LAYOUT_NAMES[plan["layout"]],
+            "tile": f"{plan['tile_rows']}x{plan['tile_cols']}",
+            "threads": plan["threads"], "workgroups": plan["tiles"],
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "frac_of_copy": round(achieved / copy_gbps, 4),
+        "timing": d,
+        "copy": res["copy"],
+        "memcpy_d2d": res["memcpy_d2d"],
+        "ablation": res.get("ablation"),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic() if w.key == wl.HEADLINE else None,
+        },
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+    if args.table:
+        rows = []
+        for key in sorted(wl.WORKLOADS):
+            wk = wl.WORKLOADS[key]
+            log(f"bench: table {key}")
+            r, _, _ = bench_workload(X, wk, min(args.steps, 100),
+                                     min(args.warmup, 10), stream,
+                                     layouts=True)
+            dd = r["default"]
+            rows.append((key, wk.rw_bytes, dd, r["copy"], r["ablation"]))
+            del r
+            torch.cuda.empty_cache()
+        log("| workload | R+W bytes | median us | GB/s (median) | % 8 TB/s | "
+            "copy GB/s | % copy | unpadded GB/s | pad1 GB/s | swizzle GB/s |")
+        log("|---|---|---|---|---|---|---|---|---|---|")
+        for key, b, dd, cp, ab in rows:
+            g = dd["median_GBps"]
+            log(f"| {key} | {b:,} | {dd['median_us']} | {g} | "
+                f"{100 * g / HBM_PEAK_GBS:.1f} | {cp['median_GBps']} | "
+                f"{100 * g / cp['median_GBps']:.1f} | "
+                f"{ab['unpadded']['median_GBps']} | {ab['pad1']['median_GBps']} | "
+                f"{ab['swizzle']['median_GBps']} |")
+    return 0 if parity is not False else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())

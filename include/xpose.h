@@ -1,0 +1,174 @@
+/*
+ * xpose -- out-of-place 2-D and batched matrix transpose for MI355X (gfx950).
+ *
+ * C ABI of libxpose.so.  Every entry point takes plain pointers and sizes and
+ * returns an int status (0 = success, negative = XPOSE_E* code); nothing
+ * throws across this boundary.
+ *
+ * What is computed.  For b in [0, batch), i in [0, rows), j in [0, cols):
+ *
+ *     out[b*stride_out + j*ld_out + i] = in[b*stride_in + i*ld_in + j]
+ *
+ * i.e. every input matrix (rows x cols, row-major, row pitch ld_in) lands
+ * transposed in the output (cols x rows, row-major, row pitch ld_out).  This
+ * is the operation of the tiled transpose in "Shared memory and the bank
+ * conflict" (section "Turn the tile around on chip": a block reads a tile in
+ * rows, turns it around on chip and writes it in rows), in the non-square
+ * form out[col * height + row] = in[row * width + col] of "Shared-memory
+ * tiling and bank conflicts" (section "Reference summary"), extended with
+ * row pitches and a batch stride.  Sizes, pitches and strides are counted in
+ * ELEMENTS.  Values are moved as raw bits: no rounding, no NaN
+ * canonicalisation, subnormals and -0 preserved.  Output elements outside
+ * each output matrix's cols x rows region (pitch padding, gaps between batch
+ * entries) are never written.
+ *
+ * Memory and streams.  `in` and `out` are DEVICE pointers on the current HIP
+ * device, owned by the caller, aligned to the element size.  `stream` is a
+ * hipStream_t (NULL = the null stream).  Calls are asynchronous on `stream`:
+ * they enqueue kernels and return; they never synchronise, never allocate,
+ * never copy to or from the host, and keep no state between calls except the
+ * per-thread last HIP error (xpose_last_hip_error).  The caller must keep
+ * both buffers alive until the stream has run the work.  Input and output
+ * byte ranges must not overlap (in-place transpose is not supported: the
+ * pages only show out-of-place kernels).
+ *
+ * Errors.  Arguments are validated on the host before anything is launched;
+ * an invalid call returns a negative code and enqueues nothing.  A shape
+ * with batch, rows or cols equal to zero is a successful no-op (pointers may
+ * then be NULL).
+ */
+#ifndef XPOSE_H
+#define XPOSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  Only the size matters: 4, 2, 2, 1 and 8 bytes. */
+typedef enum xpose_dtype {
+  XPOSE_F32 = 0,
+  XPOSE_F16 = 1,
+  XPOSE_BF16 = 2,
+  XPOSE_U8 = 3,
+  XPOSE_F64 = 4
+} xpose_dtype;
+
+/* Status codes. */
+enum {
+  XPOSE_OK = 0,
+  XPOSE_EINVAL = -1, /* NULL pointer with a non-empty shape, negative size,
+                        pitch or stride too small, size overflow, bad opts  */
+  XPOSE_EALIAS = -2, /* input and output byte ranges overlap               */
+  XPOSE_EDTYPE = -3, /* unknown dtype                                       */
+  XPOSE_EHIP = -4,   /* a HIP call failed; see xpose_last_hip_error()       */
+  XPOSE_EALIGN = -5, /* a pointer is not aligned to the element size        */
+  XPOSE_ENOTILE = -6 /* xpose_opts asked for a tile shape that is not built */
+};
+
+/* LDS tile layouts (the row stride of the on-chip tile).  Source: "pad or
+ * swizzle tiles when column access creates bank conflicts" ("Shared-memory
+ * tiling and bank conflicts", section "Reference summary"); the one-word pad
+ * is the tile[32][33] of "Shared Memory and Bank Conflicts", section "the
+ * classic case".  All layouts give identical results; they differ only in
+ * LDS bank conflicts. */
+typedef enum xpose_layout {
+  XPOSE_LAYOUT_AUTO = 0,     /* library default (the measured best)          */
+  XPOSE_LAYOUT_UNPADDED = 1, /* row stride = tile width (conflicted column read) */
+  XPOSE_LAYOUT_PAD1 = 2,     /* row stride = tile width + one 32-bit word     */
+  XPOSE_LAYOUT_SWIZZLE = 3   /* 16-byte chunks XOR-permuted per row            */
+} xpose_layout;
+
+/* Option flags for xpose_batched_ex. */
+enum {
+  XPOSE_FLAG_ELEMENTWISE = 1 /* force the element-wise edge path everywhere */
+};
+
+/* Optional knobs for the measured ablation.  Zero-initialise for defaults. */
+typedef struct xpose_opts {
+  int32_t layout;    /* xpose_layout                                         */
+  int32_t tile_rows; /* 0 = default; else one of the built tile shapes       */
+  int32_t tile_cols; /* 0 = default                                          */
+  int32_t flags;     /* XPOSE_FLAG_*                                         */
+} xpose_opts;
+
+/* What xpose_plan reports about the kernel a call would launch. */
+typedef struct xpose_plan_info {
+  int32_t layout;      /* resolved xpose_layout                              */
+  int32_t tile_rows;   /* tile shape in elements                             */
+  int32_t tile_cols;
+  int32_t threads;     /* threads per workgroup                              */
+  int32_t lds_bytes;   /* LDS per workgroup                                  */
+  int32_t vector_path; /* 1: interior tiles use 128-bit global accesses;
+                          0: every tile takes the element-wise path          */
+  int64_t tiles;       /* workgroups over the whole batch                    */
+  int32_t launches;    /* kernel launches the call will enqueue              */
+  int32_t reserved;
+} xpose_plan_info;
+
+/* 2-D transpose of one rows x cols matrix: the definition above with
+ * batch = 1.  ld_in >= cols, ld_out >= rows.  dtype is an xpose_dtype. */
+int xpose_2d(void *out, const void *in, int64_t rows, int64_t cols,
+             int64_t ld_in, int64_t ld_out, int32_t dtype, void *stream);
+
+/* Batched transpose: `batch` independent matrices, input matrix b starting
+ * stride_in elements after matrix b-1, output matrix b stride_out elements
+ * after output b-1.  Output matrices must not overlap each other:
+ * stride_out >= (cols-1)*ld_out + rows when batch > 1.  stride_in >= 0
+ * (input matrices may overlap or coincide; they are only read). */
+int xpose_batched(void *out, const void *in, int64_t batch, int64_t rows,
+                  int64_t cols, int64_t ld_in, int64_t ld_out,
+                  int64_t stride_in, int64_t stride_out, int32_t dtype,
+                  void *stream);
+
+/* xpose_batched with explicit layout and tile choice (opts may be NULL).
+ * Used for the layout ablation; results are identical for every choice. */
+int xpose_batched_ex(void *out, const void *in, int64_t batch, int64_t rows,
+                     int64_t cols, int64_t ld_in, int64_t ld_out,
+                     int64_t stride_in, int64_t stride_out, int32_t dtype,
+                     const xpose_opts *opts, void *stream);
+
+/* Host-only: validate a call and report the kernel it would launch, without
+ * touching the GPU.  Returns the same status the call would return (pointers
+ * are only compared and checked for alignment, never dereferenced).  `info`
+ * may be NULL. */
+int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
+               int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
+               int64_t stride_out, int32_t dtype, const xpose_opts *opts,
+               xpose_plan_info *info);
+
+/* Device-to-device copy of `bytes` bytes with 128-bit loads and stores: the
+ * practical bandwidth roofline the transpose is measured against (the
+ * "copy" yardstick of "Shared memory and the bank conflict", sections "Turn
+ * the tile around on chip" and "What to record").  Same pointer, stream and
+ * error rules as the transposes; the ranges must not overlap. */
+int xpose_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+/* LDS bank microbenchmark: one 64-lane wavefront repeatedly issues one LDS
+ * instruction in which lane l accesses byte address lane_bytes[l] (host
+ * array of 64 entries, each a multiple of `width`, below 16384) with
+ * `width` = 4, 8 or 16 bytes, as a read (is_write = 0) or a write (1).
+ * Each of `iters` iterations issues 8 such instructions.  The wave's elapsed
+ * shader-clock cycles are written to cycles_out[0] (a DEVICE buffer of two
+ * uint64), a checksum of what was read to cycles_out[1].  Used to measure
+ * the gfx950 bank model that the tile layouts are designed against
+ * ("Shared Memory and Bank Conflicts", section "the wave size
+ * complication": the conflict group on 64-lane hardware must be measured,
+ * not assumed). */
+int xpose_lds_probe(uint64_t *cycles_out, const int32_t *lane_bytes,
+                    int32_t width, int32_t is_write, int32_t iters,
+                    void *stream);
+
+/* hipError_t of the most recent failing HIP call made by this thread inside
+ * the library (0 if none). */
+int xpose_last_hip_error(void);
+
+/* Static string describing a status code (never NULL). */
+const char *xpose_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XPOSE_H */

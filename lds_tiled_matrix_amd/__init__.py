@@ -1,0 +1,239 @@
+"""Python binding of libxpose.so, the LDS-tiled transpose for MI355X.
+
+Every function here marshals arguments and calls the C ABI declared in
+``include/xpose.h``; the transpose itself runs only in the library's gfx950
+kernels.  The library must have been built (``python -m
+lds_tiled_matrix_amd.build``); importing this package without it raises
+ImportError rather than falling back to anything else.
+
+Low-level names mirror the C ABI (``xpose_2d``, ``xpose_batched``,
+``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``)
+and take raw device addresses as integers.  ``transpose`` and ``copy`` are
+conveniences over torch tensors: torch supplies the device memory and the
+stream, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libxpose.so")
+
+XPOSE_F32, XPOSE_F16, XPOSE_BF16, XPOSE_U8, XPOSE_F64 = 0, 1, 2, 3, 4
+XPOSE_OK = 0
+XPOSE_EINVAL, XPOSE_EALIAS, XPOSE_EDTYPE = -1, -2, -3
+XPOSE_EHIP, XPOSE_EALIGN, XPOSE_ENOTILE = -4, -5, -6
+LAYOUT_AUTO, LAYOUT_UNPADDED, LAYOUT_PAD1, LAYOUT_SWIZZLE = 0, 1, 2, 3
+LAYOUT_NAMES = {LAYOUT_UNPADDED: "unpadded", LAYOUT_PAD1: "pad1",
+                LAYOUT_SWIZZLE: "swizzle"}
+FLAG_ELEMENTWISE = 1
+
+# Every exported entry point, in header order.
+EXPORTS = ("xpose_2d", "xpose_batched", "xpose_batched_ex", "xpose_plan",
+           "xpose_copy", "xpose_lds_probe", "xpose_last_hip_error",
+           "xpose_strerror")
+
+
+class XposeOpts(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("tile_cols", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class XposePlanInfo(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("tile_cols", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("vector_path", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m lds_tiled_matrix_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    opts_p, info_p = ctypes.POINTER(XposeOpts), ctypes.POINTER(XposePlanInfo)
+    sig = {
+        "xpose_2d": [p, p, i64, i64, i64, i64, i32, p],
+        "xpose_batched": [p, p, i64, i64, i64, i64, i64, i64, i64, i32, p],
+        "xpose_batched_ex": [p, p, i64, i64, i64, i64, i64, i64, i64, i32,
+                             opts_p, p],
+        "xpose_plan": [p, p, i64, i64, i64, i64, i64, i64, i64, i32, opts_p,
+                       info_p],
+        "xpose_copy": [p, p, i64, p],
+        "xpose_lds_probe": [p, ctypes.POINTER(i32), i32, i32, i32, p],
+        "xpose_last_hip_error": [],
+        "xpose_strerror": [ctypes.c_int],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "xpose_strerror" else ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+class XposeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        msg = f"{what}: {strerror(code)} ({code})"
+        if code == XPOSE_EHIP:
+            msg += f", hipError {_lib.xpose_last_hip_error()}"
+        super().__init__(msg)
+
+
+def _check(code: int, what: str) -> int:
+    if code != XPOSE_OK:
+        raise XposeError(code, what)
+    return code
+
+
+def _opts(layout=LAYOUT_AUTO, tile=None, flags=0):
+    tr, tc = tile if tile else (0, 0)
+    return XposeOpts(layout, tr, tc, flags)
+
+
+# ----- C ABI, one to one -----------------------------------------------------
+
+def xpose_2d(out: int, inp: int, rows: int, cols: int, ld_in: int,
+             ld_out: int, dtype: int, stream: int = 0) -> int:
+    return _lib.xpose_2d(out, inp, rows, cols, ld_in, ld_out, dtype, stream)
+
+
+def xpose_batched(out: int, inp: int, batch: int, rows: int, cols: int,
+                  ld_in: int, ld_out: int, stride_in: int, stride_out: int,
+                  dtype: int, stream: int = 0) -> int:
+    return _lib.xpose_batched(out, inp, batch, rows, cols, ld_in, ld_out,
+                              stride_in, stride_out, dtype, stream)
+
+
+def xpose_batched_ex(out: int, inp: int, batch: int, rows: int, cols: int,
+                     ld_in: int, ld_out: int, stride_in: int, stride_out: int,
+                     dtype: int, opts: XposeOpts | None = None,
+                     stream: int = 0) -> int:
+    return _lib.xpose_batched_ex(out, inp, batch, rows, cols, ld_in, ld_out,
+                                 stride_in, stride_out, dtype,
+                                 ctypes.byref(opts) if opts else None, stream)
+
+
+def xpose_plan(out: int, inp: int, batch: int, rows: int, cols: int,
+               ld_in: int, ld_out: int, stride_in: int, stride_out: int,
+               dtype: int, opts: XposeOpts | None = None):
+    """Returns (status, XposePlanInfo)."""
+    info = XposePlanInfo()
+    rc = _lib.xpose_plan(out, inp, batch, rows, cols, ld_in, ld_out,
+                         stride_in, stride_out, dtype,
+                         ctypes.byref(opts) if opts else None,
+                         ctypes.byref(info))
+    return rc, info
+
+
+def xpose_copy(dst: int, src: int, nbytes: int, stream: int = 0) -> int:
+    return _lib.xpose_copy(dst, src, nbytes, stream)
+
+
+def xpose_lds_probe(cycles_out: int, lane_bytes, width: int, is_write: int,
+                    iters: int, stream: int = 0) -> int:
+    arr = (ctypes.c_int32 * 64)(*[int(x) for x in lane_bytes])
+    return _lib.xpose_lds_probe(cycles_out, arr, width, is_write, iters,
+                                stream)
+
+
+def xpose_last_hip_error() -> int:
+    return _lib.xpose_last_hip_error()
+
+
+def strerror(code: int) -> str:
+    return _lib.xpose_strerror(code).decode()
+
+
+# ----- torch conveniences (memory and streams only) --------------------------
+
+def dtype_code(t) -> int:
+    """xpose_dtype for a torch dtype, by element size."""
+    import torch
+    table = {torch.float32: XPOSE_F32, torch.int32: XPOSE_F32,
+             torch.uint32: XPOSE_F32, torch.float16: XPOSE_F16,
+             torch.bfloat16: XPOSE_BF16, torch.int16: XPOSE_F16,
+             torch.uint16: XPOSE_F16, torch.uint8: XPOSE_U8,
+             torch.int8: XPOSE_U8, torch.float64: XPOSE_F64,
+             torch.int64: XPOSE_F64, torch.uint64: XPOSE_F64}
+    if t not in table:
+        raise TypeError(f"unsupported dtype {t}")
+    return table[t]
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
+              flags: int = 0, stream=None):
+    """Transpose the last two dims of a 2-D or 3-D CUDA tensor whose last dim
+    is contiguous.  Row pitches and the batch stride are taken from the
+    tensor's strides.  Returns ``out`` (allocated contiguous if None)."""
+    import torch
+    if x.dim() not in (2, 3):
+        raise ValueError("expected a 2-D or 3-D tensor")
+    if x.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    batch = x.shape[0] if x.dim() == 3 else 1
+    rows, cols = x.shape[-2], x.shape[-1]
+    if out is None:
+        shape = (cols, rows) if x.dim() == 2 else (batch, cols, rows)
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or out.stride(-1) != 1:
+        raise ValueError("out must match dtype and have a contiguous last dim")
+    if tuple(out.shape[-2:]) != (cols, rows):
+        raise ValueError("out has the wrong shape")
+    ld_in = x.stride(-2) if rows > 1 else cols
+    ld_out = out.stride(-2) if cols > 1 else rows
+    stride_in = x.stride(0) if x.dim() == 3 else 0
+    stride_out = out.stride(0) if out.dim() == 3 else 0
+    code = dtype_code(x.dtype)
+    opts = _opts(layout, tile, flags) if (layout or tile or flags) else None
+    _check(xpose_batched_ex(out.data_ptr(), x.data_ptr(), batch, rows, cols,
+                            ld_in, ld_out, stride_in, stride_out, code, opts,
+                            _stream_handle(stream)), "xpose_batched_ex")
+    return out
+
+
+def copy(dst, src, stream=None):
+    """Byte copy between two contiguous CUDA tensors of equal byte size, by
+    the library's 128-bit copy kernel."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("byte sizes differ")
+    _check(xpose_copy(dst.data_ptr(), src.data_ptr(), nbytes,
+                      _stream_handle(stream)), "xpose_copy")
+    return dst
+
+
+def plan_for(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
+             flags: int = 0) -> dict:
+    """The kernel ``transpose`` would launch for these tensors (host only)."""
+    batch = x.shape[0] if x.dim() == 3 else 1
+    rows, cols = x.shape[-2], x.shape[-1]
+    ld_in = x.stride(-2) if rows > 1 else cols
+    stride_in = x.stride(0) if x.dim() == 3 else 0
+    if out is None:
+        out_ptr, ld_out, stride_out = 0x100000000000, rows, rows * cols
+    else:
+        out_ptr = out.data_ptr()
+        ld_out = out.stride(-2) if cols > 1 else rows
+        stride_out = out.stride(0) if out.dim() == 3 else 0
+    opts = _opts(layout, tile, flags) if (layout or tile or flags) else None
+    rc, info = xpose_plan(out_ptr, x.data_ptr(), batch, rows, cols, ld_in,
+                          ld_out, stride_in, stride_out, dtype_code(x.dtype),
+                          opts)
+    _check(rc, "xpose_plan")
+    return info.as_dict()

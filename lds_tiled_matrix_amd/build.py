@@ -1,0 +1,62 @@
+"""Build libxpose.so for gfx950 in-tree.
+
+    python -m lds_tiled_matrix_amd.build
+
+hipcc cross-compiles without a GPU.  The library is written next to this
+file so it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libxpose.so")
+SOURCES = ["xpose_kernels.hip", "xpose_api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc",
+                 shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Wall", "-Wno-unused-variable",
+        # No packed-fp32 instructions anywhere in device code.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + flags() + ["-o", tmp] + [os.path.join(CSRC, s)
+                                              for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def dump_isa(out_dir: str) -> None:
+    """Write the gfx950 assembly of the kernels (for checking instruction
+    selection: LDS widths, global access widths, waits)."""
+    os.makedirs(out_dir, exist_ok=True)
+    cmd = [hipcc()] + [f for f in flags() if f not in ("-shared", "-fPIC")] + [
+        "--cuda-device-only", "-S", "-o",
+        os.path.join(out_dir, "xpose_kernels.s"),
+        os.path.join(CSRC, "xpose_kernels.hip")]
+    subprocess.run(cmd, check=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-q" not in sys.argv))

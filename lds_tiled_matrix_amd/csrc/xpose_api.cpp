@@ -1,0 +1,289 @@
+// C-ABI front end of libxpose.so: argument validation, kernel choice, launch
+// and error mapping.  Validation and planning are pure host code that never
+// touches the GPU, so every error path can be exercised on a machine without
+// one.  The operation itself is defined in include/xpose.h.
+
+#include "../../include/xpose.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "xpose_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return XPOSE_EHIP;
+}
+
+int elem_bytes_of(int32_t dtype) {
+  switch (dtype) {
+    case XPOSE_F32: return 4;
+    case XPOSE_F16: return 2;
+    case XPOSE_BF16: return 2;
+    case XPOSE_U8: return 1;
+    case XPOSE_F64: return 8;
+    default: return 0;
+  }
+}
+
+// Default tile shape and layout per element size.  The layout default is the
+// one that measured conflict-free and fastest; the tile shape the fastest in
+// the shape sweep (both recorded with the measurements).
+struct Default {
+  int tile_rows, tile_cols, layout;
+};
+Default default_for(int s) {
+  switch (s) {
+    case 4: return {64, 64, xpose::kSwizzle};
+    case 2: return {64, 64, xpose::kSwizzle};
+    case 1: return {128, 128, xpose::kSwizzle};
+    default: return {32, 32, xpose::kSwizzle};
+  }
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) {
+  return !__builtin_mul_overflow(a, b, r);
+}
+bool add_ok(int64_t a, int64_t b, int64_t *r) {
+  return !__builtin_add_overflow(a, b, r);
+}
+
+// Number of elements from the first to one past the last element touched by
+// `count` matrices of `r` rows x `c` cols, pitch ld, matrix stride st.
+bool extent(int64_t count, int64_t r, int64_t c, int64_t ld, int64_t st,
+            int64_t *out) {
+  int64_t a, b, t;
+  if (!mul_ok(count - 1, st, &a) || !mul_ok(r - 1, ld, &b) ||
+      !add_ok(a, b, &t) || !add_ok(t, c, &t))
+    return false;
+  *out = t;
+  return true;
+}
+
+struct Plan {
+  const xpose::TileKernel *kernel;
+  xpose::TileArgs args;
+  int64_t batch;
+  int64_t tiles_per_matrix;
+  int64_t batch_per_launch;
+  bool empty;
+};
+
+int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
+              int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
+              int64_t stride_out, int32_t dtype, const xpose_opts *opts,
+              Plan *plan) {
+  memset(plan, 0, sizeof(*plan));
+  const int s = elem_bytes_of(dtype);
+  if (s == 0) return XPOSE_EDTYPE;
+  if (batch < 0 || rows < 0 || cols < 0) return XPOSE_EINVAL;
+  if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
+               opts->layout > XPOSE_LAYOUT_SWIZZLE ||
+               (opts->flags & ~XPOSE_FLAG_ELEMENTWISE) != 0 ||
+               opts->tile_rows < 0 || opts->tile_cols < 0))
+    return XPOSE_EINVAL;
+  if (batch == 0 || rows == 0 || cols == 0) {
+    plan->empty = true;
+    return XPOSE_OK;
+  }
+  if (!out || !in) return XPOSE_EINVAL;
+  if (ld_in < cols || ld_out < rows) return XPOSE_EINVAL;
+  if (batch > 1 && stride_in < 0) return XPOSE_EINVAL;
+  if (batch == 1) stride_in = stride_out = 0;
+
+  int64_t ext_in, ext_out;
+  if (!extent(batch, rows, cols, ld_in, stride_in, &ext_in) ||
+      !extent(1, cols, rows, ld_out, 0, &ext_out))
+    return XPOSE_EINVAL;
+  if (batch > 1) {
+    // Output matrices must not overlap one another.
+    if (stride_out < ext_out) return XPOSE_EINVAL;
+    if (!extent(batch, cols, rows, ld_out, stride_out, &ext_out))
+      return XPOSE_EINVAL;
+  }
+  int64_t bytes_in, bytes_out;
+  if (!mul_ok(ext_in, s, &bytes_in) || !mul_ok(ext_out, s, &bytes_out))
+    return XPOSE_EINVAL;
+
+  const uintptr_t pi = (uintptr_t)in, po = (uintptr_t)out;
+  if ((pi % s) || (po % s)) return XPOSE_EALIGN;
+  if (pi + (uint64_t)bytes_in < pi || po + (uint64_t)bytes_out < po)
+    return XPOSE_EINVAL;
+  if (pi < po + (uint64_t)bytes_out && po < pi + (uint64_t)bytes_in)
+    return XPOSE_EALIAS;
+
+  // Kernel choice.
+  Default d = default_for(s);
+  int layout = (opts && opts->layout) ? opts->layout : d.layout;
+  int tr = d.tile_rows, tc = d.tile_cols;
+  if (opts && (opts->tile_rows || opts->tile_cols)) {
+    tr = opts->tile_rows;
+    tc = opts->tile_cols;
+  }
+  int n = 0;
+  const xpose::TileKernel *table = xpose::tile_kernels(&n);
+  const xpose::TileKernel *k = nullptr;
+  for (int i = 0; i < n; ++i)
+    if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
+        table[i].tile_cols == tc && table[i].layout == layout)
+      k = &table[i];
+  if (!k) return XPOSE_ENOTILE;
+
+  const int64_t tiles_r = (rows + tr - 1) / tr;
+  const int64_t tiles_c = (cols + tc - 1) / tc;
+  if (tiles_r > 0x7fffffff || tiles_c > 0x7fffffff) return XPOSE_EINVAL;
+  int64_t tiles;
+  if (!mul_ok(tiles_r, tiles_c, &tiles) || tiles > 0x7fffffff)
+    return XPOSE_EINVAL;
+
+  // 128-bit accesses need every row start 4-byte aligned on both sides.
+  bool vec = true;
+  if (s < 4) {
+    const int64_t q = 4 / s;  // elements per dword
+    vec = (pi % 4 == 0) && (po % 4 == 0) && (ld_in % q == 0) &&
+          (ld_out % q == 0) &&
+          (batch == 1 || (stride_in % q == 0 && stride_out % q == 0));
+  }
+  if (opts && (opts->flags & XPOSE_FLAG_ELEMENTWISE)) vec = false;
+
+  plan->kernel = k;
+  plan->batch = batch;
+  plan->tiles_per_matrix = tiles;
+  plan->batch_per_launch = 0x7fffffff / tiles;
+  xpose::TileArgs &a = plan->args;
+  a.out = const_cast<void *>(out);
+  a.in = in;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld_in = ld_in;
+  a.ld_out = ld_out;
+  a.stride_in = stride_in;
+  a.stride_out = stride_out;
+  a.tiles_r = (uint32_t)tiles_r;
+  a.tiles_c = (uint32_t)tiles_c;
+  a.batch_first = 0;
+  a.vec_ok = vec ? 1 : 0;
+  return XPOSE_OK;
+}
+
+int run_plan(Plan &plan, void *stream) {
+  if (plan.empty) return XPOSE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int64_t b0 = 0; b0 < plan.batch; b0 += plan.batch_per_launch) {
+    int64_t nb = plan.batch - b0;
+    if (nb > plan.batch_per_launch) nb = plan.batch_per_launch;
+    // batch_first is a 32-bit field: advance the base pointers instead once
+    // the batch index would not fit.
+    xpose::TileArgs a = plan.args;
+    const int s = plan.kernel->elem_bytes;
+    a.in = static_cast<const char *>(a.in) + b0 * a.stride_in * s;
+    a.out = static_cast<char *>(a.out) + b0 * a.stride_out * s;
+    const hipError_t e =
+        plan.kernel->launch(a, (uint32_t)(nb * plan.tiles_per_matrix), st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return XPOSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int xpose_batched_ex(void *out, const void *in, int64_t batch, int64_t rows,
+                     int64_t cols, int64_t ld_in, int64_t ld_out,
+                     int64_t stride_in, int64_t stride_out, int32_t dtype,
+                     const xpose_opts *opts, void *stream) {
+  Plan plan;
+  const int rc = make_plan(out, in, batch, rows, cols, ld_in, ld_out,
+                           stride_in, stride_out, dtype, opts, &plan);
+  if (rc != XPOSE_OK) return rc;
+  return run_plan(plan, stream);
+}
+
+int xpose_batched(void *out, const void *in, int64_t batch, int64_t rows,
+                  int64_t cols, int64_t ld_in, int64_t ld_out,
+                  int64_t stride_in, int64_t stride_out, int32_t dtype,
+                  void *stream) {
+  return xpose_batched_ex(out, in, batch, rows, cols, ld_in, ld_out,
+                          stride_in, stride_out, dtype, nullptr, stream);
+}
+
+int xpose_2d(void *out, const void *in, int64_t rows, int64_t cols,
+             int64_t ld_in, int64_t ld_out, int32_t dtype, void *stream) {
+  return xpose_batched_ex(out, in, 1, rows, cols, ld_in, ld_out, 0, 0, dtype,
+                          nullptr, stream);
+}
+
+int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
+               int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
+               int64_t stride_out, int32_t dtype, const xpose_opts *opts,
+               xpose_plan_info *info) {
+  Plan plan;
+  const int rc = make_plan(out, in, batch, rows, cols, ld_in, ld_out,
+                           stride_in, stride_out, dtype, opts, &plan);
+  if (info) {
+    memset(info, 0, sizeof(*info));
+    if (rc == XPOSE_OK && !plan.empty) {
+      info->layout = plan.kernel->layout;
+      info->tile_rows = plan.kernel->tile_rows;
+      info->tile_cols = plan.kernel->tile_cols;
+      info->threads = plan.kernel->threads;
+      info->lds_bytes = plan.kernel->lds_bytes;
+      info->vector_path = plan.args.vec_ok;
+      info->tiles = plan.tiles_per_matrix * plan.batch;
+      info->launches = (int32_t)((plan.batch + plan.batch_per_launch - 1) /
+                                 plan.batch_per_launch);
+    }
+  }
+  return rc;
+}
+
+int xpose_copy(void *dst, const void *src, int64_t bytes, void *stream) {
+  if (bytes < 0) return XPOSE_EINVAL;
+  if (bytes == 0) return XPOSE_OK;
+  if (!dst || !src) return XPOSE_EINVAL;
+  const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
+  if (d + (uint64_t)bytes < d || s + (uint64_t)bytes < s) return XPOSE_EINVAL;
+  if (d < s + (uint64_t)bytes && s < d + (uint64_t)bytes) return XPOSE_EALIAS;
+  const hipError_t e =
+      xpose::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? XPOSE_OK : hip_fail(e);
+}
+
+int xpose_lds_probe(uint64_t *cycles_out, const int32_t *lane_bytes,
+                    int32_t width, int32_t is_write, int32_t iters,
+                    void *stream) {
+  if (!cycles_out || !lane_bytes) return XPOSE_EINVAL;
+  if (width != 4 && width != 8 && width != 16) return XPOSE_EINVAL;
+  if (iters < 1 || iters > (1 << 20)) return XPOSE_EINVAL;
+  if ((uintptr_t)cycles_out % 8) return XPOSE_EALIGN;
+  for (int i = 0; i < 64; ++i)
+    if (lane_bytes[i] < 0 || lane_bytes[i] >= 16384 || lane_bytes[i] % width)
+      return XPOSE_EINVAL;
+  const hipError_t e =
+      xpose::launch_lds_probe(cycles_out, lane_bytes, width, is_write != 0,
+                              iters, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? XPOSE_OK : hip_fail(e);
+}
+
+int xpose_last_hip_error(void) { return g_last_hip_error; }
+
+const char *xpose_strerror(int code) {
+  switch (code) {
+    case XPOSE_OK: return "success";
+    case XPOSE_EINVAL: return "invalid argument";
+    case XPOSE_EALIAS: return "input and output ranges overlap";
+    case XPOSE_EDTYPE: return "unknown dtype";
+    case XPOSE_EHIP: return "HIP runtime error";
+    case XPOSE_EALIGN: return "pointer not aligned to the element size";
+    case XPOSE_ENOTILE: return "no kernel built for the requested tile shape";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

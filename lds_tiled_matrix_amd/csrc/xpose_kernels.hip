@@ -1,0 +1,534 @@
+// LDS-tiled out-of-place transpose for gfx950 (CDNA4, 64-lane wavefronts).
+//
+// Method ("Shared memory and the bank conflict", section "Turn the tile
+// around on chip"): each workgroup reads one tile of the input with coalesced
+// row accesses, stores it into an on-chip tile, waits at one barrier, reads
+// the tile back column-wise and writes the columns out as coalesced rows of
+// the output.  The barrier is the only synchronisation: the second phase
+// reads words other waves wrote in the first (same page, "The barrier").
+//
+// What is re-derived for gfx950 rather than taken from the pages:
+//  * Global side: every lane moves 16 bytes per access (global_load_dwordx4 /
+//    global_store_dwordx4), so a run of 8 lanes covers one 128-byte line of a
+//    tile row; the pages' kernel moves 4 bytes per lane.
+//  * LDS unit: the tile is held as 32-bit words ("units").  1- and 2-byte
+//    elements are packed VERTICALLY, K = 4/size input rows of one column per
+//    word, by an in-register K x K byte transpose before the LDS write.  The
+//    column walk of the second phase then gathers whole words that are
+//    already output-ordered, so every element size reduces to the same word
+//    tile.  8-byte elements use 64-bit units.
+//  * Bank mapping: the column walk is the conflict site ("Shared Memory and
+//    Bank Conflicts", "the classic case").  On 64-lane hardware conflicts are
+//    resolved per group of lanes whose size must be measured ("the wave size
+//    complication"), so the lane maps below never let one 32-lane half-wave
+//    span more than eight 16-byte chunks of a tile row; with a one-word pad
+//    or a 16-byte XOR swizzle the column read is then conflict-free whether
+//    the hardware resolves 32 lanes over 32 banks or 64 lanes over 64 banks.
+//  * Edges: tiles that cross the matrix edge (or matrices whose rows are not
+//    4-byte aligned) take an element-wise path through the same LDS tile;
+//    nothing outside the logical output is written.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "xpose_kernels.h"
+
+namespace xpose {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte global access at a 4-byte-aligned address.  gfx9 global memory
+// instructions wider than a dword only need dword alignment, so a row whose
+// pitch is an odd number of fp32 elements still takes dwordx4 accesses.
+struct __attribute__((aligned(4))) Vec16 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ u32x4 load16(const char *p) {
+  const Vec16 v = *reinterpret_cast<const Vec16 *>(p);
+  return u32x4{v.w[0], v.w[1], v.w[2], v.w[3]};
+}
+
+__device__ __forceinline__ void store16(char *p, u32x4 x) {
+  Vec16 v;
+  v.w[0] = x.x;
+  v.w[1] = x.y;
+  v.w[2] = x.z;
+  v.w[3] = x.w;
+  *reinterpret_cast<Vec16 *>(p) = v;
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+template <int S> struct Elem;
+template <> struct Elem<1> { using E = uint8_t;  using U = uint32_t; static constexpr int K = 4; };
+template <> struct Elem<2> { using E = uint16_t; using U = uint32_t; static constexpr int K = 2; };
+template <> struct Elem<4> { using E = uint32_t; using U = uint32_t; static constexpr int K = 1; };
+template <> struct Elem<8> { using E = uint64_t; using U = uint64_t; static constexpr int K = 1; };
+
+// Compile-time geometry of one tile kernel.
+//   S   element bytes          TR x TC  tile in elements
+//   NT  threads per workgroup  L        LDS layout
+template <int S, int TR, int TC, int NT, int L>
+struct Tile {
+  using E = typename Elem<S>::E;
+  using U = typename Elem<S>::U;
+  static constexpr int K = Elem<S>::K;          // input rows per LDS unit
+  static constexpr int UB = (int)sizeof(U);     // unit bytes
+  static constexpr int V = 16 / S;              // elements per 16-byte vector
+  static constexpr int UPV = 16 / UB;           // units per 16-byte vector
+  static constexpr int P = TR / K;              // unit rows of the LDS tile
+  static constexpr int NCI = TC / V;            // 16-B chunks per input tile row
+  static constexpr int NCO = TR / V;            // 16-B chunks per output tile row
+  static constexpr int NCL = TC / UPV;          // 16-B chunks per LDS row
+  static constexpr int STRIDE = TC + (L == kPad1 ? 1 : 0);  // LDS row, units
+  static constexpr int NW = NT / 64;            // waves per workgroup
+  static constexpr int LIT = P * NCI / NT;      // load tasks per lane
+  static constexpr int SIT = TC * NCO / NT;     // store tasks per lane
+  static constexpr int LDS_UNITS = P * STRIDE;
+  static constexpr int LDS_BYTES = LDS_UNITS * UB;
+  // Row writes are 16-byte LDS stores unless the pad breaks their alignment.
+  static constexpr bool WIDE_WRITE = (L != kPad1);
+
+  static_assert(NT % 64 == 0, "whole wavefronts");
+  static_assert(TR % V == 0 && TC % V == 0, "tile must hold whole vectors");
+  static_assert(P * NCI % NT == 0 && TC * NCO % NT == 0, "even task split");
+  static_assert(LIT >= 1 && SIT >= 1, "every lane has work");
+  static_assert(NCL >= 1 && (NCL & (NCL - 1)) == 0, "power-of-two chunks");
+  static_assert(NCL >= K, "rotation needs at least K chunks per LDS row");
+
+  // Unit index of logical unit (p, c) in the LDS tile.
+  __device__ static __forceinline__ int lds_index(int p, int c) {
+    if constexpr (L == kSwizzle) {
+      // 16-byte chunks of row p are XOR-permuted by the row's vector group
+      // p / UPV: the UPV rows one lane gathers share a permutation (so its
+      // column reads keep constant offsets), and lanes gathering different
+      // row groups of one column land in different chunks.  With K > 1 a
+      // lane writes K adjacent chunks, one per instruction, so the chunk
+      // index is first rotated right by log2(K) bits: the chunks one
+      // instruction writes (stride K) become consecutive.
+      constexpr int NB = ilog2(NCL), KB = ilog2(K);
+      const int lc = c / UPV;
+      const int rc = KB ? ((lc >> KB) | ((lc & (K - 1)) << (NB - KB))) : lc;
+      const int chunk = rc ^ ((p / UPV) & (NCL - 1));
+      return p * TC + chunk * UPV + (c % UPV);
+    } else {
+      return p * STRIDE + c;
+    }
+  }
+};
+
+// Lane -> (row, chunk) for one wave-wide task over a block of tile rows that
+// are NCH 16-byte chunks long; wt numbers the wave tasks of a phase.
+//   SPLIT == false or NCH <= 8: consecutive lanes take consecutive chunks of
+//     a row, a wave covers 64 / NCH rows.
+//   SPLIT and NCH >= 16: a half-wave covers 8 chunks of each of 4 rows and
+//     the two halves take neighbouring 8-chunk groups of the same 4 rows, so
+//     a half-wave never spans more than 8 chunks (128 bytes) of one row.
+template <int NCH, bool SPLIT>
+__device__ __forceinline__ void lane_map(int wt, int lane, int &row,
+                                         int &chunk) {
+  if constexpr (!SPLIT || NCH <= 8) {
+    if constexpr (NCH <= 64) {
+      static_assert(64 % NCH == 0, "chunks per row divide the wave");
+      row = wt * (64 / NCH) + lane / NCH;
+      chunk = lane % NCH;
+    } else {
+      static_assert(NCH % 64 == 0, "rows span whole waves");
+      row = wt / (NCH / 64);
+      chunk = (wt % (NCH / 64)) * 64 + lane;
+    }
+  } else {
+    static_assert(NCH % 16 == 0, "split map needs 16-chunk multiples");
+    constexpr int CG = NCH / 16;
+    const int h = lane >> 5, m = lane & 31;
+    row = (wt / CG) * 4 + (m >> 3);
+    chunk = ((wt % CG) * 2 + h) * 8 + (m & 7);
+  }
+}
+
+// K input-row vectors (16 bytes each, same columns) -> V column units.
+// Unit e holds column e of the K rows, first row in the lowest bytes.
+template <int S>
+__device__ __forceinline__ void pack_units(const u32x4 *rows,
+                                           typename Elem<S>::U *u) {
+  if constexpr (S == 4) {
+    u[0] = rows[0].x; u[1] = rows[0].y; u[2] = rows[0].z; u[3] = rows[0].w;
+  } else if constexpr (S == 8) {
+    u[0] = (uint64_t)rows[0].x | ((uint64_t)rows[0].y << 32);
+    u[1] = (uint64_t)rows[0].z | ((uint64_t)rows[0].w << 32);
+  } else if constexpr (S == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = rows[0][j], b = rows[1][j];
+      u[2 * j] = (a & 0xFFFFu) | (b << 16);
+      u[2 * j + 1] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+  } else {  // S == 1: 4 x 4 byte transpose per word column
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int sh = 8 * b;
+        u[4 * j + b] = ((rows[0][j] >> sh) & 0xFFu) |
+                       (((rows[1][j] >> sh) & 0xFFu) << 8) |
+                       (((rows[2][j] >> sh) & 0xFFu) << 16) |
+                       (((rows[3][j] >> sh) & 0xFFu) << 24);
+      }
+    }
+  }
+}
+
+// UPV units gathered down one LDS column -> one 16-byte output vector.
+template <int S>
+__device__ __forceinline__ u32x4 units_to_vec(const typename Elem<S>::U *u) {
+  if constexpr (S == 8) {
+    return u32x4{(uint32_t)u[0], (uint32_t)(u[0] >> 32), (uint32_t)u[1],
+                 (uint32_t)(u[1] >> 32)};
+  } else {
+    return u32x4{u[0], u[1], u[2], u[3]};
+  }
+}
+
+// Store the V units one load task produced: row p, columns c .. c+V-1.
+template <class T>
+__device__ __forceinline__ void write_units(typename T::U *lds, int p, int c,
+                                            const typename T::U *u) {
+  if constexpr (T::WIDE_WRITE) {
+#pragma unroll
+    for (int g = 0; g < T::V / T::UPV; ++g) {
+      const int idx = T::lds_index(p, c + g * T::UPV);
+      if constexpr (T::UB == 4) {
+        *reinterpret_cast<u32x4 *>(lds + idx) =
+            u32x4{u[4 * g], u[4 * g + 1], u[4 * g + 2], u[4 * g + 3]};
+      } else {
+        *reinterpret_cast<u32x4 *>(lds + idx) =
+            u32x4{(uint32_t)u[2 * g], (uint32_t)(u[2 * g] >> 32),
+                  (uint32_t)u[2 * g + 1], (uint32_t)(u[2 * g + 1] >> 32)};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < T::V; ++e) lds[T::lds_index(p, c + e)] = u[e];
+  }
+}
+
+// Gather one output vector: units (q*UPV + k, c) for k < UPV.
+template <class T>
+__device__ __forceinline__ u32x4 read_column(const typename T::U *lds, int c,
+                                             int q) {
+  typename T::U u[T::UPV];
+#pragma unroll
+  for (int k = 0; k < T::UPV; ++k) u[k] = lds[T::lds_index(q * T::UPV + k, c)];
+  return units_to_vec<sizeof(typename T::E)>(u);
+}
+
+// Interior tile, rows 4-byte aligned: 128-bit global accesses throughout.
+template <class T>
+__device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
+                                            char *dst, int64_t ld_in,
+                                            int64_t ld_out, int wave,
+                                            int lane) {
+  constexpr int S = (int)sizeof(typename T::E);
+  constexpr bool LSPLIT = !T::WIDE_WRITE;
+  u32x4 v[T::LIT][T::K];
+#pragma unroll
+  for (int it = 0; it < T::LIT; ++it) {
+    int p, ch;
+    lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
+#pragma unroll
+    for (int k = 0; k < T::K; ++k)
+      v[it][k] = load16(src + ((int64_t)(p * T::K + k) * ld_in + ch * T::V) * S);
+  }
+#pragma unroll
+  for (int it = 0; it < T::LIT; ++it) {
+    int p, ch;
+    lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
+    typename T::U u[T::V];
+    pack_units<S>(v[it], u);
+    write_units<T>(lds, p, ch * T::V, u);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < T::SIT; ++it) {
+    int c, q;
+    lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
+    const u32x4 o = read_column<T>(lds, c, q);
+    store16(dst + ((int64_t)c * ld_out + q * T::V) * S, o);
+  }
+}
+
+// Edge tile (or unaligned rows): the same LDS tile and lane maps, but every
+// global access is one element wide and bounds-checked against the rows and
+// columns left in the matrix.
+template <class T>
+__device__ __forceinline__ void tile_elementwise(typename T::U *lds,
+                                                 const char *src, char *dst,
+                                                 int64_t ld_in, int64_t ld_out,
+                                                 int64_t rows_left,
+                                                 int64_t cols_left, int wave,
+                                                 int lane) {
+  using E = typename T::E;
+  constexpr int S = (int)sizeof(E);
+  constexpr bool LSPLIT = !T::WIDE_WRITE;
+#pragma unroll
+  for (int it = 0; it < T::LIT; ++it) {
+    int p, ch;
+    lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
+    u32x4 v[T::K];
+#pragma unroll
+    for (int k = 0; k < T::K; ++k) {
+      const int row = p * T::K + k;
+      E e[T::V];
+#pragma unroll
+      for (int x = 0; x < T::V; ++x) {
+        const int col = ch * T::V + x;
+        e[x] = (row < rows_left && col < cols_left)
+                   ? *reinterpret_cast<const E *>(
+                         src + ((int64_t)row * ld_in + col) * S)
+                   : E(0);
+      }
+      __builtin_memcpy(&v[k], e, 16);
+    }
+    typename T::U u[T::V];
+    pack_units<S>(v, u);
+    write_units<T>(lds, p, ch * T::V, u);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < T::SIT; ++it) {
+    int c, q;
+    lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
+    const u32x4 o = read_column<T>(lds, c, q);
+    if (c < cols_left) {
+      E e[T::V];
+      __builtin_memcpy(e, &o, 16);
+#pragma unroll
+      for (int x = 0; x < T::V; ++x) {
+        const int row = q * T::V + x;
+        if (row < rows_left)
+          *reinterpret_cast<E *>(dst + ((int64_t)c * ld_out + row) * S) = e[x];
+      }
+    }
+  }
+}
+
+template <int S, int TR, int TC, int NT, int L>
+__global__ __launch_bounds__(NT) void xpose_tile_kernel(TileArgs a) {
+  using T = Tile<S, TR, TC, NT, L>;
+  __shared__ __attribute__((aligned(16))) typename T::U lds[T::LDS_UNITS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t g = blockIdx.x;
+  const uint32_t tc = g % a.tiles_c;
+  g /= a.tiles_c;
+  const uint32_t tr = g % a.tiles_r;
+  const int64_t b = (int64_t)(g / a.tiles_r) + a.batch_first;
+
+  const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
+  const char *src = static_cast<const char *>(a.in) +
+                    (b * a.stride_in + r0 * a.ld_in + c0) * S;
+  char *dst = static_cast<char *>(a.out) +
+              (b * a.stride_out + c0 * a.ld_out + r0) * S;
+  const int64_t rows_left = a.rows - r0, cols_left = a.cols - c0;
+
+  // Uniform per workgroup, so the barrier inside either path is reached by
+  // every wave of the block.
+  if (a.vec_ok && rows_left >= TR && cols_left >= TC)
+    tile_vector<T>(lds, src, dst, a.ld_in, a.ld_out, wave, lane);
+  else
+    tile_elementwise<T>(lds, src, dst, a.ld_in, a.ld_out, rows_left,
+                        cols_left, wave, lane);
+}
+
+template <int S, int TR, int TC, int NT, int L>
+hipError_t launch_tile(const TileArgs &a, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((xpose_tile_kernel<S, TR, TC, NT, L>), dim3(grid),
+                     dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+#define XPOSE_TILE(S, TR, TC, NT, L)                                        \
+  TileKernel {                                                              \
+    S, TR, TC, NT, L, Tile<S, TR, TC, NT, L>::LDS_BYTES,                   \
+        &launch_tile<S, TR, TC, NT, L>                                      \
+  }
+#define XPOSE_TILE3(S, TR, TC, NT)                                          \
+  XPOSE_TILE(S, TR, TC, NT, kSwizzle), XPOSE_TILE(S, TR, TC, NT, kPad1),    \
+      XPOSE_TILE(S, TR, TC, NT, kUnpadded)
+
+static const TileKernel kTileKernels[] = {
+    XPOSE_TILE3(4, 64, 64, 256),   XPOSE_TILE3(4, 32, 32, 256),
+    XPOSE_TILE3(4, 64, 128, 256),  XPOSE_TILE3(4, 128, 64, 256),
+    XPOSE_TILE3(4, 128, 128, 256), XPOSE_TILE3(2, 64, 64, 256),
+    XPOSE_TILE3(2, 128, 128, 256), XPOSE_TILE3(2, 64, 128, 256),
+    XPOSE_TILE3(2, 128, 64, 256),  XPOSE_TILE3(1, 128, 128, 256),
+    XPOSE_TILE3(1, 64, 64, 64),    XPOSE_TILE3(8, 32, 32, 256),
+    XPOSE_TILE3(8, 64, 64, 256),
+};
+
+const TileKernel *tile_kernels(int *count) {
+  *count = (int)(sizeof(kTileKernels) / sizeof(kTileKernels[0]));
+  return kTileKernels;
+}
+
+// ---------------------------------------------------------------------------
+// Copy yardstick: same bytes per workgroup as a 64 x 64 fp32 tile (16 KiB in,
+// 16 KiB out), 16 bytes per lane per access, all loads issued before stores.
+// ---------------------------------------------------------------------------
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy16_kernel(
+    u32x4 *__restrict__ dst, const u32x4 *__restrict__ src, int64_t nvec) {
+  const int64_t base =
+      (int64_t)blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+  u32x4 r[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kCopyThreads;
+    if (i < nvec) r[u] = src[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kCopyThreads;
+    if (i < nvec) dst[i] = r[u];
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_bytes_kernel(
+    char *__restrict__ dst, const char *__restrict__ src, int64_t n) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += step)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy(void *dst, const void *src, int64_t bytes,
+                       hipStream_t stream) {
+  char *d = static_cast<char *>(dst);
+  const char *s = static_cast<const char *>(src);
+  int64_t head = 0;
+  if ((((uintptr_t)d | (uintptr_t)s) & 15) == 0) {
+    const int64_t nvec = bytes / 16;
+    if (nvec > 0) {
+      const int64_t per_block = (int64_t)kCopyThreads * kCopyUnroll;
+      const int64_t blocks = (nvec + per_block - 1) / per_block;
+      if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(copy16_kernel, dim3((uint32_t)blocks),
+                         dim3(kCopyThreads), 0, stream,
+                         reinterpret_cast<u32x4 *>(d),
+                         reinterpret_cast<const u32x4 *>(s), nvec);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    head = nvec * 16;
+  }
+  const int64_t rest = bytes - head;
+  if (rest > 0) {
+    int64_t blocks = (rest + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(copy_bytes_kernel, dim3((uint32_t)blocks), dim3(256), 0,
+                       stream, d + head, s + head, rest);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// LDS bank microbenchmark.  One wavefront; lane l accesses byte offset
+// lane_bytes[l] + k * 2048 (k = 0..7) of a 32 KiB LDS buffer with one LDS
+// instruction per k.  2048 bytes is a multiple of any plausible bank period,
+// so all eight instructions see the same bank pattern.  The instructions are
+// written as inline assembly so the compiler can neither merge nor reorder
+// them; no wait is placed between them inside the loop, so the elapsed time
+// measures issue throughput, which an n-way conflict divides by n.
+// ---------------------------------------------------------------------------
+struct ProbeLanes {
+  int32_t b[64];
+};
+
+#define PROBE_RD8(OP, T)                                                   \
+  asm volatile(OP " %0, %8\n\t" OP " %1, %8 offset:2048\n\t" OP            \
+                  " %2, %8 offset:4096\n\t" OP " %3, %8 offset:6144\n\t" OP  \
+                  " %4, %8 offset:8192\n\t" OP " %5, %8 offset:10240\n\t" OP \
+                  " %6, %8 offset:12288\n\t" OP " %7, %8 offset:14336"       \
+               : "+v"(r0), "+v"(r1), "+v"(r2), "+v"(r3), "+v"(r4), "+v"(r5), \
+                 "+v"(r6), "+v"(r7)                                          \
+               : "v"(addr))
+#define PROBE_WR8(OP)                                                        \
+  asm volatile(OP " %0, %1\n\t" OP " %0, %1 offset:2048\n\t" OP              \
+                  " %0, %1 offset:4096\n\t" OP " %0, %1 offset:6144\n\t" OP  \
+                  " %0, %1 offset:8192\n\t" OP " %0, %1 offset:10240\n\t" OP \
+                  " %0, %1 offset:12288\n\t" OP " %0, %1 offset:14336"       \
+               :                                                             \
+               : "v"(addr), "v"(r0)                                          \
+               : "memory")
+
+template <int W, bool WRITE>
+__global__ __launch_bounds__(64) void lds_probe_kernel(ProbeLanes lanes,
+                                                       int iters,
+                                                       uint64_t *out) {
+  using R = typename std::conditional<
+      W == 4, uint32_t,
+      typename std::conditional<W == 8, u32x2, u32x4>::type>::type;
+  __shared__ __attribute__((aligned(16))) uint32_t buf[8192];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < 8192; i += 64) buf[i] = (uint32_t)i * 0x9E3779B1u;
+  __syncthreads();
+  // LDS byte address of this lane's target: the buffer's own LDS offset
+  // plus the lane's byte offset.
+  const uint32_t base = (uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) uint32_t *)buf);
+  const uint32_t addr = base + (uint32_t)lanes.b[lane];
+  R r0{}, r1{}, r2{}, r3{}, r4{}, r5{}, r6{}, r7{};
+  if constexpr (WRITE) r0 = R{} + (uint32_t)lane;
+  // Materialise the address (a kernel-argument load) before the clock starts.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : "v"(addr) : "memory");
+  const uint64_t t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (WRITE) {
+      if constexpr (W == 4) PROBE_WR8("ds_write_b32");
+      else if constexpr (W == 8) PROBE_WR8("ds_write_b64");
+      else PROBE_WR8("ds_write_b128");
+    } else {
+      if constexpr (W == 4) PROBE_RD8("ds_read_b32", R);
+      else if constexpr (W == 8) PROBE_RD8("ds_read_b64", R);
+      else PROBE_RD8("ds_read_b128", R);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint64_t t1 = clock64();
+  R acc = r0 ^ r1 ^ r2 ^ r3 ^ r4 ^ r5 ^ r6 ^ r7;
+  uint32_t sum;
+  if constexpr (W == 4) sum = acc;
+  else if constexpr (W == 8) sum = acc.x ^ acc.y;
+  else sum = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (lane == 0) out[0] = t1 - t0;
+  if (lane == 0) out[1] = sum;
+}
+
+hipError_t launch_lds_probe(uint64_t *out, const int32_t *lane_bytes,
+                            int width, bool is_write, int iters,
+                            hipStream_t stream) {
+  ProbeLanes lanes;
+  for (int i = 0; i < 64; ++i) lanes.b[i] = lane_bytes[i];
+#define PROBE_LAUNCH(W, WR)                                                 \
+  hipLaunchKernelGGL((lds_probe_kernel<W, WR>), dim3(1), dim3(64), 0, stream, \
+                     lanes, iters, out)
+  if (width == 4) {
+    if (is_write) PROBE_LAUNCH(4, true); else PROBE_LAUNCH(4, false);
+  } else if (width == 8) {
+    if (is_write) PROBE_LAUNCH(8, true); else PROBE_LAUNCH(8, false);
+  } else {
+    if (is_write) PROBE_LAUNCH(16, true); else PROBE_LAUNCH(16, false);
+  }
+#undef PROBE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace xpose

@@ -1,0 +1,153 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/xpose.h declares, and validates arguments on the host
+(bogus pointer values are fine here: invalid calls return before anything
+is launched, and xpose_plan never dereferences)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lds_tiled_matrix_amd as X
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xpose.h")
+
+IN = 0x7f0000000000       # pretend device addresses, 256-byte aligned
+OUT = 0x7f1000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xpose_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(X.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(X.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = X.strerror(code)
+        assert s and s != X.strerror(-99)
+    assert X.strerror(-99) == "unknown status code"
+
+
+def plan(out=OUT, inp=IN, batch=1, rows=64, cols=64, ld_in=None, ld_out=None,
+         stride_in=0, stride_out=0, dtype=X.XPOSE_F32, opts=None):
+    ld_in = cols if ld_in is None else ld_in
+    ld_out = rows if ld_out is None else ld_out
+    return X.xpose_plan(out, inp, batch, rows, cols, ld_in, ld_out, stride_in,
+                        stride_out, dtype, opts)
+
+
+def test_valid_plan_defaults():
+    rc, info = plan(rows=8192, cols=8192)
+    assert rc == X.XPOSE_OK
+    assert (info.tile_rows, info.tile_cols) == (64, 64)
+    assert info.layout == X.LAYOUT_SWIZZLE
+    assert info.vector_path == 1 and info.tiles == 128 * 128
+    assert info.launches == 1 and info.threads == 256
+    assert info.lds_bytes == 64 * 64 * 4
+
+
+def test_ragged_and_batched_tile_counts():
+    rc, info = plan(rows=12345, cols=6789)
+    assert rc == 0 and info.tiles == 193 * 107 and info.vector_path == 1
+    rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
+                    stride_out=1024 * 2048)
+    assert rc == 0 and info.tiles == 64 * 32 * 16
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), X.XPOSE_EINVAL),
+    (dict(cols=-5), X.XPOSE_EINVAL),
+    (dict(batch=-1), X.XPOSE_EINVAL),
+    (dict(ld_in=63), X.XPOSE_EINVAL),
+    (dict(ld_out=63), X.XPOSE_EINVAL),
+    (dict(inp=0), X.XPOSE_EINVAL),
+    (dict(out=0), X.XPOSE_EINVAL),
+    (dict(dtype=7), X.XPOSE_EDTYPE),
+    (dict(dtype=-1), X.XPOSE_EDTYPE),
+    (dict(inp=IN + 2), X.XPOSE_EALIGN),
+    (dict(out=OUT + 1, dtype=X.XPOSE_F16), X.XPOSE_EALIGN),
+    # output starts inside the input
+    (dict(out=IN + 64 * 4), X.XPOSE_EALIAS),
+    # input starts inside the output
+    (dict(inp=OUT + 4 * 63 * 64), X.XPOSE_EALIAS),
+    # batch outputs would overlap each other
+    (dict(batch=2, stride_in=4096, stride_out=100), X.XPOSE_EINVAL),
+    (dict(batch=2, stride_in=-1, stride_out=4096), X.XPOSE_EINVAL),
+    # extents that overflow int64
+    (dict(rows=1 << 40, cols=1 << 40), X.XPOSE_EINVAL),
+])
+def test_invalid_calls_rejected(kw, code):
+    rc, info = plan(**kw)
+    assert rc == code
+    assert info.tiles == 0
+
+
+def test_invalid_calls_rejected_by_entry_points_too():
+    # The real entry points validate first and return without launching.
+    assert X.xpose_2d(OUT, IN, 64, 64, 63, 64, X.XPOSE_F32, 0) == X.XPOSE_EINVAL
+    assert X.xpose_2d(IN, IN, 64, 64, 64, 64, X.XPOSE_F32, 0) == X.XPOSE_EALIAS
+    assert X.xpose_batched(OUT, IN, 2, 8, 8, 8, 8, 64, 1, 9, 0) == X.XPOSE_EDTYPE
+    assert X.xpose_copy(OUT, IN, -1, 0) == X.XPOSE_EINVAL
+    assert X.xpose_copy(IN + 8, IN, 64, 0) == X.XPOSE_EALIAS
+    assert X.xpose_copy(0, IN, 64, 0) == X.XPOSE_EINVAL
+    assert X.xpose_lds_probe(OUT, [0] * 64, 12, 0, 10) == X.XPOSE_EINVAL
+    assert X.xpose_lds_probe(OUT, [16384] * 64, 4, 0, 10) == X.XPOSE_EINVAL
+    assert X.xpose_lds_probe(OUT, [2] * 64, 4, 0, 10) == X.XPOSE_EINVAL
+    assert X.xpose_lds_probe(OUT, [0] * 64, 4, 0, 0) == X.XPOSE_EINVAL
+
+
+def test_zero_sizes_are_noops_even_with_null_pointers():
+    for b, r, c in ((0, 5, 5), (1, 0, 5), (1, 5, 0)):
+        assert X.xpose_batched(0, 0, b, r, c, 5, 5, 25, 25, X.XPOSE_F32, 0) == 0
+        rc, info = X.xpose_plan(0, 0, b, r, c, 5, 5, 25, 25, X.XPOSE_F32, None)
+        assert rc == 0 and info.tiles == 0
+    assert X.xpose_2d(0, 0, 0, 0, 0, 0, X.XPOSE_F16, 0) == 0
+    assert X.xpose_copy(0, 0, 0, 0) == 0
+
+
+def test_vector_path_rules():
+    # fp16 needs 4-byte aligned rows on both sides for 128-bit accesses.
+    assert plan(dtype=X.XPOSE_F16, rows=64, cols=64)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_F16, rows=64, cols=63, ld_in=63)[1].vector_path == 0
+    assert plan(dtype=X.XPOSE_F16, rows=63, cols=64, ld_out=63)[1].vector_path == 0
+    assert plan(dtype=X.XPOSE_F16, inp=IN + 2)[1].vector_path == 0
+    assert plan(dtype=X.XPOSE_U8, rows=128, cols=128)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_U8, rows=128, cols=130, ld_in=130)[1].vector_path == 0
+    # fp32 rows are always dword aligned: odd pitches keep the vector path.
+    assert plan(rows=12345, cols=6789)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_F64, rows=33, cols=31)[1].vector_path == 1
+    forced = X.XposeOpts(0, 0, 0, X.FLAG_ELEMENTWISE)
+    assert plan(opts=forced)[1].vector_path == 0
+
+
+def test_opts_select_layout_and_tile():
+    for layout in (X.LAYOUT_UNPADDED, X.LAYOUT_PAD1, X.LAYOUT_SWIZZLE):
+        rc, info = plan(opts=X.XposeOpts(layout, 32, 32, 0))
+        assert rc == 0 and info.layout == layout
+        assert (info.tile_rows, info.tile_cols) == (32, 32)
+    assert plan(opts=X.XposeOpts(X.LAYOUT_PAD1, 0, 0, 0))[1].lds_bytes == 64 * 65 * 4
+    assert plan(opts=X.XposeOpts(0, 48, 48, 0))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.XposeOpts(9, 0, 0, 0))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.XposeOpts(0, 0, 0, 8))[0] == X.XPOSE_EINVAL
+
+
+def test_large_batch_splits_launches():
+    # 2**31 workgroups is over the grid limit: the plan splits the batch.
+    rc, info = plan(batch=1 << 20, rows=4096, cols=4096,
+                    stride_in=4096 * 4096, stride_out=4096 * 4096,
+                    out=0x100000000000000, inp=0x10000)
+    assert rc == 0
+    assert info.tiles == (1 << 20) * 64 * 64
+    assert info.launches == -(-info.tiles // (0x7fffffff // (64 * 64) * 64 * 64))

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path, called through the C ABI, against the oracle,
+bit for bit.  Needs an MI355X and the built library."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from xpose_testlib import DTYPE_OF_SIZE, check_case, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+X = pytest.importorskip("lds_tiled_matrix_amd")
+
+SIZES = (4, 2, 1, 8)
+EDGE_DIMS = (1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129)
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda", 0)
+
+
+SIGNED = {1: np.int8, 2: np.int16, 4: np.int32, 8: np.int64}
+
+
+def _to_dev(a):
+    """Host array -> device tensor through a signed view of the same width
+    (torch's unsigned 16/32/64-bit support is limited)."""
+    if a.dtype.kind == "u" and a.dtype.itemsize > 1:
+        a = a.view(SIGNED[a.dtype.itemsize])
+    return torch.from_numpy(np.ascontiguousarray(a)).to(_dev())
+
+
+def _run_workload_tensor(w, host_in):
+    """Default launch (the one the benchmark times) on a workload's input."""
+    d_in = _to_dev(host_in)
+    out_shape = (w.cols, w.rows) if w.batch == 1 else (w.batch, w.cols, w.rows)
+    d_out = torch.empty(out_shape, dtype=d_in.dtype, device=_dev())
+    code = DTYPE_OF_SIZE[w.elem_bytes]
+    if w.batch == 1:
+        rc = X.xpose_2d(d_out.data_ptr(), d_in.data_ptr(), w.rows, w.cols,
+                        w.cols, w.rows, code, 0)
+    else:
+        rc = X.xpose_batched(d_out.data_ptr(), d_in.data_ptr(), w.batch,
+                             w.rows, w.cols, w.cols, w.rows, w.rows * w.cols,
+                             w.cols * w.rows, code, 0)
+    assert rc == 0, X.strerror(rc)
+    torch.cuda.synchronize()
+    return d_out.cpu().numpy()
+
+
+def _as_raw(a, s):
+    return a.view(wl.RAW_UINT[s])
+
+
+@pytest.mark.parametrize("key", sorted(wl.WORKLOADS))
+def test_workload_full_size_bit_exact(key):
+    """Each workload at its full size, every element, against the oracle."""
+    w = wl.WORKLOADS[key]
+    s = w.elem_bytes
+    say(f"workload {key}")
+    host = wl.make_input(w)
+    got = _run_workload_tensor(w, host)
+    want = oracle.transpose(host)
+    assert got.shape == want.shape
+    assert np.array_equal(_as_raw(got, s), _as_raw(want, s))
+    if w.recipe == "index":
+        # out[r][c] == float(c * cols + r) exactly
+        r = np.arange(w.cols)[:, None]
+        c = np.arange(w.rows)[None, :]
+        assert np.array_equal(got, (c * w.cols + r).astype(np.float32))
+
+
+@pytest.mark.parametrize("key", sorted(wl.WORKLOADS))
+def test_workload_coordinate_planes(key):
+    """Raw-bit coordinate planes at each workload's shape: with in = row
+    index the output must hold its column index, and vice versa.  Both
+    planes together fix every element's destination."""
+    w = wl.WORKLOADS[key]
+    s = w.elem_bytes
+    shape = w.in_shape
+    for axis, want_axis in ((-2, -1), (-1, -2)):
+        say(f"workload {key} plane axis={axis}")
+        plane = wl.index_plane(shape, axis, s)
+        got = _as_raw(_run_workload_tensor(w, plane), s)
+        out_shape = got.shape
+        want = wl.index_plane(out_shape, want_axis, s)
+        assert np.array_equal(got, want)
+        del plane, got, want
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_edge_sweep(s):
+    """Every shape in {1,2,3,31,32,33,63,64,65,127,128,129}^2: tiles that are
+    full, one short, one over, single rows and columns."""
+    for r in EDGE_DIMS:
+        for c in EDGE_DIMS:
+            check_case(s, 1, r, c, seed=r * 1000 + c, label="edge")
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_primes_and_multi_tile_ragged(s):
+    for r, c in ((257, 509), (1021, 131), (131, 1021), (997, 1009)):
+        check_case(s, 1, r, c, seed=r + c, label="prime")
+
+
+def _tiles_for(s):
+    out = set()
+    for tr, tc in ((32, 32), (64, 64), (64, 128), (128, 64), (128, 128)):
+        rc, _ = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8, 8, 0, 0,
+                             DTYPE_OF_SIZE[s], X.XposeOpts(1, tr, tc, 0))
+        if rc == 0:
+            out.add((tr, tc))
+    return sorted(out)
+
+
+@pytest.mark.parametrize("s", SIZES)
+@pytest.mark.parametrize("layout", (X.LAYOUT_UNPADDED, X.LAYOUT_PAD1,
+                                    X.LAYOUT_SWIZZLE))
+def test_every_built_kernel(s, layout):
+    """Every compiled (element size, tile, layout) kernel on a ragged
+    multi-tile shape, on the vector path and forced element-wise."""
+    for tr, tc in _tiles_for(s):
+        for flags in (0, X.FLAG_ELEMENTWISE):
+            opts = X.XposeOpts(layout, tr, tc, flags)
+            check_case(s, 1, 3 * tr + 5, 2 * tc + 3, seed=tr * tc + flags,
+                       opts=opts, label=f"kernel {tr}x{tc} L{layout} f{flags}")
+            check_case(s, 1, 2 * tr, 3 * tc, seed=tr + tc + flags, opts=opts,
+                       label=f"kernel-full {tr}x{tc} L{layout} f{flags}")
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_pitches_and_padding_untouched(s):
+    """ld_in > cols and ld_out > rows: padding of the output keeps its
+    sentinel, guard bands before and after the output stay intact."""
+    for r, c, ldi, ldo in ((100, 70, 77, 108), (64, 64, 72, 68),
+                           (129, 255, 256, 136), (33, 65, 65, 33)):
+        check_case(s, 1, r, c, ld_in=ldi, ld_out=ldo, seed=r * c, label="ld")
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_unaligned_pointers(s):
+    """Base pointers shifted by one element: 2- and 1-byte types lose the
+    128-bit path, 4-byte types keep it at dword alignment."""
+    for shift_in, shift_out in ((1, 0), (0, 1), (3, 5)):
+        check_case(s, 1, 150, 90, seed=shift_in * 7 + shift_out,
+                   in_shift=shift_in, out_shift=shift_out, label="shift")
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_batched_strides(s):
+    # minimal strides, gaps between matrices, and a broadcast input
+    check_case(s, 5, 70, 45, seed=1, label="batch-min")
+    check_case(s, 4, 70, 45, ld_in=50, ld_out=80, stride_in=70 * 50 + 13,
+               stride_out=45 * 80 + 29, seed=2, label="batch-gaps")
+    check_case(s, 3, 40, 66, stride_in=0, seed=3, label="batch-broadcast")
+
+
+def test_2d_entry_matches():
+    check_case(4, 1, 300, 200, seed=5, entry="2d", label="2d")
+    check_case(2, 1, 300, 200, seed=6, entry="2d", label="2d")
+
+
+@pytest.mark.parametrize("s", (2, 4))
+def test_special_float_bits(s):
+    """NaN payloads, infinities, -0, subnormals move unchanged."""
+    special = wl.special_f16_bits() if s == 2 else wl.special_f32_bits()
+    src = np.resize(special, 96 * 80).astype(wl.RAW_UINT[s])
+    check_case(s, 1, 96, 80, src=src, label="special")
+
+
+def test_double_transpose_is_identity():
+    for s in SIZES:
+        a = wl.random_bits((777, 333), s, seed=s)
+        t = _to_dev(a)
+        say(f"double transpose s={s}")
+        back = X.transpose(X.transpose(t))
+        torch.cuda.synchronize()
+        assert np.array_equal(back.cpu().numpy().view(a.dtype), a)
+
+
+def test_repeated_index_check_no_races():
+    """The exact index check many times over: a read of the tile before the
+    barrier would show up as a misplaced index ("Shared memory and the bank
+    conflict", section "The barrier")."""
+    w = wl.WORKLOADS["c1_index_1024_f32"]
+    a = torch.from_numpy(wl.make_input(w)).to(_dev())
+    want = torch.from_numpy(oracle.transpose(wl.make_input(w))).to(_dev())
+    out = torch.empty_like(a)
+    for layout in (X.LAYOUT_SWIZZLE, X.LAYOUT_PAD1, X.LAYOUT_UNPADDED):
+        say(f"repeat index layout={layout}")
+        for _ in range(100):
+            out.fill_(-1.0)
+            X.transpose(a, out, layout=layout)
+            assert torch.equal(out.view(torch.int32), want.view(torch.int32))
+
+
+def test_torch_views_and_streams():
+    x = _to_dev(wl.random_bits((300, 500), 4, 11))
+    view = x[10:250, 20:470]             # ld_in = 500
+    out = torch.empty((600, 400), dtype=x.dtype, device=_dev())
+    dst = out[:450, :240]                # ld_out = 400
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        X.transpose(view, dst, stream=s)
+    s.synchronize()
+    want = oracle.transpose(view.cpu().numpy())
+    assert np.array_equal(dst.cpu().numpy(), want)
+
+
+def test_copy_kernel():
+    for nbytes, src_off, dst_off in ((1 << 20, 0, 0), (12345, 0, 0),
+                                     (100003, 3, 1), (16, 0, 0), (1, 0, 0)):
+        say(f"copy {nbytes} {src_off} {dst_off}")
+        host = wl.random_bits((nbytes + 64,), 1, nbytes)
+        src = torch.from_numpy(host).to(_dev())
+        dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device=_dev())
+        rc = X.xpose_copy(dst.data_ptr() + dst_off, src.data_ptr() + src_off,
+                          nbytes, 0)
+        assert rc == 0
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy()
+        assert np.array_equal(got[dst_off:dst_off + nbytes],
+                              host[src_off:src_off + nbytes])
+        assert not got[:dst_off].any() and not got[dst_off + nbytes:].any()
