@@ -12,9 +12,10 @@ stderr.
 
 Timing protocol ("Shared memory and the bank conflict", section "What to
 record": median of repeated runs after a warm-up, the copy measured the same
-way): W untimed launches, then K launches bracketed by device
-synchronisation (the wall-clock value) with an event pair around each
-launch (median / min / p90 / mean per launch).
+way): W untimed launches, then K launches back to back bracketed by device
+synchronisation (the wall-clock `value`), then K launches each between an
+event pair on the launch stream (median / min / p90 / mean per launch).
+A cold mode reads 1 GiB between launches to empty every cache first.
 """
 from __future__ import annotations
 
@@ -72,21 +73,26 @@ def read_traffic():
 
 
 def time_launches(launch, stream, steps, warmup):
-    """W untimed launches, then K timed ones.  Returns (wall_s, per-launch
-    event durations in seconds)."""
+    """W untimed launches; then K launches back to back bracketed by device
+    synchronisation (the wall-clock time, nothing else in the loop); then K
+    more launches each between an event pair on the launch stream (the
+    per-launch durations).  Returns (wall_s, durations_s)."""
     import torch
     for _ in range(warmup):
         launch()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        launch()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for k in range(steps):
         starts[k].record(stream)
         launch()
         ends[k].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
     return wall, durs
 
@@ -141,10 +147,37 @@ def host_cpu_name() -> str:
     return "unknown"
 
 
-def bench_workload(X, w, steps, warmup, stream, layouts=True):
+# Copy kernels measured for the yardstick: (threads, 16-byte vectors per
+# lane, cache policy).  The fastest one is the practical roofline.
+COPY_VARIANTS = ((256, 1, 2), (512, 1, 2), (256, 2, 2), (1024, 1, 2),
+                 (256, 4, 2), (256, 4, 1))
+FLUSH_BYTES = 1 << 30   # > the 256 MB Infinity Cache
+
+
+def time_cold(launch, stream, reps, flush):
+    """Per-launch event times with the caches flushed before every launch:
+    1 GiB is READ between launches, outside the events, so every cache holds
+    clean lines of another buffer (a written flush would leave dirty lines
+    whose write-back the timed kernel would pay for)."""
+    import torch
+    durs = []
+    flat = flush.view(torch.int64)
+    for k in range(reps):
+        flat.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b.record(stream)
+        b.synchronize()
+        durs.append(a.elapsed_time(b) * 1e-3)
+    return durs
+
+
+def bench_workload(X, w, steps, warmup, stream, layouts=True, cold=True):
     """Time the default launch (and each layout) on one workload plus the
-    copy yardstick over the same bytes.  Returns a dict and the device
-    tensors (input, output) so the caller can check parity."""
+    copy yardstick over the same bytes.  Returns a dict, the host input and
+    the device output of the default launch."""
     import torch
     dev = torch.device("cuda", 0)
     host = wl.make_input(w)
@@ -167,28 +200,49 @@ def bench_workload(X, w, steps, warmup, stream, layouts=True):
                 raise RuntimeError(X.strerror(rc))
         return go
 
-    # Copy yardstick: same byte count, same buffers (input -> output).
-    def copy_go():
-        rc = X.xpose_copy(y.data_ptr(), x.data_ptr(), nbytes // 2, sh)
-        if rc:
-            raise RuntimeError(X.strerror(rc))
+    def copy_with(opts):
+        # Same byte count, same buffers (input -> output).
+        def go():
+            rc = X.xpose_copy_ex(y.data_ptr(), x.data_ptr(), nbytes // 2, opts,
+                                 sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+        return go
 
     res = {}
+    n_small = max(10, min(steps, 50))
     with torch.cuda.stream(stream):
-        wall_c, durs_c = time_launches(copy_go, stream, steps, warmup)
-        res["copy"] = summarize(durs_c, nbytes)
-        res["copy"]["wall_GBps"] = round(steps * nbytes / wall_c / 1e9, 1)
-        # hipMemcpyAsync device-to-device, for context.
+        copies = {}
+        for thr, unroll, cache in COPY_VARIANTS:
+            o = X.XposeCopyOpts(thr, unroll, cache, 0)
+            _, d = time_launches(copy_with(o), stream, n_small, warmup)
+            copies[f"{thr}x{unroll} {X.CACHE_NAMES[cache]}"] = summarize(d, nbytes)
+        best = max(copies, key=lambda k: copies[k]["median_GBps"])
+        res["copy_variants_GBps"] = {k: v["median_GBps"] for k, v in copies.items()}
+        res["copy"] = dict(copies[best], kernel=best)
+        best_opts = X.XposeCopyOpts(*[int(t) for t in best.split()[0].split("x")],
+                                    X.CACHE_NT_STORE if "nt_store" in best
+                                    else X.CACHE_DEFAULT, 0)
         yb, xb = y.view(-1), x.view(-1)
-        wall_m, durs_m = time_launches(lambda: yb.copy_(xb), stream,
-                                       steps, warmup)
+        _, durs_m = time_launches(lambda: yb.copy_(xb), stream, n_small, warmup)
         res["memcpy_d2d"] = summarize(durs_m, nbytes)
         if layouts:
             res["ablation"] = {}
             for lay, name in X.LAYOUT_NAMES.items():
                 _, d = time_launches(launch_with(X.XposeOpts(lay, 0, 0, 0)),
-                                     stream, steps, warmup)
+                                     stream, n_small, warmup)
                 res["ablation"][name] = summarize(d, nbytes)
+        if cold:
+            flush = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+            reps = max(5, min(steps, 20))
+            res["cold"] = {
+                "transpose": summarize(time_cold(launch_with(None), stream,
+                                                 reps, flush), nbytes),
+                "copy": summarize(time_cold(copy_with(best_opts), stream,
+                                            reps, flush), nbytes),
+                "note": "1 GiB read between launches, outside the timing",
+            }
+            del flush
         # The default launch last, so its output stays in y.
         wall, durs = time_launches(launch_with(None), stream, steps, warmup)
     torch.cuda.synchronize()
@@ -207,6 +261,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle CPU baseline and the parity check")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache (flushed) timing")
     ap.add_argument("--table", action="store_true",
                     help="also measure every workload; markdown table to stderr")
     args = ap.parse_args(argv)
@@ -229,13 +285,14 @@ def main(argv=None):
     stream = torch.cuda.Stream()
     log(f"bench: {w.description}; steps={args.steps} warmup={args.warmup}")
     res, host, y = bench_workload(X, w, args.steps, args.warmup, stream,
-                                  layouts=not args.no_ablation)
+                                  layouts=not args.no_ablation,
+                                  cold=not args.no_cold)
     nbytes = w.rw_bytes
     wall = res["wall_s"]
     value = args.steps * nbytes / wall / 1e9
     d = res["default"]
     achieved = nbytes / (d["mean_us"] * 1e-6) / 1e9
-    copy_gbps = res["copy"]["mean_GBps"]
+    copy_gbps = res["copy"]["median_GBps"]
 
     cpu = None
     parity = None
@@ -269,12 +326,17 @@ def main(argv=None):
             "layout": X.LAYOUT_NAMES[plan["layout"]],
             "tile": f"{plan['tile_rows']}x{plan['tile_cols']}",
             "threads": plan["threads"], "workgroups": plan["tiles"],
+            "cache": X.CACHE_NAMES[plan["cache"]],
+            "tile_order": f"super-tiles {plan['group_rows']}x{plan['group_cols']}"
+                          f"{', per-XCD ranges' if plan['xcd_remap'] else ''}",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "frac_of_copy": round(achieved / copy_gbps, 4),
+        "frac_of_copy": round(d["median_GBps"] / copy_gbps, 4),
         "timing": d,
         "copy": res["copy"],
+        "copy_variants_GBps": res["copy_variants_GBps"],
         "memcpy_d2d": res["memcpy_d2d"],
+        "cold": res.get("cold"),
         "ablation": res.get("ablation"),
         "roofline": {
             "bound": "hbm",
@@ -296,19 +358,24 @@ def main(argv=None):
             log(f"bench: table {key}")
             r, _, _ = bench_workload(X, wk, min(args.steps, 100),
                                      min(args.warmup, 10), stream,
-                                     layouts=True)
+                                     layouts=True, cold=True)
             dd = r["default"]
-            rows.append((key, wk.rw_bytes, dd, r["copy"], r["ablation"]))
+            rows.append((key, wk.rw_bytes, dd, r["copy"], r["ablation"],
+                         r["cold"], r["plan"]))
             del r
             torch.cuda.empty_cache()
-        log("| workload | R+W bytes | median us | GB/s (median) | % 8 TB/s | "
-            "copy GB/s | % copy | unpadded GB/s | pad1 GB/s | swizzle GB/s |")
-        log("|---|---|---|---|---|---|---|---|---|---|")
-        for key, b, dd, cp, ab in rows:
+        log("| workload | kernel | R+W bytes | median us | GB/s | % 8 TB/s | "
+            "copy GB/s | % copy | cold GB/s | cold copy GB/s | unpadded | "
+            "pad1 | swizzle |")
+        log("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+        for key, b, dd, cp, ab, cd, pl in rows:
             g = dd["median_GBps"]
-            log(f"| {key} | {b:,} | {dd['median_us']} | {g} | "
+            kern = (f"{pl['tile_rows']}x{pl['tile_cols']} "
+                    f"{X.CACHE_NAMES[pl['cache']]}")
+            log(f"| {key} | {kern} | {b:,} | {dd['median_us']} | {g} | "
                 f"{100 * g / HBM_PEAK_GBS:.1f} | {cp['median_GBps']} | "
                 f"{100 * g / cp['median_GBps']:.1f} | "
+                f"{cd['transpose']['median_GBps']} | {cd['copy']['median_GBps']} | "
                 f"{ab['unpadded']['median_GBps']} | {ab['pad1']['median_GBps']} | "
                 f"{ab['swizzle']['median_GBps']} |")
     return 0 if parity is not False else 3

@@ -80,17 +80,37 @@ typedef enum xpose_layout {
   XPOSE_LAYOUT_SWIZZLE = 3   /* 16-byte chunks XOR-permuted per row            */
 } xpose_layout;
 
+/* Cache policy of the global accesses.  The data is touched exactly once,
+ * so marking it non-temporal can keep it from displacing other lines. */
+typedef enum xpose_cache {
+  XPOSE_CACHE_AUTO = 0,       /* library default                            */
+  XPOSE_CACHE_DEFAULT = 1,    /* plain loads and stores                     */
+  XPOSE_CACHE_NT_STORE = 2,   /* non-temporal stores                        */
+  XPOSE_CACHE_NT_ALL = 3      /* non-temporal loads and stores              */
+} xpose_cache;
+
 /* Option flags for xpose_batched_ex. */
 enum {
-  XPOSE_FLAG_ELEMENTWISE = 1 /* force the element-wise edge path everywhere */
+  XPOSE_FLAG_ELEMENTWISE = 1, /* force the element-wise edge path everywhere */
+  XPOSE_FLAG_XCD_REMAP = 2,   /* give each XCD one contiguous range of tiles */
+  XPOSE_FLAG_NO_XCD_REMAP = 4 /* the opposite, overriding the default        */
 };
 
-/* Optional knobs for the measured ablation.  Zero-initialise for defaults. */
+/* Optional knobs for the measured ablation.  Zero-initialise for defaults.
+ * Every choice gives bit-identical results. */
 typedef struct xpose_opts {
-  int32_t layout;    /* xpose_layout                                         */
-  int32_t tile_rows; /* 0 = default; else one of the built tile shapes       */
-  int32_t tile_cols; /* 0 = default                                          */
-  int32_t flags;     /* XPOSE_FLAG_*                                         */
+  int32_t layout;     /* xpose_layout                                        */
+  int32_t tile_rows;  /* 0 = default; else one of the built tile shapes      */
+  int32_t tile_cols;  /* 0 = default                                         */
+  int32_t flags;      /* XPOSE_FLAG_*                                        */
+  int32_t cache;      /* xpose_cache                                         */
+  int32_t group_rows; /* tile order: workgroups walk super-tiles of
+                         group_rows x group_cols tiles, super-tiles
+                         row-major, tile rows fastest inside one;
+                         0 = default                                         */
+  int32_t group_cols; /* 0 = default                                         */
+  int32_t threads;    /* workgroup size of the tile kernel; 0 = the default
+                         (with an explicit tile: the largest one built)     */
 } xpose_opts;
 
 /* What xpose_plan reports about the kernel a call would launch. */
@@ -104,8 +124,19 @@ typedef struct xpose_plan_info {
                           0: every tile takes the element-wise path          */
   int64_t tiles;       /* workgroups over the whole batch                    */
   int32_t launches;    /* kernel launches the call will enqueue              */
-  int32_t reserved;
+  int32_t cache;       /* resolved xpose_cache                               */
+  int32_t group_rows;  /* resolved super-tile height in tiles                 */
+  int32_t group_cols;  /* resolved super-tile width in tiles                  */
+  int32_t xcd_remap;   /* 1 if tiles are remapped per XCD                    */
 } xpose_plan_info;
+
+/* Knobs of the copy yardstick (zero-initialise for defaults). */
+typedef struct xpose_copy_opts {
+  int32_t threads; /* workgroup size; 0 = default                           */
+  int32_t unroll;  /* 16-byte vectors per lane; 0 = default                 */
+  int32_t cache;   /* xpose_cache                                           */
+  int32_t reserved;
+} xpose_copy_opts;
 
 /* 2-D transpose of one rows x cols matrix: the definition above with
  * batch = 1.  ld_in >= cols, ld_out >= rows.  dtype is an xpose_dtype. */
@@ -144,6 +175,12 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
  * the tile around on chip" and "What to record").  Same pointer, stream and
  * error rules as the transposes; the ranges must not overlap. */
 int xpose_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+/* xpose_copy with an explicit copy kernel (opts may be NULL): the copy
+ * variants are measured so the yardstick is the fastest copy built.
+ * Returns XPOSE_ENOTILE if no kernel matches the requested knobs. */
+int xpose_copy_ex(void *dst, const void *src, int64_t bytes,
+                  const xpose_copy_opts *opts, void *stream);
 
 /* LDS bank microbenchmark: one 64-lane wavefront repeatedly issues one LDS
  * instruction in which lane l accesses byte address lane_bytes[l] (host

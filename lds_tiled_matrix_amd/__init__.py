@@ -2,9 +2,9 @@
 
 Every function here marshals arguments and calls the C ABI declared in
 ``include/xpose.h``; the transpose itself runs only in the library's gfx950
-kernels.  The library must have been built (``python -m
-lds_tiled_matrix_amd.build``); importing this package without it raises
-ImportError rather than falling back to anything else.
+kernels.  The library must have been built (``python lds_tiled_matrix_amd/build.py``);
+importing this package without it raises ImportError rather than falling
+back to anything else.
 
 Low-level names mirror the C ABI (``xpose_2d``, ``xpose_batched``,
 ``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``)
@@ -27,17 +27,27 @@ XPOSE_EHIP, XPOSE_EALIGN, XPOSE_ENOTILE = -4, -5, -6
 LAYOUT_AUTO, LAYOUT_UNPADDED, LAYOUT_PAD1, LAYOUT_SWIZZLE = 0, 1, 2, 3
 LAYOUT_NAMES = {LAYOUT_UNPADDED: "unpadded", LAYOUT_PAD1: "pad1",
                 LAYOUT_SWIZZLE: "swizzle"}
-FLAG_ELEMENTWISE = 1
+FLAG_ELEMENTWISE, FLAG_XCD_REMAP, FLAG_NO_XCD_REMAP = 1, 2, 4
+CACHE_AUTO, CACHE_DEFAULT, CACHE_NT_STORE, CACHE_NT_ALL = 0, 1, 2, 3
+CACHE_NAMES = {CACHE_DEFAULT: "default", CACHE_NT_STORE: "nt_store",
+               CACHE_NT_ALL: "nt_all"}
 
 # Every exported entry point, in header order.
 EXPORTS = ("xpose_2d", "xpose_batched", "xpose_batched_ex", "xpose_plan",
-           "xpose_copy", "xpose_lds_probe", "xpose_last_hip_error",
-           "xpose_strerror")
+           "xpose_copy", "xpose_copy_ex", "xpose_lds_probe",
+           "xpose_last_hip_error", "xpose_strerror")
 
 
 class XposeOpts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
-                ("tile_cols", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("tile_cols", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
+                ("group_cols", ctypes.c_int32), ("threads", ctypes.c_int32)]
+
+
+class XposeCopyOpts(ctypes.Structure):
+    _fields_ = [("threads", ctypes.c_int32), ("unroll", ctypes.c_int32),
+                ("cache", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class XposePlanInfo(ctypes.Structure):
@@ -45,16 +55,27 @@ class XposePlanInfo(ctypes.Structure):
                 ("tile_cols", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("vector_path", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
+                ("group_cols", ctypes.c_int32), ("xcd_remap", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 def _load() -> ctypes.CDLL:
+    # libxpose.so needs libamdhip64.so.7.  PyTorch's ROCm wheel ships its own
+    # HIP and HSA runtimes under that same soname; if libxpose.so were loaded
+    # first, the process would end up with two HIP runtimes (ROCm's and
+    # torch's), each with its own device context, and launches on torch
+    # memory fail or crash.  Importing torch first makes the dynamic loader
+    # resolve libamdhip64.so.7 to the runtime torch already loaded.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m lds_tiled_matrix_amd.build`")
+            f"{LIB_PATH} is not built; run `python lds_tiled_matrix_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     opts_p, info_p = ctypes.POINTER(XposeOpts), ctypes.POINTER(XposePlanInfo)
@@ -66,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "xpose_plan": [p, p, i64, i64, i64, i64, i64, i64, i64, i32, opts_p,
                        info_p],
         "xpose_copy": [p, p, i64, p],
+        "xpose_copy_ex": [p, p, i64, ctypes.POINTER(XposeCopyOpts), p],
         "xpose_lds_probe": [p, ctypes.POINTER(i32), i32, i32, i32, p],
         "xpose_last_hip_error": [],
         "xpose_strerror": [ctypes.c_int],
@@ -95,9 +117,11 @@ def _check(code: int, what: str) -> int:
     return code
 
 
-def _opts(layout=LAYOUT_AUTO, tile=None, flags=0):
+def make_opts(layout=LAYOUT_AUTO, tile=None, flags=0, cache=CACHE_AUTO,
+              group_rows=0, group_cols=0, threads=0) -> XposeOpts:
     tr, tc = tile if tile else (0, 0)
-    return XposeOpts(layout, tr, tc, flags)
+    return XposeOpts(layout, tr, tc, flags, cache, group_rows, group_cols,
+                     threads)
 
 
 # ----- C ABI, one to one -----------------------------------------------------
@@ -139,6 +163,12 @@ def xpose_copy(dst: int, src: int, nbytes: int, stream: int = 0) -> int:
     return _lib.xpose_copy(dst, src, nbytes, stream)
 
 
+def xpose_copy_ex(dst: int, src: int, nbytes: int,
+                  opts: XposeCopyOpts | None = None, stream: int = 0) -> int:
+    return _lib.xpose_copy_ex(dst, src, nbytes,
+                              ctypes.byref(opts) if opts else None, stream)
+
+
 def xpose_lds_probe(cycles_out: int, lane_bytes, width: int, is_write: int,
                     iters: int, stream: int = 0) -> int:
     arr = (ctypes.c_int32 * 64)(*[int(x) for x in lane_bytes])
@@ -177,7 +207,8 @@ def _stream_handle(stream) -> int:
 
 
 def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
-              flags: int = 0, stream=None):
+              flags: int = 0, cache: int = CACHE_AUTO, group_rows: int = 0,
+              stream=None):
     """Transpose the last two dims of a 2-D or 3-D CUDA tensor whose last dim
     is contiguous.  Row pitches and the batch stride are taken from the
     tensor's strides.  Returns ``out`` (allocated contiguous if None)."""
@@ -200,7 +231,8 @@ def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
     stride_in = x.stride(0) if x.dim() == 3 else 0
     stride_out = out.stride(0) if out.dim() == 3 else 0
     code = dtype_code(x.dtype)
-    opts = _opts(layout, tile, flags) if (layout or tile or flags) else None
+    opts = (make_opts(layout, tile, flags, cache, group_rows)
+            if (layout or tile or flags or cache or group_rows) else None)
     _check(xpose_batched_ex(out.data_ptr(), x.data_ptr(), batch, rows, cols,
                             ld_in, ld_out, stride_in, stride_out, code, opts,
                             _stream_handle(stream)), "xpose_batched_ex")
@@ -219,7 +251,8 @@ def copy(dst, src, stream=None):
 
 
 def plan_for(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
-             flags: int = 0) -> dict:
+             flags: int = 0, cache: int = CACHE_AUTO,
+             group_rows: int = 0) -> dict:
     """The kernel ``transpose`` would launch for these tensors (host only)."""
     batch = x.shape[0] if x.dim() == 3 else 1
     rows, cols = x.shape[-2], x.shape[-1]
@@ -231,7 +264,8 @@ def plan_for(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
         out_ptr = out.data_ptr()
         ld_out = out.stride(-2) if cols > 1 else rows
         stride_out = out.stride(0) if out.dim() == 3 else 0
-    opts = _opts(layout, tile, flags) if (layout or tile or flags) else None
+    opts = (make_opts(layout, tile, flags, cache, group_rows)
+            if (layout or tile or flags or cache or group_rows) else None)
     rc, info = xpose_plan(out_ptr, x.data_ptr(), batch, rows, cols, ld_in,
                           ld_out, stride_in, stride_out, dtype_code(x.dtype),
                           opts)

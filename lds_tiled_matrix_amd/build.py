@@ -1,9 +1,10 @@
 """Build libxpose.so for gfx950 in-tree.
 
-    python -m lds_tiled_matrix_amd.build
+    python lds_tiled_matrix_amd/build.py
 
 hipcc cross-compiles without a GPU.  The library is written next to this
-file so it travels with the source tree.
+file so it travels with the source tree.  Run as a script (not with -m):
+importing the package loads the library, which may be stale or missing.
 """
 from __future__ import annotations
 

@@ -31,20 +31,46 @@ int elem_bytes_of(int32_t dtype) {
   }
 }
 
-// Default tile shape and layout per element size.  The layout default is the
-// one that measured conflict-free and fastest; the tile shape the fastest in
-// the shape sweep (both recorded with the measurements).
+// Default launch configuration, chosen from the measured sweep over tile
+// shape, workgroup size, cache policy and tile order on MI355X.
+//   row16: every row start on both sides is 16-byte aligned (pointers,
+//     pitches, batch strides).  Otherwise 16-byte accesses straddle cache
+//     lines; plain (write-back) stores then merge the partial lines in L2 and
+//     win over non-temporal ones.
+//   small: a batch of matrices of at most kSmallMatrixBytes each.  Resident
+//     workgroups then cover a few whole matrices, a dense window on both the
+//     input and the output side, and a taller tile with small super-tiles
+//     streams at copy speed.
+// cache is an xpose_cache value; group_cols 0 means all tile columns.
 struct Default {
-  int tile_rows, tile_cols, layout;
+  int tile_rows, tile_cols, threads, layout, cache, group_rows, group_cols,
+      xcd_remap;
 };
-Default default_for(int s) {
+constexpr int64_t kSmallMatrixBytes = 64ll << 20;
+
+Default default_for(int s, bool row16, bool small) {
+  if (!row16) {
+    switch (s) {
+      case 4: return {128, 64, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 32, 32, 1};
+      case 2: return {64, 64, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 16, 16, 1};
+      case 1: return {128, 128, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 16, 16, 1};
+      default: return {32, 32, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 16, 16, 1};
+    }
+  }
   switch (s) {
-    case 4: return {64, 64, xpose::kSwizzle};
-    case 2: return {64, 64, xpose::kSwizzle};
-    case 1: return {128, 128, xpose::kSwizzle};
-    default: return {32, 32, xpose::kSwizzle};
+    case 4:
+      if (small) return {128, 64, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 8, 8, 0};
+      return {32, 32, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 8, 32, 1};
+    case 2: return {128, 64, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 32, 8, 0};
+    case 1: return {128, 128, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 16, 16, 1};
+    default: return {32, 32, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 8, 32, 1};
   }
 }
+
+// The copy yardstick: one 16-byte vector per lane, non-temporal stores (the
+// fastest copy measured at every size from 512 MiB to 2 GiB).
+constexpr int kDefaultCopyThreads = 256, kDefaultCopyUnroll = 1;
+constexpr int kDefaultCopyCache = XPOSE_CACHE_NT_STORE;
 
 bool mul_ok(int64_t a, int64_t b, int64_t *r) {
   return !__builtin_mul_overflow(a, b, r);
@@ -82,9 +108,16 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const int s = elem_bytes_of(dtype);
   if (s == 0) return XPOSE_EDTYPE;
   if (batch < 0 || rows < 0 || cols < 0) return XPOSE_EINVAL;
+  const int known_flags =
+      XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP | XPOSE_FLAG_NO_XCD_REMAP;
   if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
                opts->layout > XPOSE_LAYOUT_SWIZZLE ||
-               (opts->flags & ~XPOSE_FLAG_ELEMENTWISE) != 0 ||
+               (opts->flags & ~known_flags) != 0 ||
+               ((opts->flags & XPOSE_FLAG_XCD_REMAP) &&
+                (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) ||
+               opts->cache < XPOSE_CACHE_AUTO ||
+               opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
+               opts->group_cols < 0 || opts->threads < 0 ||
                opts->tile_rows < 0 || opts->tile_cols < 0))
     return XPOSE_EINVAL;
   if (batch == 0 || rows == 0 || cols == 0) {
@@ -118,19 +151,28 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     return XPOSE_EALIAS;
 
   // Kernel choice.
-  Default d = default_for(s);
+  const bool row16 =
+      ((pi | po) % 16 == 0) && (ld_in * s) % 16 == 0 && (ld_out * s) % 16 == 0 &&
+      (batch == 1 || ((stride_in * s) % 16 == 0 && (stride_out * s) % 16 == 0));
+  const bool small = batch > 1 && rows * cols * s <= kSmallMatrixBytes;
+  Default d = default_for(s, row16, small);
   int layout = (opts && opts->layout) ? opts->layout : d.layout;
-  int tr = d.tile_rows, tc = d.tile_cols;
+  int tr = d.tile_rows, tc = d.tile_cols, nt = d.threads;
   if (opts && (opts->tile_rows || opts->tile_cols)) {
     tr = opts->tile_rows;
     tc = opts->tile_cols;
+    nt = 0;  // any built workgroup size; the largest is preferred
   }
+  if (opts && opts->threads) nt = opts->threads;
+  const int cache = (opts && opts->cache) ? opts->cache : d.cache;
   int n = 0;
   const xpose::TileKernel *table = xpose::tile_kernels(&n);
   const xpose::TileKernel *k = nullptr;
   for (int i = 0; i < n; ++i)
     if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
-        table[i].tile_cols == tc && table[i].layout == layout)
+        table[i].tile_cols == tc && table[i].layout == layout &&
+        table[i].cache == cache - 1 &&
+        (nt ? table[i].threads == nt : (!k || table[i].threads > k->threads)))
       k = &table[i];
   if (!k) return XPOSE_ENOTILE;
 
@@ -151,6 +193,14 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   }
   if (opts && (opts->flags & XPOSE_FLAG_ELEMENTWISE)) vec = false;
 
+  int64_t group_r = (opts && opts->group_rows) ? opts->group_rows : d.group_rows;
+  int64_t group_c = (opts && opts->group_cols) ? opts->group_cols : d.group_cols;
+  if (group_r > tiles_r) group_r = tiles_r;
+  if (group_c > tiles_c || group_c == 0) group_c = tiles_c;
+  int xcd = d.xcd_remap;
+  if (opts && (opts->flags & XPOSE_FLAG_XCD_REMAP)) xcd = 1;
+  if (opts && (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) xcd = 0;
+
   plan->kernel = k;
   plan->batch = batch;
   plan->tiles_per_matrix = tiles;
@@ -168,6 +218,9 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   a.tiles_c = (uint32_t)tiles_c;
   a.batch_first = 0;
   a.vec_ok = vec ? 1 : 0;
+  a.group_rows = (uint32_t)group_r;
+  a.group_cols = (uint32_t)group_c;
+  a.xcd_remap = xcd;
   return XPOSE_OK;
 }
 
@@ -238,21 +291,45 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->tiles = plan.tiles_per_matrix * plan.batch;
       info->launches = (int32_t)((plan.batch + plan.batch_per_launch - 1) /
                                  plan.batch_per_launch);
+      info->cache = plan.kernel->cache + 1;
+      info->group_rows = (int32_t)plan.args.group_rows;
+      info->group_cols = (int32_t)plan.args.group_cols;
+      info->xcd_remap = plan.args.xcd_remap;
     }
   }
   return rc;
 }
 
-int xpose_copy(void *dst, const void *src, int64_t bytes, void *stream) {
+int xpose_copy_ex(void *dst, const void *src, int64_t bytes,
+                  const xpose_copy_opts *opts, void *stream) {
   if (bytes < 0) return XPOSE_EINVAL;
+  if (opts && (opts->threads < 0 || opts->unroll < 0 ||
+               opts->cache < XPOSE_CACHE_AUTO ||
+               opts->cache > XPOSE_CACHE_NT_ALL))
+    return XPOSE_EINVAL;
+  const int threads = (opts && opts->threads) ? opts->threads : kDefaultCopyThreads;
+  const int unroll = (opts && opts->unroll) ? opts->unroll : kDefaultCopyUnroll;
+  const int cache = (opts && opts->cache) ? opts->cache : kDefaultCopyCache;
+  int n = 0;
+  const xpose::CopyKernel *table = xpose::copy_kernels(&n);
+  const xpose::CopyKernel *k = nullptr;
+  for (int i = 0; i < n; ++i)
+    if (table[i].threads == threads && table[i].unroll == unroll &&
+        table[i].cache == cache - 1)
+      k = &table[i];
+  if (!k) return XPOSE_ENOTILE;
   if (bytes == 0) return XPOSE_OK;
   if (!dst || !src) return XPOSE_EINVAL;
   const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
   if (d + (uint64_t)bytes < d || s + (uint64_t)bytes < s) return XPOSE_EINVAL;
   if (d < s + (uint64_t)bytes && s < d + (uint64_t)bytes) return XPOSE_EALIAS;
-  const hipError_t e =
-      xpose::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  const hipError_t e = xpose::launch_copy(*k, dst, src, bytes,
+                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? XPOSE_OK : hip_fail(e);
+}
+
+int xpose_copy(void *dst, const void *src, int64_t bytes, void *stream) {
+  return xpose_copy_ex(dst, src, bytes, nullptr, stream);
 }
 
 int xpose_lds_probe(uint64_t *cycles_out, const int32_t *lane_bytes,

@@ -19,21 +19,66 @@ struct TileArgs {
   int64_t rows, cols, ld_in, ld_out, stride_in, stride_out;
   uint32_t tiles_r, tiles_c;
   uint32_t batch_first;
-  int32_t vec_ok;  // 1: interior tiles may use 128-bit global accesses
+  int32_t vec_ok;      // 1: interior tiles may use 128-bit global accesses
+  uint32_t group_rows; // tile order: super-tile height in tiles (>= 1)
+  uint32_t group_cols; // tile order: super-tile width in tiles (>= 1)
+  int32_t xcd_remap;   // 1: one contiguous tile range per XCD
 };
+
+// Workgroup index -> (batch entry, tile row, tile column), for `block` of a
+// grid of `nblocks` workgroups.  A bijection from [0, nblocks) onto
+// batch x tiles_r x tiles_c whenever nblocks = batch_count * tiles_r * tiles_c
+// and 1 <= group_rows <= tiles_r, 1 <= group_cols <= tiles_c.
+//   xcd_remap: the hardware hands consecutive workgroups to the 8 XCDs in
+//     turn; remapping gives each XCD one contiguous range of tiles instead.
+//   group_rows GR x group_cols GC: tiles are walked in super-tiles of GR tile
+//     rows by GC tile columns, super-tiles row-major, tile rows fastest
+//     inside a super-tile.  The workgroups resident at one time then cover a
+//     compact block of the input AND of the output, instead of whole rows of
+//     one and a thin column band of the other.  GR = 1 with GC = tiles_c is
+//     plain row-band order.
+__host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
+                                            uint32_t nblocks, uint32_t &tr,
+                                            uint32_t &tc, int64_t &b) {
+  uint32_t g = block;
+  if (a.xcd_remap) {
+    const uint32_t q = nblocks / 8, r = nblocks % 8, x = g % 8;
+    g = x * q + (x < r ? x : r) + g / 8;
+  }
+  const uint32_t per = a.tiles_r * a.tiles_c;
+  b = (int64_t)(g / per) + a.batch_first;
+  g %= per;
+  const uint32_t GR = a.group_rows, GC = a.group_cols;
+  const uint32_t band = GR * a.tiles_c;  // tiles in one full super-tile row
+  const uint32_t sr = g / band, rem = g % band;
+  const uint32_t rows_here =
+      (sr + 1) * GR <= a.tiles_r ? GR : a.tiles_r - sr * GR;
+  const uint32_t span = rows_here * GC;  // tiles in one full super-tile
+  const uint32_t sc = rem / span, rem2 = rem % span;
+  tr = sr * GR + rem2 % rows_here;
+  tc = sc * GC + rem2 / rows_here;
+}
 
 // One compiled tile kernel.
 struct TileKernel {
-  int elem_bytes, tile_rows, tile_cols, threads, layout, lds_bytes;
+  int elem_bytes, tile_rows, tile_cols, threads, layout, cache, lds_bytes;
   hipError_t (*launch)(const TileArgs &, uint32_t grid, hipStream_t);
 };
 
 // Every compiled tile kernel; *count receives the table length.
 const TileKernel *tile_kernels(int *count);
 
-// 128-bit device-to-device copy (byte path for unaligned ends).
-hipError_t launch_copy(void *dst, const void *src, int64_t bytes,
-                       hipStream_t stream);
+// One compiled 128-bit copy kernel.
+struct CopyKernel {
+  int threads, unroll, cache;
+  hipError_t (*launch)(char *dst, const char *src, int64_t nvec, hipStream_t);
+};
+const CopyKernel *copy_kernels(int *count);
+
+// Device-to-device copy with kernel k (byte path for unaligned pointers and
+// the tail).
+hipError_t launch_copy(const CopyKernel &k, void *dst, const void *src,
+                       int64_t bytes, hipStream_t stream);
 
 // LDS bank microbenchmark; lane_bytes is a host array of 64 byte offsets.
 hipError_t launch_lds_probe(uint64_t *out, const int32_t *lane_bytes,

@@ -43,22 +43,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // 16-byte global access at a 4-byte-aligned address.  gfx9 global memory
 // instructions wider than a dword only need dword alignment, so a row whose
 // pitch is an odd number of fp32 elements still takes dwordx4 accesses.
-struct __attribute__((aligned(4))) Vec16 {
-  uint32_t w[4];
-};
+typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(4)));
 
+// Cache policy of the global accesses: plain, non-temporal stores, or
+// non-temporal loads and stores (the data is touched exactly once).
+enum CachePolicy : int { kCacheDefault = 0, kNtStore = 1, kNtLoadStore = 2 };
+
+template <int CP>
 __device__ __forceinline__ u32x4 load16(const char *p) {
-  const Vec16 v = *reinterpret_cast<const Vec16 *>(p);
-  return u32x4{v.w[0], v.w[1], v.w[2], v.w[3]};
+  const u32x4u *q = reinterpret_cast<const u32x4u *>(p);
+  if constexpr (CP == kNtLoadStore) return __builtin_nontemporal_load(q);
+  else return *q;
 }
 
+template <int CP>
 __device__ __forceinline__ void store16(char *p, u32x4 x) {
-  Vec16 v;
-  v.w[0] = x.x;
-  v.w[1] = x.y;
-  v.w[2] = x.z;
-  v.w[3] = x.w;
-  *reinterpret_cast<Vec16 *>(p) = v;
+  u32x4u *q = reinterpret_cast<u32x4u *>(p);
+  if constexpr (CP != kCacheDefault) __builtin_nontemporal_store((u32x4u)x, q);
+  else *q = x;
 }
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
@@ -71,9 +73,10 @@ template <> struct Elem<8> { using E = uint64_t; using U = uint64_t; static cons
 
 // Compile-time geometry of one tile kernel.
 //   S   element bytes          TR x TC  tile in elements
-//   NT  threads per workgroup  L        LDS layout
-template <int S, int TR, int TC, int NT, int L>
+//   NT  threads per workgroup  L        LDS layout      CP  cache policy
+template <int S, int TR, int TC, int NT, int L, int CP>
 struct Tile {
+  static constexpr int CACHE = CP;
   using E = typename Elem<S>::E;
   using U = typename Elem<S>::U;
   static constexpr int K = Elem<S>::K;          // input rows per LDS unit
@@ -241,7 +244,8 @@ __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
     lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
 #pragma unroll
     for (int k = 0; k < T::K; ++k)
-      v[it][k] = load16(src + ((int64_t)(p * T::K + k) * ld_in + ch * T::V) * S);
+      v[it][k] = load16<T::CACHE>(
+          src + ((int64_t)(p * T::K + k) * ld_in + ch * T::V) * S);
   }
 #pragma unroll
   for (int it = 0; it < T::LIT; ++it) {
@@ -257,7 +261,7 @@ __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
     int c, q;
     lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
     const u32x4 o = read_column<T>(lds, c, q);
-    store16(dst + ((int64_t)c * ld_out + q * T::V) * S, o);
+    store16<T::CACHE>(dst + ((int64_t)c * ld_out + q * T::V) * S, o);
   }
 }
 
@@ -316,18 +320,16 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
   }
 }
 
-template <int S, int TR, int TC, int NT, int L>
+template <int S, int TR, int TC, int NT, int L, int CP>
 __global__ __launch_bounds__(NT) void xpose_tile_kernel(TileArgs a) {
-  using T = Tile<S, TR, TC, NT, L>;
+  using T = Tile<S, TR, TC, NT, L, CP>;
   __shared__ __attribute__((aligned(16))) typename T::U lds[T::LDS_UNITS];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t g = blockIdx.x;
-  const uint32_t tc = g % a.tiles_c;
-  g /= a.tiles_c;
-  const uint32_t tr = g % a.tiles_r;
-  const int64_t b = (int64_t)(g / a.tiles_r) + a.batch_first;
+  uint32_t tr, tc;
+  int64_t b;
+  tile_coords(a, blockIdx.x, gridDim.x, tr, tc, b);
 
   const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
   const char *src = static_cast<const char *>(a.in) +
@@ -345,30 +347,53 @@ __global__ __launch_bounds__(NT) void xpose_tile_kernel(TileArgs a) {
                         cols_left, wave, lane);
 }
 
-template <int S, int TR, int TC, int NT, int L>
+template <int S, int TR, int TC, int NT, int L, int CP>
 hipError_t launch_tile(const TileArgs &a, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((xpose_tile_kernel<S, TR, TC, NT, L>), dim3(grid),
-                     dim3(NT), 0, stream, a);
-  return hipGetLastError();
+  TileArgs copy = a;
+  void *args[] = {&copy};
+  // hipLaunchKernel reports this launch's own status; the sticky
+  // hipGetLastError can hold an unrelated earlier error of the process.
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(&xpose_tile_kernel<S, TR, TC, NT, L, CP>),
+      dim3(grid), dim3(NT), args, 0, stream);
 }
 
-#define XPOSE_TILE(S, TR, TC, NT, L)                                        \
+#define XPOSE_TILE(S, TR, TC, NT, L, CP)                                    \
   TileKernel {                                                              \
-    S, TR, TC, NT, L, Tile<S, TR, TC, NT, L>::LDS_BYTES,                   \
-        &launch_tile<S, TR, TC, NT, L>                                      \
+    S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
+        &launch_tile<S, TR, TC, NT, L, CP>                                  \
   }
-#define XPOSE_TILE3(S, TR, TC, NT)                                          \
-  XPOSE_TILE(S, TR, TC, NT, kSwizzle), XPOSE_TILE(S, TR, TC, NT, kPad1),    \
-      XPOSE_TILE(S, TR, TC, NT, kUnpadded)
+// Every layout with plain caching and with non-temporal stores (so the
+// layout ablation compares like with like).
+#define XPOSE_TILES(S, TR, TC, NT)                                          \
+  XPOSE_TILE(S, TR, TC, NT, kSwizzle, kCacheDefault),                       \
+      XPOSE_TILE(S, TR, TC, NT, kPad1, kCacheDefault),                      \
+      XPOSE_TILE(S, TR, TC, NT, kUnpadded, kCacheDefault),                  \
+      XPOSE_TILE(S, TR, TC, NT, kSwizzle, kNtStore),                        \
+      XPOSE_TILE(S, TR, TC, NT, kPad1, kNtStore),                           \
+      XPOSE_TILE(S, TR, TC, NT, kUnpadded, kNtStore)
 
 static const TileKernel kTileKernels[] = {
-    XPOSE_TILE3(4, 64, 64, 256),   XPOSE_TILE3(4, 32, 32, 256),
-    XPOSE_TILE3(4, 64, 128, 256),  XPOSE_TILE3(4, 128, 64, 256),
-    XPOSE_TILE3(4, 128, 128, 256), XPOSE_TILE3(2, 64, 64, 256),
-    XPOSE_TILE3(2, 128, 128, 256), XPOSE_TILE3(2, 64, 128, 256),
-    XPOSE_TILE3(2, 128, 64, 256),  XPOSE_TILE3(1, 128, 128, 256),
-    XPOSE_TILE3(1, 64, 64, 64),    XPOSE_TILE3(8, 32, 32, 256),
-    XPOSE_TILE3(8, 64, 64, 256),
+    // 4-byte elements
+    XPOSE_TILES(4, 32, 32, 256), XPOSE_TILES(4, 32, 32, 128),
+    XPOSE_TILES(4, 32, 32, 64), XPOSE_TILES(4, 32, 64, 128),
+    XPOSE_TILES(4, 64, 32, 128), XPOSE_TILES(4, 64, 64, 256),
+    XPOSE_TILES(4, 64, 128, 256), XPOSE_TILES(4, 128, 64, 256),
+    XPOSE_TILES(4, 128, 128, 256), XPOSE_TILES(4, 32, 128, 256),
+    XPOSE_TILES(4, 128, 32, 256),
+    XPOSE_TILE(4, 32, 32, 256, kSwizzle, kNtLoadStore),
+    XPOSE_TILE(4, 64, 64, 256, kSwizzle, kNtLoadStore),
+    // 2-byte elements
+    XPOSE_TILES(2, 32, 32, 64), XPOSE_TILES(2, 32, 64, 128),
+    XPOSE_TILES(2, 64, 32, 128), XPOSE_TILES(2, 64, 64, 128),
+    XPOSE_TILES(2, 64, 64, 256), XPOSE_TILES(2, 128, 128, 256),
+    XPOSE_TILES(2, 64, 128, 256), XPOSE_TILES(2, 128, 64, 256),
+    // 1-byte elements
+    XPOSE_TILES(1, 64, 64, 64), XPOSE_TILES(1, 64, 128, 128),
+    XPOSE_TILES(1, 128, 64, 128), XPOSE_TILES(1, 128, 128, 256),
+    // 8-byte elements
+    XPOSE_TILES(8, 16, 16, 64), XPOSE_TILES(8, 32, 32, 128),
+    XPOSE_TILES(8, 32, 32, 256), XPOSE_TILES(8, 64, 64, 256),
 };
 
 const TileKernel *tile_kernels(int *count) {
@@ -377,26 +402,26 @@ const TileKernel *tile_kernels(int *count) {
 }
 
 // ---------------------------------------------------------------------------
-// Copy yardstick: same bytes per workgroup as a 64 x 64 fp32 tile (16 KiB in,
-// 16 KiB out), 16 bytes per lane per access, all loads issued before stores.
+// Copy yardstick.  Each workgroup moves NT * UNROLL 16-byte vectors of one
+// contiguous range, issuing all its loads before its stores, exactly the
+// access widths the transpose uses.  The default (256 threads x 4) moves the
+// same 16 KiB in and out per workgroup as a 64 x 64 fp32 tile.
 // ---------------------------------------------------------------------------
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
-
-__global__ __launch_bounds__(kCopyThreads) void copy16_kernel(
-    u32x4 *__restrict__ dst, const u32x4 *__restrict__ src, int64_t nvec) {
-  const int64_t base =
-      (int64_t)blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
-  u32x4 r[kCopyUnroll];
+template <int NT, int UNROLL, int CP>
+__global__ __launch_bounds__(NT) void copy16_kernel(char *__restrict__ dst,
+                                                    const char *__restrict__ src,
+                                                    int64_t nvec) {
+  const int64_t base = (int64_t)blockIdx.x * (NT * UNROLL) + threadIdx.x;
+  u32x4 r[UNROLL];
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t i = base + (int64_t)u * kCopyThreads;
-    if (i < nvec) r[u] = src[i];
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t i = base + (int64_t)u * NT;
+    if (i < nvec) r[u] = load16<CP>(src + i * 16);
   }
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t i = base + (int64_t)u * kCopyThreads;
-    if (i < nvec) dst[i] = r[u];
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t i = base + (int64_t)u * NT;
+    if (i < nvec) store16<CP>(dst + i * 16, r[u]);
   }
 }
 
@@ -408,33 +433,58 @@ __global__ __launch_bounds__(256) void copy_bytes_kernel(
     dst[i] = src[i];
 }
 
-hipError_t launch_copy(void *dst, const void *src, int64_t bytes,
-                       hipStream_t stream) {
+template <int NT, int UNROLL, int CP>
+hipError_t launch_copy16(char *d, const char *s, int64_t nvec,
+                         hipStream_t stream) {
+  const int64_t per_block = (int64_t)NT * UNROLL;
+  const int64_t blocks = (nvec + per_block - 1) / per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  void *args[] = {&d, &s, &nvec};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(&copy16_kernel<NT, UNROLL, CP>),
+      dim3((uint32_t)blocks), dim3(NT), args, 0, stream);
+}
+
+#define XPOSE_COPY(NT, U, CP) CopyKernel{NT, U, CP, &launch_copy16<NT, U, CP>}
+static const CopyKernel kCopyKernels[] = {
+    XPOSE_COPY(256, 1, kCacheDefault), XPOSE_COPY(256, 2, kCacheDefault),
+    XPOSE_COPY(256, 4, kCacheDefault), XPOSE_COPY(256, 8, kCacheDefault),
+    XPOSE_COPY(512, 4, kCacheDefault), XPOSE_COPY(1024, 4, kCacheDefault),
+    XPOSE_COPY(64, 4, kNtStore),       XPOSE_COPY(128, 2, kNtStore),
+    XPOSE_COPY(256, 1, kNtStore),      XPOSE_COPY(256, 2, kNtStore),
+    XPOSE_COPY(256, 4, kNtStore),      XPOSE_COPY(256, 8, kNtStore),
+    XPOSE_COPY(512, 1, kNtStore),      XPOSE_COPY(512, 2, kNtStore),
+    XPOSE_COPY(1024, 1, kNtStore),     XPOSE_COPY(256, 1, kNtLoadStore),
+    XPOSE_COPY(256, 4, kNtLoadStore),
+};
+
+const CopyKernel *copy_kernels(int *count) {
+  *count = (int)(sizeof(kCopyKernels) / sizeof(kCopyKernels[0]));
+  return kCopyKernels;
+}
+
+hipError_t launch_copy(const CopyKernel &k, void *dst, const void *src,
+                       int64_t bytes, hipStream_t stream) {
   char *d = static_cast<char *>(dst);
   const char *s = static_cast<const char *>(src);
   int64_t head = 0;
   if ((((uintptr_t)d | (uintptr_t)s) & 15) == 0) {
     const int64_t nvec = bytes / 16;
     if (nvec > 0) {
-      const int64_t per_block = (int64_t)kCopyThreads * kCopyUnroll;
-      const int64_t blocks = (nvec + per_block - 1) / per_block;
-      if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(copy16_kernel, dim3((uint32_t)blocks),
-                         dim3(kCopyThreads), 0, stream,
-                         reinterpret_cast<u32x4 *>(d),
-                         reinterpret_cast<const u32x4 *>(s), nvec);
-      const hipError_t e = hipGetLastError();
+      const hipError_t e = k.launch(d, s, nvec, stream);
       if (e != hipSuccess) return e;
     }
     head = nvec * 16;
   }
-  const int64_t rest = bytes - head;
+  int64_t rest = bytes - head;
   if (rest > 0) {
+    char *dd = d + head;
+    const char *ss = s + head;
     int64_t blocks = (rest + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(copy_bytes_kernel, dim3((uint32_t)blocks), dim3(256), 0,
-                       stream, d + head, s + head, rest);
-    return hipGetLastError();
+    void *args[] = {&dd, &ss, &rest};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&copy_bytes_kernel),
+                           dim3((uint32_t)blocks), dim3(256), args, 0, stream);
   }
   return hipSuccess;
 }
@@ -517,18 +567,18 @@ hipError_t launch_lds_probe(uint64_t *out, const int32_t *lane_bytes,
                             hipStream_t stream) {
   ProbeLanes lanes;
   for (int i = 0; i < 64; ++i) lanes.b[i] = lane_bytes[i];
-#define PROBE_LAUNCH(W, WR)                                                 \
-  hipLaunchKernelGGL((lds_probe_kernel<W, WR>), dim3(1), dim3(64), 0, stream, \
-                     lanes, iters, out)
-  if (width == 4) {
-    if (is_write) PROBE_LAUNCH(4, true); else PROBE_LAUNCH(4, false);
-  } else if (width == 8) {
-    if (is_write) PROBE_LAUNCH(8, true); else PROBE_LAUNCH(8, false);
-  } else {
-    if (is_write) PROBE_LAUNCH(16, true); else PROBE_LAUNCH(16, false);
-  }
-#undef PROBE_LAUNCH
-  return hipGetLastError();
+  const void *fn;
+  if (width == 4)
+    fn = is_write ? (const void *)&lds_probe_kernel<4, true>
+                  : (const void *)&lds_probe_kernel<4, false>;
+  else if (width == 8)
+    fn = is_write ? (const void *)&lds_probe_kernel<8, true>
+                  : (const void *)&lds_probe_kernel<8, false>;
+  else
+    fn = is_write ? (const void *)&lds_probe_kernel<16, true>
+                  : (const void *)&lds_probe_kernel<16, false>;
+  void *args[] = {&lanes, &iters, &out};
+  return hipLaunchKernel(fn, dim3(1), dim3(64), args, 0, stream);
 }
 
 }  // namespace xpose

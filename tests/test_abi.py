@@ -51,19 +51,25 @@ def plan(out=OUT, inp=IN, batch=1, rows=64, cols=64, ld_in=None, ld_out=None,
 def test_valid_plan_defaults():
     rc, info = plan(rows=8192, cols=8192)
     assert rc == X.XPOSE_OK
-    assert (info.tile_rows, info.tile_cols) == (64, 64)
+    assert (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.layout == X.LAYOUT_SWIZZLE
-    assert info.vector_path == 1 and info.tiles == 128 * 128
+    assert info.cache == X.CACHE_NT_STORE and info.xcd_remap == 1
+    assert (info.group_rows, info.group_cols) == (8, 32)
+    assert info.vector_path == 1 and info.tiles == 256 * 256
     assert info.launches == 1 and info.threads == 256
-    assert info.lds_bytes == 64 * 64 * 4
+    assert info.lds_bytes == 32 * 32 * 4
 
 
 def test_ragged_and_batched_tile_counts():
+    # Odd pitches: rows are not 16-byte aligned, a taller tile is chosen.
     rc, info = plan(rows=12345, cols=6789)
-    assert rc == 0 and info.tiles == 193 * 107 and info.vector_path == 1
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 64)
+    assert info.tiles == 97 * 107 and info.vector_path == 1
+    # A batch of small matrices: taller tiles, small super-tiles.
     rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
                     stride_out=1024 * 2048)
-    assert rc == 0 and info.tiles == 64 * 32 * 16
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 64)
+    assert info.tiles == 64 * 16 * 16 and info.xcd_remap == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -137,7 +143,13 @@ def test_opts_select_layout_and_tile():
         rc, info = plan(opts=X.XposeOpts(layout, 32, 32, 0))
         assert rc == 0 and info.layout == layout
         assert (info.tile_rows, info.tile_cols) == (32, 32)
-    assert plan(opts=X.XposeOpts(X.LAYOUT_PAD1, 0, 0, 0))[1].lds_bytes == 64 * 65 * 4
+    # The one-word pad on the default 32 x 32 fp32 tile is the pages'
+    # 4,224-byte tile[32][33].
+    assert plan(opts=X.XposeOpts(X.LAYOUT_PAD1, 0, 0, 0))[1].lds_bytes == 4224
+    assert plan(opts=X.XposeOpts(X.LAYOUT_UNPADDED, 0, 0, 0))[1].lds_bytes == 4096
+    rc, info = plan(opts=X.make_opts(tile=(32, 32), threads=64))
+    assert rc == 0 and info.threads == 64
+    assert plan(opts=X.make_opts(tile=(32, 32), threads=96))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(0, 48, 48, 0))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(9, 0, 0, 0))[0] == X.XPOSE_EINVAL
     assert plan(opts=X.XposeOpts(0, 0, 0, 8))[0] == X.XPOSE_EINVAL
@@ -149,5 +161,21 @@ def test_large_batch_splits_launches():
                     stride_in=4096 * 4096, stride_out=4096 * 4096,
                     out=0x100000000000000, inp=0x10000)
     assert rc == 0
-    assert info.tiles == (1 << 20) * 64 * 64
-    assert info.launches == -(-info.tiles // (0x7fffffff // (64 * 64) * 64 * 64))
+    per = (4096 // info.tile_rows) * (4096 // info.tile_cols)
+    assert info.tiles == (1 << 20) * per
+    assert info.launches == -(-info.tiles // (0x7fffffff // per * per))
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding (before or after torch) must leave exactly one
+    HIP runtime mapped: two runtimes in one process give each its own device
+    context, and launches on the other runtime's memory fail or crash."""
+    import subprocess
+    import sys
+    probe = ("import lds_tiled_matrix_amd, torch; "
+             "print(len({l.split()[-1] for l in open('/proc/self/maps') "
+             "if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", probe], capture_output=True,
+                         text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr[-500:]
+    assert out.stdout.strip() == "1"

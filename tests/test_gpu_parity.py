@@ -224,3 +224,39 @@ def test_copy_kernel():
         assert np.array_equal(got[dst_off:dst_off + nbytes],
                               host[src_off:src_off + nbytes])
         assert not got[:dst_off].any() and not got[dst_off + nbytes:].any()
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_tile_orders_and_cache_policies(s):
+    """Tile enumeration order, XCD remap and non-temporal accesses change
+    only the schedule: results stay bit-exact, batches included."""
+    for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE, X.CACHE_NT_ALL):
+        for gr, gc in ((1, 0), (3, 0), (1000, 0), (2, 3), (4, 1), (5, 1000)):
+            for flags in (X.FLAG_XCD_REMAP, X.FLAG_NO_XCD_REMAP):
+                opts = X.make_opts(X.LAYOUT_SWIZZLE, None, flags, cache, gr, gc)
+                tag = f"c{cache} g{gr}x{gc} f{flags}"
+                check_case(s, 1, 777, 555, seed=cache * 100 + gr + gc + flags,
+                           opts=opts, label=f"order {tag}")
+                check_case(s, 3, 301, 257, seed=gr + gc + flags, opts=opts,
+                           label=f"order-batch {tag}")
+
+
+def test_copy_variants():
+    nbytes = (3 << 20) + 44
+    host = wl.random_bits((nbytes,), 1, 123)
+    src = torch.from_numpy(host).to(_dev())
+    n_ok = 0
+    for thr in (256, 512, 1024):
+        for unroll in (4, 8, 16):
+            for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE, X.CACHE_NT_ALL):
+                opts = X.XposeCopyOpts(thr, unroll, cache, 0)
+                dst = torch.zeros(nbytes, dtype=torch.uint8, device=_dev())
+                rc = X.xpose_copy_ex(dst.data_ptr(), src.data_ptr(), nbytes, opts, 0)
+                if rc == X.XPOSE_ENOTILE:
+                    continue
+                say(f"copy variant {thr} {unroll} {cache}")
+                assert rc == 0
+                torch.cuda.synchronize()
+                assert np.array_equal(dst.cpu().numpy(), host)
+                n_ok += 1
+    assert n_ok >= 5
