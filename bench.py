@@ -11,8 +11,8 @@ core.  --table additionally writes a markdown table over every workload to
 stderr.
 
 Timing protocol ("Shared memory and the bank conflict", section "What to
-record": median of repeated runs after a warm-up, the copy measured the same
-way): W untimed launches, then K launches back to back bracketed by device
+record": warm the kernel up first, time it many times, report the median,
+and time the copy with the same procedure): W untimed launches, then K launches back to back bracketed by device
 synchronisation (the wall-clock `value`), then K launches each between an
 event pair on the launch stream (median / min / p90 / mean per launch).
 A cold mode reads 1 GiB between launches to empty every cache first.

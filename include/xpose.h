@@ -67,12 +67,12 @@ enum {
   XPOSE_ENOTILE = -6 /* xpose_opts asked for a tile shape that is not built */
 };
 
-/* LDS tile layouts (the row stride of the on-chip tile).  Source: "pad or
- * swizzle tiles when column access creates bank conflicts" ("Shared-memory
- * tiling and bank conflicts", section "Reference summary"); the one-word pad
- * is the tile[32][33] of "Shared Memory and Bank Conflicts", section "the
- * classic case".  All layouts give identical results; they differ only in
- * LDS bank conflicts. */
+/* LDS tile layouts (the row stride of the on-chip tile).  A padded or a
+ * swizzled row is the remedy the pages give for conflicted column reads
+ * ("Shared-memory tiling and bank conflicts", section "Reference summary");
+ * the one-word pad is the 33-word row of "Shared Memory and Bank Conflicts",
+ * section "the classic case".  All layouts give identical results; they
+ * differ only in LDS bank conflicts. */
 typedef enum xpose_layout {
   XPOSE_LAYOUT_AUTO = 0,     /* library default (the measured best)          */
   XPOSE_LAYOUT_UNPADDED = 1, /* row stride = tile width (conflicted column read) */

@@ -12,12 +12,13 @@ The rules, as the pages state them:
 * Lanes asking for the *same* word are served by one broadcast: a repeated
   bank alone is not a conflict, compare complete addresses.  ("how banking
   works"; "Calculate the bank mapping"; "Common errors".)
-* ``n`` different words in one bank are served one after another: an n-way
-  conflict costs n steps.  ("How Shared Memory Is Addressed"; "Banks".)
-* Conflicts are resolved per execution group; the pages' group is a 32-lane
-  warp, and on 64-lane wavefronts they say the hardware resolves the access
-  in halves, so the group is half a wavefront.  ("Shared Memory and Bank
-  Conflicts", section "the wave size complication".)
+* ``n`` distinct words that share a bank are served serially, so such a
+  request takes ``n`` steps.  ("How Shared Memory Is Addressed"; "Banks".)
+* The lanes that compete for banks form one group; on the pages' hardware
+  that is a 32-lane warp, and for 64-lane wavefronts they state that each
+  half of the wavefront is analysed on its own, so the group is 32 lanes.
+  ("Shared Memory and Bank Conflicts", section "the wave size
+  complication".)
 
 The pages leave wider accesses to the target's documentation ("Calculate the
 bank mapping").  Reading adopted here: a lane whose access spans ``k``
@@ -106,7 +107,7 @@ def column_read(stride_words: int, col: int = 0, lanes: int = 32):
 
 def row_write(stride_words: int, row: int = 0, lanes: int = 32):
     """Lane t writes tile[row][t] ("Shared memory and the bank conflict",
-    "Banks": the first loop writes a row)."""
+    "Banks": the load phase stores one tile row per warp)."""
     return scalar_words(row * stride_words + t for t in range(lanes))
 
 

@@ -8,12 +8,13 @@
  *
  * What it computes is the plain definition of a transpose: the element in
  * row i, column j of the input lands in row j, column i of the output.
- * The pages write it as the per-thread pair "load in[row][col] into the tile,
- * store tile[col][row] to the output" ("Shared memory and the bank conflict",
- * section "Turn the tile around on chip") and, for a non-square matrix of
- * width x height, as out[col * height + row] = in[row * width + col]
- * ("Shared-memory tiling and bank conflicts", section "Reference summary").
- * Both collapse to the loop below once the tile is taken away.  Leading
+ * On the pages each thread copies an input element into the on-chip tile
+ * and a second phase writes the tile's transposed element to the output
+ * ("Shared memory and the bank conflict", section "Turn the tile around on
+ * chip"); for a non-square matrix of width W and height H the element at
+ * row r, column c lands at output offset c*H + r ("Shared-memory tiling and
+ * bank conflicts", section "Reference summary").  Both collapse to the loop
+ * below once the tile is taken away.  Leading
  * dimensions and batch strides are counted in elements; a batch of matrices
  * is the same definition applied to each one.
  *

@@ -56,7 +56,7 @@ def check_golden_index(fn):
 def check_index_valued(fn, rows=1024, cols=1024):
     """Every element holds its own row-major index, so out[r][c] must hold
     c * cols + r ("Shared memory and the bank conflict", "The barrier":
-    with every element holding its own index, any misplaced element fails)."""
+    when each element carries its index, a single misplaced element shows)."""
     a = np.arange(rows * cols, dtype=np.float32).reshape(rows, cols)
     out = fn(a)
     want = (np.arange(rows, dtype=np.float32)[None, :] * np.float32(cols)
