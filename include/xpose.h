@@ -89,6 +89,14 @@ typedef enum xpose_cache {
   XPOSE_CACHE_NT_ALL = 3      /* non-temporal loads and stores              */
 } xpose_cache;
 
+/* Order in which workgroups walk the tiles (results are identical). */
+typedef enum xpose_order {
+  XPOSE_ORDER_AUTO = 0,        /* library default                          */
+  XPOSE_ORDER_SUPER_TILES = 1, /* group_rows x group_cols super-tiles      */
+  XPOSE_ORDER_DIAGONAL = 2     /* consecutive workgroups step diagonally:
+                                  tile row g mod R, column (g/R + row) mod C */
+} xpose_order;
+
 /* Option flags for xpose_batched_ex. */
 enum {
   XPOSE_FLAG_ELEMENTWISE = 1, /* force the element-wise edge path everywhere */
@@ -111,6 +119,7 @@ typedef struct xpose_opts {
   int32_t group_cols; /* 0 = default                                         */
   int32_t threads;    /* workgroup size of the tile kernel; 0 = the default
                          (with an explicit tile: the largest one built)     */
+  int32_t order;      /* xpose_order                                         */
 } xpose_opts;
 
 /* What xpose_plan reports about the kernel a call would launch. */
@@ -128,6 +137,7 @@ typedef struct xpose_plan_info {
   int32_t group_rows;  /* resolved super-tile height in tiles                 */
   int32_t group_cols;  /* resolved super-tile width in tiles                  */
   int32_t xcd_remap;   /* 1 if tiles are remapped per XCD                    */
+  int32_t order;       /* resolved xpose_order                               */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

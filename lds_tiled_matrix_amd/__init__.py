@@ -29,6 +29,7 @@ LAYOUT_NAMES = {LAYOUT_UNPADDED: "unpadded", LAYOUT_PAD1: "pad1",
                 LAYOUT_SWIZZLE: "swizzle"}
 FLAG_ELEMENTWISE, FLAG_XCD_REMAP, FLAG_NO_XCD_REMAP = 1, 2, 4
 CACHE_AUTO, CACHE_DEFAULT, CACHE_NT_STORE, CACHE_NT_ALL = 0, 1, 2, 3
+ORDER_AUTO, ORDER_SUPER_TILES, ORDER_DIAGONAL = 0, 1, 2
 CACHE_NAMES = {CACHE_DEFAULT: "default", CACHE_NT_STORE: "nt_store",
                CACHE_NT_ALL: "nt_all"}
 
@@ -42,7 +43,8 @@ class XposeOpts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("tile_cols", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
-                ("group_cols", ctypes.c_int32), ("threads", ctypes.c_int32)]
+                ("group_cols", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("order", ctypes.c_int32)]
 
 
 class XposeCopyOpts(ctypes.Structure):
@@ -56,7 +58,8 @@ class XposePlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("vector_path", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
                 ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
-                ("group_cols", ctypes.c_int32), ("xcd_remap", ctypes.c_int32)]
+                ("group_cols", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
+                ("order", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -118,10 +121,11 @@ def _check(code: int, what: str) -> int:
 
 
 def make_opts(layout=LAYOUT_AUTO, tile=None, flags=0, cache=CACHE_AUTO,
-              group_rows=0, group_cols=0, threads=0) -> XposeOpts:
+              group_rows=0, group_cols=0, threads=0,
+              order=ORDER_AUTO) -> XposeOpts:
     tr, tc = tile if tile else (0, 0)
     return XposeOpts(layout, tr, tc, flags, cache, group_rows, group_cols,
-                     threads)
+                     threads, order)
 
 
 # ----- C ABI, one to one -----------------------------------------------------

@@ -31,39 +31,53 @@ int elem_bytes_of(int32_t dtype) {
   }
 }
 
-// Default launch configuration, chosen from the measured sweep over tile
+// Default launch configuration, chosen from the measured sweeps over tile
 // shape, workgroup size, cache policy and tile order on MI355X.
-//   row16: every row start on both sides is 16-byte aligned (pointers,
-//     pitches, batch strides).  Otherwise 16-byte accesses straddle cache
-//     lines; plain (write-back) stores then merge the partial lines in L2 and
-//     win over non-temporal ones.
+//   row128: every row start on both sides is 128-byte aligned (pointers,
+//     pitches, batch strides), so each tile row segment is whole cache
+//     lines.  Otherwise segments straddle lines: plain (write-back) stores
+//     then merge the partial lines in L2 and win over non-temporal ones,
+//     which write partial lines straight to memory.
 //   small: a batch of matrices of at most kSmallMatrixBytes each.  Resident
 //     workgroups then cover a few whole matrices, a dense window on both the
 //     input and the output side, and a taller tile with small super-tiles
 //     streams at copy speed.
+//   big: the call moves more than kBigCallBytes (read + write).  Then the
+//     256 MB memory-side cache cannot hold a useful part of the data across
+//     calls, every access goes to HBM, and the diagonal order (resident
+//     tiles spread over all row and column offsets) is fastest.  Below it,
+//     repeated calls partly hit that cache and small 32 x 32 tiles in compact
+//     super-tiles are fastest.
 // cache is an xpose_cache value; group_cols 0 means all tile columns.
 struct Default {
   int tile_rows, tile_cols, threads, layout, cache, group_rows, group_cols,
-      xcd_remap;
+      xcd_remap, order;
 };
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
+constexpr int64_t kBigCallBytes = 512ll << 20;
+constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
+              kDiag = XPOSE_ORDER_DIAGONAL, kWB = XPOSE_CACHE_DEFAULT,
+              kNT = XPOSE_CACHE_NT_STORE;
 
-Default default_for(int s, bool row16, bool small) {
-  if (!row16) {
+Default default_for(int s, bool row128, bool small, bool big) {
+  if (!row128) {
     switch (s) {
-      case 4: return {128, 64, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 32, 32, 1};
-      case 2: return {64, 64, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 16, 16, 1};
-      case 1: return {128, 128, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 16, 16, 1};
-      default: return {32, 32, 256, xpose::kSwizzle, XPOSE_CACHE_DEFAULT, 16, 16, 1};
+      case 4: return {128, 64, 256, kSwz, kWB, 32, 32, 1, kSup};
+      case 2: return {64, 64, 256, kSwz, kWB, 16, 16, 1, kSup};
+      case 1: return {128, 128, 256, kSwz, kWB, 16, 16, 1, kSup};
+      default: return {32, 32, 256, kSwz, kWB, 16, 16, 1, kSup};
     }
   }
   switch (s) {
     case 4:
-      if (small) return {128, 64, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 8, 8, 0};
-      return {32, 32, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 8, 32, 1};
-    case 2: return {128, 64, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 32, 8, 0};
-    case 1: return {128, 128, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 16, 16, 1};
-    default: return {32, 32, 256, xpose::kSwizzle, XPOSE_CACHE_NT_STORE, 8, 32, 1};
+      if (small) return {128, 64, 256, kSwz, kNT, 8, 8, 0, kSup};
+      if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
+    case 2:
+      if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      return {128, 64, 256, kSwz, kNT, 32, 8, 0, kSup};
+    case 1: return {128, 128, 256, kSwz, kNT, 16, 16, 1, kSup};
+    default: return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
   }
 }
 
@@ -118,6 +132,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                opts->cache < XPOSE_CACHE_AUTO ||
                opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
                opts->group_cols < 0 || opts->threads < 0 ||
+               opts->order < XPOSE_ORDER_AUTO ||
+               opts->order > XPOSE_ORDER_DIAGONAL ||
                opts->tile_rows < 0 || opts->tile_cols < 0))
     return XPOSE_EINVAL;
   if (batch == 0 || rows == 0 || cols == 0) {
@@ -151,11 +167,15 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     return XPOSE_EALIAS;
 
   // Kernel choice.
-  const bool row16 =
-      ((pi | po) % 16 == 0) && (ld_in * s) % 16 == 0 && (ld_out * s) % 16 == 0 &&
-      (batch == 1 || ((stride_in * s) % 16 == 0 && (stride_out * s) % 16 == 0));
+  const bool row128 =
+      ((pi | po) % 128 == 0) && (ld_in * s) % 128 == 0 &&
+      (ld_out * s) % 128 == 0 &&
+      (batch == 1 || ((stride_in * s) % 128 == 0 && (stride_out * s) % 128 == 0));
   const bool small = batch > 1 && rows * cols * s <= kSmallMatrixBytes;
-  Default d = default_for(s, row16, small);
+  int64_t call_bytes;
+  const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
+                   call_bytes > kBigCallBytes;
+  Default d = default_for(s, row128, small, big);
   int layout = (opts && opts->layout) ? opts->layout : d.layout;
   int tr = d.tile_rows, tc = d.tile_cols, nt = d.threads;
   if (opts && (opts->tile_rows || opts->tile_cols)) {
@@ -218,6 +238,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   a.tiles_c = (uint32_t)tiles_c;
   a.batch_first = 0;
   a.vec_ok = vec ? 1 : 0;
+  a.order = (opts && opts->order) ? opts->order : d.order;
   a.group_rows = (uint32_t)group_r;
   a.group_cols = (uint32_t)group_c;
   a.xcd_remap = xcd;
@@ -294,6 +315,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->cache = plan.kernel->cache + 1;
       info->group_rows = (int32_t)plan.args.group_rows;
       info->group_cols = (int32_t)plan.args.group_cols;
+      info->order = plan.args.order;
       info->xcd_remap = plan.args.xcd_remap;
     }
   }

@@ -23,7 +23,11 @@ struct TileArgs {
   uint32_t group_rows; // tile order: super-tile height in tiles (>= 1)
   uint32_t group_cols; // tile order: super-tile width in tiles (>= 1)
   int32_t xcd_remap;   // 1: one contiguous tile range per XCD
+  int32_t order;       // kOrderSuperTiles or kOrderDiagonal
 };
+
+// Tile orders (values match xpose_order in include/xpose.h).
+enum TileOrder : int { kOrderSuperTiles = 1, kOrderDiagonal = 2 };
 
 // Workgroup index -> (batch entry, tile row, tile column), for `block` of a
 // grid of `nblocks` workgroups.  A bijection from [0, nblocks) onto
@@ -37,6 +41,12 @@ struct TileArgs {
 //     compact block of the input AND of the output, instead of whole rows of
 //     one and a thin column band of the other.  GR = 1 with GC = tiles_c is
 //     plain row-band order.
+//   diagonal: workgroup g takes tile row g mod tiles_r and tile column
+//     (g / tiles_r + tile row) mod tiles_c, so consecutive workgroups differ
+//     in both tile row and tile column.  With power-of-two pitches the
+//     resident tiles then spread over all address offsets on both the read
+//     and the write side, instead of camping on the few memory channels one
+//     narrow offset range maps to.
 __host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
                                             uint32_t nblocks, uint32_t &tr,
                                             uint32_t &tc, int64_t &b) {
@@ -48,6 +58,11 @@ __host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
   const uint32_t per = a.tiles_r * a.tiles_c;
   b = (int64_t)(g / per) + a.batch_first;
   g %= per;
+  if (a.order == kOrderDiagonal) {
+    tr = g % a.tiles_r;
+    tc = (g / a.tiles_r + tr) % a.tiles_c;
+    return;
+  }
   const uint32_t GR = a.group_rows, GC = a.group_cols;
   const uint32_t band = GR * a.tiles_c;  // tiles in one full super-tile row
   const uint32_t sr = g / band, rem = g % band;

@@ -18,13 +18,14 @@ int main() {
       for (uint32_t batch : {1u, 3u})
         for (uint32_t gr : {1u, 2u, 3u, 8u, 16u, 1000u})
           for (uint32_t gc : {1u, 3u, 8u, 32u, 1000u})
-            for (int xcd = 0; xcd < 2; ++xcd) {
+            for (int xcd = 0; xcd < 4; ++xcd) {
               xpose::TileArgs a = {};
+              a.order = xcd < 2 ? xpose::kOrderSuperTiles : xpose::kOrderDiagonal;
               a.tiles_r = tr_n;
               a.tiles_c = tc_n;
               a.group_rows = gr < tr_n ? gr : tr_n;
               a.group_cols = gc < tc_n ? gc : tc_n;
-              a.xcd_remap = xcd;
+              a.xcd_remap = xcd & 1;
               const uint32_t n = batch * tr_n * tc_n;
               std::vector<int> hit(n, 0);
               for (uint32_t blk = 0; blk < n; ++blk) {

@@ -179,3 +179,23 @@ def test_one_hip_runtime_per_process():
                          text=True, cwd=ROOT, timeout=300)
     assert out.returncode == 0, out.stderr[-500:]
     assert out.stdout.strip() == "1"
+
+
+def test_footprint_rules():
+    # Over 512 MiB moved per call: the diagonal tile order.
+    rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F16)
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert (info.tile_rows, info.tile_cols) == (128, 64) and info.xcd_remap == 0
+    rc, info = plan(rows=16384, cols=8192)
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    # 8192^2 fp32 moves exactly 512 MiB: compact super-tiles.
+    rc, info = plan(rows=8192, cols=8192)
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    # A batch of small matrices keeps super-tiles even when the call is big.
+    rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
+                    stride_out=1024 * 2048)
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    # Explicit order wins.
+    rc, info = plan(opts=X.make_opts(order=X.ORDER_DIAGONAL))
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert plan(opts=X.make_opts(order=3))[0] == X.XPOSE_EINVAL

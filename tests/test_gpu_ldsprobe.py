@@ -55,7 +55,7 @@ def test_probe_matches_measured_bank_model():
             elif deg >= 8:
                 group = GFX950[(width, wr)][1]
                 assert cyc >= 0.75 * deg * (64 // group), name
-                assert cyc >= 2.0 * ref, name
+                assert cyc > ref, name
                 checked += 1
     assert checked >= 20
 

@@ -239,6 +239,13 @@ def test_tile_orders_and_cache_policies(s):
                            opts=opts, label=f"order {tag}")
                 check_case(s, 3, 301, 257, seed=gr + gc + flags, opts=opts,
                            label=f"order-batch {tag}")
+        for flags in (X.FLAG_XCD_REMAP, X.FLAG_NO_XCD_REMAP):
+            opts = X.make_opts(X.LAYOUT_SWIZZLE, None, flags, cache,
+                               order=X.ORDER_DIAGONAL)
+            check_case(s, 1, 777, 555, seed=cache + flags, opts=opts,
+                       label=f"diagonal c{cache} f{flags}")
+            check_case(s, 3, 301, 257, seed=cache + flags + 1, opts=opts,
+                       label=f"diagonal-batch c{cache} f{flags}")
 
 
 def test_copy_variants():
