@@ -38,8 +38,8 @@ import workloads as wl  # noqa: E402
 METRIC = ("effective GB/s (R+W bytes) and % of HBM peak, 8192x8192 fp32 "
           "transpose, 1 GPU")
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "lds_tiled_matrix_amd", "csrc",
-                             "xpose_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "lds_tiled_matrix_amd", "csrc", f)
+                  for f in ("xpose_kernels.hip", "xpose_kernels.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_8192_f32.md")
 SIGNED = {1: np.int8, 2: np.int16, 4: np.int32, 8: np.int64}
 
@@ -49,8 +49,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the device code (kernels and the tile-order header)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -227,10 +231,14 @@ def bench_workload(X, w, steps, warmup, stream, layouts=True, cold=True):
         _, durs_m = time_launches(lambda: yb.copy_(xb), stream, n_small, warmup)
         res["memcpy_d2d"] = summarize(durs_m, nbytes)
         if layouts:
+            # The pages' record set: the copy, the tile with and without the
+            # pad (and the swizzle), and the better of the two naive kernels.
             res["ablation"] = {}
-            for lay, name in X.LAYOUT_NAMES.items():
+            for lay, name in list(X.LAYOUT_NAMES.items()) + list(X.NAIVE_NAMES.items()):
                 _, d = time_launches(launch_with(X.XposeOpts(lay, 0, 0, 0)),
-                                     stream, n_small, warmup)
+                                     stream, max(10, n_small // 5) if lay > 3
+                                     else n_small, min(warmup, 3) if lay > 3
+                                     else warmup)
                 res["ablation"][name] = summarize(d, nbytes)
         if cold:
             flush = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
@@ -366,8 +374,8 @@ def main(argv=None):
             torch.cuda.empty_cache()
         log("| workload | kernel | R+W bytes | median us | GB/s | % 8 TB/s | "
             "copy GB/s | % copy | cold GB/s | cold copy GB/s | unpadded | "
-            "pad1 | swizzle |")
-        log("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+            "pad1 | swizzle | naive (best) |")
+        log("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
         for key, b, dd, cp, ab, cd, pl in rows:
             g = dd["median_GBps"]
             kern = (f"{pl['tile_rows']}x{pl['tile_cols']} "
@@ -377,7 +385,8 @@ def main(argv=None):
                 f"{100 * g / cp['median_GBps']:.1f} | "
                 f"{cd['transpose']['median_GBps']} | {cd['copy']['median_GBps']} | "
                 f"{ab['unpadded']['median_GBps']} | {ab['pad1']['median_GBps']} | "
-                f"{ab['swizzle']['median_GBps']} |")
+                f"{ab['swizzle']['median_GBps']} | "
+                f"{max(ab['naive_read_coalesced']['median_GBps'], ab['naive_write_coalesced']['median_GBps'])} |")
     return 0 if parity is not False else 3
 
 

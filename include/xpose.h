@@ -77,7 +77,12 @@ typedef enum xpose_layout {
   XPOSE_LAYOUT_AUTO = 0,     /* library default (the measured best)          */
   XPOSE_LAYOUT_UNPADDED = 1, /* row stride = tile width (conflicted column read) */
   XPOSE_LAYOUT_PAD1 = 2,     /* row stride = tile width + one 32-bit word     */
-  XPOSE_LAYOUT_SWIZZLE = 3   /* 16-byte chunks XOR-permuted per row            */
+  XPOSE_LAYOUT_SWIZZLE = 3,  /* 16-byte chunks XOR-permuted per row            */
+  /* Not tiled, for the ablation only: one element per thread, no LDS, so one
+   * of the two global sides is uncoalesced (tile, cache and order options
+   * are ignored). */
+  XPOSE_LAYOUT_NAIVE_READ = 4,  /* threads along input rows: reads coalesced */
+  XPOSE_LAYOUT_NAIVE_WRITE = 5  /* threads along input columns: writes coalesced */
 } xpose_layout;
 
 /* Cache policy of the global accesses.  The data is touched exactly once,

@@ -25,8 +25,11 @@ XPOSE_OK = 0
 XPOSE_EINVAL, XPOSE_EALIAS, XPOSE_EDTYPE = -1, -2, -3
 XPOSE_EHIP, XPOSE_EALIGN, XPOSE_ENOTILE = -4, -5, -6
 LAYOUT_AUTO, LAYOUT_UNPADDED, LAYOUT_PAD1, LAYOUT_SWIZZLE = 0, 1, 2, 3
+LAYOUT_NAIVE_READ, LAYOUT_NAIVE_WRITE = 4, 5
 LAYOUT_NAMES = {LAYOUT_UNPADDED: "unpadded", LAYOUT_PAD1: "pad1",
                 LAYOUT_SWIZZLE: "swizzle"}
+NAIVE_NAMES = {LAYOUT_NAIVE_READ: "naive_read_coalesced",
+               LAYOUT_NAIVE_WRITE: "naive_write_coalesced"}
 FLAG_ELEMENTWISE, FLAG_XCD_REMAP, FLAG_NO_XCD_REMAP = 1, 2, 4
 CACHE_AUTO, CACHE_DEFAULT, CACHE_NT_STORE, CACHE_NT_ALL = 0, 1, 2, 3
 ORDER_AUTO, ORDER_SUPER_TILES, ORDER_DIAGONAL = 0, 1, 2

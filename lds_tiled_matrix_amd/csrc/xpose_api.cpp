@@ -106,7 +106,9 @@ bool extent(int64_t count, int64_t r, int64_t c, int64_t ld, int64_t st,
 }
 
 struct Plan {
-  const xpose::TileKernel *kernel;
+  const xpose::TileKernel *kernel;  // null for the naive kernels
+  int naive;                        // 0, xpose::kNaiveRead or kNaiveWrite
+  int elem_bytes;
   xpose::TileArgs args;
   int64_t batch;
   int64_t tiles_per_matrix;
@@ -125,7 +127,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const int known_flags =
       XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP | XPOSE_FLAG_NO_XCD_REMAP;
   if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
-               opts->layout > XPOSE_LAYOUT_SWIZZLE ||
+               opts->layout > XPOSE_LAYOUT_NAIVE_WRITE ||
                (opts->flags & ~known_flags) != 0 ||
                ((opts->flags & XPOSE_FLAG_XCD_REMAP) &&
                 (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) ||
@@ -185,6 +187,24 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   }
   if (opts && opts->threads) nt = opts->threads;
   const int cache = (opts && opts->cache) ? opts->cache : d.cache;
+  plan->elem_bytes = s;
+  if (layout == XPOSE_LAYOUT_NAIVE_READ || layout == XPOSE_LAYOUT_NAIVE_WRITE) {
+    plan->naive = layout;
+    plan->batch = batch;
+    xpose::TileArgs &a = plan->args;
+    a.out = const_cast<void *>(out);
+    a.in = in;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld_in = ld_in;
+    a.ld_out = ld_out;
+    a.stride_in = stride_in;
+    a.stride_out = stride_out;
+    const int64_t run = layout == XPOSE_LAYOUT_NAIVE_READ ? cols : rows;
+    const int64_t other = layout == XPOSE_LAYOUT_NAIVE_READ ? rows : cols;
+    plan->tiles_per_matrix = (run + 255) / 256 * other;
+    return XPOSE_OK;
+  }
   int n = 0;
   const xpose::TileKernel *table = xpose::tile_kernels(&n);
   const xpose::TileKernel *k = nullptr;
@@ -248,6 +268,12 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
 int run_plan(Plan &plan, void *stream) {
   if (plan.empty) return XPOSE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.naive) {
+    const hipError_t e =
+        xpose::launch_naive(plan.args, plan.batch, plan.elem_bytes,
+                            plan.naive == XPOSE_LAYOUT_NAIVE_READ, st);
+    return e == hipSuccess ? XPOSE_OK : hip_fail(e);
+  }
   for (int64_t b0 = 0; b0 < plan.batch; b0 += plan.batch_per_launch) {
     int64_t nb = plan.batch - b0;
     if (nb > plan.batch_per_launch) nb = plan.batch_per_launch;
@@ -302,7 +328,16 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                            stride_in, stride_out, dtype, opts, &plan);
   if (info) {
     memset(info, 0, sizeof(*info));
-    if (rc == XPOSE_OK && !plan.empty) {
+    if (rc == XPOSE_OK && !plan.empty && plan.naive) {
+      const bool rd = plan.naive == XPOSE_LAYOUT_NAIVE_READ;
+      info->layout = plan.naive;
+      info->tile_rows = rd ? 1 : 256;
+      info->tile_cols = rd ? 256 : 1;
+      info->threads = 256;
+      info->tiles = plan.tiles_per_matrix * plan.batch;
+      info->launches = 1;
+      info->cache = XPOSE_CACHE_DEFAULT;
+    } else if (rc == XPOSE_OK && !plan.empty) {
       info->layout = plan.kernel->layout;
       info->tile_rows = plan.kernel->tile_rows;
       info->tile_cols = plan.kernel->tile_cols;

@@ -8,7 +8,13 @@
 namespace xpose {
 
 // LDS tile layouts; values match xpose_layout in include/xpose.h.
-enum Layout : int { kUnpadded = 1, kPad1 = 2, kSwizzle = 3 };
+enum Layout : int {
+  kUnpadded = 1,
+  kPad1 = 2,
+  kSwizzle = 3,
+  kNaiveRead = 4,  // no LDS: one element per thread, reads coalesced
+  kNaiveWrite = 5  // no LDS: one element per thread, writes coalesced
+};
 
 // Arguments of one tiled-transpose launch.  Sizes, pitches and strides are
 // in elements; the grid is tiles_r * tiles_c * batch_count workgroups and
@@ -82,6 +88,11 @@ struct TileKernel {
 
 // Every compiled tile kernel; *count receives the table length.
 const TileKernel *tile_kernels(int *count);
+
+// Naive one-element-per-thread transpose (no LDS), `batch` matrices from
+// a.in / a.out (a.batch_first is ignored); the ablation baseline.
+hipError_t launch_naive(const TileArgs &a, int64_t batch, int elem_bytes,
+                        bool read_coalesced, hipStream_t stream);
 
 // One compiled 128-bit copy kernel.
 struct CopyKernel {

@@ -402,6 +402,76 @@ const TileKernel *tile_kernels(int *count) {
 }
 
 // ---------------------------------------------------------------------------
+// Naive single-index transposes, the ablation baseline without LDS: one
+// element per thread.  Read-coalesced blocks run along an input row (the
+// reads are contiguous, each write lands one output row further on);
+// write-coalesced blocks run along an input column (contiguous writes,
+// strided reads).  Either way one of the two global sides is uncoalesced,
+// which is the cost the LDS tile removes ("Shared memory and the bank
+// conflict", section "Turn the tile around on chip").
+//   grid.x: 256-element runs along the coalesced side; grid.y: index along
+//   the other side (offset by `other0`); grid.z: batch entry (offset by
+//   a.batch_first).
+// ---------------------------------------------------------------------------
+constexpr int kNaiveThreads = 256;
+
+template <int S, bool READ_COALESCED>
+__global__ __launch_bounds__(kNaiveThreads) void xpose_naive_kernel(
+    TileArgs a, int64_t other0) {
+  using E = typename Elem<S>::E;
+  const int64_t run = (int64_t)blockIdx.x * kNaiveThreads + threadIdx.x;
+  const int64_t other = other0 + blockIdx.y;
+  const int64_t b = (int64_t)blockIdx.z + a.batch_first;
+  const int64_t i = READ_COALESCED ? other : run;  // input row
+  const int64_t j = READ_COALESCED ? run : other;  // input column
+  if (i >= a.rows || j >= a.cols) return;
+  const E v = static_cast<const E *>(a.in)[b * a.stride_in + i * a.ld_in + j];
+  static_cast<E *>(a.out)[b * a.stride_out + j * a.ld_out + i] = v;
+}
+
+template <int S, bool RC>
+hipError_t launch_naive_s(const TileArgs &a, int64_t batch,
+                          hipStream_t stream) {
+  const int64_t run_len = RC ? a.cols : a.rows;
+  const int64_t others = RC ? a.rows : a.cols;
+  const int64_t gx = (run_len + kNaiveThreads - 1) / kNaiveThreads;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
+    for (int64_t o0 = 0; o0 < others; o0 += 65535) {
+      TileArgs c = a;
+      c.batch_first = (uint32_t)0;
+      c.in = static_cast<const char *>(a.in) + b0 * a.stride_in * S;
+      c.out = static_cast<char *>(a.out) + b0 * a.stride_out * S;
+      int64_t off = o0;
+      const dim3 grid((uint32_t)gx,
+                      (uint32_t)(others - o0 < 65535 ? others - o0 : 65535),
+                      (uint32_t)(batch - b0 < 65535 ? batch - b0 : 65535));
+      void *args[] = {&c, &off};
+      const hipError_t e = hipLaunchKernel(
+          reinterpret_cast<const void *>(&xpose_naive_kernel<S, RC>), grid,
+          dim3(kNaiveThreads), args, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_naive(const TileArgs &a, int64_t batch, int elem_bytes,
+                        bool read_coalesced, hipStream_t stream) {
+  switch (elem_bytes) {
+    case 1: return read_coalesced ? launch_naive_s<1, true>(a, batch, stream)
+                                  : launch_naive_s<1, false>(a, batch, stream);
+    case 2: return read_coalesced ? launch_naive_s<2, true>(a, batch, stream)
+                                  : launch_naive_s<2, false>(a, batch, stream);
+    case 4: return read_coalesced ? launch_naive_s<4, true>(a, batch, stream)
+                                  : launch_naive_s<4, false>(a, batch, stream);
+    case 8: return read_coalesced ? launch_naive_s<8, true>(a, batch, stream)
+                                  : launch_naive_s<8, false>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Copy yardstick.  Each workgroup moves NT * UNROLL 16-byte vectors of one
 // contiguous range, issuing all its loads before its stores, exactly the
 // access widths the transpose uses.  The default (256 threads x 4) moves the

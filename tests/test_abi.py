@@ -199,3 +199,12 @@ def test_footprint_rules():
     rc, info = plan(opts=X.make_opts(order=X.ORDER_DIAGONAL))
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
     assert plan(opts=X.make_opts(order=3))[0] == X.XPOSE_EINVAL
+
+
+def test_naive_plans():
+    rc, info = plan(rows=100, cols=700, opts=X.XposeOpts(X.LAYOUT_NAIVE_READ, 0, 0, 0))
+    assert rc == 0 and info.layout == X.LAYOUT_NAIVE_READ and info.lds_bytes == 0
+    assert info.tiles == 3 * 100
+    rc, info = plan(rows=100, cols=700, opts=X.XposeOpts(X.LAYOUT_NAIVE_WRITE, 0, 0, 0))
+    assert rc == 0 and info.tiles == 1 * 700
+    assert plan(opts=X.XposeOpts(6, 0, 0, 0))[0] == X.XPOSE_EINVAL

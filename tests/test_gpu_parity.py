@@ -230,7 +230,7 @@ def test_copy_kernel():
 def test_tile_orders_and_cache_policies(s):
     """Tile enumeration order, XCD remap and non-temporal accesses change
     only the schedule: results stay bit-exact, batches included."""
-    for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE, X.CACHE_NT_ALL):
+    for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE):
         for gr, gc in ((1, 0), (3, 0), (1000, 0), (2, 3), (4, 1), (5, 1000)):
             for flags in (X.FLAG_XCD_REMAP, X.FLAG_NO_XCD_REMAP):
                 opts = X.make_opts(X.LAYOUT_SWIZZLE, None, flags, cache, gr, gc)
@@ -246,6 +246,27 @@ def test_tile_orders_and_cache_policies(s):
                        label=f"diagonal c{cache} f{flags}")
             check_case(s, 3, 301, 257, seed=cache + flags + 1, opts=opts,
                        label=f"diagonal-batch c{cache} f{flags}")
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_naive_kernels(s):
+    """The two no-LDS ablation kernels give the same bits as the oracle."""
+    for layout in (X.LAYOUT_NAIVE_READ, X.LAYOUT_NAIVE_WRITE):
+        opts = X.XposeOpts(layout, 0, 0, 0)
+        for r, c in ((1, 1), (33, 257), (300, 70), (1, 600), (600, 1)):
+            check_case(s, 1, r, c, seed=r + c + layout, opts=opts,
+                       label=f"naive{layout}")
+        check_case(s, 3, 70, 45, ld_in=50, ld_out=80, stride_in=70 * 50 + 7,
+                   stride_out=45 * 80 + 3, seed=layout, opts=opts,
+                   label=f"naive{layout}-batch")
+
+
+def test_nontemporal_loads_variant():
+    """Non-temporal loads and stores are built for two fp32 tiles only."""
+    for tile in ((32, 32), (64, 64)):
+        opts = X.make_opts(X.LAYOUT_SWIZZLE, tile, 0, X.CACHE_NT_ALL)
+        check_case(4, 1, 777, 555, seed=9, opts=opts, label=f"nt-all {tile}")
+        check_case(4, 2, 256, 512, seed=10, opts=opts, label=f"nt-all {tile}")
 
 
 def test_copy_variants():
