@@ -125,6 +125,11 @@ typedef struct xpose_opts {
   int32_t threads;    /* workgroup size of the tile kernel; 0 = the default
                          (with an explicit tile: the largest one built)     */
   int32_t order;      /* xpose_order                                         */
+  int32_t persistent; /* 0 = one workgroup per tile (default); n > 0 = n
+                         persistent workgroups per compute unit, each
+                         walking many tiles with two LDS buffers so the
+                         next tile's loads overlap the current tile's
+                         stores (swizzled layout only)                      */
 } xpose_opts;
 
 /* What xpose_plan reports about the kernel a call would launch. */
@@ -143,6 +148,7 @@ typedef struct xpose_plan_info {
   int32_t group_cols;  /* resolved super-tile width in tiles                  */
   int32_t xcd_remap;   /* 1 if tiles are remapped per XCD                    */
   int32_t order;       /* resolved xpose_order                               */
+  int32_t persistent;  /* persistent workgroups per compute unit, 0 = none   */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

@@ -47,7 +47,7 @@ class XposeOpts(ctypes.Structure):
                 ("tile_cols", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
                 ("group_cols", ctypes.c_int32), ("threads", ctypes.c_int32),
-                ("order", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("persistent", ctypes.c_int32)]
 
 
 class XposeCopyOpts(ctypes.Structure):
@@ -62,7 +62,7 @@ class XposePlanInfo(ctypes.Structure):
                 ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
                 ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
                 ("group_cols", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("order", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("persistent", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -124,11 +124,11 @@ def _check(code: int, what: str) -> int:
 
 
 def make_opts(layout=LAYOUT_AUTO, tile=None, flags=0, cache=CACHE_AUTO,
-              group_rows=0, group_cols=0, threads=0,
-              order=ORDER_AUTO) -> XposeOpts:
+              group_rows=0, group_cols=0, threads=0, order=ORDER_AUTO,
+              persistent=0) -> XposeOpts:
     tr, tc = tile if tile else (0, 0)
     return XposeOpts(layout, tr, tc, flags, cache, group_rows, group_cols,
-                     threads, order)
+                     threads, order, persistent)
 
 
 # ----- C ABI, one to one -----------------------------------------------------
@@ -215,7 +215,7 @@ def _stream_handle(stream) -> int:
 
 def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
               flags: int = 0, cache: int = CACHE_AUTO, group_rows: int = 0,
-              stream=None):
+              order: int = ORDER_AUTO, persistent: int = 0, stream=None):
     """Transpose the last two dims of a 2-D or 3-D CUDA tensor whose last dim
     is contiguous.  Row pitches and the batch stride are taken from the
     tensor's strides.  Returns ``out`` (allocated contiguous if None)."""
@@ -238,8 +238,10 @@ def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
     stride_in = x.stride(0) if x.dim() == 3 else 0
     stride_out = out.stride(0) if out.dim() == 3 else 0
     code = dtype_code(x.dtype)
-    opts = (make_opts(layout, tile, flags, cache, group_rows)
-            if (layout or tile or flags or cache or group_rows) else None)
+    opts = (make_opts(layout, tile, flags, cache, group_rows, 0, 0, order,
+                      persistent)
+            if (layout or tile or flags or cache or group_rows or order
+                or persistent) else None)
     _check(xpose_batched_ex(out.data_ptr(), x.data_ptr(), batch, rows, cols,
                             ld_in, ld_out, stride_in, stride_out, code, opts,
                             _stream_handle(stream)), "xpose_batched_ex")

@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "xpose_kernels.h"
 
 namespace {
@@ -107,6 +109,7 @@ bool extent(int64_t count, int64_t r, int64_t c, int64_t ld, int64_t st,
 
 struct Plan {
   const xpose::TileKernel *kernel;  // null for the naive kernels
+  int persistent;                   // persistent workgroups per CU, 0 = none
   int naive;                        // 0, xpose::kNaiveRead or kNaiveWrite
   int elem_bytes;
   xpose::TileArgs args;
@@ -134,7 +137,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                opts->cache < XPOSE_CACHE_AUTO ||
                opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
                opts->group_cols < 0 || opts->threads < 0 ||
-               opts->order < XPOSE_ORDER_AUTO ||
+               opts->order < XPOSE_ORDER_AUTO || opts->persistent < 0 ||
+               opts->persistent > 64 ||
                opts->order > XPOSE_ORDER_DIAGONAL ||
                opts->tile_rows < 0 || opts->tile_cols < 0))
     return XPOSE_EINVAL;
@@ -215,6 +219,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
         (nt ? table[i].threads == nt : (!k || table[i].threads > k->threads)))
       k = &table[i];
   if (!k) return XPOSE_ENOTILE;
+  const int persistent = opts ? opts->persistent : 0;
+  if (persistent && !k->launch_persistent) return XPOSE_ENOTILE;
 
   const int64_t tiles_r = (rows + tr - 1) / tr;
   const int64_t tiles_c = (cols + tc - 1) / tc;
@@ -242,6 +248,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (opts && (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) xcd = 0;
 
   plan->kernel = k;
+  plan->persistent = persistent;
   plan->batch = batch;
   plan->tiles_per_matrix = tiles;
   plan->batch_per_launch = 0x7fffffff / tiles;
@@ -265,6 +272,28 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   return XPOSE_OK;
 }
 
+// Compute units of the current device, looked up once per device.
+hipError_t compute_units(int *out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return hipSuccess;
+}
+
 int run_plan(Plan &plan, void *stream) {
   if (plan.empty) return XPOSE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -283,8 +312,22 @@ int run_plan(Plan &plan, void *stream) {
     const int s = plan.kernel->elem_bytes;
     a.in = static_cast<const char *>(a.in) + b0 * a.stride_in * s;
     a.out = static_cast<char *>(a.out) + b0 * a.stride_out * s;
-    const hipError_t e =
-        plan.kernel->launch(a, (uint32_t)(nb * plan.tiles_per_matrix), st);
+    const uint32_t ntiles = (uint32_t)(nb * plan.tiles_per_matrix);
+    hipError_t e;
+    if (plan.persistent) {
+      int cus = 0;
+      e = compute_units(&cus);
+      if (e != hipSuccess) return hip_fail(e);
+      // A multiple of 8, so each tile stays on the XCD the remap gives it;
+      // no more than the tiles need.
+      int64_t grid = (int64_t)plan.persistent * cus;
+      const int64_t cap = ((int64_t)ntiles + 7) / 8 * 8;
+      if (grid > cap) grid = cap;
+      grid = (grid + 7) / 8 * 8;
+      e = plan.kernel->launch_persistent(a, ntiles, (uint32_t)grid, st);
+    } else {
+      e = plan.kernel->launch(a, ntiles, st);
+    }
     if (e != hipSuccess) return hip_fail(e);
   }
   return XPOSE_OK;
@@ -351,6 +394,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->group_rows = (int32_t)plan.args.group_rows;
       info->group_cols = (int32_t)plan.args.group_cols;
       info->order = plan.args.order;
+      info->persistent = plan.persistent;
       info->xcd_remap = plan.args.xcd_remap;
     }
   }

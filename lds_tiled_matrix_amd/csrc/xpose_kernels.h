@@ -83,7 +83,13 @@ __host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
 // One compiled tile kernel.
 struct TileKernel {
   int elem_bytes, tile_rows, tile_cols, threads, layout, cache, lds_bytes;
+  // One workgroup per tile: grid = tiles.
   hipError_t (*launch)(const TileArgs &, uint32_t grid, hipStream_t);
+  // Persistent, double-buffered variant (null if not built): `grid`
+  // workgroups (a multiple of 8) walk `ntiles` tiles; LDS use is twice
+  // lds_bytes.
+  hipError_t (*launch_persistent)(const TileArgs &, uint32_t ntiles,
+                                  uint32_t grid, hipStream_t);
 };
 
 // Every compiled tile kernel; *count receives the table length.

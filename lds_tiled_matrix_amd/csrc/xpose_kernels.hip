@@ -230,32 +230,54 @@ __device__ __forceinline__ u32x4 read_column(const typename T::U *lds, int c,
 }
 
 // Interior tile, rows 4-byte aligned: 128-bit global accesses throughout.
+// Split in three so the persistent kernel can keep the next tile's loads in
+// flight while it drains the current one.
 template <class T>
-__device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
-                                            char *dst, int64_t ld_in,
-                                            int64_t ld_out, int wave,
-                                            int lane) {
+struct TileRegs {
+  u32x4 v[T::LIT][T::K];
+};
+
+// Phase 1a: 16-byte row loads of one tile into registers.
+template <class T>
+__device__ __forceinline__ void vector_load(const char *src, int64_t ld_in,
+                                            int wave, int lane,
+                                            TileRegs<T> &r) {
   constexpr int S = (int)sizeof(typename T::E);
   constexpr bool LSPLIT = !T::WIDE_WRITE;
-  u32x4 v[T::LIT][T::K];
 #pragma unroll
   for (int it = 0; it < T::LIT; ++it) {
     int p, ch;
     lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
 #pragma unroll
     for (int k = 0; k < T::K; ++k)
-      v[it][k] = load16<T::CACHE>(
+      r.v[it][k] = load16<T::CACHE>(
           src + ((int64_t)(p * T::K + k) * ld_in + ch * T::V) * S);
   }
+}
+
+// Phase 1b: registers -> LDS tile (after the K x K packing).
+template <class T>
+__device__ __forceinline__ void vector_to_lds(typename T::U *lds,
+                                              const TileRegs<T> &r, int wave,
+                                              int lane) {
+  constexpr int S = (int)sizeof(typename T::E);
+  constexpr bool LSPLIT = !T::WIDE_WRITE;
 #pragma unroll
   for (int it = 0; it < T::LIT; ++it) {
     int p, ch;
     lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
     typename T::U u[T::V];
-    pack_units<S>(v[it], u);
+    pack_units<S>(r.v[it], u);
     write_units<T>(lds, p, ch * T::V, u);
   }
-  __syncthreads();
+}
+
+// Phase 2: column gathers from LDS -> 16-byte row stores.
+template <class T>
+__device__ __forceinline__ void lds_to_global(const typename T::U *lds,
+                                              char *dst, int64_t ld_out,
+                                              int wave, int lane) {
+  constexpr int S = (int)sizeof(typename T::E);
 #pragma unroll
   for (int it = 0; it < T::SIT; ++it) {
     int c, q;
@@ -263,6 +285,18 @@ __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
     const u32x4 o = read_column<T>(lds, c, q);
     store16<T::CACHE>(dst + ((int64_t)c * ld_out + q * T::V) * S, o);
   }
+}
+
+template <class T>
+__device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
+                                            char *dst, int64_t ld_in,
+                                            int64_t ld_out, int wave,
+                                            int lane) {
+  TileRegs<T> r;
+  vector_load<T>(src, ld_in, wave, lane, r);
+  vector_to_lds<T>(lds, r, wave, lane);
+  __syncthreads();
+  lds_to_global<T>(lds, dst, ld_out, wave, lane);
 }
 
 // Edge tile (or unaligned rows): the same LDS tile and lane maps, but every
@@ -320,31 +354,92 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
   }
 }
 
+// Where one tile lives.
+struct TileSpot {
+  const char *src;
+  char *dst;
+  int64_t rows_left, cols_left;
+  bool vec;  // interior tile on the 128-bit path
+};
+
+template <int S, int TR, int TC>
+__device__ __forceinline__ TileSpot tile_spot(const TileArgs &a, uint32_t t,
+                                              uint32_t ntiles) {
+  uint32_t tr, tc;
+  int64_t b;
+  tile_coords(a, t, ntiles, tr, tc, b);
+  const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
+  TileSpot p;
+  p.src = static_cast<const char *>(a.in) +
+          (b * a.stride_in + r0 * a.ld_in + c0) * S;
+  p.dst = static_cast<char *>(a.out) +
+          (b * a.stride_out + c0 * a.ld_out + r0) * S;
+  p.rows_left = a.rows - r0;
+  p.cols_left = a.cols - c0;
+  p.vec = a.vec_ok && p.rows_left >= TR && p.cols_left >= TC;
+  return p;
+}
+
+// One tile per workgroup.
 template <int S, int TR, int TC, int NT, int L, int CP>
 __global__ __launch_bounds__(NT) void xpose_tile_kernel(TileArgs a) {
   using T = Tile<S, TR, TC, NT, L, CP>;
   __shared__ __attribute__((aligned(16))) typename T::U lds[T::LDS_UNITS];
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t tr, tc;
-  int64_t b;
-  tile_coords(a, blockIdx.x, gridDim.x, tr, tc, b);
-
-  const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
-  const char *src = static_cast<const char *>(a.in) +
-                    (b * a.stride_in + r0 * a.ld_in + c0) * S;
-  char *dst = static_cast<char *>(a.out) +
-              (b * a.stride_out + c0 * a.ld_out + r0) * S;
-  const int64_t rows_left = a.rows - r0, cols_left = a.cols - c0;
-
+  const TileSpot p = tile_spot<S, TR, TC>(a, blockIdx.x, gridDim.x);
   // Uniform per workgroup, so the barrier inside either path is reached by
   // every wave of the block.
-  if (a.vec_ok && rows_left >= TR && cols_left >= TC)
-    tile_vector<T>(lds, src, dst, a.ld_in, a.ld_out, wave, lane);
+  if (p.vec)
+    tile_vector<T>(lds, p.src, p.dst, a.ld_in, a.ld_out, wave, lane);
   else
-    tile_elementwise<T>(lds, src, dst, a.ld_in, a.ld_out, rows_left,
-                        cols_left, wave, lane);
+    tile_elementwise<T>(lds, p.src, p.dst, a.ld_in, a.ld_out, p.rows_left,
+                        p.cols_left, wave, lane);
+}
+
+// Persistent workgroups: workgroup w handles tiles w, w + G, w + 2G, ... of
+// `ntiles` (G = gridDim.x, a multiple of 8 so every tile stays on the XCD the
+// per-XCD remap assigns it to).  Two LDS buffers alternate between
+// consecutive tiles, and the next tile's loads are issued right after the
+// current tile's barrier, so they are in flight while the current tile is
+// gathered and stored.  One barrier per tile is enough: buffer b is written
+// again two tiles later, after the intervening tile's barrier, which every
+// wave reaches only once it has finished reading b (the overwrite-before-
+// last-read hazard of "Shared-memory tiling and bank conflicts", section
+// "Protect tile phases and account for capacity").
+template <int S, int TR, int TC, int NT, int L, int CP>
+__global__ __launch_bounds__(NT) void xpose_tile_persistent_kernel(
+    TileArgs a, uint32_t ntiles) {
+  using T = Tile<S, TR, TC, NT, L, CP>;
+  __shared__ __attribute__((aligned(16))) typename T::U lds[2][T::LDS_UNITS];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t t = blockIdx.x;
+  if (t >= ntiles) return;  // uniform per workgroup
+  TileSpot cur = tile_spot<S, TR, TC>(a, t, ntiles);
+  TileRegs<T> r;
+  if (cur.vec) vector_load<T>(cur.src, a.ld_in, wave, lane, r);
+  int buf = 0;
+  for (;;) {
+    const uint32_t tn = t + gridDim.x;
+    const bool more = tn < ntiles;
+    TileSpot next;
+    if (more) next = tile_spot<S, TR, TC>(a, tn, ntiles);
+    if (cur.vec) {
+      vector_to_lds<T>(lds[buf], r, wave, lane);
+      __syncthreads();
+      if (more && next.vec) vector_load<T>(next.src, a.ld_in, wave, lane, r);
+      lds_to_global<T>(lds[buf], cur.dst, a.ld_out, wave, lane);
+    } else {
+      tile_elementwise<T>(lds[buf], cur.src, cur.dst, a.ld_in, a.ld_out,
+                          cur.rows_left, cur.cols_left, wave, lane);
+      if (more && next.vec) vector_load<T>(next.src, a.ld_in, wave, lane, r);
+    }
+    if (!more) break;
+    cur = next;
+    t = tn;
+    buf ^= 1;
+  }
 }
 
 template <int S, int TR, int TC, int NT, int L, int CP>
@@ -358,18 +453,37 @@ hipError_t launch_tile(const TileArgs &a, uint32_t grid, hipStream_t stream) {
       dim3(grid), dim3(NT), args, 0, stream);
 }
 
+template <int S, int TR, int TC, int NT, int L, int CP>
+hipError_t launch_tile_persistent(const TileArgs &a, uint32_t ntiles,
+                                  uint32_t grid, hipStream_t stream) {
+  TileArgs copy = a;
+  uint32_t n = ntiles;
+  void *args[] = {&copy, &n};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(
+          &xpose_tile_persistent_kernel<S, TR, TC, NT, L, CP>),
+      dim3(grid), dim3(NT), args, 0, stream);
+}
+
 #define XPOSE_TILE(S, TR, TC, NT, L, CP)                                    \
   TileKernel {                                                              \
     S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
-        &launch_tile<S, TR, TC, NT, L, CP>                                  \
+        &launch_tile<S, TR, TC, NT, L, CP>, nullptr                         \
+  }
+// Also built as a persistent, double-buffered kernel.
+#define XPOSE_TILE_P(S, TR, TC, NT, L, CP)                                  \
+  TileKernel {                                                              \
+    S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
+        &launch_tile<S, TR, TC, NT, L, CP>,                                 \
+        &launch_tile_persistent<S, TR, TC, NT, L, CP>                       \
   }
 // Every layout with plain caching and with non-temporal stores (so the
 // layout ablation compares like with like).
 #define XPOSE_TILES(S, TR, TC, NT)                                          \
-  XPOSE_TILE(S, TR, TC, NT, kSwizzle, kCacheDefault),                       \
+  XPOSE_TILE_P(S, TR, TC, NT, kSwizzle, kCacheDefault),                     \
       XPOSE_TILE(S, TR, TC, NT, kPad1, kCacheDefault),                      \
       XPOSE_TILE(S, TR, TC, NT, kUnpadded, kCacheDefault),                  \
-      XPOSE_TILE(S, TR, TC, NT, kSwizzle, kNtStore),                        \
+      XPOSE_TILE_P(S, TR, TC, NT, kSwizzle, kNtStore),                      \
       XPOSE_TILE(S, TR, TC, NT, kPad1, kNtStore),                           \
       XPOSE_TILE(S, TR, TC, NT, kUnpadded, kNtStore)
 

@@ -208,3 +208,12 @@ def test_naive_plans():
     rc, info = plan(rows=100, cols=700, opts=X.XposeOpts(X.LAYOUT_NAIVE_WRITE, 0, 0, 0))
     assert rc == 0 and info.tiles == 1 * 700
     assert plan(opts=X.XposeOpts(6, 0, 0, 0))[0] == X.XPOSE_EINVAL
+
+
+def test_persistent_option():
+    rc, info = plan(opts=X.make_opts(persistent=4))
+    assert rc == 0 and info.persistent == 4
+    # only the swizzled layout is built persistent
+    assert plan(opts=X.make_opts(layout=X.LAYOUT_PAD1, persistent=2))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.make_opts(persistent=-1))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.make_opts(persistent=65))[0] == X.XPOSE_EINVAL

@@ -261,6 +261,40 @@ def test_naive_kernels(s):
                    label=f"naive{layout}-batch")
 
 
+@pytest.mark.parametrize("s", SIZES)
+def test_persistent_kernels(s):
+    """Persistent double-buffered workgroups: each walks many tiles, interior
+    and edge, cycling both LDS buffers; every tile order, both cache
+    policies, batches."""
+    tiles = {4: ((32, 32), (128, 64)), 2: ((128, 64), (64, 64)),
+             1: ((128, 128),), 8: ((32, 32),)}[s]
+    for tile in tiles:
+        for per_cu in (1, 3):
+            for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE):
+                for order, flags in ((X.ORDER_SUPER_TILES, X.FLAG_XCD_REMAP),
+                                     (X.ORDER_DIAGONAL, X.FLAG_NO_XCD_REMAP)):
+                    opts = X.make_opts(X.LAYOUT_SWIZZLE, tile, flags, cache,
+                                       order=order, persistent=per_cu)
+                    tag = f"persistent {tile} x{per_cu} c{cache} o{order}"
+                    check_case(s, 1, 2000, 1777, seed=per_cu + cache + order,
+                               opts=opts, label=tag)
+                    check_case(s, 3, 301, 513, seed=7 + per_cu, opts=opts,
+                               label=tag + " batch")
+
+
+def test_persistent_repeated_index_check():
+    w = wl.WORKLOADS["c1_index_1024_f32"]
+    a = torch.from_numpy(wl.make_input(w)).to(_dev())
+    want = torch.from_numpy(oracle.transpose(wl.make_input(w))).to(_dev())
+    out = torch.empty_like(a)
+    say("persistent repeat index")
+    for per_cu in (1, 2):
+        for _ in range(50):
+            out.fill_(-1.0)
+            X.transpose(a, out, tile=(32, 32), persistent=per_cu)
+            assert torch.equal(out.view(torch.int32), want.view(torch.int32))
+
+
 def test_nontemporal_loads_variant():
     """Non-temporal loads and stores are built for two fp32 tiles only."""
     for tile in ((32, 32), (64, 64)):
