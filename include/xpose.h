@@ -106,7 +106,10 @@ typedef enum xpose_order {
 enum {
   XPOSE_FLAG_ELEMENTWISE = 1, /* force the element-wise edge path everywhere */
   XPOSE_FLAG_XCD_REMAP = 2,   /* give each XCD one contiguous range of tiles */
-  XPOSE_FLAG_NO_XCD_REMAP = 4 /* the opposite, overriding the default        */
+  XPOSE_FLAG_NO_XCD_REMAP = 4, /* the opposite, overriding the default       */
+  XPOSE_FLAG_DIRECT_LDS = 8    /* interior tiles load straight into LDS
+                                  (global_load_lds_dwordx4, 4- and 8-byte
+                                  elements, unpadded or swizzled layout)     */
 };
 
 /* Optional knobs for the measured ablation.  Zero-initialise for defaults.
@@ -149,6 +152,7 @@ typedef struct xpose_plan_info {
   int32_t xcd_remap;   /* 1 if tiles are remapped per XCD                    */
   int32_t order;       /* resolved xpose_order                               */
   int32_t persistent;  /* persistent workgroups per compute unit, 0 = none   */
+  int32_t direct_lds;  /* 1 if interior tiles load straight into LDS         */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

@@ -127,8 +127,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const int s = elem_bytes_of(dtype);
   if (s == 0) return XPOSE_EDTYPE;
   if (batch < 0 || rows < 0 || cols < 0) return XPOSE_EINVAL;
-  const int known_flags =
-      XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP | XPOSE_FLAG_NO_XCD_REMAP;
+  const int known_flags = XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP |
+                          XPOSE_FLAG_NO_XCD_REMAP | XPOSE_FLAG_DIRECT_LDS;
   if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
                opts->layout > XPOSE_LAYOUT_NAIVE_WRITE ||
                (opts->flags & ~known_flags) != 0 ||
@@ -209,13 +209,14 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     plan->tiles_per_matrix = (run + 255) / 256 * other;
     return XPOSE_OK;
   }
+  const bool direct = opts && (opts->flags & XPOSE_FLAG_DIRECT_LDS);
   int n = 0;
   const xpose::TileKernel *table = xpose::tile_kernels(&n);
   const xpose::TileKernel *k = nullptr;
   for (int i = 0; i < n; ++i)
     if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
         table[i].tile_cols == tc && table[i].layout == layout &&
-        table[i].cache == cache - 1 &&
+        table[i].cache == cache - 1 && table[i].direct_lds == direct &&
         (nt ? table[i].threads == nt : (!k || table[i].threads > k->threads)))
       k = &table[i];
   if (!k) return XPOSE_ENOTILE;
@@ -395,6 +396,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->group_cols = (int32_t)plan.args.group_cols;
       info->order = plan.args.order;
       info->persistent = plan.persistent;
+      info->direct_lds = plan.kernel->direct_lds ? 1 : 0;
       info->xcd_remap = plan.args.xcd_remap;
     }
   }

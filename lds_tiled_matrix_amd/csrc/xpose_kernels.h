@@ -90,6 +90,8 @@ struct TileKernel {
   // lds_bytes.
   hipError_t (*launch_persistent)(const TileArgs &, uint32_t ntiles,
                                   uint32_t grid, hipStream_t);
+  // Interior tiles are loaded straight into LDS (global_load_lds_dwordx4).
+  bool direct_lds;
 };
 
 // Every compiled tile kernel; *count receives the table length.

@@ -74,9 +74,12 @@ template <> struct Elem<8> { using E = uint64_t; using U = uint64_t; static cons
 // Compile-time geometry of one tile kernel.
 //   S   element bytes          TR x TC  tile in elements
 //   NT  threads per workgroup  L        LDS layout      CP  cache policy
-template <int S, int TR, int TC, int NT, int L, int CP>
+template <int S, int TR, int TC, int NT, int L, int CP, bool DIRECT = false>
 struct Tile {
   static constexpr int CACHE = CP;
+  // Interior tiles load straight from global memory into LDS
+  // (global_load_lds_dwordx4), skipping the trip through registers.
+  static constexpr bool DIRECT_LDS = DIRECT;
   using E = typename Elem<S>::E;
   using U = typename Elem<S>::U;
   static constexpr int K = Elem<S>::K;          // input rows per LDS unit
@@ -95,6 +98,8 @@ struct Tile {
   static constexpr int LDS_BYTES = LDS_UNITS * UB;
   // Row writes are 16-byte LDS stores unless the pad breaks their alignment.
   static constexpr bool WIDE_WRITE = (L != kPad1);
+  static constexpr int LAYOUT = L;
+  static constexpr int TCOLS = TC;
 
   static_assert(NT % 64 == 0, "whole wavefronts");
   static_assert(TR % V == 0 && TC % V == 0, "tile must hold whole vectors");
@@ -102,6 +107,8 @@ struct Tile {
   static_assert(LIT >= 1 && SIT >= 1, "every lane has work");
   static_assert(NCL >= 1 && (NCL & (NCL - 1)) == 0, "power-of-two chunks");
   static_assert(NCL >= K, "rotation needs at least K chunks per LDS row");
+  static_assert(!DIRECT || (K == 1 && L != kPad1 && NCI <= 64 && 64 % NCI == 0),
+                "direct loads need whole 16-byte units in contiguous LDS rows");
 
   // Unit index of logical unit (p, c) in the LDS tile.
   __device__ static __forceinline__ int lds_index(int p, int c) {
@@ -287,14 +294,49 @@ __device__ __forceinline__ void lds_to_global(const typename T::U *lds,
   }
 }
 
+// Phase 1, direct variant (4- and 8-byte elements, rows contiguous in LDS):
+// one global_load_lds_dwordx4 per wave task puts the 64 lanes' 16 bytes at
+// 64 consecutive 16-byte slots of LDS, slot l for lane l.  Lane l therefore
+// fetches the logical chunk that belongs in physical slot l: the swizzle is
+// applied to the global address instead of the LDS address (XOR is its own
+// inverse).  The permutation stays inside one tile row, so each row's loads
+// remain one contiguous, coalesced range.
+template <class T>
+__device__ __forceinline__ void direct_load_to_lds(typename T::U *lds,
+                                                   const char *src,
+                                                   int64_t ld_in, int wave,
+                                                   int lane) {
+  constexpr int S = (int)sizeof(typename T::E);
+  constexpr int RPW = 64 / T::NCI;  // tile rows per wave task
+#pragma unroll
+  for (int it = 0; it < T::LIT; ++it) {
+    const int wt = it * T::NW + wave;
+    const int p = wt * RPW + lane / T::NCI;
+    const int slot = lane % T::NCI;
+    int chunk = slot;
+    if constexpr (T::LAYOUT == kSwizzle) chunk = slot ^ ((p / T::UPV) & (T::NCL - 1));
+    const char *g = src + ((int64_t)p * ld_in + chunk * T::V) * S;
+    __builtin_amdgcn_global_load_lds(
+        g, (__attribute__((address_space(3))) void *)(lds + wt * RPW * T::TCOLS),
+        16, 0, 0);
+  }
+  // The data reaches LDS through the vector-memory path: wait for it before
+  // the barrier publishes the tile.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <class T>
 __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
                                             char *dst, int64_t ld_in,
                                             int64_t ld_out, int wave,
                                             int lane) {
-  TileRegs<T> r;
-  vector_load<T>(src, ld_in, wave, lane, r);
-  vector_to_lds<T>(lds, r, wave, lane);
+  if constexpr (T::DIRECT_LDS) {
+    direct_load_to_lds<T>(lds, src, ld_in, wave, lane);
+  } else {
+    TileRegs<T> r;
+    vector_load<T>(src, ld_in, wave, lane, r);
+    vector_to_lds<T>(lds, r, wave, lane);
+  }
   __syncthreads();
   lds_to_global<T>(lds, dst, ld_out, wave, lane);
 }
@@ -381,9 +423,9 @@ __device__ __forceinline__ TileSpot tile_spot(const TileArgs &a, uint32_t t,
 }
 
 // One tile per workgroup.
-template <int S, int TR, int TC, int NT, int L, int CP>
+template <int S, int TR, int TC, int NT, int L, int CP, bool DIRECT = false>
 __global__ __launch_bounds__(NT) void xpose_tile_kernel(TileArgs a) {
-  using T = Tile<S, TR, TC, NT, L, CP>;
+  using T = Tile<S, TR, TC, NT, L, CP, DIRECT>;
   __shared__ __attribute__((aligned(16))) typename T::U lds[T::LDS_UNITS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -442,14 +484,15 @@ __global__ __launch_bounds__(NT) void xpose_tile_persistent_kernel(
   }
 }
 
-template <int S, int TR, int TC, int NT, int L, int CP>
+template <int S, int TR, int TC, int NT, int L, int CP, bool DIRECT = false>
 hipError_t launch_tile(const TileArgs &a, uint32_t grid, hipStream_t stream) {
   TileArgs copy = a;
   void *args[] = {&copy};
   // hipLaunchKernel reports this launch's own status; the sticky
   // hipGetLastError can hold an unrelated earlier error of the process.
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(&xpose_tile_kernel<S, TR, TC, NT, L, CP>),
+      reinterpret_cast<const void *>(
+          &xpose_tile_kernel<S, TR, TC, NT, L, CP, DIRECT>),
       dim3(grid), dim3(NT), args, 0, stream);
 }
 
@@ -468,14 +511,20 @@ hipError_t launch_tile_persistent(const TileArgs &a, uint32_t ntiles,
 #define XPOSE_TILE(S, TR, TC, NT, L, CP)                                    \
   TileKernel {                                                              \
     S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
-        &launch_tile<S, TR, TC, NT, L, CP>, nullptr                         \
+        &launch_tile<S, TR, TC, NT, L, CP>, nullptr, false                  \
+  }
+// Interior tiles loaded straight into LDS.
+#define XPOSE_TILE_D(S, TR, TC, NT, L, CP)                                  \
+  TileKernel {                                                              \
+    S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP, true>::LDS_BYTES,     \
+        &launch_tile<S, TR, TC, NT, L, CP, true>, nullptr, true             \
   }
 // Also built as a persistent, double-buffered kernel.
 #define XPOSE_TILE_P(S, TR, TC, NT, L, CP)                                  \
   TileKernel {                                                              \
     S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
         &launch_tile<S, TR, TC, NT, L, CP>,                                 \
-        &launch_tile_persistent<S, TR, TC, NT, L, CP>                       \
+        &launch_tile_persistent<S, TR, TC, NT, L, CP>, false                \
   }
 // Every layout with plain caching and with non-temporal stores (so the
 // layout ablation compares like with like).
@@ -496,6 +545,15 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILES(4, 128, 128, 256), XPOSE_TILES(4, 32, 128, 256),
     XPOSE_TILES(4, 128, 32, 256),
     XPOSE_TILE(4, 32, 32, 256, kSwizzle, kNtLoadStore),
+    XPOSE_TILE_D(4, 32, 32, 256, kSwizzle, kNtStore),
+    XPOSE_TILE_D(4, 32, 32, 256, kSwizzle, kCacheDefault),
+    XPOSE_TILE_D(4, 32, 32, 256, kUnpadded, kNtStore),
+    XPOSE_TILE_D(4, 64, 64, 256, kSwizzle, kNtStore),
+    XPOSE_TILE_D(4, 64, 64, 256, kSwizzle, kCacheDefault),
+    XPOSE_TILE_D(4, 128, 64, 256, kSwizzle, kNtStore),
+    XPOSE_TILE_D(4, 128, 64, 256, kSwizzle, kCacheDefault),
+    XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kNtStore),
+    XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kCacheDefault),
     XPOSE_TILE(4, 64, 64, 256, kSwizzle, kNtLoadStore),
     // 2-byte elements
     XPOSE_TILES(2, 32, 32, 64), XPOSE_TILES(2, 32, 64, 128),

@@ -152,7 +152,7 @@ def test_opts_select_layout_and_tile():
     assert plan(opts=X.make_opts(tile=(32, 32), threads=96))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(0, 48, 48, 0))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(9, 0, 0, 0))[0] == X.XPOSE_EINVAL
-    assert plan(opts=X.XposeOpts(0, 0, 0, 8))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.XposeOpts(0, 0, 0, 16))[0] == X.XPOSE_EINVAL
 
 
 def test_large_batch_splits_launches():
@@ -217,3 +217,13 @@ def test_persistent_option():
     assert plan(opts=X.make_opts(layout=X.LAYOUT_PAD1, persistent=2))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.make_opts(persistent=-1))[0] == X.XPOSE_EINVAL
     assert plan(opts=X.make_opts(persistent=65))[0] == X.XPOSE_EINVAL
+
+
+def test_direct_lds_option():
+    rc, info = plan(opts=X.make_opts(tile=(32, 32), flags=X.FLAG_DIRECT_LDS))
+    assert rc == 0 and info.direct_lds == 1
+    rc, info = plan(opts=X.make_opts(tile=(32, 32)))
+    assert rc == 0 and info.direct_lds == 0
+    # not built for packed sub-word elements or the padded layout
+    assert plan(dtype=X.XPOSE_F16, opts=X.make_opts(flags=X.FLAG_DIRECT_LDS))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.make_opts(layout=X.LAYOUT_PAD1, flags=X.FLAG_DIRECT_LDS))[0] == X.XPOSE_ENOTILE

@@ -295,6 +295,30 @@ def test_persistent_repeated_index_check():
             assert torch.equal(out.view(torch.int32), want.view(torch.int32))
 
 
+@pytest.mark.parametrize("s", (4, 8))
+def test_direct_lds_kernels(s):
+    """Interior tiles loaded straight into LDS with the swizzle applied on the
+    global side: bit-exact for every built shape, layout and cache policy."""
+    built = []
+    for tile in ((32, 32), (64, 64), (128, 64)):
+        for layout in (X.LAYOUT_SWIZZLE, X.LAYOUT_UNPADDED):
+            for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE):
+                opts = X.make_opts(layout, tile, X.FLAG_DIRECT_LDS, cache)
+                rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8, 8,
+                                        0, 0, DTYPE_OF_SIZE[s], opts)
+                if rc == 0:
+                    assert info.direct_lds == 1
+                    built.append((tile, layout, cache, opts))
+    assert built
+    for tile, layout, cache, opts in built:
+        tag = f"direct {tile} L{layout} c{cache}"
+        check_case(s, 1, 5 * tile[0] + 3, 3 * tile[1] + 7, seed=layout + cache,
+                   opts=opts, label=tag)
+        check_case(s, 1, 4 * tile[0], 4 * tile[1], seed=11, opts=opts, label=tag)
+        check_case(s, 3, 2 * tile[0] + 1, 2 * tile[1], seed=12, opts=opts,
+                   label=tag + " batch")
+
+
 def test_nontemporal_loads_variant():
     """Non-temporal loads and stores are built for two fp32 tiles only."""
     for tile in ((32, 32), (64, 64)):
