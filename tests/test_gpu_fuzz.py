@@ -1,0 +1,62 @@
+"""Seeded random cases through the C ABI against the oracle (GPU): random
+shapes, pitches, batch strides, pointer offsets, element sizes and every
+launch option, so that option interactions no targeted test names are
+still checked bit for bit."""
+import random
+
+import pytest
+
+from xpose_testlib import DTYPE_OF_SIZE, check_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+X = pytest.importorskip("lds_tiled_matrix_amd")
+
+TILES = ((32, 32), (64, 64), (128, 64), (64, 128), (128, 128), (32, 64),
+         (64, 32), (16, 16))
+
+
+def random_opts(rng, s):
+    """A random valid option set for element size s (None = defaults)."""
+    if rng.random() < 0.25:
+        return None
+    for _ in range(50):
+        layout = rng.choice((0, 1, 2, 3, 3, 3, 4, 5))
+        tile = rng.choice(TILES + (None,))
+        flags = rng.choice((0, 0, X.FLAG_XCD_REMAP, X.FLAG_NO_XCD_REMAP,
+                            X.FLAG_ELEMENTWISE, X.FLAG_DIRECT_LDS))
+        cache = rng.choice((0, 1, 2))
+        order = rng.choice((0, 1, 2))
+        gr, gc = rng.choice(((0, 0), (1, 0), (3, 5), (8, 32), (1000, 2)))
+        persistent = rng.choice((0, 0, 0, 1, 2))
+        opts = X.make_opts(layout, tile, flags, cache, gr, gc, 0, order,
+                           persistent)
+        rc, _ = X.xpose_plan(0x100000, 0x40000000, 1, 64, 64, 64, 64, 0, 0,
+                             DTYPE_OF_SIZE[s], opts)
+        if rc == 0:
+            return opts
+    return None
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_cases(seed):
+    rng = random.Random(1000 + seed)
+    for case in range(25):
+        s = rng.choice((1, 2, 4, 8))
+        batch = rng.choice((1, 1, 1, 2, 5))
+        rows = rng.choice((1, rng.randint(1, 40), rng.randint(1, 700),
+                           rng.randint(100, 1500)))
+        cols = rng.choice((1, rng.randint(1, 40), rng.randint(1, 700),
+                           rng.randint(100, 1500)))
+        ld_in = cols + rng.choice((0, 0, 1, 3, 16, 37))
+        ld_out = rows + rng.choice((0, 0, 1, 2, 32, 41))
+        stride_in = rows * ld_in + rng.choice((0, 0, 5, 64))
+        stride_out = cols * ld_out + rng.choice((0, 0, 3, 128))
+        opts = random_opts(rng, s)
+        check_case(s, batch, rows, cols, ld_in=ld_in, ld_out=ld_out,
+                   stride_in=stride_in, stride_out=stride_out,
+                   seed=seed * 100 + case, opts=opts,
+                   in_shift=rng.choice((0, 0, 1, 3)),
+                   out_shift=rng.choice((0, 0, 1, 2)),
+                   label=f"fuzz {seed}/{case}")
