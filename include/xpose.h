@@ -107,9 +107,20 @@ enum {
   XPOSE_FLAG_ELEMENTWISE = 1, /* force the element-wise edge path everywhere */
   XPOSE_FLAG_XCD_REMAP = 2,   /* give each XCD one contiguous range of tiles */
   XPOSE_FLAG_NO_XCD_REMAP = 4, /* the opposite, overriding the default       */
-  XPOSE_FLAG_DIRECT_LDS = 8    /* interior tiles load straight into LDS
+  XPOSE_FLAG_DIRECT_LDS = 8,   /* interior tiles load straight into LDS
                                   (global_load_lds_dwordx4, 4- and 8-byte
                                   elements, unpadded or swizzled layout)     */
+  XPOSE_FLAG_ALIGN_OUT = 16,   /* line-aligned output tiles (4-byte elements,
+                                  swizzled layout): each output row's segment
+                                  is shifted to start on a 128-byte line, so
+                                  stores are whole lines even when output
+                                  rows are not line-aligned.  The default for
+                                  4-byte elements with such output rows; with
+                                  this flag, a call whose element size, tile,
+                                  workgroup size or cache policy has no such
+                                  kernel returns XPOSE_ENOTILE                */
+  XPOSE_FLAG_NO_ALIGN_OUT = 32 /* ordinary tiles even where line-aligned output
+                                  tiles are the default                       */
 };
 
 /* Optional knobs for the measured ablation.  Zero-initialise for defaults.
@@ -153,6 +164,7 @@ typedef struct xpose_plan_info {
   int32_t order;       /* resolved xpose_order                               */
   int32_t persistent;  /* persistent workgroups per compute unit, 0 = none   */
   int32_t direct_lds;  /* 1 if interior tiles load straight into LDS         */
+  int32_t aligned_out; /* 1 if output segments are shifted onto lines        */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

@@ -44,6 +44,13 @@ int elem_bytes_of(int32_t dtype) {
 //     workgroups then cover a few whole matrices, a dense window on both the
 //     input and the output side, and a taller tile with small super-tiles
 //     streams at copy speed.
+//   align: line-aligned output tiles (each output segment shifted onto a
+//     line), the default for 4-byte elements whose output rows are not
+//     line-aligned: every store is a whole line again, so non-temporal
+//     stores win.  Explicit knobs they are not built with (another layout,
+//     elementwise or direct loads, persistent workgroups, a tile shape,
+//     workgroup size or cache policy without such a kernel) select the
+//     ordinary tiles with their own defaults instead.
 //   big: the call moves more than kBigCallBytes (read + write).  Then the
 //     256 MB memory-side cache cannot hold a useful part of the data across
 //     calls, every access goes to HBM, and the diagonal order (resident
@@ -54,6 +61,7 @@ int elem_bytes_of(int32_t dtype) {
 struct Default {
   int tile_rows, tile_cols, threads, layout, cache, group_rows, group_cols,
       xcd_remap, order;
+  bool align_out = false;
 };
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
 constexpr int64_t kBigCallBytes = 512ll << 20;
@@ -61,7 +69,9 @@ constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
               kDiag = XPOSE_ORDER_DIAGONAL, kWB = XPOSE_CACHE_DEFAULT,
               kNT = XPOSE_CACHE_NT_STORE;
 
-Default default_for(int s, bool row128, bool small, bool big) {
+Default default_for(int s, bool row128, bool small, bool big, bool align) {
+  if (s == 4 && align)
+    return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
   if (!row128) {
     switch (s) {
       case 4: return {128, 64, 256, kSwz, kWB, 32, 32, 1, kSup};
@@ -128,12 +138,17 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (s == 0) return XPOSE_EDTYPE;
   if (batch < 0 || rows < 0 || cols < 0) return XPOSE_EINVAL;
   const int known_flags = XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP |
-                          XPOSE_FLAG_NO_XCD_REMAP | XPOSE_FLAG_DIRECT_LDS;
+                          XPOSE_FLAG_NO_XCD_REMAP | XPOSE_FLAG_DIRECT_LDS |
+                          XPOSE_FLAG_ALIGN_OUT | XPOSE_FLAG_NO_ALIGN_OUT;
   if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
                opts->layout > XPOSE_LAYOUT_NAIVE_WRITE ||
                (opts->flags & ~known_flags) != 0 ||
                ((opts->flags & XPOSE_FLAG_XCD_REMAP) &&
                 (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) ||
+               ((opts->flags & XPOSE_FLAG_ALIGN_OUT) &&
+                (opts->flags & (XPOSE_FLAG_NO_ALIGN_OUT |
+                                XPOSE_FLAG_ELEMENTWISE |
+                                XPOSE_FLAG_DIRECT_LDS))) ||
                opts->cache < XPOSE_CACHE_AUTO ||
                opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
                opts->group_cols < 0 || opts->threads < 0 ||
@@ -173,24 +188,29 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     return XPOSE_EALIAS;
 
   // Kernel choice.
-  const bool row128 =
-      ((pi | po) % 128 == 0) && (ld_in * s) % 128 == 0 &&
-      (ld_out * s) % 128 == 0 &&
-      (batch == 1 || ((stride_in * s) % 128 == 0 && (stride_out * s) % 128 == 0));
+  const bool out_row128 = po % 128 == 0 && (ld_out * s) % 128 == 0 &&
+                          (batch == 1 || (stride_out * s) % 128 == 0);
+  const bool row128 = out_row128 && pi % 128 == 0 && (ld_in * s) % 128 == 0 &&
+                      (batch == 1 || (stride_in * s) % 128 == 0);
   const bool small = batch > 1 && rows * cols * s <= kSmallMatrixBytes;
   int64_t call_bytes;
   const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
                    call_bytes > kBigCallBytes;
-  Default d = default_for(s, row128, small, big);
-  int layout = (opts && opts->layout) ? opts->layout : d.layout;
-  int tr = d.tile_rows, tc = d.tile_cols, nt = d.threads;
-  if (opts && (opts->tile_rows || opts->tile_cols)) {
-    tr = opts->tile_rows;
-    tc = opts->tile_cols;
-    nt = 0;  // any built workgroup size; the largest is preferred
-  }
-  if (opts && opts->threads) nt = opts->threads;
-  const int cache = (opts && opts->cache) ? opts->cache : d.cache;
+  const bool direct = opts && (opts->flags & XPOSE_FLAG_DIRECT_LDS);
+  // Line-aligned output tiles are the default where they apply, unless a
+  // knob asks for something they are not built with; XPOSE_FLAG_ALIGN_OUT
+  // requests them outright.
+  const bool want_align = opts && (opts->flags & XPOSE_FLAG_ALIGN_OUT);
+  const bool align_ok =
+      want_align ||
+      !(opts && ((opts->flags & (XPOSE_FLAG_NO_ALIGN_OUT |
+                                 XPOSE_FLAG_ELEMENTWISE |
+                                 XPOSE_FLAG_DIRECT_LDS)) ||
+                 (opts->layout && opts->layout != XPOSE_LAYOUT_SWIZZLE) ||
+                 opts->persistent));
+  Default d = default_for(s, row128, small, big,
+                          want_align || (align_ok && !out_row128));
+  const int layout = (opts && opts->layout) ? opts->layout : d.layout;
   plan->elem_bytes = s;
   if (layout == XPOSE_LAYOUT_NAIVE_READ || layout == XPOSE_LAYOUT_NAIVE_WRITE) {
     plan->naive = layout;
@@ -209,21 +229,43 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     plan->tiles_per_matrix = (run + 255) / 256 * other;
     return XPOSE_OK;
   }
-  const bool direct = opts && (opts->flags & XPOSE_FLAG_DIRECT_LDS);
   int n = 0;
   const xpose::TileKernel *table = xpose::tile_kernels(&n);
-  const xpose::TileKernel *k = nullptr;
-  for (int i = 0; i < n; ++i)
-    if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
-        table[i].tile_cols == tc && table[i].layout == layout &&
-        table[i].cache == cache - 1 && table[i].direct_lds == direct &&
-        (nt ? table[i].threads == nt : (!k || table[i].threads > k->threads)))
-      k = &table[i];
+  auto lookup = [&](const Default &dd, bool align) {
+    int tr = dd.tile_rows, tc = dd.tile_cols, nt = dd.threads;
+    if (opts && (opts->tile_rows || opts->tile_cols)) {
+      tr = opts->tile_rows;
+      tc = opts->tile_cols;
+      nt = 0;  // any built workgroup size; the largest is preferred
+    }
+    if (opts && opts->threads) nt = opts->threads;
+    const int cache = (opts && opts->cache) ? opts->cache : dd.cache;
+    const xpose::TileKernel *k = nullptr;
+    for (int i = 0; i < n; ++i)
+      if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
+          table[i].tile_cols == tc && table[i].layout == layout &&
+          table[i].cache == cache - 1 && table[i].direct_lds == direct &&
+          table[i].aligned_out == align &&
+          (nt ? table[i].threads == nt
+              : (!k || table[i].threads > k->threads)))
+        k = &table[i];
+    return k;
+  };
+  const xpose::TileKernel *k = lookup(d, d.align_out || want_align);
+  if (!k && d.align_out && !want_align) {
+    // The explicit tile, threads or cache exist only as ordinary tiles:
+    // fall back to those, with their own defaults for the other knobs.
+    d = default_for(s, row128, small, big, false);
+    k = lookup(d, false);
+  }
   if (!k) return XPOSE_ENOTILE;
+  const int tr = k->tile_rows, tc = k->tile_cols;
   const int persistent = opts ? opts->persistent : 0;
   if (persistent && !k->launch_persistent) return XPOSE_ENOTILE;
 
-  const int64_t tiles_r = (rows + tr - 1) / tr;
+  // Line-aligned output tiles shift each segment back by up to 31 rows, so
+  // one more partial tile row may be needed to reach the last row.
+  const int64_t tiles_r = (rows + (k->aligned_out ? 31 : 0) + tr - 1) / tr;
   const int64_t tiles_c = (cols + tc - 1) / tc;
   if (tiles_r > 0x7fffffff || tiles_c > 0x7fffffff) return XPOSE_EINVAL;
   int64_t tiles;
@@ -397,6 +439,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->order = plan.args.order;
       info->persistent = plan.persistent;
       info->direct_lds = plan.kernel->direct_lds ? 1 : 0;
+      info->aligned_out = plan.kernel->aligned_out ? 1 : 0;
       info->xcd_remap = plan.args.xcd_remap;
     }
   }

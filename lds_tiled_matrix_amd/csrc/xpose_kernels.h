@@ -92,6 +92,10 @@ struct TileKernel {
                                   uint32_t grid, hipStream_t);
   // Interior tiles are loaded straight into LDS (global_load_lds_dwordx4).
   bool direct_lds;
+  // Line-aligned output tiles: each output row's segment is shifted back to
+  // start on a 128-byte line; the grid needs ceil((rows + 31) / tile_rows)
+  // tile rows (4-byte elements only).
+  bool aligned_out;
 };
 
 // Every compiled tile kernel; *count receives the table length.

@@ -508,23 +508,149 @@ hipError_t launch_tile_persistent(const TileArgs &a, uint32_t ntiles,
       dim3(grid), dim3(NT), args, 0, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Line-aligned output tiles (4-byte elements).  When output rows do not start
+// on a 128-byte line, a tile's output segments [r0, r0 + TR) straddle lines
+// at both ends; non-temporal writes of such partial lines go to memory as
+// partial lines.  Here each tile shifts its segment in output row j back by
+//   d_j = (byte address of output row j / 4) mod 32   (elements, < 32),
+// so the segment [r0 - d_j, r0 - d_j + TR) starts on a line and is whole
+// lines.  Over tile rows tr = 0 .. tiles_r - 1, with tiles_r = ceil((rows +
+// 31) / TR), the shifted segments of each output row partition [0, rows).
+// The LDS tile therefore holds TR + 32 input rows, [r0 - 32, r0 + TR): a
+// halo of one line above the tile, which the previous tile row has just
+// read (the super-tile order walks tile rows fastest).  The 16-byte XOR
+// swizzle keeps the shifted column gathers conflict-free: for each column
+// the 8 row groups a half-wave reads still cover all 8 chunk slots.
+// ---------------------------------------------------------------------------
+template <int TR, int TC, int NT, int CP>
+struct ShiftTile {
+  static constexpr int HALO = 32;             // fp32 elements per line
+  static constexpr int P = TR + HALO;         // LDS rows
+  static constexpr int NCI = TC / 4;          // 16-B chunks per input row
+  static constexpr int NCO = TR / 4;          // 16-B chunks per output segment
+  static constexpr int NCL = TC / 4;          // 16-B chunks per LDS row
+  static constexpr int NW = NT / 64;
+  static constexpr int LIT = P * NCI / NT;
+  static constexpr int SIT = TC * NCO / NT;
+  static constexpr int LDS_BYTES = P * TC * 4;
+  static_assert(TR % HALO == 0, "segments must stay line-aligned");
+  static_assert(P * NCI % NT == 0 && TC * NCO % NT == 0, "even task split");
+  static_assert(NCI <= 64 && 64 % NCI == 0, "rows fit a wave");
+  static_assert((NCL & (NCL - 1)) == 0, "power-of-two chunks");
+  __device__ static __forceinline__ int lds_index(int p, int c) {
+    return p * TC + (((c >> 2) ^ ((p >> 2) & (NCL - 1))) << 2) + (c & 3);
+  }
+};
+
+template <int TR, int TC, int NT, int CP>
+__global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
+  using T = ShiftTile<TR, TC, NT, CP>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[T::P * TC];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t tr, tc;
+  int64_t b;
+  tile_coords(a, blockIdx.x, gridDim.x, tr, tc, b);
+  const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
+  const int64_t top = r0 - T::HALO;  // input row of LDS row 0
+  const uint32_t *in = static_cast<const uint32_t *>(a.in) + b * a.stride_in;
+  uint32_t *out = static_cast<uint32_t *>(a.out) + b * a.stride_out;
+  const int64_t cols_left = a.cols - c0;
+
+  // Phase 1: rows [top, top + P) x columns [c0, c0 + TC); rows outside the
+  // matrix read as zero (they are never stored).
+  if (cols_left >= TC) {
+#pragma unroll
+    for (int it = 0; it < T::LIT; ++it) {
+      int p, ch;
+      lane_map<T::NCI, false>(it * T::NW + wave, lane, p, ch);
+      const int64_t row = top + p;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (row >= 0 && row < a.rows)
+        v = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(
+            reinterpret_cast<const char *>(in + row * a.ld_in + c0 + ch * 4));
+      *reinterpret_cast<u32x4 *>(lds + T::lds_index(p, ch * 4)) = v;
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < T::LIT; ++it) {
+      int p, ch;
+      lane_map<T::NCI, false>(it * T::NW + wave, lane, p, ch);
+      const int64_t row = top + p;
+      uint32_t e[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int col = ch * 4 + x;
+        e[x] = (row >= 0 && row < a.rows && col < cols_left)
+                   ? in[row * a.ld_in + c0 + col]
+                   : 0u;
+      }
+      *reinterpret_cast<u32x4 *>(lds + T::lds_index(p, ch * 4)) =
+          u32x4{e[0], e[1], e[2], e[3]};
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: output row j = c0 + c, line-aligned segment starting at input
+  // row r0 - d_j; chunk q holds input rows r0 - d_j + 4q .. + 3, which sit
+  // at LDS rows 32 - d_j + 4q .. + 3 (always inside [1, P)).
+#pragma unroll
+  for (int it = 0; it < T::SIT; ++it) {
+    int c, q;
+    lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
+    if (c < cols_left) {
+      uint32_t *row_out = out + (c0 + c) * a.ld_out;
+      const int d = (int)(((uintptr_t)row_out >> 2) & 31);
+      const int64_t first = r0 - d + 4 * q;  // input row of element 0
+      const int rho = T::HALO - d + 4 * q;
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) w[x] = lds[T::lds_index(rho + x, c)];
+      if (first >= 0 && first + 3 < a.rows) {
+        store16<CP>(reinterpret_cast<char *>(row_out + first),
+                    u32x4{w[0], w[1], w[2], w[3]});
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (first + x >= 0 && first + x < a.rows) row_out[first + x] = w[x];
+      }
+    }
+  }
+}
+
+template <int TR, int TC, int NT, int CP>
+hipError_t launch_shift(const TileArgs &a, uint32_t grid, hipStream_t stream) {
+  TileArgs copy = a;
+  void *args[] = {&copy};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(&xpose_shift_kernel<TR, TC, NT, CP>),
+      dim3(grid), dim3(NT), args, 0, stream);
+}
+
+#define XPOSE_SHIFT(TR, TC, NT, CP)                                         \
+  TileKernel {                                                              \
+    4, TR, TC, NT, kSwizzle, CP, ShiftTile<TR, TC, NT, CP>::LDS_BYTES,     \
+        &launch_shift<TR, TC, NT, CP>, nullptr, false, true                 \
+  }
+
 #define XPOSE_TILE(S, TR, TC, NT, L, CP)                                    \
   TileKernel {                                                              \
     S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
-        &launch_tile<S, TR, TC, NT, L, CP>, nullptr, false                  \
+        &launch_tile<S, TR, TC, NT, L, CP>, nullptr, false, false           \
   }
 // Interior tiles loaded straight into LDS.
 #define XPOSE_TILE_D(S, TR, TC, NT, L, CP)                                  \
   TileKernel {                                                              \
     S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP, true>::LDS_BYTES,     \
-        &launch_tile<S, TR, TC, NT, L, CP, true>, nullptr, true             \
+        &launch_tile<S, TR, TC, NT, L, CP, true>, nullptr, true, false      \
   }
 // Also built as a persistent, double-buffered kernel.
 #define XPOSE_TILE_P(S, TR, TC, NT, L, CP)                                  \
   TileKernel {                                                              \
     S, TR, TC, NT, L, CP, Tile<S, TR, TC, NT, L, CP>::LDS_BYTES,           \
         &launch_tile<S, TR, TC, NT, L, CP>,                                 \
-        &launch_tile_persistent<S, TR, TC, NT, L, CP>, false                \
+        &launch_tile_persistent<S, TR, TC, NT, L, CP>, false, false         \
   }
 // Every layout with plain caching and with non-temporal stores (so the
 // layout ablation compares like with like).
@@ -554,6 +680,11 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILE_D(4, 128, 64, 256, kSwizzle, kCacheDefault),
     XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kNtStore),
     XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kCacheDefault),
+    // Line-aligned output tiles (4-byte elements).
+    XPOSE_SHIFT(64, 64, 256, kNtStore), XPOSE_SHIFT(64, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(128, 64, 256, kNtStore), XPOSE_SHIFT(128, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(256, 64, 256, kNtStore), XPOSE_SHIFT(256, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(128, 32, 256, kNtStore), XPOSE_SHIFT(64, 32, 128, kNtStore),
     XPOSE_TILE(4, 64, 64, 256, kSwizzle, kNtLoadStore),
     // 2-byte elements
     XPOSE_TILES(2, 32, 32, 64), XPOSE_TILES(2, 32, 64, 128),

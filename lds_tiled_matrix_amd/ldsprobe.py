@@ -110,6 +110,15 @@ def run_transposes(out=sys.stdout):
                       f"{plan['tile_rows']}x{plan['tile_cols']} "
                       f"{X.LAYOUT_NAMES[layout]}", file=out, flush=True)
         del x
+    # Odd pitches: the default there is the line-aligned output tile, whose
+    # column gathers start at a different row offset for every column.
+    x = torch.zeros((12345, 6789), dtype=torch.float32, device="cuda")
+    plan = X.plan_for(x)
+    X.transpose(x)
+    torch.cuda.synchronize()
+    print(f"xpose  12345x6789 float32 tile {plan['tile_rows']}x"
+          f"{plan['tile_cols']} swizzle, line-aligned output "
+          f"({plan['aligned_out']})", file=out, flush=True)
 
 
 def main(argv=None):

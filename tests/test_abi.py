@@ -61,10 +61,17 @@ def test_valid_plan_defaults():
 
 
 def test_ragged_and_batched_tile_counts():
-    # Odd pitches: rows are not 16-byte aligned, a taller tile is chosen.
+    # Odd pitches: output rows are not line-aligned, so line-aligned output
+    # tiles are chosen, with one extra tile row for the shifted segments.
     rc, info = plan(rows=12345, cols=6789)
-    assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 64)
-    assert info.tiles == 97 * 107 and info.vector_path == 1
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (64, 64)
+    assert info.aligned_out == 1 and info.cache == X.CACHE_NT_STORE
+    assert info.tiles == 194 * 107 and info.vector_path == 1
+    # 12288 rows fill 192 tile rows; shifted segments need a 193rd.
+    rc, info = plan(rows=12288, cols=6789, ld_out=12289)
+    assert rc == 0 and info.aligned_out == 1 and info.tiles == 193 * 107
+    rc, info = plan(rows=12288, cols=6789)
+    assert rc == 0 and info.aligned_out == 0 and info.tiles == 96 * 107
     # A batch of small matrices: taller tiles, small super-tiles.
     rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
                     stride_out=1024 * 2048)
@@ -152,7 +159,7 @@ def test_opts_select_layout_and_tile():
     assert plan(opts=X.make_opts(tile=(32, 32), threads=96))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(0, 48, 48, 0))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(9, 0, 0, 0))[0] == X.XPOSE_EINVAL
-    assert plan(opts=X.XposeOpts(0, 0, 0, 16))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.XposeOpts(0, 0, 0, 64))[0] == X.XPOSE_EINVAL
 
 
 def test_large_batch_splits_launches():
@@ -227,3 +234,33 @@ def test_direct_lds_option():
     # not built for packed sub-word elements or the padded layout
     assert plan(dtype=X.XPOSE_F16, opts=X.make_opts(flags=X.FLAG_DIRECT_LDS))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.make_opts(layout=X.LAYOUT_PAD1, flags=X.FLAG_DIRECT_LDS))[0] == X.XPOSE_ENOTILE
+
+
+def test_align_out_option():
+    # fp32 with line-aligned output rows: the ordinary tiles
+    assert plan(rows=8192, cols=8192)[1].aligned_out == 0
+    # output pitch off the line: aligned-out tiles by default, either way
+    # selectable explicitly
+    assert plan(rows=1000, cols=512)[1].aligned_out == 1
+    assert plan(rows=1000, cols=512, opts=X.make_opts(flags=X.FLAG_NO_ALIGN_OUT))[1].aligned_out == 0
+    rc, info = plan(rows=1024, cols=512, opts=X.make_opts(tile=(64, 64), flags=X.FLAG_ALIGN_OUT))
+    assert rc == 0 and info.aligned_out == 1 and info.tiles == 17 * 8
+    # not for other element sizes or layouts, nor with contradicting flags
+    assert plan(dtype=X.XPOSE_F16, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.make_opts(layout=X.LAYOUT_PAD1, flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.make_opts(flags=X.FLAG_ALIGN_OUT | X.FLAG_ELEMENTWISE))[0] == X.XPOSE_EINVAL
+    # an explicit knob with no aligned-out kernel falls back to the ordinary
+    # tiles, with their defaults (write-back stores for unaligned rows)
+    rc, info = plan(rows=1000, cols=512, opts=X.make_opts(tile=(32, 32)))
+    assert rc == 0 and info.aligned_out == 0 and info.cache == X.CACHE_DEFAULT
+    rc, info = plan(rows=1000, cols=512, opts=X.make_opts(tile=(32, 32), cache=X.CACHE_NT_STORE))
+    assert rc == 0 and info.aligned_out == 0 and info.cache == X.CACHE_NT_STORE
+    rc, info = plan(rows=1000, cols=512, opts=X.make_opts(layout=X.LAYOUT_PAD1))
+    assert rc == 0 and info.aligned_out == 0 and info.layout == X.LAYOUT_PAD1
+    rc, info = plan(rows=1000, cols=512, opts=X.make_opts(tile=(64, 64), cache=X.CACHE_NT_ALL))
+    assert rc == 0 and info.aligned_out == 0 and info.cache == X.CACHE_NT_ALL
+    # ... but not when aligned-out tiles were asked for
+    assert plan(rows=1000, cols=512, opts=X.make_opts(tile=(32, 32), flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
+    # asked for on line-aligned rows: the aligned-out default tile
+    rc, info = plan(rows=8192, cols=8192, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))
+    assert rc == 0 and info.aligned_out == 1 and info.tiles == -(-(8192 + 31) // info.tile_rows) * (8192 // info.tile_cols)

@@ -319,6 +319,31 @@ def test_direct_lds_kernels(s):
                    label=tag + " batch")
 
 
+def test_aligned_out_kernels():
+    """Line-aligned output tiles (fp32): every built shape and cache policy,
+    output pitches and pointers at every 4-byte offset within a line, edge
+    tiles in both dimensions, batches with odd strides."""
+    built = []
+    for tile in ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32)):
+        for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE):
+            opts = X.make_opts(X.LAYOUT_SWIZZLE, tile, X.FLAG_ALIGN_OUT, cache)
+            rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8, 8, 0,
+                                    0, X.XPOSE_F32, opts)
+            if rc == 0:
+                assert info.aligned_out == 1
+                built.append((tile, cache, opts))
+    assert len(built) >= 5
+    for tile, cache, opts in built:
+        tag = f"align-out {tile} c{cache}"
+        for r, c, pad, shift in ((777, 555, 3, 0), (2 * tile[0] + 31, 130, 0, 5),
+                                 (1000, 3 * tile[1], 13, 31), (33, 7, 1, 2),
+                                 (tile[0], tile[1], 32, 0)):
+            check_case(4, 1, r, c, ld_out=r + pad, out_shift=shift,
+                       seed=r + c + cache, opts=opts, label=tag)
+        check_case(4, 3, 301, 257, ld_out=305, stride_out=257 * 305 + 9,
+                   seed=3, opts=opts, label=tag + " batch")
+
+
 def test_nontemporal_loads_variant():
     """Non-temporal loads and stores are built for two fp32 tiles only."""
     for tile in ((32, 32), (64, 64)):
