@@ -240,6 +240,12 @@ def bench_workload(X, w, steps, warmup, stream, layouts=True, cold=True):
                                      else n_small, min(warmup, 3) if lay > 3
                                      else warmup)
                 res["ablation"][name] = summarize(d, nbytes)
+            if w.elem_bytes in (1, 2):
+                # The same swizzled tile read back with LDS transpose reads.
+                _, d = time_launches(
+                    launch_with(X.make_opts(flags=X.FLAG_TR_READ)), stream,
+                    n_small, warmup)
+                res["ablation"]["swizzle_tr_read"] = summarize(d, nbytes)
         if cold:
             flush = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
             reps = max(5, min(steps, 20))
@@ -374,8 +380,8 @@ def main(argv=None):
             torch.cuda.empty_cache()
         log("| workload | kernel | R+W bytes | median us | GB/s | % 8 TB/s | "
             "copy GB/s | % copy | cold GB/s | cold copy GB/s | unpadded | "
-            "pad1 | swizzle | naive (best) |")
-        log("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+            "pad1 | swizzle | swizzle, transpose reads | naive (best) |")
+        log("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
         for key, b, dd, cp, ab, cd, pl in rows:
             g = dd["median_GBps"]
             kern = (f"{pl['tile_rows']}x{pl['tile_cols']} "
@@ -386,6 +392,7 @@ def main(argv=None):
                 f"{cd['transpose']['median_GBps']} | {cd['copy']['median_GBps']} | "
                 f"{ab['unpadded']['median_GBps']} | {ab['pad1']['median_GBps']} | "
                 f"{ab['swizzle']['median_GBps']} | "
+                f"{ab['swizzle_tr_read']['median_GBps'] if 'swizzle_tr_read' in ab else '—'} | "
                 f"{max(ab['naive_read_coalesced']['median_GBps'], ab['naive_write_coalesced']['median_GBps'])} |")
     return 0 if parity is not False else 3
 

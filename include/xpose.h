@@ -88,7 +88,9 @@ typedef enum xpose_layout {
 /* Cache policy of the global accesses.  The data is touched exactly once,
  * so marking it non-temporal can keep it from displacing other lines. */
 typedef enum xpose_cache {
-  XPOSE_CACHE_AUTO = 0,       /* library default                            */
+  XPOSE_CACHE_AUTO = 0,       /* library default for the case; where the
+                                 requested kernel is not built with it, any
+                                 policy it is built with                    */
   XPOSE_CACHE_DEFAULT = 1,    /* plain loads and stores                     */
   XPOSE_CACHE_NT_STORE = 2,   /* non-temporal stores                        */
   XPOSE_CACHE_NT_ALL = 3      /* non-temporal loads and stores              */
@@ -108,8 +110,10 @@ enum {
   XPOSE_FLAG_XCD_REMAP = 2,   /* give each XCD one contiguous range of tiles */
   XPOSE_FLAG_NO_XCD_REMAP = 4, /* the opposite, overriding the default       */
   XPOSE_FLAG_DIRECT_LDS = 8,   /* interior tiles load straight into LDS
-                                  (global_load_lds_dwordx4, 4- and 8-byte
-                                  elements, unpadded or swizzled layout)     */
+                                  (global_load_lds_dwordx4): 4- and 8-byte
+                                  elements, unpadded or swizzled layout, or
+                                  1- and 2-byte elements together with
+                                  XPOSE_FLAG_TR_READ                         */
   XPOSE_FLAG_ALIGN_OUT = 16,   /* line-aligned output tiles (4-byte elements,
                                   swizzled layout): each output row's segment
                                   is shifted to start on a 128-byte line, so
@@ -119,8 +123,16 @@ enum {
                                   this flag, a call whose element size, tile,
                                   workgroup size or cache policy has no such
                                   kernel returns XPOSE_ENOTILE                */
-  XPOSE_FLAG_NO_ALIGN_OUT = 32 /* ordinary tiles even where line-aligned output
-                                  tiles are the default                       */
+  XPOSE_FLAG_NO_ALIGN_OUT = 32, /* ordinary tiles even where line-aligned
+                                  output tiles are the default               */
+  XPOSE_FLAG_TR_READ = 64      /* 1- and 2-byte elements, swizzled layout: the
+                                  LDS tile holds the input rows unchanged and
+                                  the column walk uses gfx950's LDS transpose
+                                  reads (ds_read_b64_tr_b16 / _tr_b8) instead
+                                  of packing rows in registers.  Not combined
+                                  with XPOSE_FLAG_ALIGN_OUT (XPOSE_EINVAL);
+                                  sizes without such a kernel return
+                                  XPOSE_ENOTILE                              */
 };
 
 /* Optional knobs for the measured ablation.  Zero-initialise for defaults.
@@ -165,6 +177,7 @@ typedef struct xpose_plan_info {
   int32_t persistent;  /* persistent workgroups per compute unit, 0 = none   */
   int32_t direct_lds;  /* 1 if interior tiles load straight into LDS         */
   int32_t aligned_out; /* 1 if output segments are shifted onto lines        */
+  int32_t tr_read;     /* 1 if the column walk uses LDS transpose reads      */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

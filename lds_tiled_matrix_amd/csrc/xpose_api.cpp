@@ -139,7 +139,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (batch < 0 || rows < 0 || cols < 0) return XPOSE_EINVAL;
   const int known_flags = XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP |
                           XPOSE_FLAG_NO_XCD_REMAP | XPOSE_FLAG_DIRECT_LDS |
-                          XPOSE_FLAG_ALIGN_OUT | XPOSE_FLAG_NO_ALIGN_OUT;
+                          XPOSE_FLAG_ALIGN_OUT | XPOSE_FLAG_NO_ALIGN_OUT |
+                          XPOSE_FLAG_TR_READ;
   if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
                opts->layout > XPOSE_LAYOUT_NAIVE_WRITE ||
                (opts->flags & ~known_flags) != 0 ||
@@ -148,7 +149,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                ((opts->flags & XPOSE_FLAG_ALIGN_OUT) &&
                 (opts->flags & (XPOSE_FLAG_NO_ALIGN_OUT |
                                 XPOSE_FLAG_ELEMENTWISE |
-                                XPOSE_FLAG_DIRECT_LDS))) ||
+                                XPOSE_FLAG_DIRECT_LDS |
+                                XPOSE_FLAG_TR_READ))) ||
                opts->cache < XPOSE_CACHE_AUTO ||
                opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
                opts->group_cols < 0 || opts->threads < 0 ||
@@ -197,6 +199,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
                    call_bytes > kBigCallBytes;
   const bool direct = opts && (opts->flags & XPOSE_FLAG_DIRECT_LDS);
+  const bool tr_read = opts && (opts->flags & XPOSE_FLAG_TR_READ);
   // Line-aligned output tiles are the default where they apply, unless a
   // knob asks for something they are not built with; XPOSE_FLAG_ALIGN_OUT
   // requests them outright.
@@ -205,7 +208,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       want_align ||
       !(opts && ((opts->flags & (XPOSE_FLAG_NO_ALIGN_OUT |
                                  XPOSE_FLAG_ELEMENTWISE |
-                                 XPOSE_FLAG_DIRECT_LDS)) ||
+                                 XPOSE_FLAG_DIRECT_LDS |
+                                 XPOSE_FLAG_TR_READ)) ||
                  (opts->layout && opts->layout != XPOSE_LAYOUT_SWIZZLE) ||
                  opts->persistent));
   Default d = default_for(s, row128, small, big,
@@ -239,16 +243,21 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       nt = 0;  // any built workgroup size; the largest is preferred
     }
     if (opts && opts->threads) nt = opts->threads;
-    const int cache = (opts && opts->cache) ? opts->cache : dd.cache;
+    // An explicit cache policy must be built; otherwise the default one is
+    // preferred, then any policy built for the requested kernel.
+    const int want[3] = {(opts && opts->cache) ? opts->cache : dd.cache, kWB,
+                         kNT};
+    const int tries = (opts && opts->cache) ? 1 : 3;
     const xpose::TileKernel *k = nullptr;
-    for (int i = 0; i < n; ++i)
-      if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
-          table[i].tile_cols == tc && table[i].layout == layout &&
-          table[i].cache == cache - 1 && table[i].direct_lds == direct &&
-          table[i].aligned_out == align &&
-          (nt ? table[i].threads == nt
-              : (!k || table[i].threads > k->threads)))
-        k = &table[i];
+    for (int t = 0; t < tries && !k; ++t)
+      for (int i = 0; i < n; ++i)
+        if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
+            table[i].tile_cols == tc && table[i].layout == layout &&
+            table[i].cache == want[t] - 1 && table[i].direct_lds == direct &&
+            table[i].aligned_out == align && table[i].tr_read == tr_read &&
+            (nt ? table[i].threads == nt
+                : (!k || table[i].threads > k->threads)))
+          k = &table[i];
     return k;
   };
   const xpose::TileKernel *k = lookup(d, d.align_out || want_align);
@@ -440,6 +449,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->persistent = plan.persistent;
       info->direct_lds = plan.kernel->direct_lds ? 1 : 0;
       info->aligned_out = plan.kernel->aligned_out ? 1 : 0;
+      info->tr_read = plan.kernel->tr_read ? 1 : 0;
       info->xcd_remap = plan.args.xcd_remap;
     }
   }

@@ -96,6 +96,9 @@ struct TileKernel {
   // start on a 128-byte line; the grid needs ceil((rows + 31) / tile_rows)
   // tile rows (4-byte elements only).
   bool aligned_out;
+  // Row-major LDS tile of raw elements read back with the LDS transpose
+  // reads (ds_read_b64_tr_b16 / _b8; 1- and 2-byte elements only).
+  bool tr_read = false;
 };
 
 // Every compiled tile kernel; *count receives the table length.

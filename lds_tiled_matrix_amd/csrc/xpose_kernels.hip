@@ -27,6 +27,10 @@
 //  * Edges: tiles that cross the matrix edge (or matrices whose rows are not
 //    4-byte aligned) take an element-wise path through the same LDS tile;
 //    nothing outside the logical output is written.
+//  * Variants, each measured against the default: persistent double-buffered
+//    workgroups, direct global->LDS loads, 1- and 2-byte tiles read back
+//    with the LDS transpose reads, line-aligned output tiles for output rows
+//    off the 128-byte line, and two naive kernels without LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -628,6 +632,207 @@ hipError_t launch_shift(const TileArgs &a, uint32_t grid, hipStream_t stream) {
       dim3(grid), dim3(NT), args, 0, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Transpose-read tiles (1- and 2-byte elements).  gfx950's LDS transpose
+// reads turn small blocks around on the way out of LDS.  Within each 16-lane
+// group, with HR = 8 / S elements per 8 bytes and NQ = 16 / HR:
+//   ds_read_b64_tr_b16 / _b8 give lane i, as its element m (m < HR),
+//   element i % HR of the 8 bytes addressed by lane NQ * m + i / HR.
+// (Checked on the hardware with distinct values at every address.)  So if
+// lane NQ * m + q addresses 8-byte column unit cu of tile row R(q) + m, lane
+// i receives column cu * HR + i % HR of rows R(i / HR) .. R(i / HR) + HR - 1.
+// Two such reads give one 16-byte output vector of V = 2 HR rows.
+//
+// The LDS tile holds the input rows unchanged (no in-register packing).
+// One group covers the HR columns of one 8-byte unit over 32 rows (NQ
+// vectors per column); the four groups of a wave take four consecutive
+// 32-row blocks of the same unit, so one store instruction writes up to 128
+// consecutive rows of each of its HR output rows: whole 128-byte lines once
+// TR >= 64 (2-byte elements) or 128 (1-byte).
+//
+// Banks: one read of a half-wave touches the same 8-byte unit of 32 rows,
+// 256 bytes, which the 64 banks serve in one pass only if the 32 rows sit in
+// 32 different 8-byte slots.  The rows differ in bits 0..5 except bit
+// log2(HR); rows that the 256-byte window already separates by their row
+// offset need nothing, the remaining varying bits XOR the 8-byte unit
+// index.  A 16-byte chunk then keeps its two halves together, swapped when
+// the mask is odd, so the row writes stay one ds_write_b128 per chunk.
+// Direct global->LDS loads cannot swap halves: there the mask's lowest bit
+// is dropped and the reads are 2-way conflicted.
+// ---------------------------------------------------------------------------
+template <int S, int TR, int TC, int NT, int CP, bool DIRECT>
+struct TrTile {
+  static constexpr int V = 16 / S;          // elements per output vector
+  static constexpr int HR = V / 2;          // rows per transpose read
+  static constexpr int NQ = 16 / HR;        // row vectors per group
+  static constexpr int RB = TC * S;         // bytes per LDS row
+  static constexpr int NCL = RB / 16;       // 16-byte chunks per row
+  static constexpr int NU = RB / 8;         // 8-byte units per row
+  static constexpr int NW = NT / 64;
+  static constexpr int NRB = TR / 32;       // 32-row blocks
+  static constexpr int LIT = TR * NCL / NT; // load tasks per lane
+  static constexpr int SIT = NRB * NU / (4 * NW);  // store tasks per lane
+  static constexpr int LDS_BYTES = TR * RB;
+  static constexpr int WB = ilog2(256 / RB);  // log2(rows per 256 B)
+  static_assert(S == 1 || S == 2, "transpose reads move 8- or 16-bit elements");
+  static_assert(NQ * V == 32, "a group covers 32 rows");
+  static_assert(NCL >= 4 && NCL <= 16, "rows of 64 to 256 bytes");
+  static_assert(NRB % 2 == 0, "a half-wave takes two 32-row blocks");
+  static_assert(TR * NCL % NT == 0 && LIT >= 1, "even load split");
+  static_assert(NRB * NU % (4 * NW) == 0 && SIT >= 1, "even store split");
+  static_assert(64 % NCL == 0, "rows fit a wave");
+  // XOR mask of the 8-byte unit index in row `row`.
+  __device__ static __forceinline__ int swz(int row) {
+    const int v = (row & (HR - 1)) | ((row >> 1) & ~(HR - 1) & 31);
+    const int f = (v >> WB) & (NU - 1);
+    return DIRECT ? (f & ~1) : f;
+  }
+  // Byte offset of 8-byte unit `u` of row `row`.
+  __device__ static __forceinline__ int unit_at(int row, int u) {
+    return row * RB + ((u ^ swz(row)) << 3);
+  }
+  // The 16-byte chunk `ch` of row `row`: its offset, and whether its two
+  // halves are stored swapped.
+  __device__ static __forceinline__ void chunk_at(int row, int ch, int &off,
+                                                  bool &swap) {
+    const int f = swz(row);
+    off = row * RB + ((ch ^ (f >> 1)) << 4);
+    swap = f & 1;
+  }
+};
+
+// One transpose read at byte offset `off` (the address this lane supplies
+// to its group).
+template <int S>
+__device__ __forceinline__ u32x2 tr_read(const uint8_t *lds, int off) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef int v2i32 __attribute__((ext_vector_type(2)));
+  auto *p = (__attribute__((address_space(3))) uint8_t *)(lds + off);
+  if constexpr (S == 2) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)p);
+    return __builtin_bit_cast(u32x2, r);
+  } else {
+    const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i32 *)p);
+    return __builtin_bit_cast(u32x2, r);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void tr_write_chunk(uint8_t *lds, int row, int ch,
+                                               u32x4 w) {
+  int off;
+  bool swap;
+  T::chunk_at(row, ch, off, swap);
+  *reinterpret_cast<u32x4 *>(lds + off) = swap ? u32x4{w.z, w.w, w.x, w.y} : w;
+}
+
+template <int S, int TR, int TC, int NT, int CP, bool DIRECT>
+__global__ __launch_bounds__(NT) void xpose_tr_kernel(TileArgs a) {
+  using T = TrTile<S, TR, TC, NT, CP, DIRECT>;
+  using E = typename Elem<S>::E;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const TileSpot p = tile_spot<S, TR, TC>(a, blockIdx.x, gridDim.x);
+  constexpr int RPT = 64 / T::NCL;  // tile rows per wave load task
+
+  // Phase 1: rows of the tile into LDS, 16 bytes per lane.
+  if (p.vec) {
+    if constexpr (DIRECT) {
+      // Lane l fills physical slot l of the wave's 1 KiB: it fetches the
+      // logical chunk that the (even) mask puts there.
+#pragma unroll
+      for (int it = 0; it < T::LIT; ++it) {
+        const int wt = it * T::NW + wave;
+        const int row = wt * RPT + lane / T::NCL;
+        const int chunk = (lane % T::NCL) ^ (T::swz(row) >> 1);
+        __builtin_amdgcn_global_load_lds(
+            p.src + (int64_t)row * a.ld_in * S + chunk * 16,
+            (__attribute__((address_space(3))) void *)(lds + wt * 1024), 16,
+            0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      u32x4 v[T::LIT];
+#pragma unroll
+      for (int it = 0; it < T::LIT; ++it) {
+        const int row = (it * T::NW + wave) * RPT + lane / T::NCL;
+        v[it] = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(
+            p.src + (int64_t)row * a.ld_in * S + (lane % T::NCL) * 16);
+      }
+#pragma unroll
+      for (int it = 0; it < T::LIT; ++it) {
+        const int row = (it * T::NW + wave) * RPT + lane / T::NCL;
+        tr_write_chunk<T>(lds, row, lane % T::NCL, v[it]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < T::LIT; ++it) {
+      const int row = (it * T::NW + wave) * RPT + lane / T::NCL;
+      const int ch = lane % T::NCL;
+      E e[T::V];
+#pragma unroll
+      for (int x = 0; x < T::V; ++x) {
+        const int col = ch * T::V + x;
+        e[x] = (row < p.rows_left && col < p.cols_left)
+                   ? *reinterpret_cast<const E *>(
+                         p.src + ((int64_t)row * a.ld_in + col) * S)
+                   : E(0);
+      }
+      u32x4 w;
+      __builtin_memcpy(&w, e, 16);
+      tr_write_chunk<T>(lds, row, ch, w);
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: group q of the wave takes 32-row block rb of 8-byte column
+  // unit cu; the four groups of a wave take consecutive row blocks.
+  const int q = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int it = 0; it < T::SIT; ++it) {
+    const int gt = (it * T::NW + wave) * 4 + q;
+    const int rb = gt % T::NRB, cu = gt / T::NRB;
+    u32x2 h[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = rb * 32 + (i % T::NQ) * T::V + k * T::HR + i / T::NQ;
+      h[k] = tr_read<S>(lds, T::unit_at(row, cu));
+    }
+    const u32x4 o = u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
+    const int c = cu * T::HR + i % T::HR;       // output row in the tile
+    const int r = rb * 32 + (i / T::HR) * T::V;  // first input row
+    char *dst = p.dst + ((int64_t)c * a.ld_out + r) * S;
+    if (p.vec) {
+      store16<CP>(dst, o);
+    } else if (c < p.cols_left) {
+      E e[T::V];
+      __builtin_memcpy(e, &o, 16);
+#pragma unroll
+      for (int x = 0; x < T::V; ++x)
+        if (r + x < p.rows_left) reinterpret_cast<E *>(dst)[x] = e[x];
+    }
+  }
+}
+
+template <int S, int TR, int TC, int NT, int CP, bool DIRECT>
+hipError_t launch_tr(const TileArgs &a, uint32_t grid, hipStream_t stream) {
+  TileArgs copy = a;
+  void *args[] = {&copy};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(&xpose_tr_kernel<S, TR, TC, NT, CP, DIRECT>),
+      dim3(grid), dim3(NT), args, 0, stream);
+}
+
+#define XPOSE_TR(S, TR, TC, NT, CP, D)                                      \
+  TileKernel {                                                              \
+    S, TR, TC, NT, kSwizzle, CP, TrTile<S, TR, TC, NT, CP, D>::LDS_BYTES,  \
+        &launch_tr<S, TR, TC, NT, CP, D>, nullptr, D, false, true           \
+  }
+
 #define XPOSE_SHIFT(TR, TC, NT, CP)                                         \
   TileKernel {                                                              \
     4, TR, TC, NT, kSwizzle, CP, ShiftTile<TR, TC, NT, CP>::LDS_BYTES,     \
@@ -691,9 +896,31 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILES(2, 64, 32, 128), XPOSE_TILES(2, 64, 64, 128),
     XPOSE_TILES(2, 64, 64, 256), XPOSE_TILES(2, 128, 128, 256),
     XPOSE_TILES(2, 64, 128, 256), XPOSE_TILES(2, 128, 64, 256),
+    // 2-byte elements through LDS transpose reads
+    XPOSE_TR(2, 64, 64, 256, kNtStore, false),
+    XPOSE_TR(2, 64, 64, 256, kCacheDefault, false),
+    XPOSE_TR(2, 128, 64, 256, kNtStore, false),
+    XPOSE_TR(2, 128, 64, 256, kCacheDefault, false),
+    XPOSE_TR(2, 64, 128, 256, kNtStore, false),
+    XPOSE_TR(2, 64, 128, 256, kCacheDefault, false),
+    XPOSE_TR(2, 128, 128, 256, kNtStore, false),
+    XPOSE_TR(2, 128, 128, 256, kCacheDefault, false),
+    XPOSE_TR(2, 64, 32, 128, kNtStore, false),
+    XPOSE_TR(2, 64, 64, 256, kNtStore, true),
+    XPOSE_TR(2, 64, 64, 256, kCacheDefault, true),
+    XPOSE_TR(2, 128, 64, 256, kNtStore, true),
+    XPOSE_TR(2, 128, 64, 256, kCacheDefault, true),
+    XPOSE_TR(2, 128, 128, 256, kNtStore, true),
     // 1-byte elements
     XPOSE_TILES(1, 64, 64, 64), XPOSE_TILES(1, 64, 128, 128),
     XPOSE_TILES(1, 128, 64, 128), XPOSE_TILES(1, 128, 128, 256),
+    XPOSE_TR(1, 128, 128, 256, kNtStore, false),
+    XPOSE_TR(1, 128, 128, 256, kCacheDefault, false),
+    XPOSE_TR(1, 64, 128, 128, kNtStore, false),
+    XPOSE_TR(1, 128, 64, 128, kNtStore, false),
+    XPOSE_TR(1, 128, 256, 256, kNtStore, false),
+    XPOSE_TR(1, 128, 128, 256, kNtStore, true),
+    XPOSE_TR(1, 128, 128, 256, kCacheDefault, true),
     // 8-byte elements
     XPOSE_TILES(8, 16, 16, 64), XPOSE_TILES(8, 32, 32, 128),
     XPOSE_TILES(8, 32, 32, 256), XPOSE_TILES(8, 64, 64, 256),

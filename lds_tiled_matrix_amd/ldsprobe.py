@@ -95,7 +95,9 @@ def run_patterns(iters=1000, out=sys.stdout):
 
 def run_transposes(out=sys.stdout):
     """Each LDS layout once on the 8192 x 8192 fp32 and 16384 x 16384 fp16
-    transposes, with the default tile shape and with a 64 x 64 tile."""
+    transposes, with the default tile shape and with a 64 x 64 tile (for
+    fp16 also read back with LDS transpose reads), and the default on the
+    odd-pitch 12345 x 6789 fp32 transpose."""
     import torch
     import lds_tiled_matrix_amd as X
     for rows, cols, dt in ((8192, 8192, torch.float32),
@@ -109,6 +111,14 @@ def run_transposes(out=sys.stdout):
                 print(f"xpose  {rows}x{cols} {str(dt).split('.')[-1]} tile "
                       f"{plan['tile_rows']}x{plan['tile_cols']} "
                       f"{X.LAYOUT_NAMES[layout]}", file=out, flush=True)
+            if dt == torch.int16:
+                # the swizzled tile read back with LDS transpose reads
+                plan = X.plan_for(x, tile=tile, flags=X.FLAG_TR_READ)
+                X.transpose(x, tile=tile, flags=X.FLAG_TR_READ)
+                torch.cuda.synchronize()
+                print(f"xpose  {rows}x{cols} {str(dt).split('.')[-1]} tile "
+                      f"{plan['tile_rows']}x{plan['tile_cols']} swizzle, "
+                      f"transpose reads", file=out, flush=True)
         del x
     # Odd pitches: the default there is the line-aligned output tile, whose
     # column gathers start at a different row offset for every column.

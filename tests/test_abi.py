@@ -159,7 +159,7 @@ def test_opts_select_layout_and_tile():
     assert plan(opts=X.make_opts(tile=(32, 32), threads=96))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(0, 48, 48, 0))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(9, 0, 0, 0))[0] == X.XPOSE_EINVAL
-    assert plan(opts=X.XposeOpts(0, 0, 0, 64))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.XposeOpts(0, 0, 0, 128))[0] == X.XPOSE_EINVAL
 
 
 def test_large_batch_splits_launches():
@@ -264,3 +264,44 @@ def test_align_out_option():
     # asked for on line-aligned rows: the aligned-out default tile
     rc, info = plan(rows=8192, cols=8192, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))
     assert rc == 0 and info.aligned_out == 1 and info.tiles == -(-(8192 + 31) // info.tile_rows) * (8192 // info.tile_cols)
+
+
+def test_tr_read_option():
+    """LDS transpose-read tiles: 1- and 2-byte elements, swizzled layout."""
+    f16, u8 = X.XPOSE_F16, X.XPOSE_U8
+    rc, info = plan(rows=8192, cols=8192, dtype=f16, opts=X.make_opts(flags=X.FLAG_TR_READ))
+    assert rc == 0 and info.tr_read == 1 and info.layout == X.LAYOUT_SWIZZLE
+    assert info.lds_bytes == info.tile_rows * info.tile_cols * 2
+    rc, info = plan(rows=4096, cols=4096, dtype=u8, opts=X.make_opts(flags=X.FLAG_TR_READ))
+    assert rc == 0 and info.tr_read == 1
+    assert info.lds_bytes == info.tile_rows * info.tile_cols
+    # bf16 moves by size like fp16
+    assert plan(dtype=X.XPOSE_BF16, opts=X.make_opts(flags=X.FLAG_TR_READ))[1].tr_read == 1
+    # combined with direct loads
+    rc, info = plan(rows=8192, cols=8192, dtype=f16,
+                    opts=X.make_opts(tile=(128, 64), flags=X.FLAG_TR_READ | X.FLAG_DIRECT_LDS))
+    assert rc == 0 and info.tr_read == 1 and info.direct_lds == 1
+    # without the flag: the packed-register tiles
+    assert plan(dtype=f16)[1].tr_read == 0
+    # not for 4- or 8-byte elements, other layouts, persistent workgroups
+    assert plan(opts=X.make_opts(flags=X.FLAG_TR_READ))[0] == X.XPOSE_ENOTILE
+    assert plan(dtype=X.XPOSE_F64, opts=X.make_opts(flags=X.FLAG_TR_READ))[0] == X.XPOSE_ENOTILE
+    assert plan(dtype=f16, opts=X.make_opts(layout=X.LAYOUT_PAD1, flags=X.FLAG_TR_READ))[0] == X.XPOSE_ENOTILE
+    assert plan(dtype=f16, opts=X.make_opts(flags=X.FLAG_TR_READ, persistent=1))[0] == X.XPOSE_ENOTILE
+    assert plan(dtype=f16, opts=X.make_opts(tile=(32, 32), flags=X.FLAG_TR_READ))[0] == X.XPOSE_ENOTILE
+    # contradicts line-aligned output tiles
+    assert plan(opts=X.make_opts(flags=X.FLAG_TR_READ | X.FLAG_ALIGN_OUT))[0] == X.XPOSE_EINVAL
+    # unaligned fp32 output rows with the flag: no line-aligned default either
+    assert plan(rows=1000, cols=512, opts=X.make_opts(flags=X.FLAG_TR_READ))[0] == X.XPOSE_ENOTILE
+
+
+def test_auto_cache_takes_a_built_policy():
+    # fp16 64 x 32 transpose-read tiles are built with non-temporal stores
+    # only; unaligned rows default to write-back, so AUTO takes the other.
+    opts = X.make_opts(tile=(64, 32), flags=X.FLAG_TR_READ)
+    rc, info = plan(rows=100, cols=100, ld_in=101 * 2, ld_out=103 * 2,
+                    dtype=X.XPOSE_F16, opts=opts)
+    assert rc == 0 and info.cache == X.CACHE_NT_STORE
+    explicit = X.make_opts(tile=(64, 32), flags=X.FLAG_TR_READ, cache=X.CACHE_DEFAULT)
+    assert plan(rows=100, cols=100, ld_in=202, ld_out=206, dtype=X.XPOSE_F16,
+                opts=explicit)[0] == X.XPOSE_ENOTILE

@@ -60,3 +60,44 @@ def test_random_cases(seed):
                    in_shift=rng.choice((0, 0, 1, 3)),
                    out_shift=rng.choice((0, 0, 1, 2)),
                    label=f"fuzz {seed}/{case}")
+
+
+TR_TILES = {2: ((64, 64), (128, 64), (64, 128), (128, 128), (64, 32), None),
+            1: ((128, 128), (64, 128), (128, 64), (128, 256), None)}
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_tr_cases(seed):
+    """The same kind of random cases through the LDS transpose-read tiles."""
+    rng = random.Random(2000 + seed)
+    for case in range(25):
+        s = rng.choice((1, 2))
+        opts = None
+        for _ in range(50):
+            flags = X.FLAG_TR_READ | rng.choice(
+                (0, 0, X.FLAG_DIRECT_LDS, X.FLAG_ELEMENTWISE, X.FLAG_XCD_REMAP,
+                 X.FLAG_NO_XCD_REMAP | X.FLAG_DIRECT_LDS))
+            gr, gc = rng.choice(((0, 0), (1, 0), (3, 5), (8, 32)))
+            cand = X.make_opts(X.LAYOUT_SWIZZLE, rng.choice(TR_TILES[s]), flags,
+                               rng.choice((0, 1, 2)), gr, gc, 0,
+                               rng.choice((0, 1, 2)))
+            if X.xpose_plan(0x100000, 0x40000000, 1, 64, 64, 64, 64, 0, 0,
+                            DTYPE_OF_SIZE[s], cand)[0] == 0:
+                opts = cand
+                break
+        assert opts is not None
+        batch = rng.choice((1, 1, 2, 4))
+        rows = rng.choice((rng.randint(1, 70), rng.randint(1, 900),
+                           rng.randint(200, 1500)))
+        cols = rng.choice((rng.randint(1, 70), rng.randint(1, 900),
+                           rng.randint(200, 1500)))
+        ld_in = cols + rng.choice((0, 0, 1, 4, 16, 37))
+        ld_out = rows + rng.choice((0, 0, 2, 4, 32, 41))
+        stride_in = rows * ld_in + rng.choice((0, 0, 4, 64))
+        stride_out = cols * ld_out + rng.choice((0, 0, 8, 128))
+        check_case(s, batch, rows, cols, ld_in=ld_in, ld_out=ld_out,
+                   stride_in=stride_in, stride_out=stride_out,
+                   seed=seed * 100 + case, opts=opts,
+                   in_shift=rng.choice((0, 0, 1, 2, 4)),
+                   out_shift=rng.choice((0, 0, 2, 4)),
+                   label=f"tr fuzz {seed}/{case}")

@@ -344,6 +344,55 @@ def test_aligned_out_kernels():
                    seed=3, opts=opts, label=tag + " batch")
 
 
+TR_TILES = {2: ((64, 64), (128, 64), (64, 128), (128, 128), (64, 32)),
+            1: ((128, 128), (64, 128), (128, 64), (128, 256))}
+
+
+def test_tr_read_kernels():
+    """LDS transpose-read tiles (1- and 2-byte elements): every built shape,
+    both cache policies and direct loads, interior and edge tiles, pitches,
+    pointers off 16-byte alignment, elementwise (unaligned rows) and
+    batches."""
+    built = 0
+    for s, tiles in TR_TILES.items():
+        for tile in tiles:
+            for flags in (X.FLAG_TR_READ, X.FLAG_TR_READ | X.FLAG_DIRECT_LDS):
+                for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE):
+                    opts = X.make_opts(X.LAYOUT_SWIZZLE, tile, flags, cache)
+                    rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, 512, 512,
+                                            512, 512, 0, 0, DTYPE_OF_SIZE[s], opts)
+                    if rc != 0:
+                        continue
+                    assert info.tr_read == 1
+                    built += 1
+                    tag = f"tr s{s} {tile} f{flags} c{cache}"
+                    tr, tc = tile
+                    for r, c, pi, po in ((2 * tr, 3 * tc, 0, 0), (777, 555, 0, 0),
+                                         (tr + 1, tc - 1, 4, 8), (33, 17, 0, 0),
+                                         (3 * tr + 5, 2 * tc + 7, 16, 2)):
+                        check_case(s, 1, r, c, ld_in=c + pi, ld_out=r + po,
+                                   seed=r * 7 + c + cache, opts=opts, label=tag)
+                    # rows 4-byte aligned but not 16: still the vector path
+                    check_case(s, 1, 2 * tr, 2 * tc, ld_in=2 * tc + 4 // s * 3,
+                               ld_out=2 * tr + 4 // s, in_shift=4 // s,
+                               out_shift=4 // s, seed=5, opts=opts, label=tag + " off16")
+                    # odd pitches (rows not 4-byte aligned): elementwise tiles
+                    check_case(s, 1, 2 * tr + 3, tc + 9, ld_in=tc + 9 + 1,
+                               ld_out=2 * tr + 3 + 1, in_shift=1, seed=6,
+                               opts=opts, label=tag + " odd")
+                    check_case(s, 3, tr + 17, tc + 33, ld_in=tc + 40,
+                               ld_out=tr + 20, stride_in=(tr + 17) * (tc + 40) + 8,
+                               stride_out=(tc + 33) * (tr + 20) + 16, seed=7,
+                               opts=opts, label=tag + " batch")
+    assert built >= 20
+
+
+def test_tr_read_forced_elementwise():
+    for s, tile in ((2, (128, 64)), (1, (128, 128))):
+        opts = X.make_opts(X.LAYOUT_SWIZZLE, tile, X.FLAG_TR_READ | X.FLAG_ELEMENTWISE)
+        check_case(s, 2, 300, 259, seed=11, opts=opts, label=f"tr elementwise s{s}")
+
+
 def test_nontemporal_loads_variant():
     """Non-temporal loads and stores are built for two fp32 tiles only."""
     for tile in ((32, 32), (64, 64)):
