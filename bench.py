@@ -39,7 +39,7 @@ METRIC = ("effective GB/s (R+W bytes) and % of HBM peak, 8192x8192 fp32 "
           "transpose, 1 GPU")
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "lds_tiled_matrix_amd", "csrc", f)
-                  for f in ("xpose_kernels.hip", "xpose_kernels.h")]
+                  for f in ("xpose_kernels.hip", "xpose_kernels.h", "xpose_lanes.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_8192_f32.md")
 SIGNED = {1: np.int8, 2: np.int16, 4: np.int32, 8: np.int64}
 

@@ -14,6 +14,7 @@ cycles per instruction.
 """
 import pytest
 
+from gfx950_banks import GFX950
 from oracle import bankmodel as bm
 
 pytestmark = pytest.mark.gpu
@@ -21,10 +22,6 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 X = pytest.importorskip("lds_tiled_matrix_amd")
 from lds_tiled_matrix_amd import ldsprobe  # noqa: E402
-
-# (width, is_write) -> (banks, lanes per group)
-GFX950 = {(4, 0): (32, 32), (4, 1): (32, 32), (8, 0): (64, 32), (8, 1): (32, 16),
-          (16, 0): (64, 16), (16, 1): (32, 8)}
 
 
 def model_degree(width, is_write, lanes):
