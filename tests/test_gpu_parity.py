@@ -209,6 +209,43 @@ def test_torch_views_and_streams():
     assert np.array_equal(dst.cpu().numpy(), want)
 
 
+def test_hip_graph_capture_and_replay():
+    """Calls only enqueue kernels (no allocation, memset or synchronisation),
+    so they can be captured into a HIP graph.  Every replay, with eager work
+    on the same buffers in between, must match the oracle."""
+    cases = [(wl.random_bits((777, 1031), 2, 21), None),              # fp16 packed
+             (wl.random_bits((3, 300, 517), 4, 22), None),            # line-aligned out
+             (wl.random_bits((512, 640), 1, 23), X.FLAG_TR_READ),     # transpose reads
+             (wl.random_bits((256, 384), 8, 24), None)]               # f64
+    devs, outs, wants = [], [], []
+    for host, _ in cases:
+        x = _to_dev(host)
+        devs.append(x)
+        shape = host.shape[:-2] + (host.shape[-1], host.shape[-2])
+        outs.append(torch.empty(shape, dtype=x.dtype, device=_dev()))
+        wants.append(oracle.transpose(host))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # eager warm-up on the capture stream
+        for (host, fl), x, y in zip(cases, devs, outs):
+            X.transpose(x, y, flags=fl or 0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (host, fl), x, y in zip(cases, devs, outs):
+            X.transpose(x, y, flags=fl or 0)
+    for rep in range(3):
+        for y in outs:
+            y.fill_(rep + 1)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (y, want) in enumerate(zip(outs, wants)):
+            got = y.cpu().numpy().view(want.dtype)
+            assert np.array_equal(got, want), f"replay {rep}, case {i}"
+
+
 def test_copy_kernel():
     for nbytes, src_off, dst_off in ((1 << 20, 0, 0), (12345, 0, 0),
                                      (100003, 3, 1), (16, 0, 0), (1, 0, 0)):
