@@ -165,7 +165,9 @@ typedef struct xpose_plan_info {
   int32_t tile_cols;
   int32_t threads;     /* threads per workgroup                              */
   int32_t lds_bytes;   /* LDS per workgroup                                  */
-  int32_t vector_path; /* 1: interior tiles use 128-bit global accesses;
+  int32_t vector_path; /* 1: interior tiles use 128-bit global accesses (at
+                          any alignment; direct global->LDS loads need
+                          4-byte aligned input rows);
                           0: every tile takes the element-wise path          */
   int64_t tiles;       /* workgroups over the whole batch                    */
   int32_t launches;    /* kernel launches the call will enqueue              */

@@ -281,13 +281,13 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (!mul_ok(tiles_r, tiles_c, &tiles) || tiles > 0x7fffffff)
     return XPOSE_EINVAL;
 
-  // 128-bit accesses need every row start 4-byte aligned on both sides.
+  // Interior tiles take 128-bit accesses at any alignment, except that
+  // direct global->LDS loads need every row start 4-byte aligned.
   bool vec = true;
-  if (s < 4) {
+  if (s < 4 && k->direct_lds) {
     const int64_t q = 4 / s;  // elements per dword
-    vec = (pi % 4 == 0) && (po % 4 == 0) && (ld_in % q == 0) &&
-          (ld_out % q == 0) &&
-          (batch == 1 || (stride_in % q == 0 && stride_out % q == 0));
+    vec = (pi % 4 == 0) && (ld_in % q == 0) &&
+          (batch == 1 || stride_in % q == 0);
   }
   if (opts && (opts->flags & XPOSE_FLAG_ELEMENTWISE)) vec = false;
 

@@ -45,10 +45,13 @@ namespace xpose {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// 16-byte global access at a 4-byte-aligned address.  gfx9 global memory
-// instructions wider than a dword only need dword alignment, so a row whose
-// pitch is an odd number of fp32 elements still takes dwordx4 accesses.
-typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(4)));
+// 16-byte global access at any byte address.  Under the ROCm runtime the
+// gfx9 family runs in unaligned-access mode and global_load/store_dwordx4
+// take any address (the memory pipeline splits an access that straddles
+// cache lines), so rows whose pitch is an odd number of 1-, 2- or 4-byte
+// elements still take one 16-byte access per lane.  (Direct global->LDS
+// loads are the exception: their rows must be 4-byte aligned.)
+typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(1)));
 
 template <int CP>
 __device__ __forceinline__ u32x4 load16(const char *p) {

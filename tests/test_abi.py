@@ -131,16 +131,24 @@ def test_zero_sizes_are_noops_even_with_null_pointers():
 
 
 def test_vector_path_rules():
-    # fp16 needs 4-byte aligned rows on both sides for 128-bit accesses.
+    # 128-bit accesses at any alignment: odd pitches and shifted pointers of
+    # 1- and 2-byte elements keep the vector path ...
     assert plan(dtype=X.XPOSE_F16, rows=64, cols=64)[1].vector_path == 1
-    assert plan(dtype=X.XPOSE_F16, rows=64, cols=63, ld_in=63)[1].vector_path == 0
-    assert plan(dtype=X.XPOSE_F16, rows=63, cols=64, ld_out=63)[1].vector_path == 0
-    assert plan(dtype=X.XPOSE_F16, inp=IN + 2)[1].vector_path == 0
+    assert plan(dtype=X.XPOSE_F16, rows=64, cols=63, ld_in=63)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_F16, rows=63, cols=64, ld_out=63)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_F16, inp=IN + 2)[1].vector_path == 1
     assert plan(dtype=X.XPOSE_U8, rows=128, cols=128)[1].vector_path == 1
-    assert plan(dtype=X.XPOSE_U8, rows=128, cols=130, ld_in=130)[1].vector_path == 0
-    # fp32 rows are always dword aligned: odd pitches keep the vector path.
+    assert plan(dtype=X.XPOSE_U8, rows=128, cols=130, ld_in=130)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_U8, inp=IN + 1, out=OUT + 3)[1].vector_path == 1
     assert plan(rows=12345, cols=6789)[1].vector_path == 1
     assert plan(dtype=X.XPOSE_F64, rows=33, cols=31)[1].vector_path == 1
+    # ... except into direct global->LDS loads, which need 4-byte aligned
+    # input rows (output rows may be anything)
+    direct = X.make_opts(tile=(128, 64), flags=X.FLAG_TR_READ | X.FLAG_DIRECT_LDS)
+    assert plan(dtype=X.XPOSE_F16, rows=256, cols=128, opts=direct)[1].vector_path == 1
+    assert plan(dtype=X.XPOSE_F16, rows=256, cols=128, ld_in=129, opts=direct)[1].vector_path == 0
+    assert plan(dtype=X.XPOSE_F16, rows=256, cols=128, inp=IN + 2, opts=direct)[1].vector_path == 0
+    assert plan(dtype=X.XPOSE_F16, rows=256, cols=128, ld_out=257, opts=direct)[1].vector_path == 1
     forced = X.XposeOpts(0, 0, 0, X.FLAG_ELEMENTWISE)
     assert plan(opts=forced)[1].vector_path == 0
 

@@ -413,7 +413,7 @@ def test_tr_read_kernels():
                     check_case(s, 1, 2 * tr, 2 * tc, ld_in=2 * tc + 4 // s * 3,
                                ld_out=2 * tr + 4 // s, in_shift=4 // s,
                                out_shift=4 // s, seed=5, opts=opts, label=tag + " off16")
-                    # odd pitches (rows not 4-byte aligned): elementwise tiles
+                    # odd pitches (rows not 4-byte aligned): unaligned vectors
                     check_case(s, 1, 2 * tr + 3, tc + 9, ld_in=tc + 9 + 1,
                                ld_out=2 * tr + 3 + 1, in_shift=1, seed=6,
                                opts=opts, label=tag + " odd")
