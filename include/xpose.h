@@ -114,13 +114,13 @@ enum {
                                   elements, unpadded or swizzled layout, or
                                   1- and 2-byte elements together with
                                   XPOSE_FLAG_TR_READ                         */
-  XPOSE_FLAG_ALIGN_OUT = 16,   /* line-aligned output tiles (4-byte elements,
-                                  swizzled layout): each output row's segment
-                                  is shifted to start on a 128-byte line, so
-                                  stores are whole lines even when output
-                                  rows are not line-aligned.  The default for
-                                  4-byte elements with such output rows; with
-                                  this flag, a call whose element size, tile,
+  XPOSE_FLAG_ALIGN_OUT = 16,   /* line-aligned output tiles (2-, 4- and
+                                  8-byte elements, swizzled layout): each
+                                  output row's segment is shifted to start on
+                                  a 128-byte line, so stores are whole lines
+                                  even when output rows are not line-aligned.
+                                  The default for such output rows; with this
+                                  flag, a call whose element size, tile,
                                   workgroup size or cache policy has no such
                                   kernel returns XPOSE_ENOTILE                */
   XPOSE_FLAG_NO_ALIGN_OUT = 32, /* ordinary tiles even where line-aligned

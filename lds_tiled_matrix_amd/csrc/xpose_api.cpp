@@ -45,9 +45,10 @@ int elem_bytes_of(int32_t dtype) {
 //     input and the output side, and a taller tile with small super-tiles
 //     streams at copy speed.
 //   align: line-aligned output tiles (each output segment shifted onto a
-//     line), the default for 4-byte elements whose output rows are not
-//     line-aligned: every store is a whole line again, so non-temporal
-//     stores win.  Explicit knobs they are not built with (another layout,
+//     line), the default for 2-, 4- and 8-byte elements whose output rows
+//     are not line-aligned: every store is a whole line again, so
+//     non-temporal stores win.  (1-byte elements: no gain measured, none
+//     built.)  Explicit knobs they are not built with (another layout,
 //     elementwise or direct loads, persistent workgroups, a tile shape,
 //     workgroup size or cache policy without such a kernel) select the
 //     ordinary tiles with their own defaults instead.
@@ -70,8 +71,14 @@ constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
               kNT = XPOSE_CACHE_NT_STORE;
 
 Default default_for(int s, bool row128, bool small, bool big, bool align) {
-  if (s == 4 && align)
-    return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
+  if (align) {
+    switch (s) {
+      case 4:
+      case 2: return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
+      case 8: return {32, 32, 256, kSwz, kNT, 16, 16, 1, kSup, true};
+      default: break;  // no line-aligned tiles for 1-byte elements
+    }
+  }
   if (!row128) {
     switch (s) {
       case 4: return {128, 64, 256, kSwz, kWB, 32, 32, 1, kSup};
@@ -272,9 +279,10 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const int persistent = opts ? opts->persistent : 0;
   if (persistent && !k->launch_persistent) return XPOSE_ENOTILE;
 
-  // Line-aligned output tiles shift each segment back by up to 31 rows, so
-  // one more partial tile row may be needed to reach the last row.
-  const int64_t tiles_r = (rows + (k->aligned_out ? 31 : 0) + tr - 1) / tr;
+  // Line-aligned output tiles shift each segment back by up to 128 / s - 1
+  // rows, so one more partial tile row may be needed to reach the last row.
+  const int64_t tiles_r =
+      (rows + (k->aligned_out ? 128 / s - 1 : 0) + tr - 1) / tr;
   const int64_t tiles_c = (cols + tc - 1) / tc;
   if (tiles_r > 0x7fffffff || tiles_c > 0x7fffffff) return XPOSE_EINVAL;
   int64_t tiles;

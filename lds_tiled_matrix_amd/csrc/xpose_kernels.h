@@ -93,8 +93,8 @@ struct TileKernel {
   // Interior tiles are loaded straight into LDS (global_load_lds_dwordx4).
   bool direct_lds;
   // Line-aligned output tiles: each output row's segment is shifted back to
-  // start on a 128-byte line; the grid needs ceil((rows + 31) / tile_rows)
-  // tile rows (4-byte elements only).
+  // start on a 128-byte line; the grid needs ceil((rows + 128 / elem_bytes
+  // - 1) / tile_rows) tile rows (2-, 4- and 8-byte elements).
   bool aligned_out;
   // Row-major LDS tile of raw elements read back with the LDS transpose
   // reads (ds_read_b64_tr_b16 / _b8; 1- and 2-byte elements only).

@@ -417,25 +417,48 @@ hipError_t launch_tile_persistent(const TileArgs &a, uint32_t ntiles,
 }
 
 // ---------------------------------------------------------------------------
-// Line-aligned output tiles (4-byte elements).  When output rows do not start
-// on a 128-byte line, a tile's output segments [r0, r0 + TR) straddle lines
-// at both ends; non-temporal writes of such partial lines go to memory as
-// partial lines.  Here each tile shifts its segment in output row j back by
-//   d_j = (byte address of output row j / 4) mod 32   (elements, < 32),
+// Line-aligned output tiles (2-, 4- and 8-byte elements).  When output rows
+// do not start on a 128-byte line, a tile's output segments [r0, r0 + TR)
+// straddle lines at both ends; non-temporal writes of such partial lines go
+// to memory as partial lines.  Here each tile shifts its segment in output
+// row j back by
+//   d_j = (byte address of output row j mod 128) / S   (elements, < 128 / S),
 // so the segment [r0 - d_j, r0 - d_j + TR) starts on a line and is whole
 // lines.  Over tile rows tr = 0 .. tiles_r - 1, with tiles_r = ceil((rows +
-// 31) / TR), the shifted segments of each output row partition [0, rows).
-// The LDS tile therefore holds TR + 32 input rows, [r0 - 32, r0 + TR): a
-// halo of one line above the tile, which the previous tile row has just
-// read (the super-tile order walks tile rows fastest).  The 16-byte XOR
-// swizzle keeps the shifted column gathers conflict-free: for each column
-// the 8 row groups a half-wave reads still cover all 8 chunk slots.
+// 128 / S - 1) / TR), the shifted segments of each output row partition
+// [0, rows).  The LDS tile therefore holds TR + 128 / S input rows, [r0 -
+// 128 / S, r0 + TR): a halo of one line above the tile, which the previous
+// tile row has just read (the super-tile order walks tile rows fastest).
+// For 2-byte elements, packed two rows per 32-bit unit, a segment starting
+// at an odd row takes each output word from two units (shift_gather).
 // ---------------------------------------------------------------------------
 
-template <int TR, int TC, int NT, int CP>
+template <class T>
+__device__ __forceinline__ u32x4 shift_gather(const typename T::U *lds,
+                                              int rel, int c) {
+  int ur, shift;
+  T::gather_rows(rel, ur, shift);
+  typename T::U w[T::GATHER_UNITS];
+#pragma unroll
+  for (int k = 0; k < T::GATHER_UNITS; ++k)
+    w[k] = lds[T::unit_index(ur + k, c)];
+  if constexpr (T::K == 1) {
+    return units_to_vec<sizeof(typename T::Base::E)>(w);
+  } else {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], shift);
+    return o;
+  }
+}
+
+template <int S, int TR, int TC, int NT, int CP>
 __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
-  using T = ShiftTile<TR, TC, NT, CP>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[T::P * TC];
+  using T = ShiftTile<S, TR, TC, NT, CP>;
+  using B = typename T::Base;
+  using E = typename Elem<S>::E;
+  __shared__ __attribute__((aligned(16))) typename B::U lds[T::LDS_UNITS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint32_t tr, tc;
@@ -443,77 +466,74 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
   tile_coords(a, blockIdx.x, gridDim.x, tr, tc, b);
   const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
   const int64_t top = r0 - T::HALO;  // input row of LDS row 0
-  const uint32_t *in = static_cast<const uint32_t *>(a.in) + b * a.stride_in;
-  uint32_t *out = static_cast<uint32_t *>(a.out) + b * a.stride_out;
+  const char *in = static_cast<const char *>(a.in) + b * a.stride_in * S;
+  char *out = static_cast<char *>(a.out) + b * a.stride_out * S;
   const int64_t cols_left = a.cols - c0;
 
-  // Phase 1: rows [top, top + P) x columns [c0, c0 + TC); rows outside the
-  // matrix read as zero (they are never stored).
-  if (cols_left >= TC) {
+  // Phase 1: rows [top, top + PR) x columns [c0, c0 + TC) as an ordinary
+  // swizzled tile; rows outside the matrix read as zero (never stored).
 #pragma unroll
-    for (int it = 0; it < T::LIT; ++it) {
-      int p, ch;
-      lane_map<T::NCI, false>(it * T::NW + wave, lane, p, ch);
-      const int64_t row = top + p;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (row >= 0 && row < a.rows)
-        v = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(
-            reinterpret_cast<const char *>(in + row * a.ld_in + c0 + ch * 4));
-      *reinterpret_cast<u32x4 *>(lds + T::lds_index(p, ch * 4)) = v;
-    }
-  } else {
+  for (int it = 0; it < B::LIT; ++it) {
+    int p, ch;
+    lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
+    u32x4 v[T::K];
 #pragma unroll
-    for (int it = 0; it < T::LIT; ++it) {
-      int p, ch;
-      lane_map<T::NCI, false>(it * T::NW + wave, lane, p, ch);
-      const int64_t row = top + p;
-      uint32_t e[4];
+    for (int k = 0; k < T::K; ++k) {
+      const int64_t row = top + p * T::K + k;
+      const bool in_rows = row >= 0 && row < a.rows;
+      const char *src = in + (row * a.ld_in + c0 + ch * T::V) * S;
+      if (cols_left >= TC) {
+        v[k] = in_rows
+                   ? load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src)
+                   : u32x4{0, 0, 0, 0};
+      } else {
+        E e[T::V];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int col = ch * 4 + x;
-        e[x] = (row >= 0 && row < a.rows && col < cols_left)
-                   ? in[row * a.ld_in + c0 + col]
-                   : 0u;
+        for (int x = 0; x < T::V; ++x)
+          e[x] = (in_rows && ch * T::V + x < cols_left)
+                     ? reinterpret_cast<const E *>(src)[x]
+                     : E(0);
+        __builtin_memcpy(&v[k], e, 16);
       }
-      *reinterpret_cast<u32x4 *>(lds + T::lds_index(p, ch * 4)) =
-          u32x4{e[0], e[1], e[2], e[3]};
     }
+    typename B::U u[T::V];
+    pack_units<S>(v, u);
+    write_units<B>(lds, p, ch * T::V, u);
   }
   __syncthreads();
 
   // Phase 2: output row j = c0 + c, line-aligned segment starting at input
-  // row r0 - d_j; chunk q holds input rows r0 - d_j + 4q .. + 3, which sit
-  // at LDS rows 32 - d_j + 4q .. + 3 (always inside [1, P)).
+  // row r0 - d_j; chunk q holds input rows r0 - d_j + V q .. + V - 1, LDS
+  // input rows HALO - d_j + V q .. (always inside [1, PR)).
 #pragma unroll
   for (int it = 0; it < T::SIT; ++it) {
     int c, q;
     lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
     if (c < cols_left) {
-      uint32_t *row_out = out + (c0 + c) * a.ld_out;
-      const int d = (int)(((uintptr_t)row_out >> 2) & 31);
-      const int64_t first = r0 - d + 4 * q;  // input row of element 0
-      const int rho = T::HALO - d + 4 * q;
-      uint32_t w[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) w[x] = lds[T::lds_index(rho + x, c)];
-      if (first >= 0 && first + 3 < a.rows) {
-        store16<CP>(reinterpret_cast<char *>(row_out + first),
-                    u32x4{w[0], w[1], w[2], w[3]});
+      char *row_out = out + (c0 + c) * a.ld_out * S;
+      const int d = (int)(((uintptr_t)row_out & 127) / S);
+      const int64_t first = r0 - d + T::V * q;  // input row of element 0
+      const u32x4 o = shift_gather<T>(lds, T::HALO - d + T::V * q, c);
+      if (first >= 0 && first + T::V - 1 < a.rows) {
+        store16<CP>(row_out + first * S, o);
       } else {
+        E e[T::V];
+        __builtin_memcpy(e, &o, 16);
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          if (first + x >= 0 && first + x < a.rows) row_out[first + x] = w[x];
+        for (int x = 0; x < T::V; ++x)
+          if (first + x >= 0 && first + x < a.rows)
+            reinterpret_cast<E *>(row_out)[first + x] = e[x];
       }
     }
   }
 }
 
-template <int TR, int TC, int NT, int CP>
+template <int S, int TR, int TC, int NT, int CP>
 hipError_t launch_shift(const TileArgs &a, uint32_t grid, hipStream_t stream) {
   TileArgs copy = a;
   void *args[] = {&copy};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(&xpose_shift_kernel<TR, TC, NT, CP>),
+      reinterpret_cast<const void *>(&xpose_shift_kernel<S, TR, TC, NT, CP>),
       dim3(grid), dim3(NT), args, 0, stream);
 }
 
@@ -678,10 +698,10 @@ hipError_t launch_tr(const TileArgs &a, uint32_t grid, hipStream_t stream) {
         &launch_tr<S, TR, TC, NT, CP, D>, nullptr, D, false, true           \
   }
 
-#define XPOSE_SHIFT(TR, TC, NT, CP)                                         \
+#define XPOSE_SHIFT(S, TR, TC, NT, CP)                                      \
   TileKernel {                                                              \
-    4, TR, TC, NT, kSwizzle, CP, ShiftTile<TR, TC, NT, CP>::LDS_BYTES,     \
-        &launch_shift<TR, TC, NT, CP>, nullptr, false, true                 \
+    S, TR, TC, NT, kSwizzle, CP, ShiftTile<S, TR, TC, NT, CP>::LDS_BYTES,  \
+        &launch_shift<S, TR, TC, NT, CP>, nullptr, false, true              \
   }
 
 #define XPOSE_TILE(S, TR, TC, NT, L, CP)                                    \
@@ -731,16 +751,25 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kNtStore),
     XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kCacheDefault),
     // Line-aligned output tiles (4-byte elements).
-    XPOSE_SHIFT(64, 64, 256, kNtStore), XPOSE_SHIFT(64, 64, 256, kCacheDefault),
-    XPOSE_SHIFT(128, 64, 256, kNtStore), XPOSE_SHIFT(128, 64, 256, kCacheDefault),
-    XPOSE_SHIFT(256, 64, 256, kNtStore), XPOSE_SHIFT(256, 64, 256, kCacheDefault),
-    XPOSE_SHIFT(128, 32, 256, kNtStore), XPOSE_SHIFT(64, 32, 128, kNtStore),
+    XPOSE_SHIFT(4, 64, 64, 256, kNtStore),
+    XPOSE_SHIFT(4, 64, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(4, 128, 64, 256, kNtStore),
+    XPOSE_SHIFT(4, 128, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(4, 256, 64, 256, kNtStore),
+    XPOSE_SHIFT(4, 256, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(4, 128, 32, 256, kNtStore), XPOSE_SHIFT(4, 64, 32, 128, kNtStore),
     XPOSE_TILE(4, 64, 64, 256, kSwizzle, kNtLoadStore),
     // 2-byte elements
     XPOSE_TILES(2, 32, 32, 64), XPOSE_TILES(2, 32, 64, 128),
     XPOSE_TILES(2, 64, 32, 128), XPOSE_TILES(2, 64, 64, 128),
     XPOSE_TILES(2, 64, 64, 256), XPOSE_TILES(2, 128, 128, 256),
     XPOSE_TILES(2, 64, 128, 256), XPOSE_TILES(2, 128, 64, 256),
+    // Line-aligned output tiles (2-byte elements).
+    XPOSE_SHIFT(2, 64, 64, 256, kNtStore),
+    XPOSE_SHIFT(2, 64, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(2, 128, 64, 256, kNtStore),
+    XPOSE_SHIFT(2, 128, 64, 256, kCacheDefault),
+    XPOSE_SHIFT(2, 256, 64, 256, kNtStore),
     // 2-byte elements through LDS transpose reads
     XPOSE_TR(2, 64, 64, 256, kNtStore, false),
     XPOSE_TR(2, 64, 64, 256, kCacheDefault, false),
@@ -769,6 +798,12 @@ static const TileKernel kTileKernels[] = {
     // 8-byte elements
     XPOSE_TILES(8, 32, 32, 128),
     XPOSE_TILES(8, 32, 32, 256), XPOSE_TILES(8, 64, 64, 256),
+    // Line-aligned output tiles (8-byte elements).
+    XPOSE_SHIFT(8, 32, 32, 256, kNtStore),
+    XPOSE_SHIFT(8, 32, 32, 256, kCacheDefault),
+    XPOSE_SHIFT(8, 64, 32, 256, kNtStore),
+    XPOSE_SHIFT(8, 64, 64, 256, kNtStore),
+    XPOSE_SHIFT(8, 64, 64, 256, kCacheDefault),
 };
 
 const TileKernel *tile_kernels(int *count) {

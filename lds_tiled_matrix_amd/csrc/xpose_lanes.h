@@ -139,28 +139,45 @@ XPOSE_HD inline void lane_map(int wt, int lane, int &row,
 }
 
 
-// Line-aligned output tiles (4-byte elements): the LDS tile holds TR + 32
-// input rows; each output row's segment is shifted onto a 128-byte line.
-template <int TR, int TC, int NT, int CP>
+// Line-aligned output tiles (2-, 4- and 8-byte elements): the LDS tile holds
+// the HALO = 128 / S input rows above the tile as well, laid out as an
+// ordinary swizzled tile of TR + HALO rows (Base); each output row's segment
+// is shifted back onto a 128-byte line.  gather() assembles the 16-byte
+// output vector whose first element is input row `rel` of the LDS tile
+// (counted in input rows): for 2-byte elements `rel` may be odd, and the
+// vector then straddles two packed units in each word, which one byte
+// funnel shift (v_alignbyte) per word puts back together.
+template <int S, int TR, int TC, int NT, int CP>
 struct ShiftTile {
-  static constexpr int HALO = 32;             // fp32 elements per line
-  static constexpr int P = TR + HALO;         // LDS rows
-  static constexpr int NCI = TC / 4;          // 16-B chunks per input row
-  static constexpr int NCO = TR / 4;          // 16-B chunks per output segment
-  static constexpr int NCL = TC / 4;          // 16-B chunks per LDS row
+  static constexpr int HALO = 128 / S;        // elements per 128-byte line
+  static constexpr int PR = TR + HALO;        // input rows held in LDS
+  using Base = Tile<S, PR, TC, NT, kSwizzle, CP>;
+  using U = typename Base::U;
+  static constexpr int K = Base::K, V = Base::V, UPV = Base::UPV;
+  static constexpr int NCO = TR / V;          // 16-B chunks per output segment
   static constexpr int NW = NT / 64;
-  static constexpr int LIT = P * NCI / NT;
-  static constexpr int SIT = TC * NCO / NT;
-  static constexpr int LDS_BYTES = P * TC * 4;
+  static constexpr int SIT = TC * NCO / NT;   // store tasks per lane
+  // Packed units: one spare unit row after the tile, so the fifth unit a
+  // gather reads (used only when the segment starts mid-unit) is always
+  // inside the array and never aliases a bank the other lanes read.
+  static constexpr int LDS_UNITS = Base::LDS_UNITS + (K > 1 ? TC : 0);
+  static constexpr int LDS_BYTES = LDS_UNITS * (int)sizeof(U);
+  static_assert(S == 2 || S == 4 || S == 8, "2-, 4- or 8-byte elements");
   static_assert(TR % HALO == 0, "segments must stay line-aligned");
-  static_assert(P * NCI % NT == 0 && TC * NCO % NT == 0, "even task split");
-  static_assert(NCI <= 64 && 64 % NCI == 0, "rows fit a wave");
-  static_assert((NCL & (NCL - 1)) == 0, "power-of-two chunks");
-  XPOSE_HD static inline int lds_index(int p, int c) {
-    return p * TC + (((c >> 2) ^ ((p >> 2) & (NCL - 1))) << 2) + (c & 3);
+  static_assert(TC * NCO % NT == 0 && SIT >= 1, "even store split");
+  // Unit (Base::U) index of unit row `ur` (at most Base::P, the spare
+  // row), column c.
+  XPOSE_HD static inline int unit_index(int ur, int c) {
+    return Base::lds_index(ur, c);
   }
+  // First unit row and byte shift of the vector starting at input row rel.
+  XPOSE_HD static inline void gather_rows(int rel, int &ur, int &shift) {
+    ur = rel / K;
+    shift = (rel % K) * S;
+  }
+  // Unit rows gather() reads: UPV, plus one to funnel-shift across units.
+  static constexpr int GATHER_UNITS = K > 1 ? UPV + 1 : UPV;
 };
-
 
 // Transpose-read tiles (1- and 2-byte elements): input rows unchanged in
 // LDS, 8-byte units XOR-permuted per row (the full reasoning is with the

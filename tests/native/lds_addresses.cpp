@@ -79,37 +79,43 @@ static void tiles() {
   tile<S, TR, TC, NT, kSwizzle>();
 }
 
-// Line-aligned output tiles: the shift patterns of every output pitch
-// (mod 32 words) at three base addresses (d_j = (base + j * ld_out) mod 32
-// in 4-byte words).
-template <int TR, int TC, int NT>
+// Line-aligned output tiles: the phase-1 writes of the underlying swizzled
+// tile of TR + 128 / S rows, and the shifted gathers for the segment starts
+// of every output pitch (mod one line) at three base addresses: output row
+// j starts d_j = ((base + j * ld_out * S) mod 128) / S elements past a line.
+template <int S, int TR, int TC, int NT>
 static void shift() {
-  using T = ShiftTile<TR, TC, NT, kCacheDefault>;
+  using T = ShiftTile<S, TR, TC, NT, kCacheDefault>;
+  using B = typename T::Base;
   char name[96];
-  snprintf(name, sizeof name, "shift/s4/%dx%d/%d/swizzle", TR, TC, NT);
+  snprintf(name, sizeof name, "shift/s%d/%dx%d/%d/swizzle", S, TR, TC, NT);
+  constexpr int UB = (int)sizeof(typename B::U);
   int a[64];
-  for (int wave = 0; wave < T::NW; ++wave) {
-    for (int it = 0; it < T::LIT; ++it) {
-      for (int lane = 0; lane < 64; ++lane) {
-        int p, ch;
-        lane_map<T::NCI, false>(it * T::NW + wave, lane, p, ch);
-        a[lane] = T::lds_index(p, ch * 4) * 4;
+  for (int wave = 0; wave < B::NW; ++wave)
+    for (int it = 0; it < B::LIT; ++it)
+      for (int g = 0; g < B::V / B::UPV; ++g) {
+        for (int lane = 0; lane < 64; ++lane) {
+          int p, ch;
+          lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
+          a[lane] = B::lds_index(p, ch * B::V + g * B::UPV) * UB;
+        }
+        emit(name, "write", 16, 1, a);
       }
-      emit(name, "write", 16, 1, a);
-    }
-    for (int ld = 0; ld < 32; ++ld)
-      for (int base : {0, 5, 31})
+  for (int wave = 0; wave < T::NW; ++wave)
+    for (int ld = 0; ld < 128 / S; ++ld)
+      for (int base : {0, (5 * S) % 128, 128 - S})
         for (int it = 0; it < T::SIT; ++it)
-          for (int x = 0; x < 4; ++x) {
+          for (int k = 0; k < T::GATHER_UNITS; ++k) {
             for (int lane = 0; lane < 64; ++lane) {
               int c, q;
               lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
-              const int d = (base + c * ld) & 31;
-              a[lane] = T::lds_index(T::HALO - d + 4 * q + x, c) * 4;
+              const int d = ((base + c * ld * S) & 127) / S;
+              int ur, shift;
+              T::gather_rows(T::HALO - d + T::V * q, ur, shift);
+              a[lane] = T::unit_index(ur + k, c) * UB;
             }
-            emit(name, "read", 4, 0, a);
+            emit(name, "read", UB, 0, a);
           }
-  }
 }
 
 // Transpose-read tiles: chunk writes and the transpose reads.
@@ -154,12 +160,13 @@ int main() {
   tiles<4, 64, 128, 256>(); tiles<4, 128, 64, 256>();
   tiles<4, 128, 128, 256>(); tiles<4, 32, 128, 256>();
   tiles<4, 128, 32, 256>();
-  shift<64, 64, 256>(); shift<128, 64, 256>(); shift<256, 64, 256>();
-  shift<128, 32, 256>(); shift<64, 32, 128>();
+  shift<4, 64, 64, 256>(); shift<4, 128, 64, 256>(); shift<4, 256, 64, 256>();
+  shift<4, 128, 32, 256>(); shift<4, 64, 32, 128>();
   // 2-byte elements
   tiles<2, 32, 32, 64>(); tiles<2, 32, 64, 128>(); tiles<2, 64, 32, 128>();
   tiles<2, 64, 64, 128>(); tiles<2, 64, 64, 256>(); tiles<2, 128, 128, 256>();
   tiles<2, 64, 128, 256>(); tiles<2, 128, 64, 256>();
+  shift<2, 64, 64, 256>(); shift<2, 128, 64, 256>(); shift<2, 256, 64, 256>();
   tr<2, 64, 64, 256, false>(); tr<2, 128, 64, 256, false>();
   tr<2, 64, 128, 256, false>(); tr<2, 128, 128, 256, false>();
   tr<2, 64, 32, 128, false>(); tr<2, 64, 64, 256, true>();
@@ -173,5 +180,6 @@ int main() {
   // 8-byte elements
   tiles<8, 32, 32, 128>(); tiles<8, 32, 32, 256>();
   tiles<8, 64, 64, 256>();
+  shift<8, 32, 32, 256>(); shift<8, 64, 32, 256>(); shift<8, 64, 64, 256>();
   return 0;
 }

@@ -253,8 +253,14 @@ def test_align_out_option():
     assert plan(rows=1000, cols=512, opts=X.make_opts(flags=X.FLAG_NO_ALIGN_OUT))[1].aligned_out == 0
     rc, info = plan(rows=1024, cols=512, opts=X.make_opts(tile=(64, 64), flags=X.FLAG_ALIGN_OUT))
     assert rc == 0 and info.aligned_out == 1 and info.tiles == 17 * 8
-    # not for other element sizes or layouts, nor with contradicting flags
-    assert plan(dtype=X.XPOSE_F16, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
+    # 2- and 8-byte elements on request; not 1-byte elements, other layouts
+    # or contradicting flags
+    for dt, s in ((X.XPOSE_F16, 2), (X.XPOSE_BF16, 2), (X.XPOSE_F64, 8)):
+        rc, info = plan(rows=1000, cols=512, ld_out=1001, dtype=dt,
+                        opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))
+        assert rc == 0 and info.aligned_out == 1
+        assert info.tiles == -(-(1000 + 128 // s - 1) // info.tile_rows) * -(-512 // info.tile_cols)
+    assert plan(dtype=X.XPOSE_U8, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.make_opts(layout=X.LAYOUT_PAD1, flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.make_opts(flags=X.FLAG_ALIGN_OUT | X.FLAG_ELEMENTWISE))[0] == X.XPOSE_EINVAL
     # an explicit knob with no aligned-out kernel falls back to the ordinary

@@ -356,29 +356,41 @@ def test_direct_lds_kernels(s):
                    label=tag + " batch")
 
 
-def test_aligned_out_kernels():
-    """Line-aligned output tiles (fp32): every built shape and cache policy,
-    output pitches and pointers at every 4-byte offset within a line, edge
-    tiles in both dimensions, batches with odd strides."""
+SHIFT_TILES = {4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32)),
+               2: ((64, 64), (128, 64), (256, 64)),
+               8: ((32, 32), (64, 32), (64, 64))}
+
+
+@pytest.mark.parametrize("s", sorted(SHIFT_TILES))
+def test_aligned_out_kernels(s):
+    """Line-aligned output tiles: every built shape and cache policy, output
+    pitches and pointers at many element offsets within a line (odd ones for
+    2-byte elements, where segments start mid-unit), edge tiles in both
+    dimensions, batches with odd strides."""
     built = []
-    for tile in ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32)):
+    for tile in SHIFT_TILES[s]:
         for cache in (X.CACHE_DEFAULT, X.CACHE_NT_STORE):
             opts = X.make_opts(X.LAYOUT_SWIZZLE, tile, X.FLAG_ALIGN_OUT, cache)
             rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8, 8, 0,
-                                    0, X.XPOSE_F32, opts)
+                                    0, DTYPE_OF_SIZE[s], opts)
             if rc == 0:
                 assert info.aligned_out == 1
                 built.append((tile, cache, opts))
-    assert len(built) >= 5
+    assert len(built) >= len(SHIFT_TILES[s])
+    line = 128 // s
     for tile, cache, opts in built:
-        tag = f"align-out {tile} c{cache}"
-        for r, c, pad, shift in ((777, 555, 3, 0), (2 * tile[0] + 31, 130, 0, 5),
-                                 (1000, 3 * tile[1], 13, 31), (33, 7, 1, 2),
-                                 (tile[0], tile[1], 32, 0)):
-            check_case(4, 1, r, c, ld_out=r + pad, out_shift=shift,
+        tag = f"align-out s{s} {tile} c{cache}"
+        for r, c, pad, shift in ((777, 555, 3, 0), (2 * tile[0] + line - 1, 130, 0, 5),
+                                 (1000, 3 * tile[1], 13, line - 1), (33, 7, 1, 2),
+                                 (tile[0], tile[1], line, 0), (301, 99, 1, 1)):
+            check_case(s, 1, r, c, ld_out=r + pad, out_shift=shift,
                        seed=r + c + cache, opts=opts, label=tag)
-        check_case(4, 3, 301, 257, ld_out=305, stride_out=257 * 305 + 9,
+        check_case(s, 3, 301, 257, ld_out=305, stride_out=257 * 305 + 9,
                    seed=3, opts=opts, label=tag + " batch")
+        # input rows off alignment as well
+        check_case(s, 1, 2 * tile[0] + 3, tile[1] + 5, ld_in=tile[1] + 6,
+                   ld_out=2 * tile[0] + 7, in_shift=1, out_shift=3, seed=4,
+                   opts=opts, label=tag + " in-shift")
 
 
 TR_TILES = {2: ((64, 64), (128, 64), (64, 128), (128, 128), (64, 32)),

@@ -74,12 +74,13 @@ def test_plan_status_matches_contract(out, inp, batch, rows, cols, pad_in,
 def test_every_default_plan_has_a_kernel(rows, cols, batch, dtype):
     """Whatever the shape, the default launch resolves to a built kernel and
     covers the matrix with whole tiles (line-aligned output tiles shift
-    segments back by up to 31 rows, hence up to one more tile row)."""
+    segments back by up to one line less one element, hence up to one more
+    tile row)."""
     rc, info = X.xpose_plan(1 << 40, 1 << 44, batch, rows, cols, cols, rows,
                             rows * cols, rows * cols, dtype, None)
     assert rc == 0
-    extra = 31 if info.aligned_out else 0
-    assert info.aligned_out in (0, 1) and (not extra or dtype == 0)
+    extra = 128 // ELEM[dtype] - 1 if info.aligned_out else 0
+    assert info.aligned_out in (0, 1) and (not extra or dtype in (0, 1, 2, 4))
     per = -(-(rows + extra) // info.tile_rows) * -(-cols // info.tile_cols)
     assert info.tiles == batch * per
     assert info.lds_bytes > 0 and info.threads in (64, 128, 256)
