@@ -141,8 +141,8 @@ def test_pitches_and_padding_untouched(s):
 
 @pytest.mark.parametrize("s", SIZES)
 def test_unaligned_pointers(s):
-    """Base pointers shifted by one element: 2- and 1-byte types lose the
-    128-bit path, 4-byte types keep it at dword alignment."""
+    """Base pointers shifted by one element: every element size keeps the
+    128-bit path (unaligned dwordx4 for 1- and 2-byte types)."""
     for shift_in, shift_out in ((1, 0), (0, 1), (3, 5)):
         check_case(s, 1, 150, 90, seed=shift_in * 7 + shift_out,
                    in_shift=shift_in, out_shift=shift_out, label="shift")
