@@ -1,0 +1,68 @@
+/* The C ABI from plain C99: include/xpose.h must compile as C with every
+ * warning an error, and a C caller must see the same struct layouts and
+ * host-only results as the Python binding.  Prints:
+ *   size <struct> <bytes>
+ *   offset <struct>.<field> <bytes>
+ *   const <name> <value>
+ *   plan <rc> <field>=<value> ...     (for the calls in main)
+ *   strerror <code> <text>
+ */
+#include <stddef.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "xpose.h"
+
+#define SIZE(T) printf("size %s %zu\n", #T, sizeof(T))
+#define OFF(T, F) printf("offset %s.%s %zu\n", #T, #F, offsetof(T, F))
+#define CONST(N) printf("const %s %d\n", #N, (int)(N))
+
+static void plan(const char *tag, void *out, const void *in, int64_t batch,
+                 int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
+                 int32_t dtype, const xpose_opts *opts) {
+  xpose_plan_info info;
+  memset(&info, 0xff, sizeof info);
+  const int rc = xpose_plan(out, in, batch, rows, cols, ld_in, ld_out,
+                            rows * ld_in, cols * ld_out, dtype, opts, &info);
+  printf("plan %s %d", tag, rc);
+  if (rc == XPOSE_OK)
+    printf(" layout=%d tile_rows=%d tile_cols=%d threads=%d lds_bytes=%d "
+           "vector_path=%d tiles=%lld launches=%d cache=%d aligned_out=%d "
+           "tr_read=%d",
+           info.layout, info.tile_rows, info.tile_cols, info.threads,
+           info.lds_bytes, info.vector_path, (long long)info.tiles,
+           info.launches, info.cache, info.aligned_out, info.tr_read);
+  printf("\n");
+}
+
+int main(void) {
+  SIZE(xpose_opts);
+  OFF(xpose_opts, layout); OFF(xpose_opts, flags); OFF(xpose_opts, threads);
+  OFF(xpose_opts, persistent);
+  SIZE(xpose_plan_info);
+  OFF(xpose_plan_info, vector_path); OFF(xpose_plan_info, tiles);
+  OFF(xpose_plan_info, launches); OFF(xpose_plan_info, tr_read);
+  SIZE(xpose_copy_opts);
+  OFF(xpose_copy_opts, cache);
+  CONST(XPOSE_F32); CONST(XPOSE_F16); CONST(XPOSE_BF16); CONST(XPOSE_U8);
+  CONST(XPOSE_F64);
+  CONST(XPOSE_OK); CONST(XPOSE_EINVAL); CONST(XPOSE_EALIAS);
+  CONST(XPOSE_EDTYPE); CONST(XPOSE_EHIP); CONST(XPOSE_EALIGN);
+  CONST(XPOSE_ENOTILE);
+  CONST(XPOSE_FLAG_TR_READ); CONST(XPOSE_FLAG_ALIGN_OUT);
+
+  char *const out = (char *)0x100000000000ull, *const in = (char *)0x200000000000ull;
+  plan("c2", out, in, 1, 8192, 8192, 8192, 8192, XPOSE_F32, NULL);
+  plan("c3", out, in, 1, 12345, 6789, 6789, 12345, XPOSE_F32, NULL);
+  plan("c4", out, in, 1, 16384, 16384, 16384, 16384, XPOSE_F16, NULL);
+  xpose_opts tr;
+  memset(&tr, 0, sizeof tr);
+  tr.flags = XPOSE_FLAG_TR_READ;
+  plan("c4tr", out, in, 1, 16384, 16384, 16384, 16384, XPOSE_F16, &tr);
+  plan("null", NULL, in, 1, 64, 64, 64, 64, XPOSE_F32, NULL);
+  plan("alias", in, in, 1, 64, 64, 64, 64, XPOSE_F32, NULL);
+  plan("dtype", out, in, 1, 64, 64, 64, 64, 9, NULL);
+  for (int code = 0; code >= -6; --code)
+    printf("strerror %d %s\n", code, xpose_strerror(code));
+  return 0;
+}
