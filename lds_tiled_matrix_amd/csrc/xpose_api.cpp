@@ -96,7 +96,9 @@ Default default_for(int s, bool row128, bool small, bool big, bool align) {
       if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
       return {128, 64, 256, kSwz, kNT, 32, 8, 0, kSup};
     case 1: return {128, 128, 256, kSwz, kNT, 16, 16, 1, kSup};
-    default: return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
+    default:
+      if (big) return {64, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
   }
 }
 

@@ -319,3 +319,13 @@ def test_auto_cache_takes_a_built_policy():
     explicit = X.make_opts(tile=(64, 32), flags=X.FLAG_TR_READ, cache=X.CACHE_DEFAULT)
     assert plan(rows=100, cols=100, ld_in=202, ld_out=206, dtype=X.XPOSE_F16,
                 opts=explicit)[0] == X.XPOSE_ENOTILE
+
+
+def test_big_f64_default_is_diagonal():
+    # more than 512 MiB read + write: 64 x 64 tiles in diagonal order
+    rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F64)
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (64, 64)
+    assert info.order == X.ORDER_DIAGONAL and info.cache == X.CACHE_NT_STORE
+    rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
+    assert info.order == X.ORDER_SUPER_TILES
