@@ -249,10 +249,14 @@ __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
   lds_to_global<T>(lds, dst, ld_out, wave, lane);
 }
 
-// Edge tile (or unaligned rows): the same LDS tile and lane maps, but every
-// global access is one element wide and bounds-checked against the rows and
-// columns left in the matrix.
-template <class T>
+// Edge tile: the same LDS tile and lane maps, with every global access
+// bounds-checked against the rows and columns left in the matrix.  With VEC
+// (the call may use 16-byte accesses) each whole 16-byte chunk or vector
+// inside the matrix still moves as one access and only the pieces that cross
+// the edge go element by element; without it (the element-wise path asked
+// for explicitly, or rows a direct-load kernel cannot take) every access is
+// one element.
+template <class T, bool VEC>
 __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
                                                  const char *src, char *dst,
                                                  int64_t ld_in, int64_t ld_out,
@@ -270,16 +274,18 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
 #pragma unroll
     for (int k = 0; k < T::K; ++k) {
       const int row = p * T::K + k;
-      E e[T::V];
+      const char *rs = src + ((int64_t)row * ld_in + ch * T::V) * S;
+      if (VEC && row < rows_left && (ch + 1) * T::V <= cols_left) {
+        v[k] = load16<T::CACHE>(rs);
+      } else {
+        E e[T::V];
 #pragma unroll
-      for (int x = 0; x < T::V; ++x) {
-        const int col = ch * T::V + x;
-        e[x] = (row < rows_left && col < cols_left)
-                   ? *reinterpret_cast<const E *>(
-                         src + ((int64_t)row * ld_in + col) * S)
-                   : E(0);
+        for (int x = 0; x < T::V; ++x)
+          e[x] = (row < rows_left && ch * T::V + x < cols_left)
+                     ? reinterpret_cast<const E *>(rs)[x]
+                     : E(0);
+        __builtin_memcpy(&v[k], e, 16);
       }
-      __builtin_memcpy(&v[k], e, 16);
     }
     typename T::U u[T::V];
     pack_units<S>(v, u);
@@ -292,16 +298,34 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
     lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
     const u32x4 o = read_column<T>(lds, c, q);
     if (c < cols_left) {
-      E e[T::V];
-      __builtin_memcpy(e, &o, 16);
+      char *d = dst + ((int64_t)c * ld_out + q * T::V) * S;
+      if (VEC && (q + 1) * T::V <= rows_left) {
+        store16<T::CACHE>(d, o);
+      } else {
+        E e[T::V];
+        __builtin_memcpy(e, &o, 16);
 #pragma unroll
-      for (int x = 0; x < T::V; ++x) {
-        const int row = q * T::V + x;
-        if (row < rows_left)
-          *reinterpret_cast<E *>(dst + ((int64_t)c * ld_out + row) * S) = e[x];
+        for (int x = 0; x < T::V; ++x)
+          if (q * T::V + x < rows_left) reinterpret_cast<E *>(d)[x] = e[x];
       }
     }
   }
+}
+
+template <class T>
+__device__ __forceinline__ void tile_edge(bool vec_ok, typename T::U *lds,
+                                          const char *src, char *dst,
+                                          int64_t ld_in, int64_t ld_out,
+                                          int64_t rows_left, int64_t cols_left,
+                                          int wave, int lane) {
+  // vec_ok is uniform over the launch, so every wave takes the same branch
+  // and reaches the barrier inside.
+  if (vec_ok)
+    tile_elementwise<T, true>(lds, src, dst, ld_in, ld_out, rows_left,
+                              cols_left, wave, lane);
+  else
+    tile_elementwise<T, false>(lds, src, dst, ld_in, ld_out, rows_left,
+                               cols_left, wave, lane);
 }
 
 // Where one tile lives.
@@ -343,8 +367,8 @@ __global__ __launch_bounds__(NT) void xpose_tile_kernel(TileArgs a) {
   if (p.vec)
     tile_vector<T>(lds, p.src, p.dst, a.ld_in, a.ld_out, wave, lane);
   else
-    tile_elementwise<T>(lds, p.src, p.dst, a.ld_in, a.ld_out, p.rows_left,
-                        p.cols_left, wave, lane);
+    tile_edge<T>(a.vec_ok, lds, p.src, p.dst, a.ld_in, a.ld_out, p.rows_left,
+                 p.cols_left, wave, lane);
 }
 
 // Persistent workgroups: workgroup w handles tiles w, w + G, w + 2G, ... of
@@ -381,8 +405,8 @@ __global__ __launch_bounds__(NT) void xpose_tile_persistent_kernel(
       if (more && next.vec) vector_load<T>(next.src, a.ld_in, wave, lane, r);
       lds_to_global<T>(lds[buf], cur.dst, a.ld_out, wave, lane);
     } else {
-      tile_elementwise<T>(lds[buf], cur.src, cur.dst, a.ld_in, a.ld_out,
-                          cur.rows_left, cur.cols_left, wave, lane);
+      tile_edge<T>(a.vec_ok, lds[buf], cur.src, cur.dst, a.ld_in, a.ld_out,
+                   cur.rows_left, cur.cols_left, wave, lane);
       if (more && next.vec) vector_load<T>(next.src, a.ld_in, wave, lane, r);
     }
     if (!more) break;
@@ -482,17 +506,16 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
       const int64_t row = top + p * T::K + k;
       const bool in_rows = row >= 0 && row < a.rows;
       const char *src = in + (row * a.ld_in + c0 + ch * T::V) * S;
-      if (cols_left >= TC) {
-        v[k] = in_rows
-                   ? load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src)
-                   : u32x4{0, 0, 0, 0};
+      if (!in_rows) {
+        v[k] = u32x4{0, 0, 0, 0};
+      } else if ((ch + 1) * T::V <= cols_left) {
+        v[k] = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src);
       } else {
         E e[T::V];
 #pragma unroll
         for (int x = 0; x < T::V; ++x)
-          e[x] = (in_rows && ch * T::V + x < cols_left)
-                     ? reinterpret_cast<const E *>(src)[x]
-                     : E(0);
+          e[x] = ch * T::V + x < cols_left ? reinterpret_cast<const E *>(src)[x]
+                                           : E(0);
         __builtin_memcpy(&v[k], e, 16);
       }
     }
@@ -634,21 +657,25 @@ __global__ __launch_bounds__(NT) void xpose_tr_kernel(TileArgs a) {
       }
     }
   } else {
+    // Edge tile: whole 16-byte chunks inside the matrix still move as one
+    // access when the call allows it (a.vec_ok is uniform over the launch).
 #pragma unroll
     for (int it = 0; it < T::LIT; ++it) {
       const int row = (it * T::NW + wave) * RPT + lane / T::NCL;
       const int ch = lane % T::NCL;
-      E e[T::V];
-#pragma unroll
-      for (int x = 0; x < T::V; ++x) {
-        const int col = ch * T::V + x;
-        e[x] = (row < p.rows_left && col < p.cols_left)
-                   ? *reinterpret_cast<const E *>(
-                         p.src + ((int64_t)row * a.ld_in + col) * S)
-                   : E(0);
-      }
+      const char *rs = p.src + ((int64_t)row * a.ld_in + ch * T::V) * S;
       u32x4 w;
-      __builtin_memcpy(&w, e, 16);
+      if (a.vec_ok && row < p.rows_left && (ch + 1) * T::V <= p.cols_left) {
+        w = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(rs);
+      } else {
+        E e[T::V];
+#pragma unroll
+        for (int x = 0; x < T::V; ++x)
+          e[x] = (row < p.rows_left && ch * T::V + x < p.cols_left)
+                     ? reinterpret_cast<const E *>(rs)[x]
+                     : E(0);
+        __builtin_memcpy(&w, e, 16);
+      }
       tr_write_chunk<T>(lds, row, ch, w);
     }
   }
@@ -671,7 +698,7 @@ __global__ __launch_bounds__(NT) void xpose_tr_kernel(TileArgs a) {
     const int c = cu * T::HR + i % T::HR;       // output row in the tile
     const int r = rb * 32 + (i / T::HR) * T::V;  // first input row
     char *dst = p.dst + ((int64_t)c * a.ld_out + r) * S;
-    if (p.vec) {
+    if (p.vec || (a.vec_ok && c < p.cols_left && r + T::V <= p.rows_left)) {
       store16<CP>(dst, o);
     } else if (c < p.cols_left) {
       E e[T::V];
