@@ -35,11 +35,12 @@ int elem_bytes_of(int32_t dtype) {
 
 // Default launch configuration, chosen from the measured sweeps over tile
 // shape, workgroup size, cache policy and tile order on MI355X.
-//   row128: every row start on both sides is 128-byte aligned (pointers,
-//     pitches, batch strides), so each tile row segment is whole cache
-//     lines.  Otherwise segments straddle lines: plain (write-back) stores
-//     then merge the partial lines in L2 and win over non-temporal ones,
-//     which write partial lines straight to memory.
+//   out_row128: every output row start is 128-byte aligned (pointer, pitch,
+//     batch stride), so each output segment is whole cache lines and
+//     non-temporal stores pay.  Otherwise segments straddle lines: plain
+//     (write-back) stores then merge the partial lines in L2 and win over
+//     non-temporal ones, which write partial lines straight to memory.  The
+//     input side's alignment does not enter: misaligned reads cost little.
 //   small: a batch of matrices of at most kSmallMatrixBytes each.  Resident
 //     workgroups then cover a few whole matrices, a dense window on both the
 //     input and the output side, and a taller tile with small super-tiles
@@ -70,7 +71,8 @@ constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
               kDiag = XPOSE_ORDER_DIAGONAL, kWB = XPOSE_CACHE_DEFAULT,
               kNT = XPOSE_CACHE_NT_STORE;
 
-Default default_for(int s, bool row128, bool small, bool big, bool align) {
+Default default_for(int s, bool out_row128, bool small, bool big,
+                    bool align) {
   if (align) {
     switch (s) {
       case 4:
@@ -79,7 +81,7 @@ Default default_for(int s, bool row128, bool small, bool big, bool align) {
       default: break;  // no line-aligned tiles for 1-byte elements
     }
   }
-  if (!row128) {
+  if (!out_row128) {
     switch (s) {
       case 4: return {128, 64, 256, kSwz, kWB, 32, 32, 1, kSup};
       case 2: return {64, 64, 256, kSwz, kWB, 16, 16, 1, kSup};
@@ -201,8 +203,6 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   // Kernel choice.
   const bool out_row128 = po % 128 == 0 && (ld_out * s) % 128 == 0 &&
                           (batch == 1 || (stride_out * s) % 128 == 0);
-  const bool row128 = out_row128 && pi % 128 == 0 && (ld_in * s) % 128 == 0 &&
-                      (batch == 1 || (stride_in * s) % 128 == 0);
   const bool small = batch > 1 && rows * cols * s <= kSmallMatrixBytes;
   int64_t call_bytes;
   const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
@@ -221,7 +221,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                                  XPOSE_FLAG_TR_READ)) ||
                  (opts->layout && opts->layout != XPOSE_LAYOUT_SWIZZLE) ||
                  opts->persistent));
-  Default d = default_for(s, row128, small, big,
+  Default d = default_for(s, out_row128, small, big,
                           want_align || (align_ok && !out_row128));
   const int layout = (opts && opts->layout) ? opts->layout : d.layout;
   plan->elem_bytes = s;
@@ -273,7 +273,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (!k && d.align_out && !want_align) {
     // The explicit tile, threads or cache exist only as ordinary tiles:
     // fall back to those, with their own defaults for the other knobs.
-    d = default_for(s, row128, small, big, false);
+    d = default_for(s, out_row128, small, big, false);
     k = lookup(d, false);
   }
   if (!k) return XPOSE_ENOTILE;

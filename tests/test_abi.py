@@ -329,3 +329,15 @@ def test_big_f64_default_is_diagonal():
     rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)
     assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.order == X.ORDER_SUPER_TILES
+
+
+def test_store_policy_follows_output_alignment():
+    # misaligned input rows with line-aligned output rows: non-temporal stores
+    rc, info = plan(rows=1024, cols=1000, ld_in=1001)
+    assert rc == 0 and info.cache == X.CACHE_NT_STORE and info.aligned_out == 0
+    rc, info = plan(rows=1024, cols=1000, dtype=X.XPOSE_U8, inp=IN + 1)
+    assert rc == 0 and info.cache == X.CACHE_NT_STORE
+    # output rows off the line: line-aligned output tiles (u8: write-back)
+    assert plan(rows=1000, cols=1024)[1].aligned_out == 1
+    rc, info = plan(rows=1000, cols=1024, dtype=X.XPOSE_U8)
+    assert rc == 0 and info.aligned_out == 0 and info.cache == X.CACHE_DEFAULT
