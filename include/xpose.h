@@ -139,7 +139,10 @@ enum {
  * Every choice gives bit-identical results. */
 typedef struct xpose_opts {
   int32_t layout;     /* xpose_layout                                        */
-  int32_t tile_rows;  /* 0 = default; else one of the built tile shapes      */
+  int32_t tile_rows;  /* 0 = default (if the default shape is not built with
+                         the requested layout, flags or workgroup size: the
+                         first built shape that is); else one of the built
+                         tile shapes                                         */
   int32_t tile_cols;  /* 0 = default                                         */
   int32_t flags;      /* XPOSE_FLAG_*                                        */
   int32_t cache;      /* xpose_cache                                         */

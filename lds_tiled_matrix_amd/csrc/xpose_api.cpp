@@ -244,13 +244,18 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   }
   int n = 0;
   const xpose::TileKernel *table = xpose::tile_kernels(&n);
-  auto lookup = [&](const Default &dd, bool align) {
+  const bool explicit_tile = opts && (opts->tile_rows || opts->tile_cols);
+  // Kernel with the resolved knobs.  any_tile: the default tile shape is not
+  // built with the requested layout, flags or workgroup size, so take the
+  // first built shape (table order) that is.
+  auto lookup = [&](const Default &dd, bool align, bool any_tile) {
     int tr = dd.tile_rows, tc = dd.tile_cols, nt = dd.threads;
-    if (opts && (opts->tile_rows || opts->tile_cols)) {
+    if (explicit_tile) {
       tr = opts->tile_rows;
       tc = opts->tile_cols;
       nt = 0;  // any built workgroup size; the largest is preferred
     }
+    if (any_tile) nt = 0;
     if (opts && opts->threads) nt = opts->threads;
     // An explicit cache policy must be built; otherwise the default one is
     // preferred, then any policy built for the requested kernel.
@@ -259,23 +264,29 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     const int tries = (opts && opts->cache) ? 1 : 3;
     const xpose::TileKernel *k = nullptr;
     for (int t = 0; t < tries && !k; ++t)
-      for (int i = 0; i < n; ++i)
-        if (table[i].elem_bytes == s && table[i].tile_rows == tr &&
-            table[i].tile_cols == tc && table[i].layout == layout &&
-            table[i].cache == want[t] - 1 && table[i].direct_lds == direct &&
-            table[i].aligned_out == align && table[i].tr_read == tr_read &&
-            (nt ? table[i].threads == nt
-                : (!k || table[i].threads > k->threads)))
-          k = &table[i];
+      for (int i = 0; i < n; ++i) {
+        const xpose::TileKernel &c = table[i];
+        if (c.elem_bytes != s || c.layout != layout ||
+            c.cache != want[t] - 1 || c.direct_lds != direct ||
+            c.aligned_out != align || c.tr_read != tr_read)
+          continue;
+        if (any_tile) {
+          if (!k && (!nt || c.threads == nt)) k = &c;
+        } else if (c.tile_rows == tr && c.tile_cols == tc &&
+                   (nt ? c.threads == nt : (!k || c.threads > k->threads))) {
+          k = &c;
+        }
+      }
     return k;
   };
-  const xpose::TileKernel *k = lookup(d, d.align_out || want_align);
+  const xpose::TileKernel *k = lookup(d, d.align_out || want_align, false);
   if (!k && d.align_out && !want_align) {
     // The explicit tile, threads or cache exist only as ordinary tiles:
     // fall back to those, with their own defaults for the other knobs.
     d = default_for(s, out_row128, small, big, false);
-    k = lookup(d, false);
+    k = lookup(d, false, false);
   }
+  if (!k && !explicit_tile) k = lookup(d, d.align_out || want_align, true);
   if (!k) return XPOSE_ENOTILE;
   const int tr = k->tile_rows, tc = k->tile_cols;
   const int persistent = opts ? opts->persistent : 0;

@@ -341,3 +341,14 @@ def test_store_policy_follows_output_alignment():
     assert plan(rows=1000, cols=1024)[1].aligned_out == 1
     rc, info = plan(rows=1000, cols=1024, dtype=X.XPOSE_U8)
     assert rc == 0 and info.aligned_out == 0 and info.cache == X.CACHE_DEFAULT
+
+
+def test_default_tile_falls_back_to_a_built_shape():
+    # fp32 with unaligned output rows: the default 128 x 64 tile has no
+    # direct-load unpadded kernel; the first built shape that has one is used
+    opts = X.make_opts(layout=X.LAYOUT_UNPADDED, flags=X.FLAG_DIRECT_LDS)
+    rc, info = plan(rows=1211, cols=1713, ld_out=1213, opts=opts)
+    assert rc == 0 and info.direct_lds == 1 and info.layout == X.LAYOUT_UNPADDED
+    # an explicit shape without such a kernel is still an error
+    opts = X.make_opts(layout=X.LAYOUT_UNPADDED, tile=(128, 64), flags=X.FLAG_DIRECT_LDS)
+    assert plan(rows=1211, cols=1713, ld_out=1213, opts=opts)[0] == X.XPOSE_ENOTILE
