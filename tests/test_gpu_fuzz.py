@@ -101,3 +101,64 @@ def test_random_tr_cases(seed):
                    in_shift=rng.choice((0, 0, 1, 2, 4)),
                    out_shift=rng.choice((0, 0, 2, 4)),
                    label=f"tr fuzz {seed}/{case}")
+
+
+SHIFT_TILES = {2: ((64, 64), (128, 64), (256, 64)),
+               4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32)),
+               8: ((32, 32), (64, 32), (64, 64))}
+
+
+def campaign_opts(rng, s):
+    """Any launch option set: the generic random options, transpose-read
+    tiles (1- and 2-byte elements) or line-aligned output tiles (2-, 4- and
+    8-byte elements), or the defaults."""
+    r = rng.random()
+    if r < 0.4:
+        return random_opts(rng, s)
+    cands = []
+    if r < 0.6 and s in (1, 2):
+        for _ in range(50):
+            fl = X.FLAG_TR_READ | rng.choice((0, X.FLAG_DIRECT_LDS, X.FLAG_ELEMENTWISE,
+                                              X.FLAG_XCD_REMAP))
+            cands.append(X.make_opts(X.LAYOUT_SWIZZLE, rng.choice(TR_TILES[s]), fl,
+                                     rng.choice((0, 1, 2)),
+                                     *rng.choice(((0, 0), (1, 0), (3, 5), (8, 32))), 0,
+                                     rng.choice((0, 1, 2))))
+    elif r < 0.85 and s in SHIFT_TILES:
+        for _ in range(50):
+            cands.append(X.make_opts(X.LAYOUT_SWIZZLE, rng.choice(SHIFT_TILES[s] + (None,)),
+                                     X.FLAG_ALIGN_OUT | rng.choice((0, 2, 4)),
+                                     rng.choice((0, 1, 2)),
+                                     *rng.choice(((0, 0), (1, 0), (3, 5), (16, 16))), 0,
+                                     rng.choice((0, 1, 2))))
+    for o in cands:
+        if X.xpose_plan(0x100000, 0x40000000, 1, 64, 64, 64, 64, 0, 0,
+                        DTYPE_OF_SIZE[s], o)[0] == 0:
+            return o
+    return None
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_campaign(chunk):
+    """25 seeds x 25 cases per chunk over every option family, pitches and
+    pointer offsets at every residue (a one-off run of 1,260 seeds of this
+    generator also passed)."""
+    for seed in range(chunk * 25, chunk * 25 + 25):
+        rng = random.Random(50000 + seed)
+        for case in range(25):
+            s = rng.choice((1, 2, 4, 8))
+            batch = rng.choice((1, 1, 1, 2, 3))
+            rows = rng.choice((1, rng.randint(1, 80), rng.randint(1, 900),
+                               rng.randint(200, 2000)))
+            cols = rng.choice((1, rng.randint(1, 80), rng.randint(1, 900),
+                               rng.randint(200, 2000)))
+            ld_in = cols + rng.choice((0, 0, 1, 2, 3, 5, 16, 37, 64))
+            ld_out = rows + rng.choice((0, 0, 1, 2, 3, 7, 32, 41, 64))
+            stride_in = rows * ld_in + rng.choice((0, 0, 5, 64, 3))
+            stride_out = cols * ld_out + rng.choice((0, 0, 3, 128, 1))
+            check_case(s, batch, rows, cols, ld_in=ld_in, ld_out=ld_out,
+                       stride_in=stride_in, stride_out=stride_out,
+                       seed=seed * 100 + case, opts=campaign_opts(rng, s),
+                       in_shift=rng.choice((0, 0, 1, 2, 3)),
+                       out_shift=rng.choice((0, 0, 1, 2, 5)),
+                       label=f"campaign {seed}/{case}")
