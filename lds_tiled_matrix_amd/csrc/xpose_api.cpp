@@ -535,7 +535,7 @@ const char *xpose_strerror(int code) {
     case XPOSE_EDTYPE: return "unknown dtype";
     case XPOSE_EHIP: return "HIP runtime error";
     case XPOSE_EALIGN: return "pointer not aligned to the element size";
-    case XPOSE_ENOTILE: return "no kernel built for the requested tile shape";
+    case XPOSE_ENOTILE: return "no kernel built for the requested options";
     default: return "unknown status code";
   }
 }
