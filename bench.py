@@ -140,6 +140,17 @@ def cpu_baseline(w, host_in, max_seconds=12.0, max_runs=6):
     }
 
 
+def system_info() -> dict:
+    """Device, toolchain and host the numbers were measured on."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "hip": torch.version.hip,
+            "torch": torch.__version__, "host_cpu": host_cpu_name(),
+            "host_cores": len(os.sched_getaffinity(0))}
+
+
 def host_cpu_name() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -341,9 +352,11 @@ def main(argv=None):
             "tile": f"{plan['tile_rows']}x{plan['tile_cols']}",
             "threads": plan["threads"], "workgroups": plan["tiles"],
             "cache": X.CACHE_NAMES[plan["cache"]],
-            "tile_order": f"super-tiles {plan['group_rows']}x{plan['group_cols']}"
-                          f"{', per-XCD ranges' if plan['xcd_remap'] else ''}",
+            "tile_order": (f"super-tiles {plan['group_rows']}x{plan['group_cols']}"
+                           if plan["order"] == X.ORDER_SUPER_TILES else "diagonal")
+                          + (", per-XCD ranges" if plan["xcd_remap"] else ""),
         },
+        "system": system_info(),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "frac_of_copy": round(d["median_GBps"] / copy_gbps, 4),
         "timing": d,
