@@ -127,7 +127,7 @@ enum {
                                   kernel returns XPOSE_ENOTILE                */
   XPOSE_FLAG_NO_ALIGN_OUT = 32, /* ordinary tiles even where line-aligned
                                   output tiles are the default               */
-  XPOSE_FLAG_TR_READ = 64      /* 1- and 2-byte elements, swizzled layout: the
+  XPOSE_FLAG_TR_READ = 64,     /* 1- and 2-byte elements, swizzled layout: the
                                   LDS tile holds the input rows unchanged and
                                   the column walk uses gfx950's LDS transpose
                                   reads (ds_read_b64_tr_b16 / _tr_b8) instead
@@ -135,6 +135,18 @@ enum {
                                   with XPOSE_FLAG_ALIGN_OUT (XPOSE_EINVAL);
                                   sizes without such a kernel return
                                   XPOSE_ENOTILE                              */
+  XPOSE_FLAG_PACKED = 128,     /* packed batch of small matrices: each
+                                  workgroup moves whole dense matrices
+                                  (ld_in = cols, ld_out = rows, strides =
+                                  rows * cols) as one contiguous block per
+                                  side.  The default for batches of dense
+                                  matrices of at most 4 KiB when no other
+                                  knob is set; with this flag, for any dense
+                                  matrix of at most 16 KiB (else
+                                  XPOSE_ENOTILE).  Not combined with the
+                                  tile flags (XPOSE_EINVAL)                  */
+  XPOSE_FLAG_NO_PACKED = 256   /* tiles even where the packed kernel is the
+                                  default                                     */
 };
 
 /* Optional knobs for the measured ablation.  Zero-initialise for defaults.
@@ -185,6 +197,9 @@ typedef struct xpose_plan_info {
   int32_t direct_lds;  /* 1 if interior tiles load straight into LDS         */
   int32_t aligned_out; /* 1 if output segments are shifted onto lines        */
   int32_t tr_read;     /* 1 if the column walk uses LDS transpose reads      */
+  int32_t packed;      /* packed small-matrix kernel: matrices per workgroup
+                          (tile_rows x tile_cols = one matrix, tiles =
+                          workgroups); 0 = tile kernels                      */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

@@ -33,6 +33,7 @@ NAIVE_NAMES = {LAYOUT_NAIVE_READ: "naive_read_coalesced",
 FLAG_ELEMENTWISE, FLAG_XCD_REMAP, FLAG_NO_XCD_REMAP = 1, 2, 4
 FLAG_DIRECT_LDS, FLAG_ALIGN_OUT, FLAG_NO_ALIGN_OUT = 8, 16, 32
 FLAG_TR_READ = 64
+FLAG_PACKED, FLAG_NO_PACKED = 128, 256
 CACHE_AUTO, CACHE_DEFAULT, CACHE_NT_STORE, CACHE_NT_ALL = 0, 1, 2, 3
 ORDER_AUTO, ORDER_SUPER_TILES, ORDER_DIAGONAL = 0, 1, 2
 CACHE_NAMES = {CACHE_DEFAULT: "default", CACHE_NT_STORE: "nt_store",
@@ -66,7 +67,7 @@ class XposePlanInfo(ctypes.Structure):
                 ("group_cols", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("persistent", ctypes.c_int32),
                 ("direct_lds", ctypes.c_int32), ("aligned_out", ctypes.c_int32),
-                ("tr_read", ctypes.c_int32)]
+                ("tr_read", ctypes.c_int32), ("packed", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

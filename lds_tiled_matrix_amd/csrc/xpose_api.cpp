@@ -129,6 +129,8 @@ bool extent(int64_t count, int64_t r, int64_t c, int64_t ld, int64_t st,
 }
 
 struct Plan {
+  const xpose::PackedKernel *packed;  // packed batch of small matrices
+  xpose::PackedArgs pk;
   const xpose::TileKernel *kernel;  // null for the naive kernels
   int persistent;                   // persistent workgroups per CU, 0 = none
   int naive;                        // 0, xpose::kNaiveRead or kNaiveWrite
@@ -139,6 +141,71 @@ struct Plan {
   int64_t batch_per_launch;
   bool empty;
 };
+
+// Packed batches of small matrices (xpose::PackedArgs): taken by default for
+// a batch of dense matrices of at most kPackedMaxBytes each, when no launch
+// knob asks for a tile; XPOSE_FLAG_PACKED asks for it for any dense matrix
+// that fits the workgroup's block, XPOSE_FLAG_NO_PACKED never.  Returns
+// kNotPacked to fall through to the tile kernels.
+constexpr int kNotPacked = 1;
+constexpr int64_t kPackedMaxBytes = 4096;
+
+int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
+                int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
+                int64_t stride_out, int s, const xpose_opts *opts,
+                Plan *plan) {
+  const int flags = opts ? opts->flags : 0;
+  const bool want = flags & XPOSE_FLAG_PACKED;
+  const bool knobs =
+      opts && (opts->layout || opts->tile_rows || opts->tile_cols ||
+               opts->threads || opts->persistent || opts->order ||
+               opts->group_rows || opts->group_cols ||
+               (flags & ~(XPOSE_FLAG_XCD_REMAP | XPOSE_FLAG_NO_XCD_REMAP |
+                          XPOSE_FLAG_PACKED)));
+  if (!want && (knobs || (flags & XPOSE_FLAG_NO_PACKED) || batch < 2))
+    return kNotPacked;
+  const int64_t m = rows * cols;  // fits: the extents were checked
+  const bool dense = ld_in == cols && ld_out == rows &&
+                     (batch == 1 || (stride_in == m && stride_out == m));
+  int n = 0;
+  const xpose::PackedKernel *table = xpose::packed_kernels(&n);
+  const int block = table[0].block_bytes;
+  if (!dense || m * s > block || (!want && m * s > kPackedMaxBytes))
+    return want ? XPOSE_ENOTILE : kNotPacked;
+  // Whole matrices per workgroup; where a multiple of 128 / gcd(m s, 128)
+  // fits, blocks are whole cache lines and non-temporal stores pay.
+  const int64_t mb = m * s;
+  int64_t g = 128, x = mb;
+  while (x) {  // gcd(mb, 128)
+    const int64_t t = g % x;
+    g = x;
+    x = t;
+  }
+  const int64_t unit = 128 / g, fit = block / mb;
+  const bool lines = unit <= fit;
+  const int64_t per = lines ? fit / unit * unit : fit;
+  const int cache =
+      (opts && opts->cache)
+          ? opts->cache
+          : ((lines && (uintptr_t)out % 128 == 0) ? XPOSE_CACHE_NT_STORE
+                                                 : XPOSE_CACHE_DEFAULT);
+  const xpose::PackedKernel *k = nullptr;
+  for (int i = 0; i < n; ++i)
+    if (table[i].elem_bytes == s && table[i].cache == cache - 1) k = &table[i];
+  if (!k) return want ? XPOSE_ENOTILE : kNotPacked;
+  plan->packed = k;
+  plan->elem_bytes = s;
+  plan->batch = batch;
+  plan->pk.out = const_cast<void *>(out);
+  plan->pk.in = in;
+  plan->pk.rows = (uint32_t)rows;
+  plan->pk.cols = (uint32_t)cols;
+  plan->pk.per_block = (uint32_t)per;
+  plan->tiles_per_matrix = 1;
+  // At most 2^30 workgroups per launch.
+  plan->batch_per_launch = per << 30;
+  return XPOSE_OK;
+}
 
 int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
               int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
@@ -151,7 +218,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const int known_flags = XPOSE_FLAG_ELEMENTWISE | XPOSE_FLAG_XCD_REMAP |
                           XPOSE_FLAG_NO_XCD_REMAP | XPOSE_FLAG_DIRECT_LDS |
                           XPOSE_FLAG_ALIGN_OUT | XPOSE_FLAG_NO_ALIGN_OUT |
-                          XPOSE_FLAG_TR_READ;
+                          XPOSE_FLAG_TR_READ | XPOSE_FLAG_PACKED |
+                          XPOSE_FLAG_NO_PACKED;
   if (opts && (opts->layout < XPOSE_LAYOUT_AUTO ||
                opts->layout > XPOSE_LAYOUT_NAIVE_WRITE ||
                (opts->flags & ~known_flags) != 0 ||
@@ -161,6 +229,10 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                 (opts->flags & (XPOSE_FLAG_NO_ALIGN_OUT |
                                 XPOSE_FLAG_ELEMENTWISE |
                                 XPOSE_FLAG_DIRECT_LDS |
+                                XPOSE_FLAG_TR_READ))) ||
+               ((opts->flags & XPOSE_FLAG_PACKED) &&
+                (opts->flags & (XPOSE_FLAG_NO_PACKED | XPOSE_FLAG_ELEMENTWISE |
+                                XPOSE_FLAG_DIRECT_LDS | XPOSE_FLAG_ALIGN_OUT |
                                 XPOSE_FLAG_TR_READ))) ||
                opts->cache < XPOSE_CACHE_AUTO ||
                opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
@@ -203,6 +275,11 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   // Kernel choice.
   const bool out_row128 = po % 128 == 0 && (ld_out * s) % 128 == 0 &&
                           (batch == 1 || (stride_out * s) % 128 == 0);
+  {
+    const int rc = plan_packed(out, in, batch, rows, cols, ld_in, ld_out,
+                               stride_in, stride_out, s, opts, plan);
+    if (rc != kNotPacked) return rc;
+  }
   const bool small = batch > 1 && rows * cols * s <= kSmallMatrixBytes;
   int64_t call_bytes;
   const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
@@ -370,6 +447,21 @@ hipError_t compute_units(int *out) {
 int run_plan(Plan &plan, void *stream) {
   if (plan.empty) return XPOSE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.packed) {
+    const int64_t mb = (int64_t)plan.pk.rows * plan.pk.cols * plan.elem_bytes;
+    for (int64_t b0 = 0; b0 < plan.batch; b0 += plan.batch_per_launch) {
+      xpose::PackedArgs a = plan.pk;
+      a.count = plan.batch - b0;
+      if (a.count > plan.batch_per_launch) a.count = plan.batch_per_launch;
+      a.in = static_cast<const char *>(a.in) + b0 * mb;
+      a.out = static_cast<char *>(a.out) + b0 * mb;
+      const uint32_t grid =
+          (uint32_t)((a.count + a.per_block - 1) / a.per_block);
+      const hipError_t e = plan.packed->launch(a, grid, st);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    return XPOSE_OK;
+  }
   if (plan.naive) {
     const hipError_t e =
         xpose::launch_naive(plan.args, plan.batch, plan.elem_bytes,
@@ -444,7 +536,19 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                            stride_in, stride_out, dtype, opts, &plan);
   if (info) {
     memset(info, 0, sizeof(*info));
-    if (rc == XPOSE_OK && !plan.empty && plan.naive) {
+    if (rc == XPOSE_OK && !plan.empty && plan.packed) {
+      const int64_t per = plan.pk.per_block;
+      info->tile_rows = (int32_t)plan.pk.rows;
+      info->tile_cols = (int32_t)plan.pk.cols;
+      info->threads = plan.packed->threads;
+      info->lds_bytes = plan.packed->block_bytes;
+      info->vector_path = 1;
+      info->tiles = (plan.batch + per - 1) / per;
+      info->launches = (int32_t)((plan.batch + plan.batch_per_launch - 1) /
+                                 plan.batch_per_launch);
+      info->cache = plan.packed->cache + 1;
+      info->packed = (int32_t)per;
+    } else if (rc == XPOSE_OK && !plan.empty && plan.naive) {
       const bool rd = plan.naive == XPOSE_LAYOUT_NAIVE_READ;
       info->layout = plan.naive;
       info->tile_rows = rd ? 1 : 256;

@@ -104,6 +104,25 @@ struct TileKernel {
 // Every compiled tile kernel; *count receives the table length.
 const TileKernel *tile_kernels(int *count);
 
+// Packed batches of small matrices: dense rows x cols matrices (ld = the
+// row length, stride = rows * cols), `per_block` whole matrices per
+// workgroup.  The block's input bytes are one contiguous range and so are
+// its output bytes: both move as 16-byte vectors, and the LDS holds the
+// block while each lane gathers its output elements.
+struct PackedArgs {
+  void *out;
+  const void *in;
+  uint32_t rows, cols;   // of one matrix
+  uint32_t per_block;    // matrices per workgroup
+  int64_t count;         // matrices in this launch
+};
+
+struct PackedKernel {
+  int elem_bytes, threads, block_bytes, cache;
+  hipError_t (*launch)(const PackedArgs &, uint32_t grid, hipStream_t);
+};
+const PackedKernel *packed_kernels(int *count);
+
 // Naive one-element-per-thread transpose (no LDS), `batch` matrices from
 // a.in / a.out (a.batch_first is ignored); the ablation baseline.
 hipError_t launch_naive(const TileArgs &a, int64_t batch, int elem_bytes,

@@ -167,7 +167,7 @@ def test_opts_select_layout_and_tile():
     assert plan(opts=X.make_opts(tile=(32, 32), threads=96))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(0, 48, 48, 0))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.XposeOpts(9, 0, 0, 0))[0] == X.XPOSE_EINVAL
-    assert plan(opts=X.XposeOpts(0, 0, 0, 128))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.XposeOpts(0, 0, 0, 512))[0] == X.XPOSE_EINVAL
 
 
 def test_large_batch_splits_launches():
@@ -352,3 +352,37 @@ def test_default_tile_falls_back_to_a_built_shape():
     # an explicit shape without such a kernel is still an error
     opts = X.make_opts(layout=X.LAYOUT_UNPADDED, tile=(128, 64), flags=X.FLAG_DIRECT_LDS)
     assert plan(rows=1211, cols=1713, ld_out=1213, opts=opts)[0] == X.XPOSE_ENOTILE
+
+
+def test_packed_batches_of_small_matrices():
+    dense = dict(batch=1000, rows=16, cols=16, stride_in=256, stride_out=256)
+    rc, info = plan(**dense)
+    assert rc == 0 and info.packed == 16 and info.tiles == -(-1000 // 16)
+    assert (info.tile_rows, info.tile_cols) == (16, 16)
+    assert info.cache == X.CACHE_NT_STORE and info.vector_path == 1
+    # 3 x 5 fp32 = 60 bytes: 32 matrices make whole lines, 256 fit a block
+    rc, info = plan(batch=10000, rows=3, cols=5, stride_in=15, stride_out=15)
+    assert rc == 0 and info.packed == 256
+    # the XCD flags leave it on; any other knob, a pitch or gap, a single
+    # matrix or a larger one selects the tiles
+    assert plan(**dense, opts=X.make_opts(flags=X.FLAG_XCD_REMAP))[1].packed == 16
+    assert plan(**dense, opts=X.make_opts(tile=(32, 32)))[1].packed == 0
+    assert plan(**dense, opts=X.make_opts(flags=X.FLAG_NO_PACKED))[1].packed == 0
+    assert plan(batch=1000, rows=16, cols=16, ld_in=17, stride_in=16 * 17,
+                stride_out=256)[1].packed == 0
+    assert plan(batch=1000, rows=16, cols=16, stride_in=260, stride_out=256)[1].packed == 0
+    assert plan(rows=16, cols=16)[1].packed == 0
+    assert plan(batch=8, rows=64, cols=64, stride_in=4096, stride_out=4096)[1].packed == 0
+    # asked for: any dense matrix that fits the 16 KiB block
+    want = X.make_opts(flags=X.FLAG_PACKED)
+    rc, info = plan(batch=8, rows=64, cols=64, stride_in=4096, stride_out=4096, opts=want)
+    assert rc == 0 and info.packed == 1
+    assert plan(rows=16, cols=16, opts=want)[1].packed >= 1
+    assert plan(batch=8, rows=128, cols=64, stride_in=8192, stride_out=8192,
+                opts=want)[0] == X.XPOSE_ENOTILE
+    assert plan(batch=8, rows=16, cols=16, ld_in=20, stride_in=320, stride_out=256,
+                opts=want)[0] == X.XPOSE_ENOTILE
+    assert plan(**dense, opts=X.make_opts(flags=X.FLAG_PACKED | X.FLAG_TR_READ))[0] == X.XPOSE_EINVAL
+    assert plan(**dense, opts=X.make_opts(flags=X.FLAG_PACKED | X.FLAG_NO_PACKED))[0] == X.XPOSE_EINVAL
+    # an output base off the line: write-back stores
+    assert plan(**dense, out=OUT + 4)[1].cache == X.CACHE_DEFAULT

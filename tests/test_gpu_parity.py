@@ -442,6 +442,34 @@ def test_tr_read_forced_elementwise():
         check_case(s, 2, 300, 259, seed=11, opts=opts, label=f"tr elementwise s{s}")
 
 
+PACKED_SHAPES = ((1, 1), (1, 7), (7, 1), (3, 5), (8, 8), (16, 16), (7, 100),
+                 (100, 7), (32, 32), (17, 33))
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_packed_small_matrices(s):
+    """Packed batches of dense small matrices: batches that end with a
+    partial workgroup, shifted pointers (write-back blocks), the forced
+    kernel on matrices up to the 16 KiB block, and a single matrix."""
+    for r, c in PACKED_SHAPES:
+        if r * c * s > 4096:
+            continue
+        for batch, shift in ((1000, 0), (37, 1), (2, 0), (513, 3)):
+            rc, info = X.xpose_plan(1 << 40, 1 << 44, batch, r, c, c, r, r * c,
+                                    r * c, DTYPE_OF_SIZE[s], None)
+            assert rc == 0 and info.packed >= 1, (r, c, batch)
+            check_case(s, batch, r, c, seed=r * 131 + c + batch,
+                       in_shift=shift, out_shift=shift,
+                       label=f"packed s{s} {batch}x{r}x{c}")
+    want = X.make_opts(flags=X.FLAG_PACKED)
+    for r, c in ((64, 64), (45, 91), (1, 2048 // s), (2048 // s, 2)):
+        if r * c * s <= 16384:
+            check_case(s, 19, r, c, seed=7, opts=want, label=f"packed forced s{s} {r}x{c}")
+    check_case(s, 1, 13, 29, seed=8, opts=want, label=f"packed single s{s}")
+    check_case(s, 300, 8, 8, seed=9, opts=X.make_opts(flags=X.FLAG_PACKED, cache=X.CACHE_DEFAULT),
+               label=f"packed write-back s{s}")
+
+
 def test_nontemporal_loads_variant():
     """Non-temporal loads and stores are built for two fp32 tiles only."""
     for tile in ((32, 32), (64, 64)):

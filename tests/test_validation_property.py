@@ -79,6 +79,13 @@ def test_every_default_plan_has_a_kernel(rows, cols, batch, dtype):
     rc, info = X.xpose_plan(1 << 40, 1 << 44, batch, rows, cols, cols, rows,
                             rows * cols, rows * cols, dtype, None)
     assert rc == 0
+    if info.packed:
+        # packed batch of small matrices: whole matrices per workgroup
+        assert batch > 1 and rows * cols * ELEM[dtype] <= 4096
+        assert (info.tile_rows, info.tile_cols) == (rows, cols)
+        assert info.packed * rows * cols * ELEM[dtype] <= info.lds_bytes
+        assert info.tiles == -(-batch // info.packed)
+        return
     extra = 128 // ELEM[dtype] - 1 if info.aligned_out else 0
     assert info.aligned_out in (0, 1) and (not extra or dtype in (0, 1, 2, 4))
     per = -(-(rows + extra) // info.tile_rows) * -(-cols // info.tile_cols)
