@@ -145,7 +145,7 @@ struct Plan {
 // Packed batches of small matrices (xpose::PackedArgs): taken by default for
 // a batch of dense matrices of at most kPackedMaxBytes each, when no launch
 // knob asks for a tile; XPOSE_FLAG_PACKED asks for it for any dense matrix
-// that fits the workgroup's block, XPOSE_FLAG_NO_PACKED never.  Returns
+// that fits the smallest block, XPOSE_FLAG_NO_PACKED never.  Returns
 // kNotPacked to fall through to the tile kernels.
 constexpr int kNotPacked = 1;
 constexpr int64_t kPackedMaxBytes = 4096;
@@ -169,11 +169,13 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
                      (batch == 1 || (stride_in == m && stride_out == m));
   int n = 0;
   const xpose::PackedKernel *table = xpose::packed_kernels(&n);
-  const int block = table[0].block_bytes;
-  if (!dense || m * s > block || (!want && m * s > kPackedMaxBytes))
+  const int small_block = table[0].block_bytes;
+  if (!dense || m * s > small_block || (!want && m * s > kPackedMaxBytes))
     return want ? XPOSE_ENOTILE : kNotPacked;
-  // Whole matrices per workgroup; where a multiple of 128 / gcd(m s, 128)
-  // fits, blocks are whole cache lines and non-temporal stores pay.
+  // Whole matrices per workgroup.  Where a multiple of 128 / gcd(m s, 128)
+  // fits a block (the smallest such block size is taken), blocks are whole
+  // cache lines and non-temporal stores pay; otherwise the smallest block,
+  // filled, with write-back stores.
   const int64_t mb = m * s;
   int64_t g = 128, x = mb;
   while (x) {  // gcd(mb, 128)
@@ -181,7 +183,14 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
     g = x;
     x = t;
   }
-  const int64_t unit = 128 / g, fit = block / mb;
+  const int64_t unit = 128 / g;
+  int block = small_block;
+  for (int i = 0; i < n; ++i)
+    if (unit * mb <= table[i].block_bytes) {
+      block = table[i].block_bytes;
+      break;
+    }
+  const int64_t fit = block / mb;
   const bool lines = unit <= fit;
   const int64_t per = lines ? fit / unit * unit : fit;
   const int cache =
@@ -190,8 +199,10 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
           : ((lines && (uintptr_t)out % 128 == 0) ? XPOSE_CACHE_NT_STORE
                                                  : XPOSE_CACHE_DEFAULT);
   const xpose::PackedKernel *k = nullptr;
-  for (int i = 0; i < n; ++i)
-    if (table[i].elem_bytes == s && table[i].cache == cache - 1) k = &table[i];
+  for (int i = 0; i < n && !k; ++i)
+    if (table[i].elem_bytes == s && table[i].block_bytes == block &&
+        table[i].cache == cache - 1)
+      k = &table[i];
   if (!k) return want ? XPOSE_ENOTILE : kNotPacked;
   plan->packed = k;
   plan->elem_bytes = s;

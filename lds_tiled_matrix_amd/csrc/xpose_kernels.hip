@@ -873,18 +873,29 @@ __global__ __launch_bounds__(NT) void xpose_packed_kernel(PackedArgs a) {
 
   // Phase 2: output element o of the block is element (j, i) of output
   // matrix g (o = g m + j rows + i), which is input element g m + i cols + j.
+  // The V elements of one vector step down an input column (stride cols);
+  // where the vector runs past the column's last row it continues at the
+  // next column's first row, and past the last column at the next matrix.
   for (uint32_t v = threadIdx.x; v < nv; v += NT) {
     const uint32_t o = v * V, g = o / m, t = o - g * m;
-    uint32_t j = t / rows, i = t - j * rows, base = g * m;
+    uint32_t j = t / rows, i = t - j * rows;
+    uint32_t at = g * m + i * cols + j;  // unsigned wrap-around is intended
     E e[V];
+    if (i + V <= rows) {
 #pragma unroll
-    for (int x = 0; x < V; ++x) {
-      e[x] = lds[base + i * cols + j];
-      if (++i == rows) {
-        i = 0;
-        if (++j == cols) {
-          j = 0;
-          base += m;
+      for (int x = 0; x < V; ++x) e[x] = lds[at + x * cols];
+    } else {
+#pragma unroll
+      for (int x = 0; x < V; ++x) {
+        e[x] = lds[at];
+        at += cols;
+        if (++i == rows) {  // row past the column: next column, row 0
+          i = 0;
+          at += 1 - m;
+          if (++j == cols) {  // past the last column: next matrix
+            j = 0;
+            at += m - cols;
+          }
         }
       }
     }
@@ -908,15 +919,18 @@ hipError_t launch_packed(const PackedArgs &a, uint32_t grid,
       dim3(grid), dim3(NT), args, 0, stream);
 }
 
-#define XPOSE_PACKED(S, CP) \
-  PackedKernel { S, 256, 16384, CP, &launch_packed<S, 256, 16384, CP> }
+#define XPOSE_PACKED(S, BB, CP) \
+  PackedKernel { S, 256, BB, CP, &launch_packed<S, 256, BB, CP> }
+#define XPOSE_PACKED_ALL(BB)                                               \
+  XPOSE_PACKED(1, BB, kNtStore), XPOSE_PACKED(1, BB, kCacheDefault),       \
+      XPOSE_PACKED(2, BB, kNtStore), XPOSE_PACKED(2, BB, kCacheDefault),   \
+      XPOSE_PACKED(4, BB, kNtStore), XPOSE_PACKED(4, BB, kCacheDefault),   \
+      XPOSE_PACKED(8, BB, kNtStore), XPOSE_PACKED(8, BB, kCacheDefault)
 
-static const PackedKernel kPackedKernels[] = {
-    XPOSE_PACKED(1, kNtStore), XPOSE_PACKED(1, kCacheDefault),
-    XPOSE_PACKED(2, kNtStore), XPOSE_PACKED(2, kCacheDefault),
-    XPOSE_PACKED(4, kNtStore), XPOSE_PACKED(4, kCacheDefault),
-    XPOSE_PACKED(8, kNtStore), XPOSE_PACKED(8, kCacheDefault),
-};
+// Smaller blocks first: the planner takes the first block size in which a
+// whole number of matrices makes whole cache lines.
+static const PackedKernel kPackedKernels[] = {XPOSE_PACKED_ALL(16384),
+                                              XPOSE_PACKED_ALL(32768)};
 
 const PackedKernel *packed_kernels(int *count) {
   *count = (int)(sizeof(kPackedKernels) / sizeof(kPackedKernels[0]));
