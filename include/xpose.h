@@ -140,11 +140,11 @@ enum {
                                   (ld_in = cols, ld_out = rows, strides =
                                   rows * cols) as one contiguous block per
                                   side.  The default for batches of dense
-                                  matrices of at most 4 KiB when no other
-                                  knob is set; with this flag, for any dense
-                                  matrix of at most 16 KiB (else
-                                  XPOSE_ENOTILE).  Not combined with the
-                                  tile flags (XPOSE_EINVAL)                  */
+                                  matrices of at most 16 KiB when no other
+                                  knob is set; with this flag, also for a
+                                  single such matrix (a larger or non-dense
+                                  one gives XPOSE_ENOTILE).  Not combined
+                                  with the tile flags (XPOSE_EINVAL)         */
   XPOSE_FLAG_NO_PACKED = 256   /* tiles even where the packed kernel is the
                                   default                                     */
 };

@@ -148,7 +148,7 @@ struct Plan {
 // that fits the smallest block, XPOSE_FLAG_NO_PACKED never.  Returns
 // kNotPacked to fall through to the tile kernels.
 constexpr int kNotPacked = 1;
-constexpr int64_t kPackedMaxBytes = 4096;
+constexpr int64_t kPackedMaxBytes = 16384;
 
 int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
                 int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
@@ -212,6 +212,8 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
   plan->pk.rows = (uint32_t)rows;
   plan->pk.cols = (uint32_t)cols;
   plan->pk.per_block = (uint32_t)per;
+  // Rows of 64 bytes or a multiple: pad the LDS rows (see the kernel).
+  plan->pk.pad = (cols * s) % 64 == 0 ? (s == 8 ? 1 : 4 / s) : 0;
   plan->tiles_per_matrix = 1;
   // At most 2^30 workgroups per launch.
   plan->batch_per_launch = per << 30;
@@ -552,7 +554,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->tile_rows = (int32_t)plan.pk.rows;
       info->tile_cols = (int32_t)plan.pk.cols;
       info->threads = plan.packed->threads;
-      info->lds_bytes = plan.packed->block_bytes;
+      info->lds_bytes = plan.packed->block_bytes + plan.packed->block_bytes / 8;
       info->vector_path = 1;
       info->tiles = (plan.batch + per - 1) / per;
       info->launches = (int32_t)((plan.batch + plan.batch_per_launch - 1) /

@@ -114,6 +114,7 @@ struct PackedArgs {
   const void *in;
   uint32_t rows, cols;   // of one matrix
   uint32_t per_block;    // matrices per workgroup
+  uint32_t pad;          // LDS padding per input row, in elements (0 = none)
   int64_t count;         // matrices in this launch
 };
 

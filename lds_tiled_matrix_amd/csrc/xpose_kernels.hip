@@ -849,12 +849,19 @@ const TileKernel *tile_kernels(int *count) {
 // mostly empty (a 16 x 16 fp32 matrix fills 1/32 of a 128 x 64 tile), this
 // keeps every global access whole and every lane busy.
 // ---------------------------------------------------------------------------
+// LDS padding.  Where input rows are a multiple of 64 bytes the output
+// vectors of a half-wave, which step down input columns, would fall on a few
+// banks; a pad of one 4-byte word (8 bytes for 8-byte elements) after every
+// input row makes the row stride odd in words.  Rows then start 4-byte but
+// not 16-byte aligned in LDS, so the padded block is written in 32-bit
+// words.  The pad adds at most 1/8 to the block.
 template <int S, int NT, int BB, int CP>
 __global__ __launch_bounds__(NT) void xpose_packed_kernel(PackedArgs a) {
   using E = typename Elem<S>::E;
   constexpr int V = 16 / S;
-  __shared__ __attribute__((aligned(16))) E lds[BB / S];
-  const uint32_t rows = a.rows, cols = a.cols, m = rows * cols;
+  __shared__ __attribute__((aligned(16))) E lds[(BB + BB / 8) / S];
+  const uint32_t rows = a.rows, cols = a.cols, m = rows * cols, pad = a.pad;
+  const uint32_t cs = cols + pad, mp = rows * cs;  // padded strides
   const int64_t m0 = (int64_t)blockIdx.x * a.per_block;  // first matrix
   const int64_t left = a.count - m0;
   const uint32_t nmat = left < a.per_block ? (uint32_t)left : a.per_block;
@@ -864,37 +871,52 @@ __global__ __launch_bounds__(NT) void xpose_packed_kernel(PackedArgs a) {
   const uint32_t nv = n / V;  // whole 16-byte vectors
 
   // Phase 1: the block's input bytes, in order, into LDS.
-  for (uint32_t v = threadIdx.x; v < nv; v += NT)
-    *reinterpret_cast<u32x4 *>(lds + v * V) =
-        load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src + v * 16);
-  for (uint32_t e = nv * V + threadIdx.x; e < n; e += NT)
-    lds[e] = reinterpret_cast<const E *>(src)[e];
+  if (pad == 0) {
+    for (uint32_t v = threadIdx.x; v < nv; v += NT)
+      *reinterpret_cast<u32x4 *>(lds + v * V) =
+          load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src + v * 16);
+    for (uint32_t e = nv * V + threadIdx.x; e < n; e += NT)
+      lds[e] = reinterpret_cast<const E *>(src)[e];
+  } else {
+    // Rows are whole 16-byte vectors here (cols * S is a multiple of 64).
+    for (uint32_t v = threadIdx.x; v < nv; v += NT) {
+      const uint32_t e = v * V;
+      const u32x4 w =
+          load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src + v * 16);
+      uint32_t *d = reinterpret_cast<uint32_t *>(lds + e + e / cols * pad);
+      d[0] = w.x;
+      d[1] = w.y;
+      d[2] = w.z;
+      d[3] = w.w;
+    }
+  }
   __syncthreads();
 
   // Phase 2: output element o of the block is element (j, i) of output
-  // matrix g (o = g m + j rows + i), which is input element g m + i cols + j.
-  // The V elements of one vector step down an input column (stride cols);
-  // where the vector runs past the column's last row it continues at the
-  // next column's first row, and past the last column at the next matrix.
+  // matrix g (o = g m + j rows + i), which is input element g m + i cols + j,
+  // at LDS element g mp + i cs + j.  The V elements of one vector step down
+  // an input column (stride cs); where the vector runs past the column's
+  // last row it continues at the next column's first row, and past the last
+  // column at the next matrix.
   for (uint32_t v = threadIdx.x; v < nv; v += NT) {
     const uint32_t o = v * V, g = o / m, t = o - g * m;
     uint32_t j = t / rows, i = t - j * rows;
-    uint32_t at = g * m + i * cols + j;  // unsigned wrap-around is intended
+    uint32_t at = g * mp + i * cs + j;  // unsigned wrap-around is intended
     E e[V];
     if (i + V <= rows) {
 #pragma unroll
-      for (int x = 0; x < V; ++x) e[x] = lds[at + x * cols];
+      for (int x = 0; x < V; ++x) e[x] = lds[at + x * cs];
     } else {
 #pragma unroll
       for (int x = 0; x < V; ++x) {
         e[x] = lds[at];
-        at += cols;
+        at += cs;
         if (++i == rows) {  // row past the column: next column, row 0
           i = 0;
-          at += 1 - m;
+          at += 1 - mp;
           if (++j == cols) {  // past the last column: next matrix
             j = 0;
-            at += m - cols;
+            at += mp - cols;
           }
         }
       }
@@ -905,7 +927,7 @@ __global__ __launch_bounds__(NT) void xpose_packed_kernel(PackedArgs a) {
   }
   for (uint32_t o = nv * V + threadIdx.x; o < n; o += NT) {
     const uint32_t g = o / m, t = o - g * m, j = t / rows, i = t - j * rows;
-    reinterpret_cast<E *>(dst)[o] = lds[g * m + i * cols + j];
+    reinterpret_cast<E *>(dst)[o] = lds[g * mp + i * cs + j];
   }
 }
 

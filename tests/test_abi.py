@@ -372,11 +372,10 @@ def test_packed_batches_of_small_matrices():
                 stride_out=256)[1].packed == 0
     assert plan(batch=1000, rows=16, cols=16, stride_in=260, stride_out=256)[1].packed == 0
     assert plan(rows=16, cols=16)[1].packed == 0
-    assert plan(batch=8, rows=64, cols=64, stride_in=4096, stride_out=4096)[1].packed == 0
-    # asked for: any dense matrix that fits the 16 KiB block
+    assert plan(batch=8, rows=64, cols=64, stride_in=4096, stride_out=4096)[1].packed == 1
+    assert plan(batch=8, rows=128, cols=64, stride_in=8192, stride_out=8192)[1].packed == 0
+    # asked for: also a single matrix
     want = X.make_opts(flags=X.FLAG_PACKED)
-    rc, info = plan(batch=8, rows=64, cols=64, stride_in=4096, stride_out=4096, opts=want)
-    assert rc == 0 and info.packed == 1
     assert plan(rows=16, cols=16, opts=want)[1].packed >= 1
     assert plan(batch=8, rows=128, cols=64, stride_in=8192, stride_out=8192,
                 opts=want)[0] == X.XPOSE_ENOTILE

@@ -443,16 +443,17 @@ def test_tr_read_forced_elementwise():
 
 
 PACKED_SHAPES = ((1, 1), (1, 7), (7, 1), (3, 5), (8, 8), (16, 16), (7, 100),
-                 (100, 7), (32, 32), (17, 33))
+                 (100, 7), (32, 32), (17, 33), (64, 16), (16, 64), (128, 32),
+                 (64, 64), (48, 48), (45, 91))
 
 
 @pytest.mark.parametrize("s", SIZES)
 def test_packed_small_matrices(s):
     """Packed batches of dense small matrices: batches that end with a
-    partial workgroup, shifted pointers (write-back blocks), the forced
-    kernel on matrices up to the 16 KiB block, and a single matrix."""
+    partial workgroup, shifted pointers (write-back blocks), rows of 64 bytes
+    or more (padded LDS rows), the forced kernel, and a single matrix."""
     for r, c in PACKED_SHAPES:
-        if r * c * s > 4096:
+        if r * c * s > 16384:
             continue
         for batch, shift in ((1000, 0), (37, 1), (2, 0), (513, 3)):
             rc, info = X.xpose_plan(1 << 40, 1 << 44, batch, r, c, c, r, r * c,
