@@ -114,3 +114,47 @@ def test_enumerated_shapes_are_the_built_ones(worst):
                     for v, fl in (("swizzle", 0), ("direct", X.FLAG_DIRECT_LDS)):
                         if _probe(s, tr, tc, nt, X.LAYOUT_SWIZZLE, X.FLAG_TR_READ | fl):
                             assert f"tr/s{s}/{tr}x{tc}/{nt}/{v}" in names
+
+
+def _packed_worst(rows, cols, s, pad, block=16384):
+    """Worst conflict degree of the packed kernel's gathers: lane l of a wave
+    builds output vector v = base + l, whose element x is input element
+    g m + i cols + j of the block, held at LDS element g mp + i cs + j
+    (cs = cols + pad, mp = rows cs); the reads are s-byte (8-byte units for
+    f64, else the 4-byte word holding the element)."""
+    v_el = 16 // s
+    m = rows * cols
+    n = max(1, block // (m * s)) * m
+    cs, mp = cols + pad, rows * (cols + pad)
+    width = 8 if s == 8 else 4
+    worst = 1
+    for base in range(0, min(n // v_el, 1024), 64):
+        for x in range(v_el):
+            addrs = []
+            for lane in range(64):
+                o = (base + lane) * v_el + x
+                if o >= n:
+                    addrs.append(-1)
+                    continue
+                g, t = divmod(o, m)
+                j, i = divmod(t, rows)
+                addrs.append((g * mp + i * cs + j) * s // width * width)
+            worst = max(worst, degree(width, 0, addrs))
+    return worst
+
+
+def test_packed_padding_spreads_column_reads():
+    """Rows of 64 bytes or a multiple get one word of padding (8 bytes for
+    f64) per row; it takes the worst gather of every such shape down to
+    4-way at most, from up to 32-way."""
+    before = after = 0
+    for s in (1, 2, 4, 8):
+        pad = 1 if s == 8 else 4 // s
+        for rows, cols in ((16, 16), (32, 32), (128, 32), (64, 64), (32, 128),
+                           (64, 16), (16, 64), (128, 128), (16, 128)):
+            if (cols * s) % 64 or rows * cols * s > 16384:
+                continue
+            u, p = _packed_worst(rows, cols, s, 0), _packed_worst(rows, cols, s, pad)
+            assert p <= 4 and p <= u, (s, rows, cols, u, p)
+            before, after = max(before, u), max(after, p)
+    assert before == 32 and after == 4
