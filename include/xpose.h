@@ -139,12 +139,14 @@ enum {
                                   workgroup moves whole dense matrices
                                   (ld_in = cols, ld_out = rows, strides =
                                   rows * cols) as one contiguous block per
-                                  side.  The default for batches of dense
-                                  matrices of at most 16 KiB when no other
-                                  knob is set; with this flag, also for a
-                                  single such matrix (a larger or non-dense
-                                  one gives XPOSE_ENOTILE).  Not combined
-                                  with the tile flags (XPOSE_EINVAL)         */
+                                  side.  The default, when no other knob is
+                                  set, for batches of dense matrices of at
+                                  most 16 KiB, or 32 KiB when the matrix is
+                                  not a whole number of 64 x 64 tiles (128 x
+                                  128 for 1-byte elements); with this flag,
+                                  for any dense matrix of at most 32 KiB,
+                                  a single one too (else XPOSE_ENOTILE).  Not
+                                  combined with the tile flags (XPOSE_EINVAL)*/
   XPOSE_FLAG_NO_PACKED = 256   /* tiles even where the packed kernel is the
                                   default                                     */
 };

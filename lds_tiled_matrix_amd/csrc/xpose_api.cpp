@@ -142,13 +142,16 @@ struct Plan {
   bool empty;
 };
 
-// Packed batches of small matrices (xpose::PackedArgs): taken by default for
-// a batch of dense matrices of at most kPackedMaxBytes each, when no launch
-// knob asks for a tile; XPOSE_FLAG_PACKED asks for it for any dense matrix
-// that fits the smallest block, XPOSE_FLAG_NO_PACKED never.  Returns
-// kNotPacked to fall through to the tile kernels.
+// Packed batches of small matrices (xpose::PackedArgs): taken by default,
+// when no launch knob asks for a tile, for a batch of dense matrices of at
+// most kPackedMaxBytes each, or of at most kPackedRaggedBytes when the
+// matrix is not a whole number of 64 x 64 tiles (128 x 128 for 1-byte
+// elements; whole-tile matrices of that size run faster on the tiles);
+// XPOSE_FLAG_PACKED asks for it for any dense matrix that fits the largest
+// block, XPOSE_FLAG_NO_PACKED never.  Returns kNotPacked to fall through to
+// the tile kernels.
 constexpr int kNotPacked = 1;
-constexpr int64_t kPackedMaxBytes = 16384;
+constexpr int64_t kPackedMaxBytes = 16384, kPackedRaggedBytes = 32768;
 
 int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
                 int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
@@ -169,13 +172,16 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
                      (batch == 1 || (stride_in == m && stride_out == m));
   int n = 0;
   const xpose::PackedKernel *table = xpose::packed_kernels(&n);
-  const int small_block = table[0].block_bytes;
-  if (!dense || m * s > small_block || (!want && m * s > kPackedMaxBytes))
+  const int largest_block = table[n - 1].block_bytes;
+  const int64_t edge = s == 1 ? 128 : 64;
+  const bool ragged = rows % edge || cols % edge;
+  const int64_t limit = ragged ? kPackedRaggedBytes : kPackedMaxBytes;
+  if (!dense || m * s > largest_block || (!want && m * s > limit))
     return want ? XPOSE_ENOTILE : kNotPacked;
   // Whole matrices per workgroup.  Where a multiple of 128 / gcd(m s, 128)
   // fits a block (the smallest such block size is taken), blocks are whole
-  // cache lines and non-temporal stores pay; otherwise the smallest block,
-  // filled, with write-back stores.
+  // cache lines and non-temporal stores pay; otherwise the smallest block
+  // that holds a matrix, filled, with write-back stores.
   const int64_t mb = m * s;
   int64_t g = 128, x = mb;
   while (x) {  // gcd(mb, 128)
@@ -184,12 +190,11 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
     x = t;
   }
   const int64_t unit = 128 / g;
-  int block = small_block;
-  for (int i = 0; i < n; ++i)
-    if (unit * mb <= table[i].block_bytes) {
-      block = table[i].block_bytes;
-      break;
-    }
+  int block = 0;
+  for (int i = 0; i < n && !block; ++i)
+    if (unit * mb <= table[i].block_bytes) block = table[i].block_bytes;
+  for (int i = 0; i < n && !block; ++i)
+    if (mb <= table[i].block_bytes) block = table[i].block_bytes;
   const int64_t fit = block / mb;
   const bool lines = unit <= fit;
   const int64_t per = lines ? fit / unit * unit : fit;

@@ -374,10 +374,15 @@ def test_packed_batches_of_small_matrices():
     assert plan(rows=16, cols=16)[1].packed == 0
     assert plan(batch=8, rows=64, cols=64, stride_in=4096, stride_out=4096)[1].packed == 1
     assert plan(batch=8, rows=128, cols=64, stride_in=8192, stride_out=8192)[1].packed == 0
+    # 16-32 KiB: packed only when the matrix is not a whole number of tiles
+    assert plan(batch=8, rows=64, cols=96, stride_in=6144, stride_out=6144)[1].packed == 1
+    assert plan(batch=8, rows=96, cols=96, stride_in=9216, stride_out=9216)[1].packed == 0
     # asked for: also a single matrix
     want = X.make_opts(flags=X.FLAG_PACKED)
     assert plan(rows=16, cols=16, opts=want)[1].packed >= 1
-    assert plan(batch=8, rows=128, cols=64, stride_in=8192, stride_out=8192,
+    rc, info = plan(batch=8, rows=128, cols=64, stride_in=8192, stride_out=8192, opts=want)
+    assert rc == 0 and info.packed >= 1
+    assert plan(batch=8, rows=128, cols=128, stride_in=16384, stride_out=16384,
                 opts=want)[0] == X.XPOSE_ENOTILE
     assert plan(batch=8, rows=16, cols=16, ld_in=20, stride_in=320, stride_out=256,
                 opts=want)[0] == X.XPOSE_ENOTILE
