@@ -100,6 +100,56 @@ def make_input(w: Workload) -> np.ndarray:
     raise ValueError(f"unknown recipe {w.recipe!r}")
 
 
+@dataclass(frozen=True)
+class GemmWorkload:
+    """One SGEMM job, C = alpha * A @ B + beta * C with A m x k, B k x n."""
+
+    key: str
+    m: int
+    n: int
+    k: int
+    alpha: float
+    beta: float
+    seed: int
+    description: str
+
+    @property
+    def flops(self) -> int:
+        """Algorithmic work: one multiply and one add per term of each sum."""
+        return 2 * self.m * self.n * self.k
+
+
+# The SGEMM of "Padded Shared Memory: Eliminating Bank Conflicts" is measured
+# at M = N = K = 4096 (section "Mechanics"); the pages give no values, alpha
+# or beta, so the inputs are uniform [-1, 1) and C += A @ B.
+GEMM_WORKLOADS = {
+    "sgemm_4096": GemmWorkload(
+        "sgemm_4096", 4096, 4096, 4096, 1.0, 1.0, 11,
+        "SGEMM 4096x4096x4096 fp32, C += A @ B, uniform [-1,1)"),
+}
+
+
+def uniform_f32(shape: tuple, seed: int) -> np.ndarray:
+    """float32 values uniform on [-1, 1), from a seeded generator."""
+    rng = np.random.default_rng(seed)
+    u = rng.random(shape, dtype=np.float32)
+    return u * np.float32(2) - np.float32(1)
+
+
+def small_int_f32(shape: tuple, seed: int, bound: int = 4) -> np.ndarray:
+    """float32 holding integers in [-bound, bound], from a seeded generator:
+    products and sums of such values stay exact in float32 while they stay
+    below 2**24 in magnitude."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(-bound, bound + 1, size=shape).astype(np.float32)
+
+
+def make_gemm_inputs(w: GemmWorkload) -> tuple:
+    """(A, B, C) of a GEMM workload as C-contiguous float32 arrays."""
+    return (uniform_f32((w.m, w.k), w.seed), uniform_f32((w.k, w.n), w.seed + 1),
+            uniform_f32((w.m, w.n), w.seed + 2))
+
+
 def index_plane(shape: tuple, axis: int, elem_bytes: int) -> np.ndarray:
     """Raw-bit plane whose every element holds its own coordinate on ``axis``.
 
