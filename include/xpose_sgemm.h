@@ -1,0 +1,140 @@
+/*
+ * xpose_sgemm -- the tiled single-precision GEMM whose transposed LDS store
+ * is the second bank-conflict workload of the pages, for MI355X (gfx950).
+ *
+ * C ABI of libxpose.so (the same library as include/xpose.h, whose status
+ * codes and error rules apply here too).
+ *
+ * What is computed.  Row-major fp32 matrices A (m x k, row pitch lda),
+ * B (k x n, pitch ldb) and C (m x n, pitch ldc); for i in [0, m), j in [0, n):
+ *
+ *     C[i*ldc + j] = alpha * sum_{l < k} A[i*lda + l] * B[l*ldb + j]
+ *                    + beta * C[i*ldc + j]
+ *
+ * the operation of the SGEMM in "Padded Shared Memory: Eliminating Bank
+ * Conflicts" (the kernel listed under "The Fix Is One Constant", measured at
+ * m = n = k = 4096 in "Mechanics").  With beta == 0, C is write-only: it is
+ * not read, so NaN or uninitialised contents do not reach the result (the
+ * pages' kernel always reads C; where C is finite the two agree).  Elements
+ * of C outside the m x n region (pitch padding) are never written.
+ *
+ * How.  Each workgroup computes a 128 x 128 block of C in steps of bk along
+ * k.  Per step it loads A's 128 x bk tile with 16-byte row reads and stores
+ * it TRANSPOSED in LDS (As[l][i], so the product reads consecutive i), the
+ * store the pages show to be bank-conflicted when As's row stride is a
+ * multiple of the bank count ("How Shared Memory Is Addressed"); B's bk x 128
+ * tile goes to LDS as it is.  The products run on the matrix cores
+ * (v_mfma_f32_32x32x2_f32: fp32 operands, fp32 accumulation).  The sum over
+ * l is therefore taken in a different order than a sequential loop; every
+ * element lies within (k + 3) * 2^-24 * (|alpha| * sum_l |A[i][l] B[l][j]|
+ * + |beta * C[i][j]|) of the exact value (the standard bound of an fp32 dot
+ * product of length k, plus the scaling), for operands and partial sums in
+ * the normal range.  Integer-valued inputs whose partial sums stay below
+ * 2^24 are reproduced exactly.
+ *
+ * Memory and streams.  a, b and c are DEVICE pointers on the current HIP
+ * device, owned by the caller, 4-byte aligned.  16-byte aligned a and b with
+ * lda and ldb multiples of 4 let the tile loads use 16-byte accesses; other
+ * alignments take 4-byte loads.  Calls are asynchronous on `stream` (NULL =
+ * the null stream), never synchronise, never allocate and keep no state.
+ * C's byte range must not overlap A's or B's (XPOSE_EALIAS); A and B may
+ * overlap each other.
+ *
+ * Errors (validated on the host before anything is launched):
+ *   XPOSE_EINVAL  negative m, n or k; lda < max(k, 1), ldb < max(n, 1) or
+ *                 ldc < max(n, 1); a NULL pointer that the call would use;
+ *                 an extent overflowing 64 bits; unknown option values
+ *   XPOSE_EALIGN  a pointer not 4-byte aligned
+ *   XPOSE_EALIAS  C overlaps A or B
+ *   XPOSE_ENOTILE no kernel built for the requested options
+ *   XPOSE_EHIP    the launch failed (xpose_last_hip_error())
+ * m == 0 or n == 0 is a successful no-op (pointers may then be NULL);
+ * k == 0 sets C = beta * C (a and b are not used and may be NULL).
+ */
+#ifndef XPOSE_SGEMM_H
+#define XPOSE_SGEMM_H
+
+#include <stdint.h>
+
+#include "xpose.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layout of the transposed A tile in LDS (As, bk rows of 128 floats).  All
+ * give identical results; they differ only in bank conflicts of the
+ * transposed store ("How Shared Memory Is Addressed", "The Fix Is One
+ * Constant"). */
+typedef enum xpose_as_layout {
+  XPOSE_AS_AUTO = 0,     /* library default                                   */
+  XPOSE_AS_UNPADDED = 1, /* row stride 128 floats, a multiple of the bank
+                            count: the store is (bk / 4)-way conflicted on
+                            gfx950's 32-bank, 32-lane 4-byte LDS accesses     */
+  XPOSE_AS_PADDED = 2,   /* row stride 128 + 32 / bk floats: the smallest pad
+                            that spreads one half-wave's stores over all 32
+                            banks (the pages' (32 / BK) % 8 for the built bk) */
+  XPOSE_AS_SWIZZLE = 3   /* row stride 128, the row index of each element
+                            XOR-permuted by a multiple of 128 / bk chosen
+                            from its k: conflict-free without padding        */
+} xpose_as_layout;
+
+/* Option flags of xpose_sgemm_ex. */
+enum {
+  XPOSE_SGEMM_NO_XCD_REMAP = 1 /* keep the hardware's round-robin
+                                  assignment of workgroups to XCDs instead
+                                  of one contiguous range of blocks each     */
+};
+
+/* Optional knobs (zero-initialise for defaults).  Every choice gives the
+ * same result up to the summation order within a bk step (bk changes the
+ * grouping of the sum). */
+typedef struct xpose_sgemm_opts {
+  int32_t layout;  /* xpose_as_layout                                         */
+  int32_t bk;      /* k step per LDS stage: 0 = default (16), 8, 16 or 32     */
+  int32_t group_m; /* block order: groups of group_m block rows, walked
+                      block-column by block-column; 0 = default (8)          */
+  int32_t flags;   /* XPOSE_SGEMM_*                                           */
+} xpose_sgemm_opts;
+
+/* What xpose_sgemm_plan reports about the kernel a call would launch. */
+typedef struct xpose_sgemm_info {
+  int32_t layout;       /* resolved xpose_as_layout                           */
+  int32_t bk;           /* k step                                             */
+  int32_t as_stride;    /* As row stride in floats                            */
+  int32_t lds_bytes;    /* LDS per workgroup                                  */
+  int32_t threads;      /* threads per workgroup                              */
+  int32_t tile_m;       /* rows of C per workgroup                            */
+  int32_t tile_n;       /* columns of C per workgroup                         */
+  int32_t vector_loads; /* 1: 16-byte tile loads; 0: 4-byte loads             */
+  int32_t group_m;      /* resolved block-order group height                  */
+  int32_t xcd_remap;    /* 1 if blocks are remapped per XCD                   */
+  int64_t tiles;        /* workgroups launched                                */
+} xpose_sgemm_info;
+
+/* C = alpha * A * B + beta * C with the default kernel. */
+int xpose_sgemm(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
+                int64_t lda, const float *b, int64_t ldb, float beta,
+                float *c, int64_t ldc, void *stream);
+
+/* xpose_sgemm with explicit knobs (opts may be NULL): the As layout
+ * ablation of the pages' padded-store fix. */
+int xpose_sgemm_ex(int64_t m, int64_t n, int64_t k, float alpha,
+                   const float *a, int64_t lda, const float *b, int64_t ldb,
+                   float beta, float *c, int64_t ldc,
+                   const xpose_sgemm_opts *opts, void *stream);
+
+/* Host-only: validate a call and report the kernel it would launch, without
+ * touching the GPU (pointers are compared and checked for alignment, never
+ * dereferenced).  Returns the status the call would return; `info` may be
+ * NULL. */
+int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
+                     int64_t lda, const float *b, int64_t ldb, const float *c,
+                     int64_t ldc, const xpose_sgemm_opts *opts,
+                     xpose_sgemm_info *info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XPOSE_SGEMM_H */

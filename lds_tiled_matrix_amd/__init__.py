@@ -7,8 +7,10 @@ importing this package without it raises ImportError rather than falling
 back to anything else.
 
 Low-level names mirror the C ABI (``xpose_2d``, ``xpose_batched``,
-``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``)
-and take raw device addresses as integers.  ``transpose`` and ``copy`` are
+``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``,
+and the tiled SGEMM's ``xpose_sgemm``, ``xpose_sgemm_ex``,
+``xpose_sgemm_plan`` of ``include/xpose_sgemm.h``) and take raw device
+addresses as integers.  ``transpose``, ``copy`` and ``sgemm`` are
 conveniences over torch tensors: torch supplies the device memory and the
 stream, nothing else.
 """
@@ -39,10 +41,17 @@ ORDER_AUTO, ORDER_SUPER_TILES, ORDER_DIAGONAL = 0, 1, 2
 CACHE_NAMES = {CACHE_DEFAULT: "default", CACHE_NT_STORE: "nt_store",
                CACHE_NT_ALL: "nt_all"}
 
-# Every exported entry point, in header order.
+AS_AUTO, AS_UNPADDED, AS_PADDED, AS_SWIZZLE = 0, 1, 2, 3
+AS_NAMES = {AS_UNPADDED: "unpadded", AS_PADDED: "padded",
+            AS_SWIZZLE: "swizzle"}
+SGEMM_NO_XCD_REMAP = 1
+
+# Every exported entry point, in header order (include/xpose.h, then
+# include/xpose_sgemm.h).
 EXPORTS = ("xpose_2d", "xpose_batched", "xpose_batched_ex", "xpose_plan",
            "xpose_copy", "xpose_copy_ex", "xpose_lds_probe",
-           "xpose_last_hip_error", "xpose_strerror")
+           "xpose_last_hip_error", "xpose_strerror",
+           "xpose_sgemm", "xpose_sgemm_ex", "xpose_sgemm_plan")
 
 
 class XposeOpts(ctypes.Structure):
@@ -73,6 +82,23 @@ class XposePlanInfo(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class XposeSgemmOpts(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("group_m", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class XposeSgemmInfo(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("as_stride", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("vector_loads", ctypes.c_int32),
+                ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
+                ("tiles", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 def _load() -> ctypes.CDLL:
     # libxpose.so needs libamdhip64.so.7.  PyTorch's ROCm wheel ships its own
     # HIP and HSA runtimes under that same soname; if libxpose.so were loaded
@@ -89,6 +115,7 @@ def _load() -> ctypes.CDLL:
             f"{LIB_PATH} is not built; run `python lds_tiled_matrix_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f32 = ctypes.c_float
     opts_p, info_p = ctypes.POINTER(XposeOpts), ctypes.POINTER(XposePlanInfo)
     sig = {
         "xpose_2d": [p, p, i64, i64, i64, i64, i32, p],
@@ -102,6 +129,12 @@ def _load() -> ctypes.CDLL:
         "xpose_lds_probe": [p, ctypes.POINTER(i32), i32, i32, i32, p],
         "xpose_last_hip_error": [],
         "xpose_strerror": [ctypes.c_int],
+        "xpose_sgemm": [i64, i64, i64, f32, p, i64, p, i64, f32, p, i64, p],
+        "xpose_sgemm_ex": [i64, i64, i64, f32, p, i64, p, i64, f32, p, i64,
+                           ctypes.POINTER(XposeSgemmOpts), p],
+        "xpose_sgemm_plan": [i64, i64, i64, p, i64, p, i64, p, i64,
+                             ctypes.POINTER(XposeSgemmOpts),
+                             ctypes.POINTER(XposeSgemmInfo)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -186,6 +219,37 @@ def xpose_lds_probe(cycles_out: int, lane_bytes, width: int, is_write: int,
     arr = (ctypes.c_int32 * 64)(*[int(x) for x in lane_bytes])
     return _lib.xpose_lds_probe(cycles_out, arr, width, is_write, iters,
                                 stream)
+
+
+def make_sgemm_opts(layout=AS_AUTO, bk=0, group_m=0,
+                    flags=0) -> XposeSgemmOpts:
+    return XposeSgemmOpts(layout, bk, group_m, flags)
+
+
+def xpose_sgemm(m: int, n: int, k: int, alpha: float, a: int, lda: int,
+                b: int, ldb: int, beta: float, c: int, ldc: int,
+                stream: int = 0) -> int:
+    return _lib.xpose_sgemm(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc,
+                            stream)
+
+
+def xpose_sgemm_ex(m: int, n: int, k: int, alpha: float, a: int, lda: int,
+                   b: int, ldb: int, beta: float, c: int, ldc: int,
+                   opts: XposeSgemmOpts | None = None,
+                   stream: int = 0) -> int:
+    return _lib.xpose_sgemm_ex(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc,
+                               ctypes.byref(opts) if opts else None, stream)
+
+
+def xpose_sgemm_plan(m: int, n: int, k: int, a: int, lda: int, b: int,
+                     ldb: int, c: int, ldc: int,
+                     opts: XposeSgemmOpts | None = None):
+    """Returns (status, XposeSgemmInfo)."""
+    info = XposeSgemmInfo()
+    rc = _lib.xpose_sgemm_plan(m, n, k, a, lda, b, ldb, c, ldc,
+                               ctypes.byref(opts) if opts else None,
+                               ctypes.byref(info))
+    return rc, info
 
 
 def xpose_last_hip_error() -> int:
@@ -285,3 +349,34 @@ def plan_for(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
                           opts)
     _check(rc, "xpose_plan")
     return info.as_dict()
+
+
+def sgemm(a, b, c=None, *, alpha: float = 1.0, beta: float = 0.0,
+          layout: int = AS_AUTO, bk: int = 0, stream=None):
+    """c = alpha * a @ b + beta * c for 2-D float32 CUDA tensors whose last
+    dimension is contiguous (pitches come from the row strides).  With c
+    None, a new tensor is allocated and beta must be 0.  Returns c."""
+    import torch
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("expected 2-D tensors")
+    m, k = a.shape
+    if b.shape[0] != k:
+        raise ValueError("inner dimensions differ")
+    n = b.shape[1]
+    if c is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs c")
+        c = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    for t in (a, b, c):
+        if t.dtype != torch.float32 or (t.numel() > 1 and t.stride(-1) != 1):
+            raise ValueError("float32 tensors with a contiguous last dim")
+    if tuple(c.shape) != (m, n):
+        raise ValueError("c has the wrong shape")
+    lda = a.stride(0) if m > 1 else max(k, 1)
+    ldb = b.stride(0) if k > 1 else max(n, 1)
+    ldc = c.stride(0) if m > 1 else max(n, 1)
+    opts = make_sgemm_opts(layout, bk) if (layout or bk) else None
+    _check(xpose_sgemm_ex(m, n, k, alpha, a.data_ptr(), lda, b.data_ptr(), ldb,
+                          beta, c.data_ptr(), ldc, opts,
+                          _stream_handle(stream)), "xpose_sgemm_ex")
+    return c

@@ -16,7 +16,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libxpose.so")
-SOURCES = ["xpose_kernels.hip", "xpose_api.cpp"]
+SOURCES = ["xpose_kernels.hip", "xpose_api.cpp", "sgemm_kernels.hip",
+           "sgemm_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -52,11 +53,15 @@ def dump_isa(out_dir: str) -> None:
     """Write the gfx950 assembly of the kernels (for checking instruction
     selection: LDS widths, global access widths, waits)."""
     os.makedirs(out_dir, exist_ok=True)
-    cmd = [hipcc()] + [f for f in flags() if f not in ("-shared", "-fPIC")] + [
-        "--cuda-device-only", "-S", "-o",
-        os.path.join(out_dir, "xpose_kernels.s"),
-        os.path.join(CSRC, "xpose_kernels.hip")]
-    subprocess.run(cmd, check=True)
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        cmd = [hipcc()] + [f for f in flags()
+                           if f not in ("-shared", "-fPIC")] + [
+            "--cuda-device-only", "-S", "-o",
+            os.path.join(out_dir, src.replace(".hip", ".s")),
+            os.path.join(CSRC, src)]
+        subprocess.run(cmd, check=True)
 
 
 if __name__ == "__main__":

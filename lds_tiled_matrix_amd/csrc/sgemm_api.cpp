@@ -1,0 +1,177 @@
+// C-ABI front end of the tiled SGEMM (include/xpose_sgemm.h): argument
+// validation, kernel choice and launch.  Validation and planning are host
+// code that never touches the GPU.
+
+#include "../../include/xpose_sgemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "xpose_kernels.h"
+
+namespace {
+
+constexpr int kTile = 128;          // rows and columns of C per workgroup
+constexpr int kDefaultBk = 16;
+constexpr int kDefaultLayout = XPOSE_AS_PADDED;
+constexpr int kDefaultGroupM = 8;
+
+struct SgemmPlan {
+  bool empty = false;
+  const xpose::SgemmKernel *kernel = nullptr;
+  xpose::SgemmArgs args{};
+  int64_t tiles = 0;
+};
+
+// a * b + c without overflow, all >= 0; false if it does not fit.
+bool mul_add(int64_t a, int64_t b, int64_t c, int64_t *out) {
+  int64_t p;
+  if (__builtin_mul_overflow(a, b, &p)) return false;
+  return !__builtin_add_overflow(p, c, out);
+}
+
+// Byte range [lo, hi) of a rows x cols matrix with pitch ld at p.
+bool byte_range(const void *p, int64_t rows, int64_t cols, int64_t ld,
+                uintptr_t *lo, uintptr_t *hi) {
+  int64_t last, bytes;
+  if (!mul_add(rows - 1, ld, cols, &last)) return false;
+  if (__builtin_mul_overflow(last, (int64_t)4, &bytes)) return false;
+  *lo = (uintptr_t)p;
+  if (__builtin_add_overflow(*lo, (uintptr_t)bytes, hi)) return false;
+  return true;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
+int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
+              const float *b, int64_t ldb, const float *c, int64_t ldc,
+              const xpose_sgemm_opts *opts, SgemmPlan &plan) {
+  int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM;
+  bool remap = true;
+  if (opts) {
+    if (opts->layout < XPOSE_AS_AUTO || opts->layout > XPOSE_AS_SWIZZLE)
+      return XPOSE_EINVAL;
+    if (opts->bk != 0 && opts->bk != 8 && opts->bk != 16 && opts->bk != 32)
+      return XPOSE_EINVAL;
+    if (opts->group_m < 0) return XPOSE_EINVAL;
+    if (opts->flags & ~XPOSE_SGEMM_NO_XCD_REMAP) return XPOSE_EINVAL;
+    if (opts->layout) layout = opts->layout;
+    if (opts->bk) bk = opts->bk;
+    if (opts->group_m) group_m = opts->group_m;
+    remap = !(opts->flags & XPOSE_SGEMM_NO_XCD_REMAP);
+  }
+  if (m < 0 || n < 0 || k < 0) return XPOSE_EINVAL;
+  if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) ||
+      ldc < (n > 1 ? n : 1))
+    return XPOSE_EINVAL;
+  if (m == 0 || n == 0) {
+    plan.empty = true;
+    return XPOSE_OK;
+  }
+  const bool uses_ab = k > 0;
+  if (!c || (uses_ab && (!a || !b))) return XPOSE_EINVAL;
+  if ((uintptr_t)c % 4 || (uses_ab && ((uintptr_t)a % 4 || (uintptr_t)b % 4)))
+    return XPOSE_EALIGN;
+  uintptr_t c0, c1;
+  if (!byte_range(c, m, n, ldc, &c0, &c1)) return XPOSE_EINVAL;
+  if (uses_ab) {
+    uintptr_t a0, a1, b0, b1;
+    if (!byte_range(a, m, k, lda, &a0, &a1) ||
+        !byte_range(b, k, n, ldb, &b0, &b1))
+      return XPOSE_EINVAL;
+    if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1))
+      return XPOSE_EALIAS;
+  }
+  const int64_t tiles_m = (m + kTile - 1) / kTile;
+  const int64_t tiles_n = (n + kTile - 1) / kTile;
+  int64_t tiles;
+  if (__builtin_mul_overflow(tiles_m, tiles_n, &tiles) || tiles > INT32_MAX)
+    return XPOSE_EINVAL;
+  const bool vec = !uses_ab || ((uintptr_t)a % 16 == 0 &&
+                                (uintptr_t)b % 16 == 0 && lda % 4 == 0 &&
+                                ldb % 4 == 0);
+  int count = 0;
+  const xpose::SgemmKernel *table = xpose::sgemm_kernels(&count);
+  const xpose::SgemmKernel *kern = nullptr;
+  for (int i = 0; i < count && !kern; ++i)
+    if (table[i].bk == bk && table[i].layout == layout && table[i].vec == vec)
+      kern = &table[i];
+  if (!kern) return XPOSE_ENOTILE;
+  if (group_m > tiles_m) group_m = (int)tiles_m;
+
+  xpose::SgemmArgs &g = plan.args;
+  g.a = a;
+  g.b = b;
+  g.c = const_cast<float *>(c);
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.tiles_m = (uint32_t)tiles_m;
+  g.tiles_n = (uint32_t)tiles_n;
+  g.group_m = (uint32_t)group_m;
+  g.xcd_remap = remap ? 1 : 0;
+  plan.kernel = kern;
+  plan.tiles = tiles;
+  return XPOSE_OK;
+}
+
+int run(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
+        int64_t lda, const float *b, int64_t ldb, float beta, float *c,
+        int64_t ldc, const xpose_sgemm_opts *opts, void *stream) {
+  SgemmPlan plan;
+  const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, plan);
+  if (rc != XPOSE_OK || plan.empty) return rc;
+  plan.args.alpha = alpha;
+  plan.args.beta = beta;
+  const hipError_t e = plan.kernel->launch(plan.args, (uint32_t)plan.tiles,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? XPOSE_OK : xpose::record_hip_error(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int xpose_sgemm(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
+                int64_t lda, const float *b, int64_t ldb, float beta,
+                float *c, int64_t ldc, void *stream) {
+  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, nullptr, stream);
+}
+
+int xpose_sgemm_ex(int64_t m, int64_t n, int64_t k, float alpha,
+                   const float *a, int64_t lda, const float *b, int64_t ldb,
+                   float beta, float *c, int64_t ldc,
+                   const xpose_sgemm_opts *opts, void *stream) {
+  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, opts, stream);
+}
+
+int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
+                     int64_t lda, const float *b, int64_t ldb, const float *c,
+                     int64_t ldc, const xpose_sgemm_opts *opts,
+                     xpose_sgemm_info *info) {
+  SgemmPlan plan;
+  const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, plan);
+  if (rc != XPOSE_OK || !info) return rc;
+  *info = xpose_sgemm_info{};
+  if (plan.empty) return rc;
+  const xpose::SgemmKernel &kern = *plan.kernel;
+  info->layout = kern.layout;
+  info->bk = kern.bk;
+  info->as_stride = kern.as_stride;
+  info->lds_bytes = kern.lds_bytes;
+  info->threads = kern.threads;
+  info->tile_m = kTile;
+  info->tile_n = kTile;
+  info->vector_loads = kern.vec ? 1 : 0;
+  info->group_m = (int32_t)plan.args.group_m;
+  info->xcd_remap = plan.args.xcd_remap;
+  info->tiles = plan.tiles;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// gfx950 kernel of the tiled SGEMM, C = alpha * A * B + beta * C (fp32,
+// row-major), with A's tile stored transposed in LDS: the second workload of
+// "Padded Shared Memory: Eliminating Bank Conflicts", where the transposed
+// store is the bank-conflict site and padding As's row stride is the fix
+// ("How Shared Memory Is Addressed", "The Fix Is One Constant").  Here the
+// dense contraction runs on the matrix cores (v_mfma_f32_32x32x2_f32, fp32
+// in and out); the LDS staging keeps the pages' structure: 16-byte row loads
+// of A, scalar transposed stores into As, 16-byte copies of B into Bs, a
+// barrier, the inner products, a second barrier.  The layouts and lane maps
+// are in sgemm_lanes.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sgemm_lanes.h"
+#include "xpose_kernels.h"
+
+namespace xpose {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One 16-byte vector of row `row` (of `nrows`) starting at column `col` (of
+// `ncols`) of a row-major matrix with pitch `ld`: a 16-byte load where the
+// vector is whole and VEC allows it, else 4-byte loads of the elements that
+// exist, zero elsewhere (zeros contribute nothing to the products).
+template <bool VEC>
+__device__ inline f32x4 load_vec(const float *base, int64_t row, int64_t col,
+                                 int64_t nrows, int64_t ncols, int64_t ld) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (row >= nrows) return v;
+  const float *p = base + row * ld + col;
+  if (VEC && col + 4 <= ncols) return *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (col + e < ncols) v[e] = p[e];
+  return v;
+}
+
+template <int BK, int L, bool VEC>
+__global__ __launch_bounds__(256) void xpose_sgemm_kernel(SgemmArgs a) {
+  using T = SgemmTile<BK, L>;
+  __shared__ __attribute__((aligned(16))) float As[T::AS_FLOATS];
+  __shared__ __attribute__((aligned(16))) float Bs[T::BS_FLOATS];
+
+  const int t = threadIdx.x, q = t & 63, w = t >> 6;
+  uint32_t bm, bn;
+  sgemm_block(blockIdx.x, a.tiles_m, a.tiles_n, a.group_m, a.xcd_remap, bm,
+              bn);
+  const int64_t m0 = (int64_t)bm * T::BM, n0 = (int64_t)bn * T::BN;
+  // Blocks wholly inside C take unconditional 16-byte loads for every k
+  // step but a ragged last one.
+  const bool whole_mn = VEC && m0 + T::BM <= a.m && n0 + T::BN <= a.n;
+
+  f32x4 ra[T::A_PASSES], rb[T::B_PASSES];
+  auto load = [&](int64_t k0) {
+    if (whole_mn && k0 + BK <= a.k) {
+#pragma unroll
+      for (int p = 0; p < T::A_PASSES; ++p)
+        ra[p] = *reinterpret_cast<const f32x4 *>(
+            a.a + (m0 + T::a_row(t, p)) * a.lda + k0 + T::a_col(t));
+#pragma unroll
+      for (int p = 0; p < T::B_PASSES; ++p)
+        rb[p] = *reinterpret_cast<const f32x4 *>(
+            a.b + (k0 + T::b_row(t, p)) * a.ldb + n0 + T::b_col(t));
+      return;
+    }
+#pragma unroll
+    for (int p = 0; p < T::A_PASSES; ++p)
+      ra[p] = load_vec<VEC>(a.a, m0 + T::a_row(t, p), k0 + T::a_col(t), a.m,
+                            a.k, a.lda);
+#pragma unroll
+    for (int p = 0; p < T::B_PASSES; ++p)
+      rb[p] = load_vec<VEC>(a.b, k0 + T::b_row(t, p), n0 + T::b_col(t), a.k,
+                            a.n, a.ldb);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+
+  const int wr = T::wave_row(w), wc = T::wave_col(w);
+  const int half = q >> 5, lane32 = q & 31;
+  if (a.k > 0) load(0);
+  for (int64_t k0 = 0; k0 < a.k; k0 += BK) {
+    // A's vectors go into As transposed, one 4-byte store per element: the
+    // store whose banks the layout decides.  B's rows are copied as they are.
+#pragma unroll
+    for (int p = 0; p < T::A_PASSES; ++p) {
+      const int i = T::a_row(t, p), l = T::a_col(t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[T::as_index(l + e, i)] = ra[p][e];
+    }
+#pragma unroll
+    for (int p = 0; p < T::B_PASSES; ++p)
+      *reinterpret_cast<f32x4 *>(&Bs[T::bs_index(T::b_row(t, p), T::b_col(t))]) =
+          rb[p];
+    __syncthreads();
+    // The next step's loads are in flight while this step's products run.
+    if (k0 + BK < a.k) load(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      const int l = kk + half;
+      const float a0 = As[T::as_index(l, wr + lane32)];
+      const float a1 = As[T::as_index(l, wr + 32 + lane32)];
+      const float b0 = Bs[T::bs_index(l, wc + lane32)];
+      const float b1 = Bs[T::bs_index(l, wc + 32 + lane32)];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // C = alpha * acc + beta * C; with beta == 0 C is not read.  32 lanes
+  // cover 32 consecutive columns of one row per store.
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int64_t j = n0 + wc + 32 * y + lane32;
+      if (j >= a.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = m0 + wr + 32 * x + T::acc_row(q, r);
+        if (i >= a.m) continue;
+        float *p = a.c + i * a.ldc + j;
+        float v = a.alpha * acc[x][y][r];
+        if (a.beta != 0.f) v = fmaf(a.beta, *p, v);
+        *p = v;
+      }
+    }
+}
+
+template <int BK, int L, bool VEC>
+hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
+  SgemmArgs copy = a;
+  void *args[] = {&copy};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(&xpose_sgemm_kernel<BK, L, VEC>),
+      dim3(grid), dim3(256), args, 0, s);
+}
+
+#define XPOSE_SGEMM(BK, L, VEC)                                              \
+  SgemmKernel {                                                              \
+    BK, L, SgemmTile<BK, L>::AS_STRIDE, SgemmTile<BK, L>::LDS_BYTES, 256,    \
+        VEC, &launch_sgemm<BK, L, VEC>                                       \
+  }
+#define XPOSE_SGEMM_BK(BK)                                                   \
+  XPOSE_SGEMM(BK, kAsUnpadded, true), XPOSE_SGEMM(BK, kAsPadded, true),      \
+      XPOSE_SGEMM(BK, kAsSwizzle, true), XPOSE_SGEMM(BK, kAsUnpadded, false), \
+      XPOSE_SGEMM(BK, kAsPadded, false), XPOSE_SGEMM(BK, kAsSwizzle, false)
+
+const SgemmKernel kSgemmKernels[] = {XPOSE_SGEMM_BK(8), XPOSE_SGEMM_BK(16),
+                                     XPOSE_SGEMM_BK(32)};
+
+}  // namespace
+
+const SgemmKernel *sgemm_kernels(int *count) {
+  *count = (int)(sizeof kSgemmKernels / sizeof kSgemmKernels[0]);
+  return kSgemmKernels;
+}
+
+}  // namespace xpose

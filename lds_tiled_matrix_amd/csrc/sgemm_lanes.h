@@ -1,0 +1,134 @@
+// LDS geometry and lane maps of the tiled SGEMM kernel: where each lane puts
+// A's and B's tile elements in LDS, where the matrix-core operands are read
+// from, and which block of C each workgroup takes.  Host and device code:
+// the kernel uses it, and a host program lists the LDS addresses of every
+// lane so the bank behaviour of each built layout is checked without a GPU.
+// Internal, not part of the ABI.
+//
+// The structure is the SGEMM of "Padded Shared Memory: Eliminating Bank
+// Conflicts": A's tile is stored transposed (As[l][i]) so the product reads
+// consecutive rows i, and that store is the conflicted one when As's row
+// stride is a multiple of the bank count ("How Shared Memory Is Addressed").
+// Here the bank count and the lanes served per pass are gfx950's, as
+// measured for 4-byte LDS accesses: 32 banks, one 32-lane half-wave per pass
+// (the same figures as the pages' 32-lane hardware, so the pads come out
+// the same, but they are derived from the measured geometry below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "xpose_kernels.h"
+
+#define SGEMM_HD __host__ __device__
+
+namespace xpose {
+
+// As layouts; values match xpose_as_layout in include/xpose_sgemm.h.
+enum AsLayout : int { kAsUnpadded = 1, kAsPadded = 2, kAsSwizzle = 3 };
+
+// Compile-time geometry of one SGEMM kernel: BK is the k step, L the As
+// layout.  A workgroup of 4 waves computes a 128 x 128 block of C; wave w
+// computes the 64 x 64 quarter at (64 * (w / 2), 64 * (w % 2)) as 2 x 2
+// matrix-core tiles of 32 x 32.
+template <int BK, int L>
+struct SgemmTile {
+  static constexpr int BM = 128, BN = 128, NT = 256;
+  static constexpr int WM = 64, WN = 64;  // C block of one wave
+
+  // A's 128 x BK tile: each lane reads one 16-byte vector (4 consecutive l)
+  // of one row i, LPR lanes per row.
+  static constexpr int LPR = BK / 4;
+  static constexpr int A_ROWS_PER_PASS = NT / LPR;
+  static constexpr int A_PASSES = BM / A_ROWS_PER_PASS;  // vectors per lane
+  // B's BK x 128 tile: 32 lanes per row of 128 floats.
+  static constexpr int B_LPR = BN / 4;
+  static constexpr int B_ROWS_PER_PASS = NT / B_LPR;
+  static constexpr int B_PASSES = BK / B_ROWS_PER_PASS;
+
+  // The transposed store of element e of a lane's vector writes
+  // As[4c + e][i] for the lane's chunk c < LPR and row i.  One half-wave
+  // (the 32 lanes one pass serves) holds HG = 32 / LPR consecutive rows i
+  // (starting at a multiple of HG) times LPR chunks.  With row stride
+  // 128 + p the lane lands on bank (4 c p + e p + i) mod 32, so
+  //   p = 0:      the bank is i mod 32 alone: LPR lanes per bank, LPR-way;
+  //   4 p = HG:   the chunks fall HG banks apart, covering all 32 once;
+  // hence the padded stride 128 + HG / 4 = 128 + 32 / BK.
+  static constexpr int HG = 32 / LPR;
+  static constexpr int PAD = L == kAsPadded ? HG / 4 : 0;
+  static constexpr int AS_STRIDE = BM + PAD;
+  static constexpr int AS_FLOATS = BK * AS_STRIDE;
+  static constexpr int BS_FLOATS = BK * BN;
+  static constexpr int LDS_BYTES = 4 * (AS_FLOATS + BS_FLOATS);
+  static constexpr int LAYOUT = L;
+  static constexpr int KSTEP = BK;
+
+  static_assert(BK == 8 || BK == 16 || BK == 32, "built k steps");
+  static_assert(A_PASSES * A_ROWS_PER_PASS == BM, "whole A tile");
+  static_assert(B_PASSES * B_ROWS_PER_PASS == BK, "whole B tile");
+  static_assert(L != kAsPadded || 4 * PAD == HG, "pad spreads the chunks");
+
+  // Swizzle: row l of As keeps stride 128 and holds element i at column
+  // i ^ x(l), x(l) = ((l / 4) mod LPR) * HG.  In one half-wave's store l / 4
+  // is the chunk c and i runs over HG consecutive rows from a multiple of
+  // HG, so the banks (i ^ c HG) mod 32 are all distinct; x(l) < 32 only
+  // permutes i inside its aligned group of 32, so the product's reads of 32
+  // consecutive i stay one full row of banks.
+  SGEMM_HD static constexpr int swz(int l) {
+    return L == kAsSwizzle ? ((l >> 2) & (LPR - 1)) * HG : 0;
+  }
+  SGEMM_HD static constexpr int as_index(int l, int i) {
+    return l * AS_STRIDE + (i ^ swz(l));
+  }
+  SGEMM_HD static constexpr int bs_index(int l, int j) { return l * BN + j; }
+
+  // Loader lane maps: thread t, pass p.
+  SGEMM_HD static constexpr int a_row(int t, int p) {
+    return p * A_ROWS_PER_PASS + t / LPR;
+  }
+  SGEMM_HD static constexpr int a_col(int t) { return 4 * (t % LPR); }
+  SGEMM_HD static constexpr int b_row(int t, int p) {
+    return p * B_ROWS_PER_PASS + t / B_LPR;
+  }
+  SGEMM_HD static constexpr int b_col(int t) { return 4 * (t % B_LPR); }
+
+  // Matrix-core operands (v_mfma_f32_32x32x2_f32): for the k pair starting
+  // at kk, lane q supplies A[i0 + q % 32][kk + q / 32] and
+  // B[kk + q / 32][j0 + q % 32]; its 16 results are C[i0 + r_row][j0 + q % 32]
+  // with r_row = 8 (r / 4) + 4 (q / 32) + r % 4 for r < 16.
+  SGEMM_HD static constexpr int wave_row(int w) { return WM * (w / 2); }
+  SGEMM_HD static constexpr int wave_col(int w) { return WN * (w % 2); }
+  SGEMM_HD static constexpr int acc_row(int q, int r) {
+    return 8 * (r / 4) + 4 * (q / 32) + r % 4;
+  }
+};
+
+// Block order: workgroup `block` of `tiles_m * tiles_n` -> block row and
+// column of C, a bijection whenever group_m >= 1.
+//   xcd_remap: the hardware hands consecutive workgroups to the 8 XCDs in
+//     turn; the remap gives each XCD one contiguous range of blocks (XCD x
+//     receives the blocks b with b mod 8 = x and numbers them from the end
+//     of XCD x - 1's range), so the blocks sharing one XCD's L2 also share
+//     rows of A and columns of B.
+//   group_m: blocks are walked in groups of group_m block rows, block column
+//     by block column inside a group (the last group may be shorter), so
+//     the resident blocks reuse a few rows of A and columns of B.
+SGEMM_HD inline void sgemm_block(uint32_t block, uint32_t tiles_m,
+                                 uint32_t tiles_n, uint32_t group_m,
+                                 int32_t xcd_remap, uint32_t &bm,
+                                 uint32_t &bn) {
+  const uint32_t total = tiles_m * tiles_n;
+  uint32_t g = block;
+  if (xcd_remap) {
+    const uint32_t q = total / 8, r = total % 8, x = block % 8;
+    g = x * q + (x < r ? x : r) + block / 8;
+  }
+  const uint32_t span = group_m * tiles_n;
+  const uint32_t grp = g / span, first = grp * group_m;
+  const uint32_t rows = tiles_m - first < group_m ? tiles_m - first : group_m;
+  const uint32_t in = g - grp * span;
+  bm = first + in % rows;
+  bn = in / rows;
+}
+
+}  // namespace xpose

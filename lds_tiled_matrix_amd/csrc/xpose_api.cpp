@@ -518,6 +518,8 @@ int run_plan(Plan &plan, void *stream) {
 
 }  // namespace
 
+int xpose::record_hip_error(hipError_t e) { return hip_fail(e); }
+
 extern "C" {
 
 int xpose_batched_ex(void *out, const void *in, int64_t batch, int64_t rows,

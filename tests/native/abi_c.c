@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include "xpose.h"
+#include "xpose_sgemm.h"
 
 #define SIZE(T) printf("size %s %zu\n", #T, sizeof(T))
 #define OFF(T, F) printf("offset %s.%s %zu\n", #T, #F, offsetof(T, F))
@@ -62,6 +63,25 @@ int main(void) {
   plan("null", NULL, in, 1, 64, 64, 64, 64, XPOSE_F32, NULL);
   plan("alias", in, in, 1, 64, 64, 64, 64, XPOSE_F32, NULL);
   plan("dtype", out, in, 1, 64, 64, 64, 64, 9, NULL);
+  SIZE(xpose_sgemm_opts);
+  OFF(xpose_sgemm_opts, bk); OFF(xpose_sgemm_opts, flags);
+  SIZE(xpose_sgemm_info);
+  OFF(xpose_sgemm_info, as_stride); OFF(xpose_sgemm_info, xcd_remap);
+  OFF(xpose_sgemm_info, tiles);
+  CONST(XPOSE_AS_UNPADDED); CONST(XPOSE_AS_PADDED); CONST(XPOSE_AS_SWIZZLE);
+  CONST(XPOSE_SGEMM_NO_XCD_REMAP);
+  {
+    xpose_sgemm_info gi;
+    memset(&gi, 0xff, sizeof gi);
+    const float *a = (const float *)0x300000000000ull;
+    const float *b = (const float *)0x310000000000ull;
+    const float *c = (const float *)0x320000000000ull;
+    const int rc = xpose_sgemm_plan(4096, 4096, 4096, a, 4096, b, 4096, c,
+                                    4096, NULL, &gi);
+    printf("sgemm %d layout=%d bk=%d as_stride=%d lds_bytes=%d tiles=%lld\n",
+           rc, gi.layout, gi.bk, gi.as_stride, gi.lds_bytes,
+           (long long)gi.tiles);
+  }
   for (int code = 0; code >= -6; --code)
     printf("strerror %d %s\n", code, xpose_strerror(code));
   return 0;

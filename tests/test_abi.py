@@ -3,6 +3,7 @@ function include/xpose.h declares, and validates arguments on the host
 (bogus pointer values are fine here: invalid calls return before anything
 is launched, and xpose_plan never dereferences)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -11,16 +12,22 @@ import pytest
 import lds_tiled_matrix_amd as X
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "xpose.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("xpose.h", "xpose_sgemm.h")]
 
 IN = 0x7f0000000000       # pretend device addresses, 256-byte aligned
 OUT = 0x7f1000000000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(xpose_\w+)\s*\(", text)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(xpose_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_header_is_known():
+    assert sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))) == sorted(HEADERS)
 
 
 def test_header_and_binding_agree():

@@ -39,7 +39,9 @@ def _entries(lines, kind):
 
 def test_struct_layouts_match_ctypes(c_output):
     structs = {"xpose_opts": X.XposeOpts, "xpose_plan_info": X.XposePlanInfo,
-               "xpose_copy_opts": X.XposeCopyOpts}
+               "xpose_copy_opts": X.XposeCopyOpts,
+               "xpose_sgemm_opts": X.XposeSgemmOpts,
+               "xpose_sgemm_info": X.XposeSgemmInfo}
     sizes = dict(_entries(c_output, "size"))
     for name, cls in structs.items():
         assert int(sizes[name]) == ctypes.sizeof(cls), name
@@ -52,9 +54,10 @@ def test_struct_layouts_match_ctypes(c_output):
 
 def test_constants_match_binding(c_output):
     consts = dict(_entries(c_output, "const"))
-    assert len(consts) == 14
+    assert len(consts) == 18
     for name, value in consts.items():
-        short = name.replace("XPOSE_FLAG_", "FLAG_")
+        short = name.replace("XPOSE_FLAG_", "FLAG_").replace("XPOSE_AS_", "AS_")
+        short = short.replace("XPOSE_SGEMM_", "SGEMM_")
         py = getattr(X, name, None)
         if py is None:
             py = getattr(X, short)
@@ -87,3 +90,15 @@ def test_plans_match_binding(c_output):
 def test_strerror_matches_binding(c_output):
     for code, text in _entries(c_output, "strerror"):
         assert X.strerror(int(code)) == text
+
+
+def test_sgemm_plan_matches_binding(c_output):
+    line = [ln for ln in c_output if ln.startswith("sgemm ")]
+    assert len(line) == 1
+    f = line[0].split()
+    fields = dict(kv.split("=") for kv in f[2:])
+    rc, info = X.xpose_sgemm_plan(4096, 4096, 4096, 0x300000000000, 4096,
+                                  0x310000000000, 4096, 0x320000000000, 4096)
+    assert int(f[1]) == rc == 0
+    for k, v in fields.items():
+        assert getattr(info, k) == int(v), k

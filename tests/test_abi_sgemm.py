@@ -1,0 +1,105 @@
+"""Host-side checks of the SGEMM entry points (include/xpose_sgemm.h): plan
+defaults, option handling and argument validation.  No GPU: bogus pointer
+values are fine, invalid calls return before anything is launched and
+xpose_sgemm_plan never dereferences."""
+import pytest
+
+import lds_tiled_matrix_amd as X
+
+A, B, C = 0x7f0000000000, 0x7f1000000000, 0x7f2000000000
+
+
+def plan(m=4096, n=4096, k=4096, a=A, lda=None, b=B, ldb=None, c=C, ldc=None,
+         opts=None):
+    lda = max(k, 1) if lda is None else lda
+    ldb = max(n, 1) if ldb is None else ldb
+    ldc = max(n, 1) if ldc is None else ldc
+    return X.xpose_sgemm_plan(m, n, k, a, lda, b, ldb, c, ldc, opts)
+
+
+def test_default_plan():
+    rc, info = plan()
+    assert rc == 0
+    assert (info.layout, info.bk, info.as_stride) == (X.AS_PADDED, 16, 130)
+    assert (info.tile_m, info.tile_n, info.threads) == (128, 128, 256)
+    assert info.tiles == 32 * 32 and info.vector_loads == 1
+    assert info.lds_bytes == 4 * (16 * 130 + 16 * 128)
+    assert info.group_m == 8 and info.xcd_remap == 1
+
+
+@pytest.mark.parametrize("bk", (8, 16, 32))
+def test_layout_strides(bk):
+    """Padded stride 128 + 32 / bk: the pad that spreads one half-wave's
+    transposed stores over the 32 banks; the others keep 128."""
+    for layout, stride in ((X.AS_UNPADDED, 128), (X.AS_PADDED, 128 + 32 // bk),
+                           (X.AS_SWIZZLE, 128)):
+        rc, info = plan(opts=X.make_sgemm_opts(layout, bk))
+        assert rc == 0 and info.as_stride == stride and info.bk == bk
+        assert info.lds_bytes == 4 * bk * (stride + 128)
+
+
+def test_ragged_tiles_and_group_clamp():
+    rc, info = plan(m=130, n=67, k=45)
+    assert rc == 0 and info.tiles == 2 * 1 and info.group_m == 2
+    rc, info = plan(m=1, n=1, k=1)
+    assert rc == 0 and info.tiles == 1 and info.group_m == 1
+    rc, info = plan(opts=X.make_sgemm_opts(group_m=3, flags=X.SGEMM_NO_XCD_REMAP))
+    assert rc == 0 and info.group_m == 3 and info.xcd_remap == 0
+
+
+def test_vector_load_rules():
+    assert plan()[1].vector_loads == 1
+    assert plan(a=A + 4)[1].vector_loads == 0          # 4-byte aligned only
+    assert plan(b=B + 8)[1].vector_loads == 0
+    assert plan(lda=4097)[1].vector_loads == 0         # pitch not a multiple of 4
+    assert plan(ldb=4098)[1].vector_loads == 0
+    assert plan(c=C + 4, ldc=4099)[1].vector_loads == 1  # C is never vector-loaded
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(m=-1), X.XPOSE_EINVAL),
+    (dict(k=-1), X.XPOSE_EINVAL),
+    (dict(lda=4095), X.XPOSE_EINVAL),
+    (dict(ldb=4095), X.XPOSE_EINVAL),
+    (dict(ldc=4095), X.XPOSE_EINVAL),
+    (dict(a=0), X.XPOSE_EINVAL),
+    (dict(b=0), X.XPOSE_EINVAL),
+    (dict(c=0), X.XPOSE_EINVAL),
+    (dict(a=A + 2), X.XPOSE_EALIGN),
+    (dict(c=C + 1), X.XPOSE_EALIGN),
+    (dict(c=A), X.XPOSE_EALIAS),
+    (dict(c=B + 4 * 4096 * 4095), X.XPOSE_EALIAS),   # C starts on B's last row
+    (dict(lda=1 << 62), X.XPOSE_EINVAL),               # extent overflows
+    (dict(opts=X.make_sgemm_opts(layout=4)), X.XPOSE_EINVAL),
+    (dict(opts=X.make_sgemm_opts(bk=12)), X.XPOSE_EINVAL),
+    (dict(opts=X.make_sgemm_opts(group_m=-1)), X.XPOSE_EINVAL),
+    (dict(opts=X.make_sgemm_opts(flags=2)), X.XPOSE_EINVAL),
+])
+def test_invalid_calls(kw, code):
+    assert plan(**kw)[0] == code
+    # the entry points validate the same way, before launching anything
+    args = dict(m=4096, n=4096, k=4096, a=A, lda=4096, b=B, ldb=4096, c=C,
+                ldc=4096, opts=None)
+    args.update(kw)
+    rc = X.xpose_sgemm_ex(args["m"], args["n"], args["k"], 1.0, args["a"],
+                          args["lda"], args["b"], args["ldb"], 0.0, args["c"],
+                          args["ldc"], args["opts"], 0)
+    assert rc == code
+
+
+def test_a_and_b_may_overlap():
+    assert plan(b=A)[0] == 0
+
+
+def test_empty_shapes_are_noops_even_with_null_pointers():
+    for m, n in ((0, 5), (5, 0), (0, 0)):
+        rc, info = plan(m=m, n=n, k=7, a=0, b=0, c=0)
+        assert rc == 0 and info.tiles == 0
+        assert X.xpose_sgemm(m, n, 7, 1.0, 0, 7, 0, max(n, 1), 0.0, 0,
+                             max(n, 1), 0) == 0
+
+
+def test_k_zero_needs_only_c():
+    rc, info = plan(k=0, a=0, b=0, lda=1)
+    assert rc == 0 and info.tiles == 1024
+    assert plan(k=0, a=0, b=0, lda=1, c=0)[0] == X.XPOSE_EINVAL

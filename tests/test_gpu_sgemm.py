@@ -1,0 +1,247 @@
+"""GPU parity of the tiled SGEMM (xpose_sgemm*, include/xpose_sgemm.h)
+against the oracle (oracle/sgemm.py), through the C ABI.
+
+* Integer-valued inputs keep every partial sum exact in float32, so there
+  the GPU must equal the oracle bit for bit, whatever the summation order.
+* Uniform [-1, 1) inputs are compared within the fp32 dot-product bound
+  (k + 3) * 2^-24 * (|alpha| |A| |B| + |beta| |C|), elementwise.
+* The m x n region is the only thing written: pitch padding and guard
+  bands around C keep their sentinels.
+* Every As layout, k step and load path sums in the same order (k pairs in
+  sequence), so all kernels must agree bit for bit with each other."""
+import numpy as np
+import pytest
+
+import oracle.sgemm as og
+import workloads as wl
+from xpose_testlib import say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+X = pytest.importorskip("lds_tiled_matrix_amd")
+
+GUARD = 64
+SENTINEL = np.float32(-12345.5)
+LAYOUTS = (X.AS_UNPADDED, X.AS_PADDED, X.AS_SWIZZLE)
+BKS = (8, 16, 32)
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda", 0)
+
+
+def _flat(M, ld, fill):
+    rows, cols = M.shape
+    buf = np.full(max(rows * ld, 1), fill, dtype=np.float32)
+    for i in range(rows):
+        buf[i * ld:i * ld + cols] = M[i]
+    return buf
+
+
+def _upload(buf, shift):
+    """Device copy of a flat buffer starting `shift` floats into a fresh
+    allocation (shift 1: 4-byte but not 16-byte aligned)."""
+    d = torch.empty(shift + buf.size, dtype=torch.float32, device=_dev())
+    d[shift:].copy_(torch.from_numpy(buf))
+    return d, d.data_ptr() + 4 * shift
+
+
+def run_case(A, B, C, alpha, beta, pads=(0, 0, 0), shifts=(0, 0, 0),
+             opts=None, stream=None, entry="ex"):
+    """Run the library; return (C buffer as read back, flat C buffer before,
+    ldc).  Both buffers include GUARD sentinels on each side."""
+    m, k = A.shape
+    n = B.shape[1]
+    lda, ldb, ldc = max(k, 1) + pads[0], max(n, 1) + pads[1], max(n, 1) + pads[2]
+    a = _flat(A, lda, np.nan)
+    b = _flat(B, ldb, np.nan)
+    c_body = _flat(C, ldc, SENTINEL)
+    c_full = np.concatenate([np.full(GUARD, SENTINEL, np.float32), c_body,
+                             np.full(GUARD, SENTINEL, np.float32)])
+    da, pa = _upload(a, shifts[0])
+    db, pb = _upload(b, shifts[1])
+    dc, pc0 = _upload(c_full, shifts[2])
+    pc = pc0 + 4 * GUARD
+    sh = 0 if stream is None else int(stream.cuda_stream)
+    say(f"sgemm m={m} n={n} k={k} pads={pads} shifts={shifts} "
+        f"opts={None if opts is None else (opts.layout, opts.bk)}")
+    if entry == "plain":
+        rc = X.xpose_sgemm(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, sh)
+    else:
+        rc = X.xpose_sgemm_ex(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
+                              opts, sh)
+    assert rc == 0, X.strerror(rc)
+    torch.cuda.synchronize()
+    got = dc[shifts[2]:].cpu().numpy()
+    return got, c_full, (a, lda, b, ldb, ldc)
+
+
+def expected(A, B, C, alpha, beta, c_full, bufs):
+    """Oracle result written into a copy of the C buffer (float32)."""
+    a, lda, b, ldb, ldc = bufs
+    m, k = A.shape
+    n = B.shape[1]
+    out = c_full.copy()
+    body = out[GUARD:out.size - GUARD]
+    og.sgemm_into(m, n, k, alpha, a, lda, b, ldb, beta, body, ldc)
+    return out
+
+
+def region_mask(m, n, ldc, size):
+    mask = np.zeros(size, dtype=bool)
+    for i in range(m):
+        mask[GUARD + i * ldc:GUARD + i * ldc + n] = True
+    return mask
+
+
+def check_exact(A, B, C, alpha, beta, **kw):
+    got, c_full, bufs = run_case(A, B, C, alpha, beta, **kw)
+    exp = expected(A, B, C, alpha, beta, c_full, bufs)
+    bad = np.flatnonzero(got.view(np.uint32) != exp.view(np.uint32))
+    assert bad.size == 0, (bad[:8], got[bad[:8]], exp[bad[:8]])
+    return got
+
+
+def check_bound(A, B, C, alpha, beta, **kw):
+    got, c_full, bufs = run_case(A, B, C, alpha, beta, **kw)
+    m, k = A.shape
+    n = B.shape[1]
+    ldc = bufs[4]
+    ref = og.sgemm(m, n, k, alpha, bufs[0], bufs[1], bufs[2], bufs[3], beta,
+                   c_full[GUARD:c_full.size - GUARD], ldc)
+    mag = abs(alpha) * (np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64)))
+    if beta != 0:
+        mag += abs(beta) * np.abs(C.astype(np.float64))
+    tol = (k + 3) * 2.0 ** -24 * mag
+    mask = region_mask(m, n, ldc, got.size)
+    g = got[mask].reshape(m, n).astype(np.float64)
+    err = np.abs(g - ref)
+    assert (err <= tol).all(), (err.max(), np.unravel_index(np.argmax(err - tol), err.shape))
+    # nothing outside the m x n region changed
+    assert np.array_equal(got[~mask].view(np.uint32), c_full[~mask].view(np.uint32))
+    return got
+
+
+EXACT_SHAPES = [(128, 128, 16), (256, 384, 512), (130, 67, 45), (1, 1, 1),
+                (300, 257, 33), (64, 200, 7), (129, 1, 300)]
+
+
+@pytest.mark.parametrize("bk", BKS)
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
+def test_exact_on_integer_inputs(layout, bk):
+    opts = X.make_sgemm_opts(layout, bk)
+    for idx, (m, n, k) in enumerate(EXACT_SHAPES):
+        A = wl.small_int_f32((m, k), 100 + idx)
+        B = wl.small_int_f32((k, n), 200 + idx)
+        C = wl.small_int_f32((m, n), 300 + idx)
+        check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(idx % 3, 2 * (idx % 2), 5))
+        # beta == 0: C is not read, NaN there must not leak
+        Cn = np.full((m, n), np.nan, np.float32)
+        got = check_exact(A, B, Cn, 1.0, 0.0, opts=opts)
+        assert np.isfinite(got[region_mask(m, n, max(n, 1), got.size)]).all()
+
+
+def test_scalar_load_path_is_exact():
+    """4-byte aligned (not 16-byte) operands and pitches that are not a
+    multiple of 4 take the 4-byte loads."""
+    m, n, k = 197, 131, 77
+    A = wl.small_int_f32((m, k), 11)
+    B = wl.small_int_f32((k, n), 12)
+    C = wl.small_int_f32((m, n), 13)
+    rc, info = X.xpose_sgemm_plan(m, n, k, 0x7f0000000004, k + 1, 0x7f1000000000,
+                                  n + 2, 0x7f2000000000, n)
+    assert rc == 0 and info.vector_loads == 0
+    for shifts, pads in (((1, 0, 0), (0, 0, 0)), ((0, 3, 1), (1, 2, 0)),
+                         ((0, 0, 0), (1, 0, 3))):
+        check_exact(A, B, C, 1.0, 1.0, shifts=shifts, pads=pads)
+
+
+def test_uniform_inputs_within_the_fp32_bound():
+    for idx, (m, n, k) in enumerate(((512, 512, 512), (1000, 777, 1025),
+                                     (33, 4097, 64), (256, 128, 4096))):
+        A = wl.uniform_f32((m, k), 400 + idx)
+        B = wl.uniform_f32((k, n), 500 + idx)
+        C = wl.uniform_f32((m, n), 600 + idx)
+        check_bound(A, B, C, 1.0, 1.0, entry="plain")
+        check_bound(A, B, C, -0.75, 0.0, pads=(3, 1, 2))
+
+
+def test_all_kernels_agree_bit_for_bit():
+    m, n, k = 384, 320, 544
+    A = wl.uniform_f32((m, k), 71)
+    B = wl.uniform_f32((k, n), 72)
+    C = wl.uniform_f32((m, n), 73)
+    ref = None
+    for layout in LAYOUTS:
+        for bk in BKS:
+            for shifts in ((0, 0, 0), (1, 1, 0)):
+                got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
+                                     opts=X.make_sgemm_opts(layout, bk))
+                if ref is None:
+                    ref = got
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+                    (layout, bk, shifts)
+
+
+def test_degenerate_shapes():
+    # k == 0: C = beta * C, a and b may be NULL
+    C = wl.uniform_f32((70, 50), 81)
+    d = torch.from_numpy(C.copy()).to(_dev())
+    say("sgemm k=0")
+    assert X.xpose_sgemm(70, 50, 0, 3.0, 0, 1, 0, 50, -0.5, d.data_ptr(), 50, 0) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), (np.float32(-0.5) * C).astype(np.float32))
+    # m == 0 or n == 0: nothing happens, NULL pointers allowed
+    assert X.xpose_sgemm(0, 50, 10, 1.0, 0, 10, 0, 50, 0.0, 0, 50, 0) == 0
+    assert X.xpose_sgemm(70, 0, 10, 1.0, 0, 10, 0, 1, 0.0, 0, 1, 0) == 0
+    # one row, one column
+    for m, n, k in ((1, 300, 129), (300, 1, 129), (1, 1, 4096)):
+        check_exact(wl.small_int_f32((m, k), 91), wl.small_int_f32((k, n), 92),
+                    wl.small_int_f32((m, n), 93), 1.0, 1.0)
+
+
+def test_side_stream():
+    s = torch.cuda.Stream()
+    A = wl.small_int_f32((160, 96), 1)
+    B = wl.small_int_f32((96, 200), 2)
+    C = wl.small_int_f32((160, 200), 3)
+    check_exact(A, B, C, 1.0, 1.0, stream=s)
+
+
+def test_page_size_default_launch_sampled():
+    """The 4096^3 workload in the launch the benchmark times: 96 sampled rows
+    of C against the oracle within the bound, and with B = 1 and integer A
+    every element of C against the row sums (a property at any size)."""
+    w = wl.GEMM_WORKLOADS["sgemm_4096"]
+    A, B, C = wl.make_gemm_inputs(w)
+    dev = _dev()
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    dC = torch.from_numpy(C).to(dev)
+    say("sgemm 4096^3 default")
+    X.sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    rows = np.random.default_rng(5).choice(w.m, 96, replace=False)
+    a_rows = np.ascontiguousarray(A[rows]).reshape(-1)
+    c_rows = np.ascontiguousarray(C[rows]).reshape(-1)
+    ref = og.sgemm(len(rows), w.n, w.k, w.alpha, a_rows, w.k, B.reshape(-1),
+                   w.n, w.beta, c_rows, w.n)
+    mag = abs(w.alpha) * (np.abs(A[rows].astype(np.float64)) @ np.abs(B.astype(np.float64)))
+    mag += abs(w.beta) * np.abs(C[rows].astype(np.float64))
+    err = np.abs(got[rows].astype(np.float64) - ref)
+    assert (err <= (w.k + 3) * 2.0 ** -24 * mag).all(), err.max()
+    del dA, dB, dC
+    # B = 1: every column of C is alpha times A's row sums, exact on integers
+    Ai = wl.small_int_f32((w.m, w.k), 6)
+    ones = np.ones((w.k, w.n), np.float32)
+    dA = torch.from_numpy(Ai).to(dev)
+    dB = torch.from_numpy(ones).to(dev)
+    say("sgemm 4096^3 row sums")
+    dC = X.sgemm(dA, dB)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    sums = og.sgemm(w.m, 1, w.k, 1.0, Ai.reshape(-1), w.k,
+                    np.ones(w.k, np.float32), 1, 0.0, np.zeros(w.m, np.float32), 1)
+    assert np.array_equal(got, np.broadcast_to(sums.astype(np.float32), got.shape))
