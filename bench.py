@@ -7,8 +7,11 @@ row-major, ld = cols) with the input already resident in HBM.  Prints ONE
 JSON line: effective GB/s = (read + write bytes) / time, with the copy
 yardstick, the LDS-layout ablation, the kernel's roofline fraction measured
 live with HIP events on the launch stream, and the oracle timed on one host
-core.  --table additionally writes a markdown table over every workload to
-stderr.
+core.  The line also carries, under "sgemm", the tiled SGEMM whose
+transposed LDS store is the pages' second bank-conflict workload (4096^3
+fp32, TFLOP/s against the matrix-core peak, its As-layout ablation);
+--sgemm-only measures just that.  --table additionally writes a markdown
+table over every workload to stderr.
 
 Timing protocol ("Shared memory and the bank conflict", section "What to
 record": warm the kernel up first, time it many times, report the median,
@@ -277,6 +280,109 @@ def bench_workload(X, w, steps, warmup, stream, layouts=True, cold=True):
     return res, host, y
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix-core peak
+
+
+def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
+    """The tiled SGEMM with the padded transposed As store at the size its
+    page measures (M = N = K = 4096, C += A B, uniform [-1, 1) inputs):
+    the default kernel with its matrix-core roofline, the As-layout
+    ablation with one and two LDS buffers, torch's fp32 addmm for context,
+    sampled parity against the oracle, and the oracle timed on a bounded
+    sample."""
+    import torch
+    import oracle.sgemm as og
+    w = wl.GEMM_WORKLOADS["sgemm_4096"]
+    A, B, C = wl.make_gemm_inputs(w)
+    dev = torch.device("cuda", 0)
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    dC = torch.from_numpy(C).to(dev)
+    sh = int(stream.cuda_stream)
+
+    def launch_with(opts):
+        def go():
+            rc = X.xpose_sgemm_ex(w.m, w.n, w.k, w.alpha, dA.data_ptr(), w.k,
+                                  dB.data_ptr(), w.n, w.beta, dC.data_ptr(),
+                                  w.n, opts, sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+        return go
+
+    def tflops(durs):
+        d = sorted(durs)
+        med, mean = statistics.median(d), sum(d) / len(d)
+        return {"median_us": round(med * 1e6, 1), "min_us": round(d[0] * 1e6, 1),
+                "mean_us": round(mean * 1e6, 1),
+                "median_TFLOPs": round(w.flops / med / 1e12, 2),
+                "mean_TFLOPs": round(w.flops / mean / 1e12, 2)}
+
+    res = {"workload": w.description, "m": w.m, "n": w.n, "k": w.k,
+           "alpha": w.alpha, "beta": w.beta, "flops": w.flops}
+    # One launch on the original C for the parity sample.
+    with torch.cuda.stream(stream):
+        launch_with(None)()
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    rows = np.random.default_rng(7).choice(w.m, 64, replace=False)
+    t0 = time.perf_counter()
+    ref = og.sgemm(len(rows), w.n, w.k, w.alpha,
+                   np.ascontiguousarray(A[rows]).reshape(-1), w.k,
+                   B.reshape(-1), w.n, w.beta,
+                   np.ascontiguousarray(C[rows]).reshape(-1), w.n)
+    t_ref = time.perf_counter() - t0
+    mag = abs(w.alpha) * (np.abs(A[rows].astype(np.float64)) @
+                          np.abs(B.astype(np.float64)))
+    mag += abs(w.beta) * np.abs(C[rows].astype(np.float64))
+    err = np.abs(got[rows].astype(np.float64) - ref)
+    res["parity_vs_oracle"] = bool((err <= (w.k + 3) * 2.0 ** -24 * mag).all())
+    res["parity_sample"] = ("64 sampled rows of C (all columns) against the "
+                            "oracle, within (k + 3) 2^-24 (|alpha||A||B| + "
+                            "|beta||C|)")
+    if with_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = 1
+        res["cpu_baseline"] = {
+            "value": round(2 * len(rows) * w.n * w.k / t_ref / 1e9, 2),
+            "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{len(rows)} rows of C (float64 numpy matmul, "
+                       f"{threads} BLAS threads), {t_ref * 1e3:.0f} ms")}
+    with torch.cuda.stream(stream):
+        ab = {}
+        n_ab = max(10, min(steps, 40))
+        for lay, name in X.AS_NAMES.items():
+            for flags, tag in ((0, ""), (X.SGEMM_DOUBLE_BUFFER, " 2 buffers")):
+                _, d = time_launches(launch_with(X.make_sgemm_opts(lay, 0, 0, flags)),
+                                     stream, n_ab, min(warmup, 5))
+                ab[name + tag] = tflops(d)["median_TFLOPs"]
+        res["ablation_TFLOPs"] = ab
+        c2 = torch.empty_like(dC)
+        _, d = time_launches(lambda: torch.addmm(dC, dA, dB, out=c2), stream,
+                             n_ab, min(warmup, 5))
+        res["torch_addmm_fp32_TFLOPs"] = tflops(d)["median_TFLOPs"]
+        del c2
+        wall, durs = time_launches(launch_with(None), stream,
+                                   max(10, min(steps, 100)), min(warmup, 10))
+    torch.cuda.synchronize()
+    t = tflops(durs)
+    rc, info = X.xpose_sgemm_plan(w.m, w.n, w.k, dA.data_ptr(), w.k,
+                                  dB.data_ptr(), w.n, dC.data_ptr(), w.n)
+    res["kernel"] = {"layout": X.AS_NAMES[info.layout], "bk": info.bk,
+                     "as_stride": info.as_stride, "stages": info.stages,
+                     "lds_bytes": info.lds_bytes, "workgroups": info.tiles,
+                     "tile": f"{info.tile_m}x{info.tile_n}"}
+    res["timing"] = t
+    achieved = t["mean_TFLOPs"]
+    res["roofline"] = {"bound": "mfma", "achieved": achieved,
+                       "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+                       "traffic": None}
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +396,10 @@ def main(argv=None):
                     help="skip the cold-cache (flushed) timing")
     ap.add_argument("--table", action="store_true",
                     help="also measure every workload; markdown table to stderr")
+    ap.add_argument("--no-sgemm", action="store_true",
+                    help="skip the tiled SGEMM (padded transposed As store)")
+    ap.add_argument("--sgemm-only", action="store_true",
+                    help="measure only the tiled SGEMM; print its JSON line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -306,8 +416,14 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
-    w = wl.WORKLOADS[args.workload]
     stream = torch.cuda.Stream()
+    if args.sgemm_only:
+        log("bench: tiled SGEMM only")
+        print(json.dumps({"sgemm": bench_sgemm(X, args.steps, args.warmup, stream,
+                                               with_cpu=not args.no_cpu)}),
+              flush=True)
+        return 0
+    w = wl.WORKLOADS[args.workload]
     log(f"bench: {w.description}; steps={args.steps} warmup={args.warmup}")
     res, host, y = bench_workload(X, w, args.steps, args.warmup, stream,
                                   layouts=not args.no_ablation,
@@ -329,6 +445,14 @@ def main(argv=None):
         cpu["host_cpu"] = host_cpu_name()
         if not parity:
             log("bench: PARITY FAILURE against the oracle")
+
+    sgemm = None
+    if not args.no_sgemm:
+        log("bench: tiled SGEMM")
+        del y
+        torch.cuda.empty_cache()
+        sgemm = bench_sgemm(X, args.steps, args.warmup, stream,
+                            with_cpu=not args.no_cpu)
 
     plan = res["plan"]
     line = {
@@ -375,6 +499,7 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "sgemm": sgemm,
     }
     print(json.dumps(line), flush=True)
 

@@ -81,9 +81,16 @@ typedef enum xpose_as_layout {
 
 /* Option flags of xpose_sgemm_ex. */
 enum {
-  XPOSE_SGEMM_NO_XCD_REMAP = 1 /* keep the hardware's round-robin
-                                  assignment of workgroups to XCDs instead
-                                  of one contiguous range of blocks each     */
+  XPOSE_SGEMM_NO_XCD_REMAP = 1, /* keep the hardware's round-robin
+                                   assignment of workgroups to XCDs instead
+                                   of one contiguous range of blocks each    */
+  XPOSE_SGEMM_DOUBLE_BUFFER = 2 /* two LDS buffers alternate, so one barrier
+                                   per k step suffices instead of the two of
+                                   the pages' loop (the remedy "What Could Be
+                                   Improved" points to: both barriers stall
+                                   the block).  Measured no faster on gfx950,
+                                   where three or four other workgroups per
+                                   compute unit fill the barrier stalls      */
 };
 
 /* Optional knobs (zero-initialise for defaults).  Every choice gives the
@@ -102,13 +109,14 @@ typedef struct xpose_sgemm_info {
   int32_t layout;       /* resolved xpose_as_layout                           */
   int32_t bk;           /* k step                                             */
   int32_t as_stride;    /* As row stride in floats                            */
-  int32_t lds_bytes;    /* LDS per workgroup                                  */
+  int32_t lds_bytes;    /* LDS per workgroup (all buffers)                    */
   int32_t threads;      /* threads per workgroup                              */
   int32_t tile_m;       /* rows of C per workgroup                            */
   int32_t tile_n;       /* columns of C per workgroup                         */
   int32_t vector_loads; /* 1: 16-byte tile loads; 0: 4-byte loads             */
   int32_t group_m;      /* resolved block-order group height                  */
   int32_t xcd_remap;    /* 1 if blocks are remapped per XCD                   */
+  int32_t stages;       /* LDS buffers per workgroup (1 or 2)                 */
   int64_t tiles;        /* workgroups launched                                */
 } xpose_sgemm_info;
 

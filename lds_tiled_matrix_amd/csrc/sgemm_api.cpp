@@ -50,17 +50,20 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
               const xpose_sgemm_opts *opts, SgemmPlan &plan) {
   int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM;
   bool remap = true;
+  int stages = 1;
   if (opts) {
     if (opts->layout < XPOSE_AS_AUTO || opts->layout > XPOSE_AS_SWIZZLE)
       return XPOSE_EINVAL;
     if (opts->bk != 0 && opts->bk != 8 && opts->bk != 16 && opts->bk != 32)
       return XPOSE_EINVAL;
     if (opts->group_m < 0) return XPOSE_EINVAL;
-    if (opts->flags & ~XPOSE_SGEMM_NO_XCD_REMAP) return XPOSE_EINVAL;
+    if (opts->flags & ~(XPOSE_SGEMM_NO_XCD_REMAP | XPOSE_SGEMM_DOUBLE_BUFFER))
+      return XPOSE_EINVAL;
     if (opts->layout) layout = opts->layout;
     if (opts->bk) bk = opts->bk;
     if (opts->group_m) group_m = opts->group_m;
     remap = !(opts->flags & XPOSE_SGEMM_NO_XCD_REMAP);
+    if (opts->flags & XPOSE_SGEMM_DOUBLE_BUFFER) stages = 2;
   }
   if (m < 0 || n < 0 || k < 0) return XPOSE_EINVAL;
   if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) ||
@@ -96,7 +99,8 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   const xpose::SgemmKernel *table = xpose::sgemm_kernels(&count);
   const xpose::SgemmKernel *kern = nullptr;
   for (int i = 0; i < count && !kern; ++i)
-    if (table[i].bk == bk && table[i].layout == layout && table[i].vec == vec)
+    if (table[i].bk == bk && table[i].layout == layout &&
+        table[i].vec == vec && table[i].stages == stages)
       kern = &table[i];
   if (!kern) return XPOSE_ENOTILE;
   if (group_m > tiles_m) group_m = (int)tiles_m;
@@ -170,6 +174,7 @@ int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
   info->vector_loads = kern.vec ? 1 : 0;
   info->group_m = (int32_t)plan.args.group_m;
   info->xcd_remap = plan.args.xcd_remap;
+  info->stages = kern.stages;
   info->tiles = plan.tiles;
   return rc;
 }

@@ -6,8 +6,8 @@
 // dense contraction runs on the matrix cores (v_mfma_f32_32x32x2_f32, fp32
 // in and out); the LDS staging keeps the pages' structure: 16-byte row loads
 // of A, scalar transposed stores into As, 16-byte copies of B into Bs, a
-// barrier, the inner products, a second barrier.  The layouts and lane maps
-// are in sgemm_lanes.h.
+// barrier, the inner products, a second barrier (or, with two LDS buffers,
+// one barrier per step).  The layouts and lane maps are in sgemm_lanes.h.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,11 +38,19 @@ __device__ inline f32x4 load_vec(const float *base, int64_t row, int64_t col,
   return v;
 }
 
-template <int BK, int L, bool VEC>
-__global__ __launch_bounds__(256) void xpose_sgemm_kernel(SgemmArgs a) {
+// STAGES = 1 is the pages' loop: stage the step's tiles, barrier, products,
+// barrier.  STAGES = 2 keeps two LDS buffers: the next step's tiles are
+// staged into the other buffer right after this step's products, so one
+// barrier per step separates the writes of one buffer from the reads of
+// the other.  Either way the next step's global loads are issued before
+// this step's products and land in registers while the matrix cores run.
+template <int BK, int L, bool VEC, int STAGES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    SgemmTile<BK, L>::waves_per_simd(STAGES)))) void
+xpose_sgemm_kernel(SgemmArgs a) {
   using T = SgemmTile<BK, L>;
-  __shared__ __attribute__((aligned(16))) float As[T::AS_FLOATS];
-  __shared__ __attribute__((aligned(16))) float Bs[T::BS_FLOATS];
+  __shared__ __attribute__((aligned(16))) float As[STAGES * T::AS_FLOATS];
+  __shared__ __attribute__((aligned(16))) float Bs[STAGES * T::BS_FLOATS];
 
   const int t = threadIdx.x, q = t & 63, w = t >> 6;
   uint32_t bm, bn;
@@ -75,6 +83,22 @@ __global__ __launch_bounds__(256) void xpose_sgemm_kernel(SgemmArgs a) {
       rb[p] = load_vec<VEC>(a.b, k0 + T::b_row(t, p), n0 + T::b_col(t), a.k,
                             a.n, a.ldb);
   };
+  // A's vectors go into As transposed, one 4-byte store per element: the
+  // store whose banks the layout decides.  B's rows are copied as they are.
+  auto stage = [&](int buf) {
+    float *as = As + buf * T::AS_FLOATS;
+    float *bs = Bs + buf * T::BS_FLOATS;
+#pragma unroll
+    for (int p = 0; p < T::A_PASSES; ++p) {
+      const int i = T::a_row(t, p), l = T::a_col(t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) as[T::as_index(l + e, i)] = ra[p][e];
+    }
+#pragma unroll
+    for (int p = 0; p < T::B_PASSES; ++p)
+      *reinterpret_cast<f32x4 *>(&bs[T::bs_index(T::b_row(t, p), T::b_col(t))]) =
+          rb[p];
+  };
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -86,36 +110,44 @@ __global__ __launch_bounds__(256) void xpose_sgemm_kernel(SgemmArgs a) {
 
   const int wr = T::wave_row(w), wc = T::wave_col(w);
   const int half = q >> 5, lane32 = q & 31;
-  if (a.k > 0) load(0);
-  for (int64_t k0 = 0; k0 < a.k; k0 += BK) {
-    // A's vectors go into As transposed, one 4-byte store per element: the
-    // store whose banks the layout decides.  B's rows are copied as they are.
-#pragma unroll
-    for (int p = 0; p < T::A_PASSES; ++p) {
-      const int i = T::a_row(t, p), l = T::a_col(t);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[T::as_index(l + e, i)] = ra[p][e];
-    }
-#pragma unroll
-    for (int p = 0; p < T::B_PASSES; ++p)
-      *reinterpret_cast<f32x4 *>(&Bs[T::bs_index(T::b_row(t, p), T::b_col(t))]) =
-          rb[p];
-    __syncthreads();
-    // The next step's loads are in flight while this step's products run.
-    if (k0 + BK < a.k) load(k0 + BK);
+  auto products = [&](int buf) {
+    const float *as = As + buf * T::AS_FLOATS;
+    const float *bs = Bs + buf * T::BS_FLOATS;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 2) {
       const int l = kk + half;
-      const float a0 = As[T::as_index(l, wr + lane32)];
-      const float a1 = As[T::as_index(l, wr + 32 + lane32)];
-      const float b0 = Bs[T::bs_index(l, wc + lane32)];
-      const float b1 = Bs[T::bs_index(l, wc + 32 + lane32)];
+      const float a0 = as[T::as_index(l, wr + lane32)];
+      const float a1 = as[T::as_index(l, wr + 32 + lane32)];
+      const float b0 = bs[T::bs_index(l, wc + lane32)];
+      const float b1 = bs[T::bs_index(l, wc + 32 + lane32)];
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
+  };
+
+  if (a.k > 0) {
+    load(0);
+    stage(0);
     __syncthreads();
+  }
+  int buf = 0;
+  for (int64_t k0 = 0; k0 < a.k; k0 += BK) {
+    const bool more = k0 + BK < a.k;
+    if (more) load(k0 + BK);
+    products(buf);
+    if (STAGES == 1) {
+      __syncthreads();
+      if (more) {
+        stage(0);
+        __syncthreads();
+      }
+    } else {
+      if (more) stage(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
   // C = alpha * acc + beta * C; with beta == 0 C is not read.  32 lanes
@@ -138,27 +170,29 @@ __global__ __launch_bounds__(256) void xpose_sgemm_kernel(SgemmArgs a) {
     }
 }
 
-template <int BK, int L, bool VEC>
+template <int BK, int L, bool VEC, int STAGES>
 hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
   SgemmArgs copy = a;
   void *args[] = {&copy};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(&xpose_sgemm_kernel<BK, L, VEC>),
+      reinterpret_cast<const void *>(&xpose_sgemm_kernel<BK, L, VEC, STAGES>),
       dim3(grid), dim3(256), args, 0, s);
 }
 
-#define XPOSE_SGEMM(BK, L, VEC)                                              \
+#define XPOSE_SGEMM(BK, L, VEC, ST)                                          \
   SgemmKernel {                                                              \
-    BK, L, SgemmTile<BK, L>::AS_STRIDE, SgemmTile<BK, L>::LDS_BYTES, 256,    \
-        VEC, &launch_sgemm<BK, L, VEC>                                       \
+    BK, L, SgemmTile<BK, L>::AS_STRIDE, ST * SgemmTile<BK, L>::LDS_BYTES,    \
+        256, VEC, ST, &launch_sgemm<BK, L, VEC, ST>                          \
   }
-#define XPOSE_SGEMM_BK(BK)                                                   \
-  XPOSE_SGEMM(BK, kAsUnpadded, true), XPOSE_SGEMM(BK, kAsPadded, true),      \
-      XPOSE_SGEMM(BK, kAsSwizzle, true), XPOSE_SGEMM(BK, kAsUnpadded, false), \
-      XPOSE_SGEMM(BK, kAsPadded, false), XPOSE_SGEMM(BK, kAsSwizzle, false)
+#define XPOSE_SGEMM_L(BK, L, ST)                                             \
+  XPOSE_SGEMM(BK, L, true, ST), XPOSE_SGEMM(BK, L, false, ST)
+#define XPOSE_SGEMM_BK(BK, ST)                                               \
+  XPOSE_SGEMM_L(BK, kAsUnpadded, ST), XPOSE_SGEMM_L(BK, kAsPadded, ST),      \
+      XPOSE_SGEMM_L(BK, kAsSwizzle, ST)
 
-const SgemmKernel kSgemmKernels[] = {XPOSE_SGEMM_BK(8), XPOSE_SGEMM_BK(16),
-                                     XPOSE_SGEMM_BK(32)};
+const SgemmKernel kSgemmKernels[] = {
+    XPOSE_SGEMM_BK(8, 1),  XPOSE_SGEMM_BK(16, 1), XPOSE_SGEMM_BK(32, 1),
+    XPOSE_SGEMM_BK(8, 2),  XPOSE_SGEMM_BK(16, 2), XPOSE_SGEMM_BK(32, 2)};
 
 }  // namespace
 

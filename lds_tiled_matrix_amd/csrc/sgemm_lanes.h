@@ -62,6 +62,16 @@ struct SgemmTile {
   static constexpr int LDS_BYTES = 4 * (AS_FLOATS + BS_FLOATS);
   static constexpr int LAYOUT = L;
   static constexpr int KSTEP = BK;
+  // Waves per SIMD the register budget is set for (one wave per SIMD per
+  // 256-thread workgroup): as many workgroups as the LDS of `stages`
+  // buffers lets share a compute unit's 160 KiB, at most four (128
+  // registers per lane) where the k step's prefetch registers fit beside
+  // the 64 accumulators, else three.
+  SGEMM_HD static constexpr int waves_per_simd(int stages) {
+    return (160 * 1024) / (stages * LDS_BYTES) < (BK <= 16 ? 4 : 3)
+               ? (160 * 1024) / (stages * LDS_BYTES)
+               : (BK <= 16 ? 4 : 3);
+  }
 
   static_assert(BK == 8 || BK == 16 || BK == 32, "built k steps");
   static_assert(A_PASSES * A_ROWS_PER_PASS == BM, "whole A tile");

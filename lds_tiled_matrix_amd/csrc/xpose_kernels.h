@@ -155,7 +155,8 @@ struct SgemmArgs {
 
 struct SgemmKernel {
   int bk, layout, as_stride, lds_bytes, threads;
-  bool vec;  // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)
+  bool vec;    // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)
+  int stages;  // LDS buffers: 1 = two barriers per k step, 2 = one
   hipError_t (*launch)(const SgemmArgs &, uint32_t grid, hipStream_t);
 };
 const SgemmKernel *sgemm_kernels(int *count);

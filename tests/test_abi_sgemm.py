@@ -24,7 +24,10 @@ def test_default_plan():
     assert (info.tile_m, info.tile_n, info.threads) == (128, 128, 256)
     assert info.tiles == 32 * 32 and info.vector_loads == 1
     assert info.lds_bytes == 4 * (16 * 130 + 16 * 128)
-    assert info.group_m == 8 and info.xcd_remap == 1
+    assert info.group_m == 8 and info.xcd_remap == 1 and info.stages == 1
+    rc, info = plan(opts=X.make_sgemm_opts(flags=X.SGEMM_DOUBLE_BUFFER))
+    assert rc == 0 and info.stages == 2
+    assert info.lds_bytes == 2 * 4 * (16 * 130 + 16 * 128)
 
 
 @pytest.mark.parametrize("bk", (8, 16, 32))
@@ -73,7 +76,7 @@ def test_vector_load_rules():
     (dict(opts=X.make_sgemm_opts(layout=4)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(bk=12)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(group_m=-1)), X.XPOSE_EINVAL),
-    (dict(opts=X.make_sgemm_opts(flags=2)), X.XPOSE_EINVAL),
+    (dict(opts=X.make_sgemm_opts(flags=4)), X.XPOSE_EINVAL),
 ])
 def test_invalid_calls(kw, code):
     assert plan(**kw)[0] == code

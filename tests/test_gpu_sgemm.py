@@ -66,7 +66,7 @@ def run_case(A, B, C, alpha, beta, pads=(0, 0, 0), shifts=(0, 0, 0),
     pc = pc0 + 4 * GUARD
     sh = 0 if stream is None else int(stream.cuda_stream)
     say(f"sgemm m={m} n={n} k={k} pads={pads} shifts={shifts} "
-        f"opts={None if opts is None else (opts.layout, opts.bk)}")
+        f"opts={None if opts is None else (opts.layout, opts.bk, opts.flags)}")
     if entry == "plain":
         rc = X.xpose_sgemm(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, sh)
     else:
@@ -128,10 +128,12 @@ EXACT_SHAPES = [(128, 128, 16), (256, 384, 512), (130, 67, 45), (1, 1, 1),
                 (300, 257, 33), (64, 200, 7), (129, 1, 300)]
 
 
+@pytest.mark.parametrize("stages", (2, 1))
 @pytest.mark.parametrize("bk", BKS)
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
-def test_exact_on_integer_inputs(layout, bk):
-    opts = X.make_sgemm_opts(layout, bk)
+def test_exact_on_integer_inputs(layout, bk, stages):
+    opts = X.make_sgemm_opts(layout, bk,
+                             flags=X.SGEMM_DOUBLE_BUFFER if stages == 2 else 0)
     for idx, (m, n, k) in enumerate(EXACT_SHAPES):
         A = wl.small_int_f32((m, k), 100 + idx)
         B = wl.small_int_f32((k, n), 200 + idx)
@@ -176,13 +178,14 @@ def test_all_kernels_agree_bit_for_bit():
     ref = None
     for layout in LAYOUTS:
         for bk in BKS:
-            for shifts in ((0, 0, 0), (1, 1, 0)):
-                got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
-                                     opts=X.make_sgemm_opts(layout, bk))
-                if ref is None:
-                    ref = got
-                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
-                    (layout, bk, shifts)
+            for flags in (0, X.SGEMM_DOUBLE_BUFFER):
+                for shifts in ((0, 0, 0), (1, 1, 0)):
+                    got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
+                                         opts=X.make_sgemm_opts(layout, bk, 0, flags))
+                    if ref is None:
+                        ref = got
+                    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+                        (layout, bk, flags, shifts)
 
 
 def test_degenerate_shapes():
