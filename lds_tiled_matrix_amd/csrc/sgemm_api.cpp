@@ -7,7 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "xpose_kernels.h"
+#include "sgemm_kernels.h"
 
 namespace {
 

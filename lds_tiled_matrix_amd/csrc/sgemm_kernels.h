@@ -1,0 +1,36 @@
+// Internal interface between the SGEMM front end (sgemm_api.cpp) and its
+// gfx950 kernels (sgemm_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xpose {
+
+// Tiled SGEMM, C = alpha * A * B + beta * C (fp32, row-major; pitches in
+// floats).  Grid = tiles_m * tiles_n workgroups of 128 x 128 blocks of C.
+struct SgemmArgs {
+  const float *a, *b;
+  float *c;
+  int64_t m, n, k, lda, ldb, ldc;
+  float alpha, beta;
+  uint32_t tiles_m, tiles_n;
+  uint32_t group_m;   // block order: group height in block rows (>= 1)
+  int32_t xcd_remap;  // 1: one contiguous range of blocks per XCD
+};
+
+struct SgemmKernel {
+  int bk, layout, as_stride, lds_bytes, threads;
+  bool vec;    // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)
+  int stages;  // LDS buffers: 1 = two barriers per k step, 2 = one
+  hipError_t (*launch)(const SgemmArgs &, uint32_t grid, hipStream_t);
+};
+
+// Every compiled SGEMM kernel; *count receives the table length.
+const SgemmKernel *sgemm_kernels(int *count);
+
+// Records a failed HIP call for xpose_last_hip_error (kept by the transpose
+// front end, xpose_api.cpp) and returns XPOSE_EHIP.
+int record_hip_error(hipError_t e);
+
+}  // namespace xpose

@@ -13,7 +13,7 @@
 #include <stdint.h>
 
 #include "sgemm_lanes.h"
-#include "xpose_kernels.h"
+#include "sgemm_kernels.h"
 
 namespace xpose {
 namespace {

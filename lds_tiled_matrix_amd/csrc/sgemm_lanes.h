@@ -18,7 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "xpose_kernels.h"
+#include "sgemm_kernels.h"
 
 #define SGEMM_HD __host__ __device__
 

@@ -11,6 +11,7 @@
 
 #include <atomic>
 
+#include "sgemm_kernels.h"
 #include "xpose_kernels.h"
 
 namespace {

@@ -141,29 +141,6 @@ const CopyKernel *copy_kernels(int *count);
 hipError_t launch_copy(const CopyKernel &k, void *dst, const void *src,
                        int64_t bytes, hipStream_t stream);
 
-// Tiled SGEMM, C = alpha * A * B + beta * C (fp32, row-major; pitches in
-// floats).  Grid = tiles_m * tiles_n workgroups of 128 x 128 blocks of C.
-struct SgemmArgs {
-  const float *a, *b;
-  float *c;
-  int64_t m, n, k, lda, ldb, ldc;
-  float alpha, beta;
-  uint32_t tiles_m, tiles_n;
-  uint32_t group_m;   // block order: group height in block rows (>= 1)
-  int32_t xcd_remap;  // 1: one contiguous range of blocks per XCD
-};
-
-struct SgemmKernel {
-  int bk, layout, as_stride, lds_bytes, threads;
-  bool vec;    // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)
-  int stages;  // LDS buffers: 1 = two barriers per k step, 2 = one
-  hipError_t (*launch)(const SgemmArgs &, uint32_t grid, hipStream_t);
-};
-const SgemmKernel *sgemm_kernels(int *count);
-
-// Records a failed HIP call for xpose_last_hip_error and returns XPOSE_EHIP.
-int record_hip_error(hipError_t e);
-
 // LDS bank microbenchmark; lane_bytes is a host array of 64 byte offsets.
 hipError_t launch_lds_probe(uint64_t *out, const int32_t *lane_bytes,
                             int width, bool is_write, int iters,
