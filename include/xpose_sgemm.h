@@ -15,8 +15,10 @@
  * Conflicts" (the kernel listed under "The Fix Is One Constant", measured at
  * m = n = k = 4096 in "Mechanics").  With beta == 0, C is write-only: it is
  * not read, so NaN or uninitialised contents do not reach the result (the
- * pages' kernel always reads C; where C is finite the two agree).  Elements
- * of C outside the m x n region (pitch padding) are never written.
+ * pages' kernel always reads C; where C is finite the two agree).  A and B
+ * are always read when k > 0, also with alpha == 0, so NaN or Inf there
+ * reach C as alpha * NaN.  Elements of C outside the m x n region (pitch
+ * padding) are never written.
  *
  * How.  Each workgroup computes a 128 x 128 block of C in steps of bk along
  * k.  Per step it loads A's 128 x bk tile with 16-byte row reads and stores
