@@ -471,6 +471,29 @@ def test_packed_small_matrices(s):
                label=f"packed write-back s{s}")
 
 
+# Dense matrices of 16-32 KiB that are not a whole number of tiles: packed
+# by default into 32 KiB blocks.
+RAGGED_32K = {4: ((64, 96), (90, 90), (70, 117)), 2: ((100, 100), (127, 127), (90, 150)),
+              1: ((150, 150), (181, 181), (100, 300)), 8: ((45, 60), (63, 63))}
+
+
+@pytest.mark.parametrize("s", SIZES)
+def test_packed_ragged_up_to_32k(s):
+    for r, c in RAGGED_32K[s]:
+        assert 16384 < r * c * s <= 32768
+        for batch, shift in ((300, 0), (29, 1)):
+            rc, info = X.xpose_plan(1 << 40, 1 << 44, batch, r, c, c, r, r * c,
+                                    r * c, DTYPE_OF_SIZE[s], None)
+            assert rc == 0 and info.packed >= 1, (r, c, batch)
+            check_case(s, batch, r, c, seed=r * 7 + c + batch, in_shift=shift,
+                       out_shift=shift, label=f"packed 32k s{s} {batch}x{r}x{c}")
+    # forced: a whole-tile matrix of 32 KiB, a single matrix
+    r, c = (128, 64) if s == 4 else (128, 128) if s == 2 else (128, 256) if s == 1 else (64, 64)
+    want = X.make_opts(flags=X.FLAG_PACKED)
+    check_case(s, 9, r, c, seed=3, opts=want, label=f"packed forced 32k s{s} {r}x{c}")
+    check_case(s, 1, r, c, seed=4, opts=want, label=f"packed forced single 32k s{s}")
+
+
 def test_nontemporal_loads_variant():
     """Non-temporal loads and stores are built for two fp32 tiles only."""
     for tile in ((32, 32), (64, 64)):
