@@ -86,13 +86,19 @@ enum {
   XPOSE_SGEMM_NO_XCD_REMAP = 1, /* keep the hardware's round-robin
                                    assignment of workgroups to XCDs instead
                                    of one contiguous range of blocks each    */
-  XPOSE_SGEMM_DOUBLE_BUFFER = 2 /* two LDS buffers alternate, so one barrier
+  XPOSE_SGEMM_DOUBLE_BUFFER = 2, /* two LDS buffers alternate, so one barrier
                                    per k step suffices instead of the two of
                                    the pages' loop (the remedy "What Could Be
                                    Improved" points to: both barriers stall
                                    the block).  Measured no faster on gfx950,
                                    where three or four other workgroups per
                                    compute unit fill the barrier stalls      */
+  XPOSE_SGEMM_NO_BUFFER_LOADS = 4 /* load whole tiles with 64-bit-address
+                                   global loads instead of buffer loads (a
+                                   descriptor per k step, 32-bit lane
+                                   offsets), the default where the pitches
+                                   allow it (lda <= 4161790 and
+                                   ldb <= 16647160)                          */
 };
 
 /* Optional knobs (zero-initialise for defaults).  Every choice gives the
@@ -119,6 +125,7 @@ typedef struct xpose_sgemm_info {
   int32_t group_m;      /* resolved block-order group height                  */
   int32_t xcd_remap;    /* 1 if blocks are remapped per XCD                   */
   int32_t stages;       /* LDS buffers per workgroup (1 or 2)                 */
+  int32_t buffer_loads; /* 1: whole tiles are read with buffer loads          */
   int64_t tiles;        /* workgroups launched                                */
 } xpose_sgemm_info;
 

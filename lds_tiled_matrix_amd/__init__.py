@@ -44,7 +44,7 @@ CACHE_NAMES = {CACHE_DEFAULT: "default", CACHE_NT_STORE: "nt_store",
 AS_AUTO, AS_UNPADDED, AS_PADDED, AS_SWIZZLE = 0, 1, 2, 3
 AS_NAMES = {AS_UNPADDED: "unpadded", AS_PADDED: "padded",
             AS_SWIZZLE: "swizzle"}
-SGEMM_NO_XCD_REMAP, SGEMM_DOUBLE_BUFFER = 1, 2
+SGEMM_NO_XCD_REMAP, SGEMM_DOUBLE_BUFFER, SGEMM_NO_BUFFER_LOADS = 1, 2, 4
 
 # Every exported entry point, in header order (include/xpose.h, then
 # include/xpose_sgemm.h).
@@ -93,7 +93,8 @@ class XposeSgemmInfo(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("vector_loads", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("stages", ctypes.c_int32), ("tiles", ctypes.c_int64)]
+                ("stages", ctypes.c_int32), ("buffer_loads", ctypes.c_int32),
+                ("tiles", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

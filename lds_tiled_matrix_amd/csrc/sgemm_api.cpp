@@ -15,6 +15,9 @@ constexpr int kTile = 128;          // rows and columns of C per workgroup
 constexpr int kDefaultBk = 16;
 constexpr int kDefaultLayout = XPOSE_AS_PADDED;
 constexpr int kDefaultGroupM = 8;
+// Largest lda for buffer loads: 128 rows of the A tile (plus the k step)
+// within a 31-bit byte offset; ldb may be 4x larger (at most 32 rows of B).
+constexpr int64_t kMaxBufferPitch = ((int64_t)1 << 31) / (4 * (kTile + 1));
 
 struct SgemmPlan {
   bool empty = false;
@@ -49,7 +52,7 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
               const float *b, int64_t ldb, const float *c, int64_t ldc,
               const xpose_sgemm_opts *opts, SgemmPlan &plan) {
   int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM;
-  bool remap = true;
+  bool remap = true, buffers = true;
   int stages = 1;
   if (opts) {
     if (opts->layout < XPOSE_AS_AUTO || opts->layout > XPOSE_AS_SWIZZLE)
@@ -57,13 +60,15 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
     if (opts->bk != 0 && opts->bk != 8 && opts->bk != 16 && opts->bk != 32)
       return XPOSE_EINVAL;
     if (opts->group_m < 0) return XPOSE_EINVAL;
-    if (opts->flags & ~(XPOSE_SGEMM_NO_XCD_REMAP | XPOSE_SGEMM_DOUBLE_BUFFER))
+    if (opts->flags & ~(XPOSE_SGEMM_NO_XCD_REMAP | XPOSE_SGEMM_DOUBLE_BUFFER |
+                        XPOSE_SGEMM_NO_BUFFER_LOADS))
       return XPOSE_EINVAL;
     if (opts->layout) layout = opts->layout;
     if (opts->bk) bk = opts->bk;
     if (opts->group_m) group_m = opts->group_m;
     remap = !(opts->flags & XPOSE_SGEMM_NO_XCD_REMAP);
     if (opts->flags & XPOSE_SGEMM_DOUBLE_BUFFER) stages = 2;
+    if (opts->flags & XPOSE_SGEMM_NO_BUFFER_LOADS) buffers = false;
   }
   if (m < 0 || n < 0 || k < 0) return XPOSE_EINVAL;
   if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) ||
@@ -119,6 +124,9 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   g.tiles_n = (uint32_t)tiles_n;
   g.group_m = (uint32_t)group_m;
   g.xcd_remap = remap ? 1 : 0;
+  // Buffer-load byte offsets within one k step's tiles must fit in 31 bits.
+  g.buf_ok = buffers && vec && uses_ab && lda <= kMaxBufferPitch &&
+             ldb <= kMaxBufferPitch * kTile / 32;
   plan.kernel = kern;
   plan.tiles = tiles;
   return XPOSE_OK;
@@ -175,6 +183,7 @@ int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
   info->group_m = (int32_t)plan.args.group_m;
   info->xcd_remap = plan.args.xcd_remap;
   info->stages = kern.stages;
+  info->buffer_loads = plan.args.buf_ok;
   info->tiles = plan.tiles;
   return rc;
 }

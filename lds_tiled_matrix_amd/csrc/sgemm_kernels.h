@@ -17,6 +17,10 @@ struct SgemmArgs {
   uint32_t tiles_m, tiles_n;
   uint32_t group_m;   // block order: group height in block rows (>= 1)
   int32_t xcd_remap;  // 1: one contiguous range of blocks per XCD
+  // 1: whole tiles are loaded with buffer loads (a descriptor per k step
+  // and 32-bit lane offsets); needs 16-byte tile loads and 128 * lda and
+  // 32 * ldb floats to fit in a 31-bit byte offset
+  int32_t buf_ok;
 };
 
 struct SgemmKernel {

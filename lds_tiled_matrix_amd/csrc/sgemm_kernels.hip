@@ -21,6 +21,10 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Fourth word of a raw buffer descriptor on gfx9-family GPUs: 32-bit data
+// format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
+
 // One 16-byte vector of row `row` (of `nrows`) starting at column `col` (of
 // `ncols`) of a row-major matrix with pitch `ld`: a 16-byte load where the
 // vector is whole and VEC allows it, else 4-byte loads of the elements that
@@ -44,6 +48,15 @@ __device__ inline f32x4 load_vec(const float *base, int64_t row, int64_t col,
 // barrier per step separates the writes of one buffer from the reads of
 // the other.  Either way the next step's global loads are issued before
 // this step's products and land in registers while the matrix cores run.
+// The same pointer in every lane, made visibly uniform so the buffer
+// descriptor built from it lives in scalar registers (without this the
+// compiler may wrap each buffer load in a loop over distinct descriptors).
+__device__ inline float *uniform(const float *p) {
+  return reinterpret_cast<float *>(uniform_bits(
+      reinterpret_cast<uint64_t>(p),
+      [](int x) { return __builtin_amdgcn_readfirstlane(x); }));
+}
+
 template <int BK, int L, bool VEC, int STAGES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     SgemmTile<BK, L>::waves_per_simd(STAGES)))) void
@@ -63,6 +76,32 @@ xpose_sgemm_kernel(SgemmArgs a) {
 
   f32x4 ra[T::A_PASSES], rb[T::B_PASSES];
   auto load = [&](int64_t k0) {
+    if (whole_mn && k0 + BK <= a.k && a.buf_ok) {
+      // Buffer loads: the k step's A and B tiles each get a descriptor
+      // (scalar base and extent), the lanes 32-bit byte offsets, which
+      // saves the 64-bit address arithmetic of global loads.
+      const float *ab = uniform(a.a + m0 * a.lda + k0);
+      const float *bb = uniform(a.b + k0 * a.ldb + n0);
+      const __amdgpu_buffer_rsrc_t ra_d = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float *>(ab), 0,
+          (int)(((T::BM - 1) * a.lda + BK) * 4), kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rb_d = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float *>(bb), 0,
+          (int)(((BK - 1) * a.ldb + T::BN) * 4), kBufferWord3);
+#pragma unroll
+      for (int p = 0; p < T::A_PASSES; ++p)
+        ra[p] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ra_d, (int)((T::a_row(t, p) * a.lda + T::a_col(t)) * 4),
+                       0, 0));
+#pragma unroll
+      for (int p = 0; p < T::B_PASSES; ++p)
+        rb[p] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rb_d, (int)((T::b_row(t, p) * a.ldb + T::b_col(t)) * 4),
+                       0, 0));
+      return;
+    }
     if (whole_mn && k0 + BK <= a.k) {
 #pragma unroll
       for (int p = 0; p < T::A_PASSES; ++p)

@@ -113,6 +113,18 @@ struct SgemmTile {
   }
 };
 
+// A 64-bit value rebuilt from the first lane's copies of its two 32-bit
+// halves; `first_lane` has the signature of the lane-broadcast builtin,
+// int(int).  Both halves are taken back as unsigned: a low half with bit 31
+// set, converted from int straight to 64 bits, would sign-extend over the
+// high half and turn an address into 0xffffffff'xxxxxxxx.
+template <class F>
+SGEMM_HD inline uint64_t uniform_bits(uint64_t v, F first_lane) {
+  const uint32_t lo = (uint32_t)first_lane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)first_lane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Block order: workgroup `block` of `tiles_m * tiles_n` -> block row and
 // column of C, a bijection whenever group_m >= 1.
 //   xcd_remap: the hardware hands consecutive workgroups to the 8 XCDs in

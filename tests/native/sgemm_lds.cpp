@@ -114,7 +114,20 @@ static void block_order(uint32_t tm, uint32_t tn, uint32_t g, int remap) {
   check(what, ok);
 }
 
+// uniform_bits with an identity broadcast of the builtin's int(int) shape
+// must give back every address, low halves with bit 31 set included.
+static void uniform_addresses() {
+  const uint64_t vals[] = {0x00007f12c0001000ull, 0x00007f1240001000ull,
+                           0x0000000080000000ull, 0x00007fffffffffffull,
+                           0xffffffff00000000ull, 0x0000000000000010ull};
+  bool ok = true;
+  for (uint64_t v : vals)
+    ok &= uniform_bits(v, [](int x) { return x; }) == v;
+  check("uniform_bits/identity", ok);
+}
+
 int main() {
+  uniform_addresses();
   kernel<8, kAsUnpadded>(); kernel<8, kAsPadded>(); kernel<8, kAsSwizzle>();
   kernel<16, kAsUnpadded>(); kernel<16, kAsPadded>(); kernel<16, kAsSwizzle>();
   kernel<32, kAsUnpadded>(); kernel<32, kAsPadded>(); kernel<32, kAsSwizzle>();

@@ -54,7 +54,7 @@ def test_struct_layouts_match_ctypes(c_output):
 
 def test_constants_match_binding(c_output):
     consts = dict(_entries(c_output, "const"))
-    assert len(consts) == 19
+    assert len(consts) == 20
     for name, value in consts.items():
         short = name.replace("XPOSE_FLAG_", "FLAG_").replace("XPOSE_AS_", "AS_")
         short = short.replace("XPOSE_SGEMM_", "SGEMM_")

@@ -25,6 +25,7 @@ def test_default_plan():
     assert info.tiles == 32 * 32 and info.vector_loads == 1
     assert info.lds_bytes == 4 * (16 * 130 + 16 * 128)
     assert info.group_m == 8 and info.xcd_remap == 1 and info.stages == 1
+    assert info.buffer_loads == 1
     rc, info = plan(opts=X.make_sgemm_opts(flags=X.SGEMM_DOUBLE_BUFFER))
     assert rc == 0 and info.stages == 2
     assert info.lds_bytes == 2 * 4 * (16 * 130 + 16 * 128)
@@ -59,6 +60,26 @@ def test_vector_load_rules():
     assert plan(c=C + 4, ldc=4099)[1].vector_loads == 1  # C is never vector-loaded
 
 
+def test_buffer_load_rules():
+    """Whole tiles are read with buffer loads where 128 rows of A and 32 of B
+    fit in 31-bit byte offsets, 16-byte loads are allowed and no flag turns
+    them off."""
+    assert plan()[1].buffer_loads == 1
+    assert plan(a=A + 4)[1].buffer_loads == 0            # 4-byte loads
+    big = (1 << 31) // (4 * 129)                        # 4161790
+    rc, info = plan(lda=big - 2, m=256)
+    assert rc == 0 and info.buffer_loads == 1
+    rc, info = plan(lda=big + 2, m=256)
+    assert rc == 0 and info.vector_loads == 1 and info.buffer_loads == 0
+    rc, info = plan(ldb=big * 4, k=32)
+    assert rc == 0 and info.buffer_loads == 1
+    rc, info = plan(ldb=big * 4 + 4, k=32)
+    assert rc == 0 and info.vector_loads == 1 and info.buffer_loads == 0
+    rc, info = plan(opts=X.make_sgemm_opts(flags=X.SGEMM_NO_BUFFER_LOADS))
+    assert rc == 0 and info.buffer_loads == 0 and info.vector_loads == 1
+    assert plan(k=0, a=0, b=0, lda=1)[1].buffer_loads == 0
+
+
 @pytest.mark.parametrize("kw, code", [
     (dict(m=-1), X.XPOSE_EINVAL),
     (dict(k=-1), X.XPOSE_EINVAL),
@@ -76,7 +97,7 @@ def test_vector_load_rules():
     (dict(opts=X.make_sgemm_opts(layout=4)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(bk=12)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(group_m=-1)), X.XPOSE_EINVAL),
-    (dict(opts=X.make_sgemm_opts(flags=4)), X.XPOSE_EINVAL),
+    (dict(opts=X.make_sgemm_opts(flags=8)), X.XPOSE_EINVAL),
 ])
 def test_invalid_calls(kw, code):
     assert plan(**kw)[0] == code

@@ -128,12 +128,15 @@ EXACT_SHAPES = [(128, 128, 16), (256, 384, 512), (130, 67, 45), (1, 1, 1),
                 (300, 257, 33), (64, 200, 7), (129, 1, 300)]
 
 
-@pytest.mark.parametrize("stages", (2, 1))
+FLAG_SETS = {"default": 0, "two_buffers": X.SGEMM_DOUBLE_BUFFER,
+             "global_loads": X.SGEMM_NO_BUFFER_LOADS}
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
 @pytest.mark.parametrize("bk", BKS)
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
-def test_exact_on_integer_inputs(layout, bk, stages):
-    opts = X.make_sgemm_opts(layout, bk,
-                             flags=X.SGEMM_DOUBLE_BUFFER if stages == 2 else 0)
+def test_exact_on_integer_inputs(layout, bk, flags):
+    opts = X.make_sgemm_opts(layout, bk, flags=FLAG_SETS[flags])
     for idx, (m, n, k) in enumerate(EXACT_SHAPES):
         A = wl.small_int_f32((m, k), 100 + idx)
         B = wl.small_int_f32((k, n), 200 + idx)
@@ -178,7 +181,7 @@ def test_all_kernels_agree_bit_for_bit():
     ref = None
     for layout in LAYOUTS:
         for bk in BKS:
-            for flags in (0, X.SGEMM_DOUBLE_BUFFER):
+            for flags in FLAG_SETS.values():
                 for shifts in ((0, 0, 0), (1, 1, 0)):
                     got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
                                          opts=X.make_sgemm_opts(layout, bk, 0, flags))
