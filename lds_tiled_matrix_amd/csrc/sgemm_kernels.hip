@@ -102,17 +102,8 @@ xpose_sgemm_kernel(SgemmArgs a) {
                        0, 0));
       return;
     }
-    if (whole_mn && k0 + BK <= a.k) {
-#pragma unroll
-      for (int p = 0; p < T::A_PASSES; ++p)
-        ra[p] = *reinterpret_cast<const f32x4 *>(
-            a.a + (m0 + T::a_row(t, p)) * a.lda + k0 + T::a_col(t));
-#pragma unroll
-      for (int p = 0; p < T::B_PASSES; ++p)
-        rb[p] = *reinterpret_cast<const f32x4 *>(
-            a.b + (k0 + T::b_row(t, p)) * a.ldb + n0 + T::b_col(t));
-      return;
-    }
+    // Edge tiles, and whole tiles where buffer loads are off: every 16-byte
+    // vector checked against the matrix.
 #pragma unroll
     for (int p = 0; p < T::A_PASSES; ++p)
       ra[p] = load_vec<VEC>(a.a, m0 + T::a_row(t, p), k0 + T::a_col(t), a.m,
