@@ -93,12 +93,12 @@ enum {
                                    the block).  Measured no faster on gfx950,
                                    where three or four other workgroups per
                                    compute unit fill the barrier stalls      */
-  XPOSE_SGEMM_NO_BUFFER_LOADS = 4 /* load whole tiles with 64-bit-address
-                                   global loads instead of buffer loads (a
-                                   descriptor per k step, 32-bit lane
-                                   offsets), the default where the pitches
-                                   allow it (lda <= 4161790 and
-                                   ldb <= 16647160)                          */
+  XPOSE_SGEMM_NO_BUFFER_LOADS = 4 /* load whole tiles like edge tiles, with
+                                   bounds-checked 16-byte global loads,
+                                   instead of buffer loads (a descriptor per
+                                   k step, 32-bit lane offsets), which are
+                                   the default where the pitches allow them
+                                   (lda <= 4161790 and ldb <= 16647160)      */
 };
 
 /* Optional knobs (zero-initialise for defaults).  Every choice gives the
