@@ -97,10 +97,17 @@ def region_mask(m, n, ldc, size):
 
 
 def check_exact(A, B, C, alpha, beta, **kw):
+    """Exact equality in the m x n region (an exact zero sum may come out as
+    +0 or -0 depending on the order of the terms, so zeros compare by value),
+    bit equality everywhere else (pitch padding and guards untouched)."""
     got, c_full, bufs = run_case(A, B, C, alpha, beta, **kw)
     exp = expected(A, B, C, alpha, beta, c_full, bufs)
-    bad = np.flatnonzero(got.view(np.uint32) != exp.view(np.uint32))
+    m, n = A.shape[0], B.shape[1]
+    mask = region_mask(m, n, bufs[4], got.size)
+    bad = np.flatnonzero(mask & (got != exp))
     assert bad.size == 0, (bad[:8], got[bad[:8]], exp[bad[:8]])
+    outside = np.flatnonzero(~mask & (got.view(np.uint32) != exp.view(np.uint32)))
+    assert outside.size == 0, outside[:8]
     return got
 
 
@@ -251,3 +258,27 @@ def test_page_size_default_launch_sampled():
     sums = og.sgemm(w.m, 1, w.k, 1.0, Ai.reshape(-1), w.k,
                     np.ones(w.k, np.float32), 1, 0.0, np.zeros(w.m, np.float32), 1)
     assert np.array_equal(got, np.broadcast_to(sums.astype(np.float32), got.shape))
+
+
+def test_random_campaign():
+    """Seeded random cases over shapes (ragged, thin, empty k), pitches,
+    pointer offsets, scalars and every option; integer inputs keep the
+    result exact, so each case is compared bit for bit."""
+    rng = np.random.default_rng(2024)
+    dims = [1, 2, 3, 5, 17, 31, 64, 127, 128, 129, 200, 255, 256, 300, 513]
+    for case in range(60):
+        m, n = int(rng.choice(dims)), int(rng.choice(dims))
+        k = int(rng.choice(dims + [0, 0]))
+        pads = tuple(int(x) for x in rng.choice([0, 0, 1, 3, 4, 8], 3))
+        shifts = tuple(int(x) for x in rng.choice([0, 0, 0, 1, 2, 3], 3))
+        alpha = float(rng.choice([1.0, 2.0, -1.0, 0.5, 0.0]))
+        beta = float(rng.choice([0.0, 1.0, -2.0, 0.25]))
+        flags = int(rng.choice([0, 0, X.SGEMM_DOUBLE_BUFFER, X.SGEMM_NO_BUFFER_LOADS,
+                                X.SGEMM_NO_XCD_REMAP]))
+        opts = X.make_sgemm_opts(int(rng.choice(LAYOUTS)), int(rng.choice(BKS)),
+                                 int(rng.choice([0, 1, 3, 8])), flags)
+        A = wl.small_int_f32((m, k), 10_000 + case)
+        B = wl.small_int_f32((k, n), 20_000 + case)
+        C = wl.small_int_f32((m, n), 30_000 + case)
+        say(f"campaign case {case}")
+        check_exact(A, B, C, alpha, beta, pads=pads, shifts=shifts, opts=opts)
