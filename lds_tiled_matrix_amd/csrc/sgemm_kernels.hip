@@ -42,12 +42,6 @@ __device__ inline f32x4 load_vec(const float *base, int64_t row, int64_t col,
   return v;
 }
 
-// STAGES = 1 is the pages' loop: stage the step's tiles, barrier, products,
-// barrier.  STAGES = 2 keeps two LDS buffers: the next step's tiles are
-// staged into the other buffer right after this step's products, so one
-// barrier per step separates the writes of one buffer from the reads of
-// the other.  Either way the next step's global loads are issued before
-// this step's products and land in registers while the matrix cores run.
 // The same pointer in every lane, made visibly uniform so the buffer
 // descriptor built from it lives in scalar registers (without this the
 // compiler may wrap each buffer load in a loop over distinct descriptors).
@@ -57,6 +51,12 @@ __device__ inline float *uniform(const float *p) {
       [](int x) { return __builtin_amdgcn_readfirstlane(x); }));
 }
 
+// STAGES = 1 is the pages' loop: stage the step's tiles, barrier, products,
+// barrier.  STAGES = 2 keeps two LDS buffers: the next step's tiles are
+// staged into the other buffer right after this step's products, so one
+// barrier per step separates the writes of one buffer from the reads of
+// the other.  Either way the next step's global loads are issued before
+// this step's products and land in registers while the matrix cores run.
 template <int BK, int L, bool VEC, int STAGES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     SgemmTile<BK, L>::waves_per_simd(STAGES)))) void
@@ -70,8 +70,8 @@ xpose_sgemm_kernel(SgemmArgs a) {
   sgemm_block(blockIdx.x, a.tiles_m, a.tiles_n, a.group_m, a.xcd_remap, bm,
               bn);
   const int64_t m0 = (int64_t)bm * T::BM, n0 = (int64_t)bn * T::BN;
-  // Blocks wholly inside C take unconditional 16-byte loads for every k
-  // step but a ragged last one.
+  // Blocks wholly inside C read every k step but a ragged last one as whole
+  // tiles, without per-vector checks.
   const bool whole_mn = VEC && m0 + T::BM <= a.m && n0 + T::BN <= a.n;
 
   f32x4 ra[T::A_PASSES], rb[T::B_PASSES];
