@@ -71,14 +71,18 @@ extern "C" {
 typedef enum xpose_as_layout {
   XPOSE_AS_AUTO = 0,     /* library default                                   */
   XPOSE_AS_UNPADDED = 1, /* row stride 128 floats, a multiple of the bank
-                            count: the store is (bk / 4)-way conflicted on
-                            gfx950's 32-bank, 32-lane 4-byte LDS accesses     */
-  XPOSE_AS_PADDED = 2,   /* row stride 128 + 32 / bk floats: the smallest pad
-                            that spreads one half-wave's stores over all 32
-                            banks (the pages' (32 / BK) % 8 for the built bk) */
+                            count: the store is (min(bk, 32) / 4)-way
+                            conflicted on gfx950's 32-bank, 32-lane 4-byte
+                            LDS accesses                                      */
+  XPOSE_AS_PADDED = 2,   /* row stride 128 + 32 / min(bk, 32) floats: the
+                            smallest pad that spreads one half-wave's stores
+                            over all 32 banks (the pages' (32 / BK) % 8 for
+                            bk = 8, 16, 32; A's tile is read in strips of at
+                            most 32 columns)                                 */
   XPOSE_AS_SWIZZLE = 3   /* row stride 128, the row index of each element
-                            XOR-permuted by a multiple of 128 / bk chosen
-                            from its k: conflict-free without padding        */
+                            XOR-permuted by a multiple of 128 / min(bk, 32)
+                            chosen from its k: conflict-free without
+                            padding                                          */
 } xpose_as_layout;
 
 /* Option flags of xpose_sgemm_ex. */
@@ -98,7 +102,7 @@ enum {
                                    instead of buffer loads (a descriptor per
                                    k step, 32-bit lane offsets), which are
                                    the default where the pitches allow them
-                                   (lda <= 4161790 and ldb <= 16647160)      */
+                                   (lda <= 4161790 and ldb <= 8323580)       */
 };
 
 /* Optional knobs (zero-initialise for defaults).  Every choice gives the
@@ -106,7 +110,7 @@ enum {
  * grouping of the sum). */
 typedef struct xpose_sgemm_opts {
   int32_t layout;  /* xpose_as_layout                                         */
-  int32_t bk;      /* k step per LDS stage: 0 = default (16), 8, 16 or 32     */
+  int32_t bk;      /* k step per LDS stage: 0 = default (16), 8, 16, 32 or 64 */
   int32_t group_m; /* block order: groups of group_m block rows, walked
                       block-column by block-column; 0 = default (8)          */
   int32_t flags;   /* XPOSE_SGEMM_*                                           */

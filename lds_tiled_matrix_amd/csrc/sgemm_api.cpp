@@ -16,7 +16,7 @@ constexpr int kDefaultBk = 16;
 constexpr int kDefaultLayout = XPOSE_AS_PADDED;
 constexpr int kDefaultGroupM = 8;
 // Largest lda for buffer loads: 128 rows of the A tile (plus the k step)
-// within a 31-bit byte offset; ldb may be 4x larger (at most 32 rows of B).
+// within a 31-bit byte offset; ldb may be 2x larger (at most 64 rows of B).
 constexpr int64_t kMaxBufferPitch = ((int64_t)1 << 31) / (4 * (kTile + 1));
 
 struct SgemmPlan {
@@ -57,7 +57,8 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   if (opts) {
     if (opts->layout < XPOSE_AS_AUTO || opts->layout > XPOSE_AS_SWIZZLE)
       return XPOSE_EINVAL;
-    if (opts->bk != 0 && opts->bk != 8 && opts->bk != 16 && opts->bk != 32)
+    if (opts->bk != 0 && opts->bk != 8 && opts->bk != 16 && opts->bk != 32 &&
+        opts->bk != 64)
       return XPOSE_EINVAL;
     if (opts->group_m < 0) return XPOSE_EINVAL;
     if (opts->flags & ~(XPOSE_SGEMM_NO_XCD_REMAP | XPOSE_SGEMM_DOUBLE_BUFFER |
@@ -126,7 +127,7 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   g.xcd_remap = remap ? 1 : 0;
   // Buffer-load byte offsets within one k step's tiles must fit in 31 bits.
   g.buf_ok = buffers && vec && uses_ab && lda <= kMaxBufferPitch &&
-             ldb <= kMaxBufferPitch * kTile / 32;
+             ldb <= kMaxBufferPitch * kTile / 64;
   plan.kernel = kern;
   plan.tiles = tiles;
   return XPOSE_OK;

@@ -92,7 +92,7 @@ xpose_sgemm_kernel(SgemmArgs a) {
       for (int p = 0; p < T::A_PASSES; ++p)
         ra[p] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       ra_d, (int)((T::a_row(t, p) * a.lda + T::a_col(t)) * 4),
+                       ra_d, (int)((T::a_row(t, p) * a.lda + T::a_col(t, p)) * 4),
                        0, 0));
 #pragma unroll
       for (int p = 0; p < T::B_PASSES; ++p)
@@ -106,7 +106,7 @@ xpose_sgemm_kernel(SgemmArgs a) {
     // vector checked against the matrix.
 #pragma unroll
     for (int p = 0; p < T::A_PASSES; ++p)
-      ra[p] = load_vec<VEC>(a.a, m0 + T::a_row(t, p), k0 + T::a_col(t), a.m,
+      ra[p] = load_vec<VEC>(a.a, m0 + T::a_row(t, p), k0 + T::a_col(t, p), a.m,
                             a.k, a.lda);
 #pragma unroll
     for (int p = 0; p < T::B_PASSES; ++p)
@@ -120,7 +120,7 @@ xpose_sgemm_kernel(SgemmArgs a) {
     float *bs = Bs + buf * T::BS_FLOATS;
 #pragma unroll
     for (int p = 0; p < T::A_PASSES; ++p) {
-      const int i = T::a_row(t, p), l = T::a_col(t);
+      const int i = T::a_row(t, p), l = T::a_col(t, p);
 #pragma unroll
       for (int e = 0; e < 4; ++e) as[T::as_index(l + e, i)] = ra[p][e];
     }
@@ -221,8 +221,9 @@ hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
       XPOSE_SGEMM_L(BK, kAsSwizzle, ST)
 
 const SgemmKernel kSgemmKernels[] = {
-    XPOSE_SGEMM_BK(8, 1),  XPOSE_SGEMM_BK(16, 1), XPOSE_SGEMM_BK(32, 1),
-    XPOSE_SGEMM_BK(8, 2),  XPOSE_SGEMM_BK(16, 2), XPOSE_SGEMM_BK(32, 2)};
+    XPOSE_SGEMM_BK(8, 1), XPOSE_SGEMM_BK(16, 1), XPOSE_SGEMM_BK(32, 1),
+    XPOSE_SGEMM_BK(64, 1), XPOSE_SGEMM_BK(8, 2), XPOSE_SGEMM_BK(16, 2),
+    XPOSE_SGEMM_BK(32, 2), XPOSE_SGEMM_BK(64, 2)};
 
 }  // namespace
 

@@ -36,24 +36,29 @@ struct SgemmTile {
   static constexpr int BM = 128, BN = 128, NT = 256;
   static constexpr int WM = 64, WN = 64;  // C block of one wave
 
-  // A's 128 x BK tile: each lane reads one 16-byte vector (4 consecutive l)
-  // of one row i, LPR lanes per row.
-  static constexpr int LPR = BK / 4;
+  // A's 128 x BK tile is read in strips of LK = min(BK, 32) columns: each
+  // lane reads one 16-byte vector (4 consecutive l) of one row i of a
+  // strip, LPR lanes per strip row.
+  static constexpr int LK = BK < 32 ? BK : 32;
+  static constexpr int LPR = LK / 4;
   static constexpr int A_ROWS_PER_PASS = NT / LPR;
-  static constexpr int A_PASSES = BM / A_ROWS_PER_PASS;  // vectors per lane
+  static constexpr int A_ROW_PASSES = BM / A_ROWS_PER_PASS;
+  static constexpr int A_PASSES = A_ROW_PASSES * (BK / LK);  // vectors per lane
   // B's BK x 128 tile: 32 lanes per row of 128 floats.
   static constexpr int B_LPR = BN / 4;
   static constexpr int B_ROWS_PER_PASS = NT / B_LPR;
   static constexpr int B_PASSES = BK / B_ROWS_PER_PASS;
 
   // The transposed store of element e of a lane's vector writes
-  // As[4c + e][i] for the lane's chunk c < LPR and row i.  One half-wave
-  // (the 32 lanes one pass serves) holds HG = 32 / LPR consecutive rows i
-  // (starting at a multiple of HG) times LPR chunks.  With row stride
-  // 128 + p the lane lands on bank (4 c p + e p + i) mod 32, so
+  // As[s LK + 4c + e][i] for the strip s, the lane's chunk c < LPR and row i.
+  // One half-wave (the 32 lanes one pass serves) holds HG = 32 / LPR
+  // consecutive rows i (starting at a multiple of HG) times LPR chunks of
+  // one strip.  With row stride 128 + p the lane lands on bank
+  // (s LK p + 4 c p + e p + i) mod 32, the first term the same for the whole
+  // half-wave, so
   //   p = 0:      the bank is i mod 32 alone: LPR lanes per bank, LPR-way;
   //   4 p = HG:   the chunks fall HG banks apart, covering all 32 once;
-  // hence the padded stride 128 + HG / 4 = 128 + 32 / BK.
+  // hence the padded stride 128 + HG / 4 = 128 + 32 / LK.
   static constexpr int HG = 32 / LPR;
   static constexpr int PAD = L == kAsPadded ? HG / 4 : 0;
   static constexpr int AS_STRIDE = BM + PAD;
@@ -73,15 +78,16 @@ struct SgemmTile {
                : (BK <= 16 ? 4 : 3);
   }
 
-  static_assert(BK == 8 || BK == 16 || BK == 32, "built k steps");
-  static_assert(A_PASSES * A_ROWS_PER_PASS == BM, "whole A tile");
+  static_assert(BK == 8 || BK == 16 || BK == 32 || BK == 64, "built k steps");
+  static_assert(A_ROW_PASSES * A_ROWS_PER_PASS == BM, "whole A tile");
   static_assert(B_PASSES * B_ROWS_PER_PASS == BK, "whole B tile");
   static_assert(L != kAsPadded || 4 * PAD == HG, "pad spreads the chunks");
 
   // Swizzle: row l of As keeps stride 128 and holds element i at column
-  // i ^ x(l), x(l) = ((l / 4) mod LPR) * HG.  In one half-wave's store l / 4
-  // is the chunk c and i runs over HG consecutive rows from a multiple of
-  // HG, so the banks (i ^ c HG) mod 32 are all distinct; x(l) < 32 only
+  // i ^ x(l), x(l) = ((l / 4) mod LPR) * HG.  In one half-wave's store
+  // (l / 4) mod LPR is the chunk c and i runs over HG consecutive rows from
+  // a multiple of HG, so the banks (i ^ c HG) mod 32 are all distinct;
+  // x(l) < 32 only
   // permutes i inside its aligned group of 32, so the product's reads of 32
   // consecutive i stay one full row of banks.
   SGEMM_HD static constexpr int swz(int l) {
@@ -92,11 +98,14 @@ struct SgemmTile {
   }
   SGEMM_HD static constexpr int bs_index(int l, int j) { return l * BN + j; }
 
-  // Loader lane maps: thread t, pass p.
+  // Loader lane maps: thread t, pass p (A: row passes within a strip, then
+  // strips).
   SGEMM_HD static constexpr int a_row(int t, int p) {
-    return p * A_ROWS_PER_PASS + t / LPR;
+    return (p % A_ROW_PASSES) * A_ROWS_PER_PASS + t / LPR;
   }
-  SGEMM_HD static constexpr int a_col(int t) { return 4 * (t % LPR); }
+  SGEMM_HD static constexpr int a_col(int t, int p) {
+    return (p / A_ROW_PASSES) * LK + 4 * (t % LPR);
+  }
   SGEMM_HD static constexpr int b_row(int t, int p) {
     return p * B_ROWS_PER_PASS + t / B_LPR;
   }

@@ -44,7 +44,7 @@ static void kernel() {
       for (int e = 0; e < 4; ++e) {
         for (int q = 0; q < 64; ++q) {
           const int t = 64 * w + q;
-          const int idx = T::as_index(T::a_col(t) + e, T::a_row(t, p));
+          const int idx = T::as_index(T::a_col(t, p) + e, T::a_row(t, p));
           in_bounds &= idx >= 0 && idx < T::AS_FLOATS;
           if (idx >= 0 && idx < T::AS_FLOATS) ++hits[idx];
           a[q] = 4 * idx;
@@ -131,6 +131,7 @@ int main() {
   kernel<8, kAsUnpadded>(); kernel<8, kAsPadded>(); kernel<8, kAsSwizzle>();
   kernel<16, kAsUnpadded>(); kernel<16, kAsPadded>(); kernel<16, kAsSwizzle>();
   kernel<32, kAsUnpadded>(); kernel<32, kAsPadded>(); kernel<32, kAsSwizzle>();
+  kernel<64, kAsUnpadded>(); kernel<64, kAsPadded>(); kernel<64, kAsSwizzle>();
   const uint32_t dims[] = {1, 2, 3, 7, 8, 9, 32, 33};
   for (uint32_t tm : dims)
     for (uint32_t tn : dims)

@@ -31,11 +31,11 @@ def test_default_plan():
     assert info.lds_bytes == 2 * 4 * (16 * 130 + 16 * 128)
 
 
-@pytest.mark.parametrize("bk", (8, 16, 32))
+@pytest.mark.parametrize("bk", (8, 16, 32, 64))
 def test_layout_strides(bk):
-    """Padded stride 128 + 32 / bk: the pad that spreads one half-wave's
-    transposed stores over the 32 banks; the others keep 128."""
-    for layout, stride in ((X.AS_UNPADDED, 128), (X.AS_PADDED, 128 + 32 // bk),
+    """Padded stride 128 + 32 / min(bk, 32): the pad that spreads one
+    half-wave's transposed stores over the 32 banks; the others keep 128."""
+    for layout, stride in ((X.AS_UNPADDED, 128), (X.AS_PADDED, 128 + 32 // min(bk, 32)),
                            (X.AS_SWIZZLE, 128)):
         rc, info = plan(opts=X.make_sgemm_opts(layout, bk))
         assert rc == 0 and info.as_stride == stride and info.bk == bk
@@ -71,9 +71,9 @@ def test_buffer_load_rules():
     assert rc == 0 and info.buffer_loads == 1
     rc, info = plan(lda=big + 2, m=256)
     assert rc == 0 and info.vector_loads == 1 and info.buffer_loads == 0
-    rc, info = plan(ldb=big * 4, k=32)
+    rc, info = plan(ldb=big * 2, k=32)
     assert rc == 0 and info.buffer_loads == 1
-    rc, info = plan(ldb=big * 4 + 4, k=32)
+    rc, info = plan(ldb=big * 2 + 4, k=32)
     assert rc == 0 and info.vector_loads == 1 and info.buffer_loads == 0
     rc, info = plan(opts=X.make_sgemm_opts(flags=X.SGEMM_NO_BUFFER_LOADS))
     assert rc == 0 and info.buffer_loads == 0 and info.vector_loads == 1
@@ -96,6 +96,7 @@ def test_buffer_load_rules():
     (dict(lda=1 << 62), X.XPOSE_EINVAL),               # extent overflows
     (dict(opts=X.make_sgemm_opts(layout=4)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(bk=12)), X.XPOSE_EINVAL),
+    (dict(opts=X.make_sgemm_opts(bk=128)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(group_m=-1)), X.XPOSE_EINVAL),
     (dict(opts=X.make_sgemm_opts(flags=8)), X.XPOSE_EINVAL),
 ])

@@ -24,7 +24,7 @@ X = pytest.importorskip("lds_tiled_matrix_amd")
 GUARD = 64
 SENTINEL = np.float32(-12345.5)
 LAYOUTS = (X.AS_UNPADDED, X.AS_PADDED, X.AS_SWIZZLE)
-BKS = (8, 16, 32)
+BKS = (8, 16, 32, 64)
 
 
 def _dev():
