@@ -50,7 +50,10 @@ int elem_bytes_of(int32_t dtype) {
 //     line), the default for 2-, 4- and 8-byte elements whose output rows
 //     are not line-aligned: every store is a whole line again, so
 //     non-temporal stores win.  (1-byte elements: no gain measured, none
-//     built.)  Explicit knobs they are not built with (another layout,
+//     built.  2-byte elements in matrices of fewer than kShortAlignRows
+//     rows: the extra halo tile row costs more than whole lines gain, e.g.
+//     a batch of 150 x 150 fp16 runs 2.3 TB/s line-aligned, 3.6 without.)
+//     Explicit knobs they are not built with (another layout,
 //     elementwise or direct loads, persistent workgroups, a tile shape,
 //     workgroup size or cache policy without such a kernel) select the
 //     ordinary tiles with their own defaults instead.
@@ -67,6 +70,7 @@ struct Default {
   bool align_out = false;
 };
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
+constexpr int64_t kShortAlignRows = 256;
 constexpr int64_t kBigCallBytes = 512ll << 20;
 constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
               kDiag = XPOSE_ORDER_DIAGONAL, kWB = XPOSE_CACHE_DEFAULT,
@@ -317,8 +321,9 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                                  XPOSE_FLAG_TR_READ)) ||
                  (opts->layout && opts->layout != XPOSE_LAYOUT_SWIZZLE) ||
                  opts->persistent));
+  const bool short_rows = s == 2 && rows < kShortAlignRows;
   Default d = default_for(s, out_row128, small, big,
-                          want_align || (align_ok && !out_row128));
+                          want_align || (align_ok && !out_row128 && !short_rows));
   const int layout = (opts && opts->layout) ? opts->layout : d.layout;
   plan->elem_bytes = s;
   if (layout == XPOSE_LAYOUT_NAIVE_READ || layout == XPOSE_LAYOUT_NAIVE_WRITE) {

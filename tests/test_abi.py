@@ -282,6 +282,15 @@ def test_align_out_option():
     assert rc == 0 and info.aligned_out == 0 and info.cache == X.CACHE_NT_ALL
     # ... but not when aligned-out tiles were asked for
     assert plan(rows=1000, cols=512, opts=X.make_opts(tile=(32, 32), flags=X.FLAG_ALIGN_OUT))[0] == X.XPOSE_ENOTILE
+    # 2-byte elements: by default only from 256 rows on (a short matrix pays
+    # more for the halo tile row than whole lines gain); on request always
+    kw = dict(dtype=X.XPOSE_F16, batch=40, cols=600, stride_in=600 * 1000,
+              stride_out=600 * 1000)
+    assert plan(rows=255, ld_out=255, **kw)[1].aligned_out == 0
+    assert plan(rows=256, ld_out=257, **kw)[1].aligned_out == 1
+    assert plan(rows=150, ld_out=150, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT), **kw)[1].aligned_out == 1
+    assert plan(rows=150, ld_out=150, dtype=X.XPOSE_F32, batch=40, cols=600,
+                stride_in=600 * 150, stride_out=600 * 150)[1].aligned_out == 1
     # asked for on line-aligned rows: the aligned-out default tile
     rc, info = plan(rows=8192, cols=8192, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))
     assert rc == 0 and info.aligned_out == 1 and info.tiles == -(-(8192 + 31) // info.tile_rows) * (8192 // info.tile_cols)
