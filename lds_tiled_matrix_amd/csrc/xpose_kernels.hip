@@ -277,6 +277,14 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
       const char *rs = src + ((int64_t)row * ld_in + ch * T::V) * S;
       if (VEC && row < rows_left && (ch + 1) * T::V <= cols_left) {
         v[k] = load16<T::CACHE>(rs);
+      } else if (VEC && S <= 2) {
+        // 1- and 2-byte elements: the chunk's elements inside the matrix
+        // in at most four pieces instead of up to 16 element loads.
+        const int64_t have = row < rows_left ? cols_left - ch * T::V : 0;
+        uint64_t lo, hi;
+        load_head(rs, have > 0 ? (int)(have * S) : 0, lo, hi);
+        v[k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                     (uint32_t)(hi >> 32)};
       } else {
         E e[T::V];
 #pragma unroll
@@ -301,6 +309,11 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
       char *d = dst + ((int64_t)c * ld_out + q * T::V) * S;
       if (VEC && (q + 1) * T::V <= rows_left) {
         store16<T::CACHE>(d, o);
+      } else if (VEC && S <= 2) {
+        const int64_t have = rows_left - q * T::V;
+        store_head(d, have > 0 ? (int)(have * S) : 0,
+                   (uint64_t)o.x | ((uint64_t)o.y << 32),
+                   (uint64_t)o.z | ((uint64_t)o.w << 32));
       } else {
         E e[T::V];
         __builtin_memcpy(e, &o, 16);

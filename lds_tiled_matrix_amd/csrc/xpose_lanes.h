@@ -14,6 +14,61 @@
 
 namespace xpose {
 
+// Partial 16-byte vectors at a matrix edge: the first n bytes (0 <= n < 16)
+// of a vector move with at most four accesses of 8, 4, 2 and 1 bytes,
+// largest first, so each piece sits at a multiple of its own size and none
+// straddles the vector's two 8-byte halves (lo = bytes 0-7, hi = 8-15).
+// Bytes past n are neither read nor written; loaded ones come back zero.
+// Addresses need no alignment (gfx950 serves unaligned global accesses).
+typedef uint64_t u64_any __attribute__((aligned(1)));
+typedef uint32_t u32_any __attribute__((aligned(1)));
+typedef uint16_t u16_any __attribute__((aligned(1)));
+
+XPOSE_HD inline void put_piece(uint64_t &lo, uint64_t &hi, int off,
+                               uint64_t v) {
+  if (off >= 8) hi |= v << (8 * (off - 8));
+  else lo |= v << (8 * off);
+}
+XPOSE_HD inline uint64_t get_piece(uint64_t lo, uint64_t hi, int off) {
+  return off >= 8 ? hi >> (8 * (off - 8)) : lo >> (8 * off);
+}
+
+XPOSE_HD inline void load_head(const char *p, int n, uint64_t &lo,
+                               uint64_t &hi) {
+  lo = hi = 0;
+  int off = 0;
+  if (n & 8) {
+    lo = *reinterpret_cast<const u64_any *>(p);
+    off = 8;
+  }
+  if (n & 4) {
+    put_piece(lo, hi, off, *reinterpret_cast<const u32_any *>(p + off));
+    off += 4;
+  }
+  if (n & 2) {
+    put_piece(lo, hi, off, *reinterpret_cast<const u16_any *>(p + off));
+    off += 2;
+  }
+  if (n & 1) put_piece(lo, hi, off, (uint8_t)p[off]);
+}
+
+XPOSE_HD inline void store_head(char *p, int n, uint64_t lo, uint64_t hi) {
+  int off = 0;
+  if (n & 8) {
+    *reinterpret_cast<u64_any *>(p) = lo;
+    off = 8;
+  }
+  if (n & 4) {
+    *reinterpret_cast<u32_any *>(p + off) = (uint32_t)get_piece(lo, hi, off);
+    off += 4;
+  }
+  if (n & 2) {
+    *reinterpret_cast<u16_any *>(p + off) = (uint16_t)get_piece(lo, hi, off);
+    off += 2;
+  }
+  if (n & 1) p[off] = (char)get_piece(lo, hi, off);
+}
+
 // Cache policy of the global accesses: plain, non-temporal stores, or
 // non-temporal loads and stores (the data is touched exactly once).
 enum CachePolicy : int { kCacheDefault = 0, kNtStore = 1, kNtLoadStore = 2 };
