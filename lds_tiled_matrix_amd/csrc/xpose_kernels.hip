@@ -523,13 +523,6 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
         v[k] = u32x4{0, 0, 0, 0};
       } else if ((ch + 1) * T::V <= cols_left) {
         v[k] = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src);
-      } else if (S <= 4) {
-        // the chunk's elements inside the matrix, in at most four pieces
-        const int64_t have = cols_left - ch * T::V;
-        uint64_t lo, hi;
-        load_head(src, have > 0 ? (int)(have * S) : 0, lo, hi);
-        v[k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
-                     (uint32_t)(hi >> 32)};
       } else {
         E e[T::V];
 #pragma unroll
@@ -559,14 +552,6 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
       const u32x4 o = shift_gather<T>(lds, T::HALO - d + T::V * q, c);
       if (first >= 0 && first + T::V - 1 < a.rows) {
         store16<CP>(row_out + first * S, o);
-      } else if (S <= 4) {
-        // elements first + x inside [0, rows): bytes [x0 S, x1 S) of o
-        const int64_t x0 = first < 0 ? -first : 0;
-        const int64_t x1 = a.rows - first < T::V ? a.rows - first : T::V;
-        if (x0 < x1)
-          store_range(row_out + first * S, (int)(x0 * S), (int)(x1 * S),
-                      (uint64_t)o.x | ((uint64_t)o.y << 32),
-                      (uint64_t)o.z | ((uint64_t)o.w << 32));
       } else {
         E e[T::V];
         __builtin_memcpy(e, &o, 16);

@@ -52,23 +52,6 @@ XPOSE_HD inline void load_head(const char *p, int n, uint64_t &lo,
   if (n & 1) put_piece(lo, hi, off, (uint8_t)p[off]);
 }
 
-// Bytes [b0, b1) of the vector (0 <= b0 <= b1 <= 16) stored at p + b0 in
-// pieces of at most 8 bytes, each the largest that starts at a multiple of
-// its size and ends by b1 (at most six pieces).
-XPOSE_HD inline void store_range(char *p, int b0, int b1, uint64_t lo,
-                                 uint64_t hi) {
-  while (b0 < b1) {
-    int w = 8;
-    while (w > 1 && (b0 % w != 0 || b0 + w > b1)) w >>= 1;
-    const uint64_t v = get_piece(lo, hi, b0);
-    if (w == 8) *reinterpret_cast<u64_any *>(p + b0) = v;
-    else if (w == 4) *reinterpret_cast<u32_any *>(p + b0) = (uint32_t)v;
-    else if (w == 2) *reinterpret_cast<u16_any *>(p + b0) = (uint16_t)v;
-    else p[b0] = (char)v;
-    b0 += w;
-  }
-}
-
 XPOSE_HD inline void store_head(char *p, int n, uint64_t lo, uint64_t hi) {
   int off = 0;
   if (n & 8) {

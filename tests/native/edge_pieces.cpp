@@ -54,34 +54,6 @@ int main() {
       memcpy(lo_guard, before, 16 + n + shift);
     }
   }
-  // store_range: every [b0, b1) within the vector, the vector placed so
-  // that byte b1 - 1 ends the readable page; bytes outside the range keep
-  // their values.
-  for (int b0 = 0; b0 <= 16; ++b0) {
-    for (int b1 = b0; b1 <= 16; ++b1) {
-      char *p = end - (b1 > 0 ? b1 : 1);
-      unsigned char before[48];
-      char *lo_guard = p - 16;
-      const int span = 16 + (b1 > 0 ? b1 : 1);
-      memcpy(before, lo_guard, span);
-      const uint64_t slo = 0x1122334455667788ull ^ (uint64_t)b0,
-                     shi = 0x99aabbccddeeff00ull ^ (uint64_t)b1;
-      store_range(p, b0, b1, slo, shi);
-      unsigned char pat[16];
-      memcpy(pat, &slo, 8);
-      memcpy(pat + 8, &shi, 8);
-      for (int i = 0; i < span; ++i) {
-        const int v = i - 16;  // byte index in the vector
-        const unsigned char want =
-            (v >= b0 && v < b1) ? pat[v] : before[i];
-        if ((unsigned char)lo_guard[i] != want) {
-          printf("store_range b0=%d b1=%d byte %d wrong\n", b0, b1, v);
-          return 1;
-        }
-      }
-      memcpy(lo_guard, before, span);
-    }
-  }
   printf("ok\n");
   return 0;
 }

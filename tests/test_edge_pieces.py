@@ -1,8 +1,8 @@
-"""The transpose edge paths move the partial 16-byte vectors of small
-elements in pieces of 8, 4, 2 and 1 bytes (load_head, store_head and
-store_range in xpose_lanes.h); a host program built from the same header
-checks, against a no-access guard page, that every length, range and
-alignment reads and writes exactly its bytes."""
+"""The transpose edge path moves the partial 16-byte vectors of 1- and
+2-byte elements in pieces of 8, 4, 2 and 1 bytes (load_head and store_head
+in xpose_lanes.h); a host program built from the same header checks,
+against a no-access guard page, that every length and alignment reads and
+writes exactly its bytes."""
 import os
 import subprocess
 import tempfile
