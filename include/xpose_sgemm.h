@@ -20,8 +20,8 @@
  * reach C as alpha * NaN.  Elements of C outside the m x n region (pitch
  * padding) are never written.
  *
- * How.  Each workgroup computes a 128 x 128 block of C in steps of bk along
- * k.  Per step it loads A's 128 x bk tile with 16-byte row reads and stores
+ * How.  Each workgroup computes a 128 x 128 (or 256 x 128) block of C in
+ * steps of bk along k.  Per step it loads A's tile with 16-byte row reads and stores
  * it TRANSPOSED in LDS (As[l][i], so the product reads consecutive i), the
  * store the pages show to be bank-conflicted when As's row stride is a
  * multiple of the bank count ("How Shared Memory Is Addressed"); B's bk x 128
@@ -102,7 +102,8 @@ enum {
                                    instead of buffer loads (a descriptor per
                                    k step, 32-bit lane offsets), which are
                                    the default where the pitches allow them
-                                   (lda <= 4161790 and ldb <= 8323580)       */
+                                   (lda <= 2^31 / (4 (tile_m + 1)), i.e.
+                                   4161790 or 2089014, and ldb <= 8323580)   */
 };
 
 /* Optional knobs (zero-initialise for defaults).  Every choice gives the
@@ -114,6 +115,9 @@ typedef struct xpose_sgemm_opts {
   int32_t group_m; /* block order: groups of group_m block rows, walked
                       block-column by block-column; 0 = default (8)          */
   int32_t flags;   /* XPOSE_SGEMM_*                                           */
+  int32_t tile_m;  /* rows of C per workgroup: 0 = default (128), 128 (4
+                      waves) or 256 (8 waves; k steps 16 and 32, one LDS
+                      buffer); blocks are 128 columns wide                  */
 } xpose_sgemm_opts;
 
 /* What xpose_sgemm_plan reports about the kernel a call would launch. */

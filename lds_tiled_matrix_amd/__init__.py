@@ -84,7 +84,8 @@ class XposePlanInfo(ctypes.Structure):
 
 class XposeSgemmOpts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("bk", ctypes.c_int32),
-                ("group_m", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("group_m", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32)]
 
 
 class XposeSgemmInfo(ctypes.Structure):
@@ -222,9 +223,9 @@ def xpose_lds_probe(cycles_out: int, lane_bytes, width: int, is_write: int,
                                 stream)
 
 
-def make_sgemm_opts(layout=AS_AUTO, bk=0, group_m=0,
-                    flags=0) -> XposeSgemmOpts:
-    return XposeSgemmOpts(layout, bk, group_m, flags)
+def make_sgemm_opts(layout=AS_AUTO, bk=0, group_m=0, flags=0,
+                    tile_m=0) -> XposeSgemmOpts:
+    return XposeSgemmOpts(layout, bk, group_m, flags, tile_m)
 
 
 def xpose_sgemm(m: int, n: int, k: int, alpha: float, a: int, lda: int,

@@ -11,13 +11,17 @@
 
 namespace {
 
-constexpr int kTile = 128;          // rows and columns of C per workgroup
+constexpr int kTileN = 128;         // columns of C per workgroup
+constexpr int kDefaultTileM = 128;
 constexpr int kDefaultBk = 16;
 constexpr int kDefaultLayout = XPOSE_AS_PADDED;
 constexpr int kDefaultGroupM = 8;
-// Largest lda for buffer loads: 128 rows of the A tile (plus the k step)
-// within a 31-bit byte offset; ldb may be 2x larger (at most 64 rows of B).
-constexpr int64_t kMaxBufferPitch = ((int64_t)1 << 31) / (4 * (kTile + 1));
+// Largest pitches for buffer loads: the tile_m rows of A's tile (plus the k
+// step) and the at most 64 rows of B's tile within a 31-bit byte offset.
+constexpr int64_t max_buffer_lda(int tile_m) {
+  return ((int64_t)1 << 31) / (4 * (tile_m + 1));
+}
+constexpr int64_t kMaxBufferLdb = ((int64_t)1 << 31) / (4 * 129) * 2;
 
 struct SgemmPlan {
   bool empty = false;
@@ -51,7 +55,8 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
 int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
               const float *b, int64_t ldb, const float *c, int64_t ldc,
               const xpose_sgemm_opts *opts, SgemmPlan &plan) {
-  int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM;
+  int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM,
+      tile_m = kDefaultTileM;
   bool remap = true, buffers = true;
   int stages = 1;
   if (opts) {
@@ -61,12 +66,15 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
         opts->bk != 64)
       return XPOSE_EINVAL;
     if (opts->group_m < 0) return XPOSE_EINVAL;
+    if (opts->tile_m != 0 && opts->tile_m != 128 && opts->tile_m != 256)
+      return XPOSE_EINVAL;
     if (opts->flags & ~(XPOSE_SGEMM_NO_XCD_REMAP | XPOSE_SGEMM_DOUBLE_BUFFER |
                         XPOSE_SGEMM_NO_BUFFER_LOADS))
       return XPOSE_EINVAL;
     if (opts->layout) layout = opts->layout;
     if (opts->bk) bk = opts->bk;
     if (opts->group_m) group_m = opts->group_m;
+    if (opts->tile_m) tile_m = opts->tile_m;
     remap = !(opts->flags & XPOSE_SGEMM_NO_XCD_REMAP);
     if (opts->flags & XPOSE_SGEMM_DOUBLE_BUFFER) stages = 2;
     if (opts->flags & XPOSE_SGEMM_NO_BUFFER_LOADS) buffers = false;
@@ -93,8 +101,8 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
     if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1))
       return XPOSE_EALIAS;
   }
-  const int64_t tiles_m = (m + kTile - 1) / kTile;
-  const int64_t tiles_n = (n + kTile - 1) / kTile;
+  const int64_t tiles_m = (m + tile_m - 1) / tile_m;
+  const int64_t tiles_n = (n + kTileN - 1) / kTileN;
   int64_t tiles;
   if (__builtin_mul_overflow(tiles_m, tiles_n, &tiles) || tiles > INT32_MAX)
     return XPOSE_EINVAL;
@@ -106,7 +114,8 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   const xpose::SgemmKernel *kern = nullptr;
   for (int i = 0; i < count && !kern; ++i)
     if (table[i].bk == bk && table[i].layout == layout &&
-        table[i].vec == vec && table[i].stages == stages)
+        table[i].vec == vec && table[i].stages == stages &&
+        table[i].tile_m == tile_m)
       kern = &table[i];
   if (!kern) return XPOSE_ENOTILE;
   if (group_m > tiles_m) group_m = (int)tiles_m;
@@ -126,8 +135,8 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   g.group_m = (uint32_t)group_m;
   g.xcd_remap = remap ? 1 : 0;
   // Buffer-load byte offsets within one k step's tiles must fit in 31 bits.
-  g.buf_ok = buffers && vec && uses_ab && lda <= kMaxBufferPitch &&
-             ldb <= kMaxBufferPitch * kTile / 64;
+  g.buf_ok = buffers && vec && uses_ab && lda <= max_buffer_lda(tile_m) &&
+             ldb <= kMaxBufferLdb;
   plan.kernel = kern;
   plan.tiles = tiles;
   return XPOSE_OK;
@@ -178,8 +187,8 @@ int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
   info->as_stride = kern.as_stride;
   info->lds_bytes = kern.lds_bytes;
   info->threads = kern.threads;
-  info->tile_m = kTile;
-  info->tile_n = kTile;
+  info->tile_m = kern.tile_m;
+  info->tile_n = kTileN;
   info->vector_loads = kern.vec ? 1 : 0;
   info->group_m = (int32_t)plan.args.group_m;
   info->xcd_remap = plan.args.xcd_remap;

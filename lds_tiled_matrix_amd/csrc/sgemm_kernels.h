@@ -8,7 +8,7 @@
 namespace xpose {
 
 // Tiled SGEMM, C = alpha * A * B + beta * C (fp32, row-major; pitches in
-// floats).  Grid = tiles_m * tiles_n workgroups of 128 x 128 blocks of C.
+// floats).  Grid = tiles_m * tiles_n workgroups of tile_m x 128 blocks of C.
 struct SgemmArgs {
   const float *a, *b;
   float *c;
@@ -27,6 +27,7 @@ struct SgemmKernel {
   int bk, layout, as_stride, lds_bytes, threads;
   bool vec;    // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)
   int stages;  // LDS buffers: 1 = two barriers per k step, 2 = one
+  int tile_m;  // rows of C per workgroup (128 or 256; 128 columns)
   hipError_t (*launch)(const SgemmArgs &, uint32_t grid, hipStream_t);
 };
 

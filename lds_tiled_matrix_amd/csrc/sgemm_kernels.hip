@@ -57,11 +57,11 @@ __device__ inline float *uniform(const float *p) {
 // barrier per step separates the writes of one buffer from the reads of
 // the other.  Either way the next step's global loads are issued before
 // this step's products and land in registers while the matrix cores run.
-template <int BK, int L, bool VEC, int STAGES>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    SgemmTile<BK, L>::waves_per_simd(STAGES)))) void
+template <int BK, int L, bool VEC, int STAGES, int BM = 128>
+__global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(
+    SgemmTile<BK, L, BM>::waves_per_simd(STAGES)))) void
 xpose_sgemm_kernel(SgemmArgs a) {
-  using T = SgemmTile<BK, L>;
+  using T = SgemmTile<BK, L, BM>;
   __shared__ __attribute__((aligned(16))) float As[STAGES * T::AS_FLOATS];
   __shared__ __attribute__((aligned(16))) float Bs[STAGES * T::BS_FLOATS];
 
@@ -200,30 +200,37 @@ xpose_sgemm_kernel(SgemmArgs a) {
     }
 }
 
-template <int BK, int L, bool VEC, int STAGES>
+template <int BK, int L, bool VEC, int STAGES, int BM>
 hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
   SgemmArgs copy = a;
   void *args[] = {&copy};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(&xpose_sgemm_kernel<BK, L, VEC, STAGES>),
-      dim3(grid), dim3(256), args, 0, s);
+      reinterpret_cast<const void *>(
+          &xpose_sgemm_kernel<BK, L, VEC, STAGES, BM>),
+      dim3(grid), dim3(SgemmTile<BK, L, BM>::NT), args, 0, s);
 }
 
-#define XPOSE_SGEMM(BK, L, VEC, ST)                                          \
+#define XPOSE_SGEMM(BK, L, VEC, ST, BM)                                      \
   SgemmKernel {                                                              \
-    BK, L, SgemmTile<BK, L>::AS_STRIDE, ST * SgemmTile<BK, L>::LDS_BYTES,    \
-        256, VEC, ST, &launch_sgemm<BK, L, VEC, ST>                          \
+    BK, L, SgemmTile<BK, L, BM>::AS_STRIDE,                                  \
+        ST * SgemmTile<BK, L, BM>::LDS_BYTES, SgemmTile<BK, L, BM>::NT, VEC, \
+        ST, BM, &launch_sgemm<BK, L, VEC, ST, BM>                            \
   }
-#define XPOSE_SGEMM_L(BK, L, ST)                                             \
-  XPOSE_SGEMM(BK, L, true, ST), XPOSE_SGEMM(BK, L, false, ST)
-#define XPOSE_SGEMM_BK(BK, ST)                                               \
-  XPOSE_SGEMM_L(BK, kAsUnpadded, ST), XPOSE_SGEMM_L(BK, kAsPadded, ST),      \
-      XPOSE_SGEMM_L(BK, kAsSwizzle, ST)
+#define XPOSE_SGEMM_L(BK, L, ST, BM)                                         \
+  XPOSE_SGEMM(BK, L, true, ST, BM), XPOSE_SGEMM(BK, L, false, ST, BM)
+#define XPOSE_SGEMM_BK(BK, ST, BM)                                           \
+  XPOSE_SGEMM_L(BK, kAsUnpadded, ST, BM), XPOSE_SGEMM_L(BK, kAsPadded, ST, BM), \
+      XPOSE_SGEMM_L(BK, kAsSwizzle, ST, BM)
 
+// 128-row blocks for every k step and buffer count; 256-row blocks (8
+// waves) for the k steps whose B tile covers every lane (16 and 32), one
+// LDS buffer.
 const SgemmKernel kSgemmKernels[] = {
-    XPOSE_SGEMM_BK(8, 1), XPOSE_SGEMM_BK(16, 1), XPOSE_SGEMM_BK(32, 1),
-    XPOSE_SGEMM_BK(64, 1), XPOSE_SGEMM_BK(8, 2), XPOSE_SGEMM_BK(16, 2),
-    XPOSE_SGEMM_BK(32, 2), XPOSE_SGEMM_BK(64, 2)};
+    XPOSE_SGEMM_BK(8, 1, 128),  XPOSE_SGEMM_BK(16, 1, 128),
+    XPOSE_SGEMM_BK(32, 1, 128), XPOSE_SGEMM_BK(64, 1, 128),
+    XPOSE_SGEMM_BK(8, 2, 128),  XPOSE_SGEMM_BK(16, 2, 128),
+    XPOSE_SGEMM_BK(32, 2, 128), XPOSE_SGEMM_BK(64, 2, 128),
+    XPOSE_SGEMM_BK(16, 1, 256), XPOSE_SGEMM_BK(32, 1, 256)};
 
 }  // namespace
 

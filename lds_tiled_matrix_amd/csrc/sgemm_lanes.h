@@ -28,12 +28,13 @@ namespace xpose {
 enum AsLayout : int { kAsUnpadded = 1, kAsPadded = 2, kAsSwizzle = 3 };
 
 // Compile-time geometry of one SGEMM kernel: BK is the k step, L the As
-// layout.  A workgroup of 4 waves computes a 128 x 128 block of C; wave w
-// computes the 64 x 64 quarter at (64 * (w / 2), 64 * (w % 2)) as 2 x 2
-// matrix-core tiles of 32 x 32.
-template <int BK, int L>
+// layout, BM_ the rows of C per workgroup (128 or 256).  A workgroup of
+// BM_ / 32 waves computes a BM_ x 128 block of C; wave w computes the
+// 64 x 64 block at (64 * (w / 2), 64 * (w % 2)) as 2 x 2 matrix-core tiles
+// of 32 x 32.
+template <int BK, int L, int BM_ = 128>
 struct SgemmTile {
-  static constexpr int BM = 128, BN = 128, NT = 256;
+  static constexpr int BM = BM_, BN = 128, NT = 2 * BM_;
   static constexpr int WM = 64, WN = 64;  // C block of one wave
 
   // A's 128 x BK tile is read in strips of LK = min(BK, 32) columns: each
@@ -79,6 +80,8 @@ struct SgemmTile {
   }
 
   static_assert(BK == 8 || BK == 16 || BK == 32 || BK == 64, "built k steps");
+  static_assert(BM == 128 || BM == 256, "built block heights");
+  static_assert(B_PASSES >= 1, "every lane loads part of B's tile");
   static_assert(A_ROW_PASSES * A_ROWS_PER_PASS == BM, "whole A tile");
   static_assert(B_PASSES * B_ROWS_PER_PASS == BK, "whole B tile");
   static_assert(L != kAsPadded || 4 * PAD == HG, "pad spreads the chunks");

@@ -65,6 +65,7 @@ int main(void) {
   plan("dtype", out, in, 1, 64, 64, 64, 64, 9, NULL);
   SIZE(xpose_sgemm_opts);
   OFF(xpose_sgemm_opts, bk); OFF(xpose_sgemm_opts, flags);
+  OFF(xpose_sgemm_opts, tile_m);
   SIZE(xpose_sgemm_info);
   OFF(xpose_sgemm_info, as_stride); OFF(xpose_sgemm_info, xcd_remap);
   OFF(xpose_sgemm_info, tiles);

@@ -29,12 +29,13 @@ static void check(const std::string &what, bool ok, const char *detail = "") {
   printf("check %s %s %s\n", what.c_str(), ok ? "ok" : "FAIL", detail);
 }
 
-template <int BK, int L>
+template <int BK, int L, int BM = 128>
 static void kernel() {
-  using T = SgemmTile<BK, L>;
+  using T = SgemmTile<BK, L, BM>;
   const char *lname = L == kAsUnpadded ? "unpadded"
                       : L == kAsPadded ? "padded" : "swizzle";
-  const std::string name = "sgemm/bk" + std::to_string(BK) + "/" + lname;
+  const std::string name = "sgemm/bk" + std::to_string(BK) + "/" + lname +
+                           (BM == 128 ? "" : "/m" + std::to_string(BM));
   int a[64];
   // Every (l, i) of As written exactly once, inside the array.
   std::vector<int> hits(T::AS_FLOATS, 0);
@@ -132,6 +133,9 @@ int main() {
   kernel<16, kAsUnpadded>(); kernel<16, kAsPadded>(); kernel<16, kAsSwizzle>();
   kernel<32, kAsUnpadded>(); kernel<32, kAsPadded>(); kernel<32, kAsSwizzle>();
   kernel<64, kAsUnpadded>(); kernel<64, kAsPadded>(); kernel<64, kAsSwizzle>();
+  kernel<16, kAsUnpadded, 256>(); kernel<16, kAsPadded, 256>();
+  kernel<16, kAsSwizzle, 256>(); kernel<32, kAsUnpadded, 256>();
+  kernel<32, kAsPadded, 256>(); kernel<32, kAsSwizzle, 256>();
   const uint32_t dims[] = {1, 2, 3, 7, 8, 9, 32, 33};
   for (uint32_t tm : dims)
     for (uint32_t tn : dims)

@@ -42,6 +42,24 @@ def test_layout_strides(bk):
         assert info.lds_bytes == 4 * bk * (stride + 128)
 
 
+def test_tall_blocks():
+    """256 x 128 blocks (8 waves) for k steps 16 and 32, one LDS buffer."""
+    for bk in (16, 32):
+        rc, info = plan(opts=X.make_sgemm_opts(bk=bk, tile_m=256))
+        assert rc == 0 and (info.tile_m, info.tile_n, info.threads) == (256, 128, 512)
+        assert info.tiles == 16 * 32
+        assert info.lds_bytes == 4 * bk * ((256 + 32 // bk) + 128)
+    rc, info = plan(m=300, n=129, opts=X.make_sgemm_opts(tile_m=256))
+    assert rc == 0 and info.tiles == 2 * 2
+    assert plan(opts=X.make_sgemm_opts(bk=8, tile_m=256))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.make_sgemm_opts(tile_m=256, flags=X.SGEMM_DOUBLE_BUFFER))[0] == X.XPOSE_ENOTILE
+    assert plan(opts=X.make_sgemm_opts(tile_m=64))[0] == X.XPOSE_EINVAL
+    # buffer loads: half the lda limit of 128-row blocks
+    big = (1 << 31) // (4 * 257)
+    assert plan(m=512, lda=big - big % 4, opts=X.make_sgemm_opts(tile_m=256))[1].buffer_loads == 1
+    assert plan(m=512, lda=big + 4 - big % 4, opts=X.make_sgemm_opts(tile_m=256))[1].buffer_loads == 0
+
+
 def test_ragged_tiles_and_group_clamp():
     rc, info = plan(m=130, n=67, k=45)
     assert rc == 0 and info.tiles == 2 * 1 and info.group_m == 2

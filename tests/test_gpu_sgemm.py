@@ -66,7 +66,7 @@ def run_case(A, B, C, alpha, beta, pads=(0, 0, 0), shifts=(0, 0, 0),
     pc = pc0 + 4 * GUARD
     sh = 0 if stream is None else int(stream.cuda_stream)
     say(f"sgemm m={m} n={n} k={k} pads={pads} shifts={shifts} "
-        f"opts={None if opts is None else (opts.layout, opts.bk, opts.flags)}")
+        f"opts={None if opts is None else (opts.layout, opts.bk, opts.flags, opts.tile_m)}")
     if entry == "plain":
         rc = X.xpose_sgemm(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, sh)
     else:
@@ -155,6 +155,19 @@ def test_exact_on_integer_inputs(layout, bk, flags):
         assert np.isfinite(got[region_mask(m, n, max(n, 1), got.size)]).all()
 
 
+@pytest.mark.parametrize("bk", (16, 32))
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
+def test_exact_tall_blocks(layout, bk):
+    """256 x 128 blocks (8 waves), buffer and global loads."""
+    for flags in (0, X.SGEMM_NO_BUFFER_LOADS):
+        opts = X.make_sgemm_opts(layout, bk, 0, flags, 256)
+        for idx, (m, n, k) in enumerate(EXACT_SHAPES + [(512, 256, 96), (257, 300, 65)]):
+            A = wl.small_int_f32((m, k), 700 + idx)
+            B = wl.small_int_f32((k, n), 800 + idx)
+            C = wl.small_int_f32((m, n), 900 + idx)
+            check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(idx % 3, 2 * (idx % 2), 5))
+
+
 def test_scalar_load_path_is_exact():
     """4-byte aligned (not 16-byte) operands and pitches that are not a
     multiple of 4 take the 4-byte loads."""
@@ -189,13 +202,16 @@ def test_all_kernels_agree_bit_for_bit():
     for layout in LAYOUTS:
         for bk in BKS:
             for flags in FLAG_SETS.values():
-                for shifts in ((0, 0, 0), (1, 1, 0)):
-                    got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
-                                         opts=X.make_sgemm_opts(layout, bk, 0, flags))
-                    if ref is None:
-                        ref = got
-                    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
-                        (layout, bk, flags, shifts)
+                for tile_m in (128, 256):
+                    if tile_m == 256 and (bk not in (16, 32) or flags == X.SGEMM_DOUBLE_BUFFER):
+                        continue
+                    for shifts in ((0, 0, 0), (1, 1, 0)):
+                        got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
+                                             opts=X.make_sgemm_opts(layout, bk, 0, flags, tile_m))
+                        if ref is None:
+                            ref = got
+                        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+                            (layout, bk, flags, tile_m, shifts)
 
 
 def test_degenerate_shapes():
@@ -275,8 +291,10 @@ def test_random_campaign():
         beta = float(rng.choice([0.0, 1.0, -2.0, 0.25]))
         flags = int(rng.choice([0, 0, X.SGEMM_DOUBLE_BUFFER, X.SGEMM_NO_BUFFER_LOADS,
                                 X.SGEMM_NO_XCD_REMAP]))
-        opts = X.make_sgemm_opts(int(rng.choice(LAYOUTS)), int(rng.choice(BKS)),
-                                 int(rng.choice([0, 1, 3, 8])), flags)
+        bk = int(rng.choice(BKS))
+        tile_m = int(rng.choice([128, 256])) if bk in (16, 32) and flags != X.SGEMM_DOUBLE_BUFFER else 128
+        opts = X.make_sgemm_opts(int(rng.choice(LAYOUTS)), bk,
+                                 int(rng.choice([0, 1, 3, 8])), flags, tile_m)
         A = wl.small_int_f32((m, k), 10_000 + case)
         B = wl.small_int_f32((k, n), 20_000 + case)
         C = wl.small_int_f32((m, n), 30_000 + case)

@@ -52,16 +52,17 @@ def worst(listing):
 
 def test_self_checks_pass(listing):
     checks = [ln.split() for ln in listing if ln.startswith("check ")]
-    assert len(checks) > 12 * 4
+    assert len(checks) > 18 * 4
     bad = [c for c in checks if c[2] != "ok"]
     assert not bad, bad[:5]
 
 
-@pytest.mark.parametrize("bk", (8, 16, 32, 64))
-def test_transposed_store(worst, bk):
-    assert worst[(f"sgemm/bk{bk}/unpadded", "a_store")] == min(bk, 32) // 4
-    assert worst[(f"sgemm/bk{bk}/padded", "a_store")] == 1
-    assert worst[(f"sgemm/bk{bk}/swizzle", "a_store")] == 1
+@pytest.mark.parametrize("bk, m", [(8, ""), (16, ""), (32, ""), (64, ""),
+                                   (16, "/m256"), (32, "/m256")])
+def test_transposed_store(worst, bk, m):
+    assert worst[(f"sgemm/bk{bk}/unpadded{m}", "a_store")] == min(bk, 32) // 4
+    assert worst[(f"sgemm/bk{bk}/padded{m}", "a_store")] == 1
+    assert worst[(f"sgemm/bk{bk}/swizzle{m}", "a_store")] == 1
 
 
 def test_reads_and_b_copies_conflict_free(worst):
@@ -72,5 +73,6 @@ def test_reads_and_b_copies_conflict_free(worst):
 
 def test_every_built_kernel_listed(worst):
     names = {n for n, _ in worst}
-    assert names == {f"sgemm/bk{bk}/{l}" for bk in (8, 16, 32, 64)
-                     for l in ("unpadded", "padded", "swizzle")}
+    layouts = ("unpadded", "padded", "swizzle")
+    assert names == ({f"sgemm/bk{bk}/{l}" for bk in (8, 16, 32, 64) for l in layouts} |
+                     {f"sgemm/bk{bk}/{l}/m256" for bk in (16, 32) for l in layouts})
