@@ -300,3 +300,51 @@ def test_random_campaign():
         C = wl.small_int_f32((m, n), 30_000 + case)
         say(f"campaign case {case}")
         check_exact(A, B, C, alpha, beta, pads=pads, shifts=shifts, opts=opts)
+
+
+def test_hip_graph_capture_and_replay():
+    """The SGEMM only enqueues its kernel (no allocation, memset or
+    synchronisation), so it can be captured into a HIP graph.  C is reset
+    eagerly between replays, and every replay must match the oracle."""
+    dev = _dev()
+    cases = [((300, 257, 100), 2.0, -1.0, None),
+             ((512, 384, 64), 1.0, 0.0, X.make_sgemm_opts(X.AS_SWIZZLE, 32)),
+             ((256, 256, 48), 1.0, 1.0, X.make_sgemm_opts(X.AS_PADDED, 16, 0, 0, 256))]
+    bufs = []
+    for idx, ((m, n, k), alpha, beta, opts) in enumerate(cases):
+        A = wl.small_int_f32((m, k), 60 + idx)
+        B = wl.small_int_f32((k, n), 70 + idx)
+        C = wl.small_int_f32((m, n), 80 + idx)
+        want = og.sgemm(m, n, k, alpha, A.reshape(-1), k, B.reshape(-1), n, beta,
+                        C.reshape(-1), n).astype(np.float32)
+        bufs.append((torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                     torch.from_numpy(C).to(dev), torch.from_numpy(C).to(dev),
+                     alpha, beta, opts, want))
+
+    def enqueue():
+        sh = int(torch.cuda.current_stream().cuda_stream)
+        for dA, dB, dC, _, alpha, beta, opts, _ in bufs:
+            m, k = dA.shape
+            n = dB.shape[1]
+            assert X.xpose_sgemm_ex(m, n, k, alpha, dA.data_ptr(), k, dB.data_ptr(), n,
+                                    beta, dC.data_ptr(), n, opts, sh) == 0
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # eager warm-up on the capture stream
+        say("sgemm graph warm-up")
+        enqueue()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue()
+    for rep in range(3):
+        for _, _, dC, dC0, *_ in bufs:
+            dC.copy_(dC0)  # eager work between replays: C back to its input
+        torch.cuda.synchronize()
+        say(f"sgemm graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (_, _, dC, _, _, _, _, want) in enumerate(bufs):
+            assert np.array_equal(dC.cpu().numpy(), want), f"replay {rep}, case {i}"
