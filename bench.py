@@ -291,7 +291,6 @@ def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
     sampled parity against the oracle, and the oracle timed on a bounded
     sample."""
     import torch
-    import oracle.sgemm as og
     w = wl.GEMM_WORKLOADS["sgemm_4096"]
     A, B, C = wl.make_gemm_inputs(w)
     dev = torch.device("cuda", 0)
@@ -318,27 +317,31 @@ def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
 
     res = {"workload": w.description, "m": w.m, "n": w.n, "k": w.k,
            "alpha": w.alpha, "beta": w.beta, "flops": w.flops}
-    # One launch on the original C for the parity sample.
-    with torch.cuda.stream(stream):
-        launch_with(None)()
-    torch.cuda.synchronize()
-    got = dC.cpu().numpy()
-    rows = np.random.default_rng(7).choice(w.m, 64, replace=False)
-    t0 = time.perf_counter()
-    ref = og.sgemm(len(rows), w.n, w.k, w.alpha,
-                   np.ascontiguousarray(A[rows]).reshape(-1), w.k,
-                   B.reshape(-1), w.n, w.beta,
-                   np.ascontiguousarray(C[rows]).reshape(-1), w.n)
-    t_ref = time.perf_counter() - t0
-    mag = abs(w.alpha) * (np.abs(A[rows].astype(np.float64)) @
-                          np.abs(B.astype(np.float64)))
-    mag += abs(w.beta) * np.abs(C[rows].astype(np.float64))
-    err = np.abs(got[rows].astype(np.float64) - ref)
-    res["parity_vs_oracle"] = bool((err <= (w.k + 3) * 2.0 ** -24 * mag).all())
-    res["parity_sample"] = ("64 sampled rows of C (all columns) against the "
-                            "oracle, within (k + 3) 2^-24 (|alpha||A||B| + "
-                            "|beta||C|)")
     if with_cpu:
+        # The CPU leg: the oracle on a bounded sample (64 rows of C), timed,
+        # and the GPU's rows from one launch on the original C checked
+        # against it.
+        import oracle.sgemm as og
+        with torch.cuda.stream(stream):
+            launch_with(None)()
+        torch.cuda.synchronize()
+        got = dC.cpu().numpy()
+        rows = np.random.default_rng(7).choice(w.m, 64, replace=False)
+        t0 = time.perf_counter()
+        ref = og.sgemm(len(rows), w.n, w.k, w.alpha,
+                       np.ascontiguousarray(A[rows]).reshape(-1), w.k,
+                       B.reshape(-1), w.n, w.beta,
+                       np.ascontiguousarray(C[rows]).reshape(-1), w.n)
+        t_ref = time.perf_counter() - t0
+        mag = abs(w.alpha) * (np.abs(A[rows].astype(np.float64)) @
+                              np.abs(B.astype(np.float64)))
+        mag += abs(w.beta) * np.abs(C[rows].astype(np.float64))
+        err = np.abs(got[rows].astype(np.float64) - ref)
+        res["parity_vs_oracle"] = bool(
+            (err <= (w.k + 3) * 2.0 ** -24 * mag).all())
+        res["parity_sample"] = ("64 sampled rows of C (all columns) against "
+                                "the oracle, within (k + 3) 2^-24 "
+                                "(|alpha||A||B| + |beta||C|)")
         try:
             from threadpoolctl import threadpool_info
             threads = max([i.get("num_threads", 1) for i in threadpool_info()
