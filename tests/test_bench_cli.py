@@ -1,0 +1,46 @@
+"""bench.py's host-side contract, without a GPU: more than one GPU is
+refused with a message, a host without a GPU is reported, and the traffic
+summary it reads back parses."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused():
+    out = run("--gpus", "2")
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr and not out.stdout.strip()
+
+
+def test_bad_step_counts_are_rejected():
+    out = run("--steps", "0")
+    assert out.returncode != 0 and not out.stdout.strip()
+
+
+def test_no_gpu_is_reported():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    out = run("--steps", "1", "--warmup", "0")
+    assert out.returncode == 1 and "no GPU" in out.stderr
+
+
+def test_traffic_summary_parses():
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and int(h, 16) >= 0
+    t = bench.read_traffic()
+    assert t is None or (isinstance(t, int) and t > 0)
+    if t is not None:
+        # HBM bytes of one 8192 x 8192 fp32 transpose: close to 2 x 256 MiB
+        assert abs(t / (2 * 8192 * 8192 * 4) - 1) < 0.05
