@@ -94,6 +94,30 @@ static void kernel() {
       }
   check(name + "/reads_in_bounds", in_bounds);
   check(name + "/lds_bytes", T::LDS_BYTES == 4 * BK * (T::AS_STRIDE + 128));
+  // The whole-block epilogue addresses C element (row, col) of the block as
+  // one per-lane offset (row acc_row(q, 0) of the wave's block) plus a
+  // per-register row offset (acc_row(0, r)): the sum must be the lane's own
+  // accumulator row, and every element must fall inside the descriptor's
+  // extent, (BM - 1) * ldc + BN floats, for the largest pitch it takes.
+  bool sum_ok = true, extent_ok = true;
+  const int64_t ldc = ((int64_t)1 << 29) / T::BM;
+  const int64_t records = ((T::BM - 1) * ldc + T::BN) * 4;
+  for (int w = 0; w < T::NT / 64; ++w)
+    for (int q = 0; q < 64; ++q)
+      for (int x = 0; x < 2; ++x)
+        for (int y = 0; y < 2; ++y)
+          for (int r = 0; r < 16; ++r) {
+            sum_ok &= T::acc_row(q, r) == T::acc_row(q, 0) + T::acc_row(0, r);
+            const int64_t lane_off =
+                ((T::wave_row(w) + T::acc_row(q, 0)) * ldc + T::wave_col(w) +
+                 q % 32) * 4;
+            const int64_t off = lane_off + 128 * y +
+                                (32 * x + T::acc_row(0, r)) * ldc * 4;
+            extent_ok &= lane_off < INT32_MAX && off >= 0 && off + 4 <= records &&
+                         records <= INT32_MAX;
+          }
+  check(name + "/epilogue_rows", sum_ok);
+  check(name + "/epilogue_extent", extent_ok);
 }
 
 // The block order must be a bijection onto the tiles_m x tiles_n blocks.

@@ -242,3 +242,40 @@ def test_large_sgemm(case):
     assert bad.size == 0, [(rows[p[0]], p[1]) for p in bad[:4]]
     del a_store, A, B, C0, C
     _free()
+
+
+@pytest.mark.parametrize("tile_m", (128, 256))
+@pytest.mark.parametrize("past", (0, 4), ids=("at_limit", "past_limit"))
+def test_sgemm_c_pitch_at_the_epilogue_limit(tile_m, past):
+    """Whole blocks write C through one buffer descriptor while the block
+    spans at most 2^31 bytes (ldc <= 2^29 / tile_m), and through checked
+    global stores past that: both sides of the limit, exact against the
+    oracle on every element, pitch padding untouched."""
+    dev = _dev()
+    m, n, k = 2 * tile_m, 256, 48
+    ldc = (1 << 29) // tile_m + past
+    say(f"sgemm C pitch: tile_m={tile_m} ldc={ldc} m={m} n={n} k={k}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(47)
+    A = _int_matrix(gen, (m, k), dev)
+    B = _int_matrix(gen, (k, n), dev)
+    c_store = torch.full(((m - 1) * ldc + n,), -7.5, dtype=torch.float32,
+                         device=dev)
+    C = c_store.as_strided((m, n), (ldc, 1))
+    C0 = _int_matrix(gen, (m, n), dev)
+    C.copy_(C0)
+    opts = X.make_sgemm_opts(tile_m=tile_m)
+    rc = X.xpose_sgemm_ex(m, n, k, 2.0, A.data_ptr(), k, B.data_ptr(), n, -1.0,
+                          C.data_ptr(), ldc, opts, 0)
+    assert rc == 0, X.strerror(rc)
+    torch.cuda.synchronize()
+    exp = og.sgemm(m, n, k, 2.0, A.cpu().numpy().reshape(-1), k,
+                   B.cpu().numpy().reshape(-1), n, -1.0,
+                   C0.cpu().numpy().reshape(-1), n)
+    got = C.cpu().numpy()
+    bad = np.argwhere(got != exp.astype(np.float32))
+    assert bad.size == 0, bad[:4].tolist()
+    pad = c_store.as_strided((m - 1, 4096), (ldc, 1), n)
+    assert bool((pad == -7.5).all())
+    del A, B, c_store, C, C0
+    _free()
