@@ -39,12 +39,29 @@ def flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + ["-o", tmp] + [os.path.join(CSRC, s)
-                                              for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object in parallel (the kernel files take
+    most of the time), then link the shared library."""
+    import tempfile
+    compile_flags = [f for f in flags() if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="xpose_build_") as tmpdir:
+        procs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [hipcc()] + compile_flags + ["-c", "-o", obj,
+                                               os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd)))
+            objs.append(obj)
+        failed = [src for src, p in procs if p.wait() != 0]
+        if failed:
+            raise subprocess.CalledProcessError(1, f"hipcc -c {failed}")
+        tmp = LIB + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o",
+               tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
 
