@@ -287,7 +287,8 @@ def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
     """The tiled SGEMM with the padded transposed As store at the size its
     page measures (M = N = K = 4096, C += A B, uniform [-1, 1) inputs):
     the default kernel with its matrix-core roofline, the As-layout
-    ablation with one and two LDS buffers, torch's fp32 addmm for context,
+    ablation with one and two LDS buffers and with 256-row blocks, torch's
+    fp32 addmm for context,
     sampled parity against the oracle, and the oracle timed on a bounded
     sample."""
     import torch
@@ -357,9 +358,12 @@ def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
         ab = {}
         n_ab = max(10, min(steps, 40))
         for lay, name in X.AS_NAMES.items():
-            for flags, tag in ((0, ""), (X.SGEMM_DOUBLE_BUFFER, " 2 buffers")):
-                _, d = time_launches(launch_with(X.make_sgemm_opts(lay, 0, 0, flags)),
-                                     stream, n_ab, min(warmup, 5))
+            for flags, tile_m, tag in ((0, 0, ""),
+                                       (X.SGEMM_DOUBLE_BUFFER, 0, " 2 buffers"),
+                                       (0, 256, " 256-row blocks")):
+                opts = X.make_sgemm_opts(lay, 0, 0, flags, tile_m)
+                _, d = time_launches(launch_with(opts), stream, n_ab,
+                                     min(warmup, 5))
                 ab[name + tag] = tflops(d)["median_TFLOPs"]
         res["ablation_TFLOPs"] = ab
         c2 = torch.empty_like(dC)
