@@ -182,11 +182,22 @@ xpose_sgemm_kernel(SgemmArgs a) {
       }
     }
   };
-  if (VEC && a.buf_ok && m0 + T::BM <= a.m && n0 + T::BN <= a.n &&
-      a.k % BK == 0)
-    k_loop(load_whole);
-  else
+  // Whole blocks with a ragged k take buffer loads for every whole k step
+  // and checked loads for the last, partial one.
+  auto load_ragged_k = [&](int64_t k0) __attribute__((always_inline)) {
+    if (k0 + BK <= a.k)
+      load_whole(k0);
+    else
+      load_checked(k0);
+  };
+  if (VEC && a.buf_ok && m0 + T::BM <= a.m && n0 + T::BN <= a.n) {
+    if (a.k % BK == 0)
+      k_loop(load_whole);
+    else
+      k_loop(load_ragged_k);
+  } else {
     k_loop(load_checked);
+  }
 
   // C = alpha * acc + beta * C; with beta == 0 C is not read.  32 lanes
   // cover 32 consecutive columns of one row per store.  When the grid is one
