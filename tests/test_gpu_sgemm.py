@@ -168,6 +168,26 @@ def test_exact_tall_blocks(layout, bk):
             check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(idx % 3, 2 * (idx % 2), 5))
 
 
+@pytest.mark.parametrize("bk, tile_m", [(8, 128), (16, 128), (32, 128), (64, 128),
+                                         (16, 256), (32, 256)])
+def test_whole_blocks_with_ragged_k(bk, tile_m):
+    """Blocks wholly inside C with k not a multiple of the k step: buffer
+    loads for every whole k step, checked loads for the last one.  A's
+    pitch padding holds NaN, so a read past column k would show."""
+    for layout in LAYOUTS:
+        opts = X.make_sgemm_opts(layout, bk, 0, 0, tile_m)
+        for idx, (m, n, k) in enumerate([(2 * tile_m, 256, 45), (tile_m, 384, 100),
+                                         (tile_m, 128, bk + 1), (2 * tile_m, 128, 3)]):
+            pad_a = (-k) % 4 + 4        # lda a multiple of 4: 16-byte loads
+            rc, info = X.xpose_sgemm_plan(m, n, k, 1 << 40, k + pad_a,
+                                          1 << 41, n, 1 << 42, n, opts)
+            assert rc == 0 and info.vector_loads == 1 and info.buffer_loads == 1
+            A = wl.small_int_f32((m, k), 1000 + idx)
+            B = wl.small_int_f32((k, n), 1100 + idx)
+            C = wl.small_int_f32((m, n), 1200 + idx)
+            check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(pad_a, 0, 3))
+
+
 def test_scalar_load_path_is_exact():
     """4-byte aligned (not 16-byte) operands and pitches that are not a
     multiple of 4 take the 4-byte loads."""
