@@ -209,6 +209,69 @@ def test_torch_views_and_streams():
     assert np.array_equal(dst.cpu().numpy(), want)
 
 
+def test_threads_on_their_own_streams():
+    """Calls are reentrant: four host threads, each with its own stream,
+    enqueue transposes of every element size and SGEMMs at the same time
+    (ctypes releases the interpreter lock during each call).  Every result
+    must equal the oracle's."""
+    import threading
+
+    import oracle.sgemm as og
+    dev = _dev()
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            torch.cuda.set_device(dev)
+            s = torch.cuda.Stream()
+            rng = np.random.default_rng(500 + tid)
+            jobs = []
+            with torch.cuda.stream(s):
+                for it in range(12):
+                    size = (1, 2, 4, 8)[(tid + it) % 4]
+                    r, c = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+                    h = wl.random_bits((r, c), size, 1000 * tid + it)
+                    if size > 1:
+                        h = h.view(SIGNED[size])
+                    y = X.transpose(torch.from_numpy(h).to(dev), stream=s)
+                    jobs.append(("t", h, y))
+                    if it % 4 == 0:
+                        m, n, k = (int(v) for v in rng.integers(1, 300, 3))
+                        A = wl.small_int_f32((m, k), 2000 + 10 * tid + it)
+                        B = wl.small_int_f32((k, n), 3000 + 10 * tid + it)
+                        C = wl.small_int_f32((m, n), 4000 + 10 * tid + it)
+                        dC = torch.from_numpy(C.copy()).to(dev)
+                        X.sgemm(torch.from_numpy(A).to(dev),
+                                torch.from_numpy(B).to(dev), dC,
+                                alpha=2.0, beta=-1.0, stream=s)
+                        jobs.append(("g", (A, B, C), dC))
+            s.synchronize()
+            results[tid] = [(kind, src, out.cpu().numpy()) for kind, src, out in jobs]
+        except Exception as e:  # reported by the main thread
+            errors.append((tid, repr(e)))
+
+    say("4 threads, own streams, transposes and SGEMMs")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    for tid, jobs in results.items():
+        for kind, src, got in jobs:
+            if kind == "t":
+                assert np.array_equal(got, oracle.transpose(src)), (tid, src.shape)
+            else:
+                A, B, C = src
+                m, k = A.shape
+                n = B.shape[1]
+                want = og.sgemm(m, n, k, 2.0, A.reshape(-1), k, B.reshape(-1), n,
+                                -1.0, C.reshape(-1), n)
+                assert np.array_equal(got, want.astype(np.float32)), (tid, m, n, k)
+    assert len(results) == 4
+
+
 def test_hip_graph_capture_and_replay():
     """Calls only enqueue kernels (no allocation, memset or synchronisation),
     so they can be captured into a HIP graph.  Every replay, with eager work
