@@ -284,11 +284,11 @@ FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix-core peak
 
 
 def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
-    """The tiled SGEMM with the padded transposed As store at the size its
-    page measures (M = N = K = 4096, C += A B, uniform [-1, 1) inputs):
-    the default kernel with its matrix-core roofline, the As-layout
-    ablation with one and two LDS buffers and with 256-row blocks, torch's
-    fp32 addmm for context,
+    """The tiled SGEMM with the transposed As store at the size its page
+    measures (M = N = K = 4096, C += A B, uniform [-1, 1) inputs): the
+    library's default kernel for that shape with its matrix-core roofline,
+    the As-layout ablation (unpadded, padded, swizzle) with one and two LDS
+    buffers and with 256-row blocks, torch's fp32 addmm for context,
     sampled parity against the oracle, and the oracle timed on a bounded
     sample."""
     import torch

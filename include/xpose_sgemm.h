@@ -69,7 +69,15 @@ extern "C" {
  * transposed store ("How Shared Memory Is Addressed", "The Fix Is One
  * Constant"). */
 typedef enum xpose_as_layout {
-  XPOSE_AS_AUTO = 0,     /* library default                                   */
+  XPOSE_AS_AUTO = 0,     /* library default: XPOSE_AS_PADDED with 128-row
+                            blocks; when no layout, k step, block height or
+                            second buffer is asked for and the shape is large
+                            and round (m a multiple of 256, n of 128,
+                            k >= 1024, and (m / 256) (n / 128) a multiple of
+                            512: whole rounds of two 512-thread workgroups
+                            on each of MI355X's 256 compute units),
+                            XPOSE_AS_SWIZZLE with 256-row blocks, measured
+                            2.5-4% faster there                               */
   XPOSE_AS_UNPADDED = 1, /* row stride 128 floats, a multiple of the bank
                             count: the store is (min(bk, 32) / 4)-way
                             conflicted on gfx950's 32-bank, 32-lane 4-byte
@@ -115,9 +123,10 @@ typedef struct xpose_sgemm_opts {
   int32_t group_m; /* block order: groups of group_m block rows, walked
                       block-column by block-column; 0 = default (8)          */
   int32_t flags;   /* XPOSE_SGEMM_*                                           */
-  int32_t tile_m;  /* rows of C per workgroup: 0 = default (128), 128 (4
-                      waves) or 256 (8 waves; k steps 16 and 32, one LDS
-                      buffer); blocks are 128 columns wide                  */
+  int32_t tile_m;  /* rows of C per workgroup: 0 = default (128, or 256
+                      under the rule of XPOSE_AS_AUTO), 128 (4 waves) or
+                      256 (8 waves; k steps 16 and 32, one LDS buffer);
+                      blocks are 128 columns wide                           */
 } xpose_sgemm_opts;
 
 /* What xpose_sgemm_plan reports about the kernel a call would launch. */

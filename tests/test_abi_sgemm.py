@@ -18,17 +18,54 @@ def plan(m=4096, n=4096, k=4096, a=A, lda=None, b=B, ldb=None, c=C, ldc=None,
 
 
 def test_default_plan():
-    rc, info = plan()
+    """The pages' padded store in 128 x 128 blocks; large round shapes
+    (4096^3: 512 blocks of 256 x 128, one full round) take the swizzled
+    layout in 256-row blocks."""
+    rc, info = plan(m=3072)
     assert rc == 0
     assert (info.layout, info.bk, info.as_stride) == (X.AS_PADDED, 16, 130)
     assert (info.tile_m, info.tile_n, info.threads) == (128, 128, 256)
-    assert info.tiles == 32 * 32 and info.vector_loads == 1
+    assert info.tiles == 24 * 32 and info.vector_loads == 1
     assert info.lds_bytes == 4 * (16 * 130 + 16 * 128)
     assert info.group_m == 8 and info.xcd_remap == 1 and info.stages == 1
     assert info.buffer_loads == 1
+    rc, info = plan()
+    assert rc == 0
+    assert (info.layout, info.bk, info.as_stride) == (X.AS_SWIZZLE, 16, 256)
+    assert (info.tile_m, info.tile_n, info.threads) == (256, 128, 512)
+    assert info.tiles == 16 * 32 and info.lds_bytes == 4 * (16 * 256 + 16 * 128)
     rc, info = plan(opts=X.make_sgemm_opts(flags=X.SGEMM_DOUBLE_BUFFER))
-    assert rc == 0 and info.stages == 2
+    assert rc == 0 and info.stages == 2 and info.layout == X.AS_PADDED
     assert info.lds_bytes == 2 * 4 * (16 * 130 + 16 * 128)
+
+
+@pytest.mark.parametrize("m, n, k, tall", [
+    (4096, 4096, 4096, True), (8192, 4096, 4096, True), (2048, 16384, 4096, True),
+    (16384, 16384, 2048, True), (4096, 4096, 1024, True),
+    (4096, 4096, 1023, False),       # k below the rule
+    (3072, 4096, 4096, False),       # 384 blocks: a partial round
+    (4096, 4100, 4096, False),       # n not a multiple of 128
+    (4224, 4096, 4096, False),       # m not a multiple of 256
+    (6144, 6144, 6144, False),       # 1152 blocks: 2.25 rounds
+    (0, 4096, 4096, False)])
+def test_default_tall_rule(m, n, k, tall):
+    rc, info = plan(m=m, n=n, k=k)
+    assert rc == 0
+    if m == 0:
+        return
+    assert (info.layout, info.tile_m) == ((X.AS_SWIZZLE, 256) if tall else (X.AS_PADDED, 128))
+
+
+def test_any_choice_turns_the_tall_rule_off():
+    for opts in (X.make_sgemm_opts(layout=X.AS_PADDED), X.make_sgemm_opts(bk=16),
+                 X.make_sgemm_opts(tile_m=128), X.make_sgemm_opts(flags=X.SGEMM_DOUBLE_BUFFER)):
+        rc, info = plan(opts=opts)
+        assert rc == 0 and info.tile_m == 128
+    # block order and load options keep it
+    for opts in (X.make_sgemm_opts(group_m=3), X.make_sgemm_opts(flags=X.SGEMM_NO_BUFFER_LOADS),
+                 X.make_sgemm_opts(flags=X.SGEMM_NO_XCD_REMAP)):
+        rc, info = plan(opts=opts)
+        assert rc == 0 and (info.layout, info.tile_m) == (X.AS_SWIZZLE, 256)
 
 
 @pytest.mark.parametrize("bk", (8, 16, 32, 64))
