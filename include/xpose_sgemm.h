@@ -144,6 +144,11 @@ typedef struct xpose_sgemm_info {
   int32_t stages;       /* LDS buffers per workgroup (1 or 2)                 */
   int32_t buffer_loads; /* 1: whole tiles are read with buffer loads          */
   int64_t tiles;        /* workgroups launched                                */
+  int32_t whole_matrix; /* 1: the kernel built for whole blocks only (no edge
+                           code), taken when m and n are multiples of the
+                           block, k of the k step, buffer loads are allowed,
+                           ldc <= 2^29 / tile_m and one LDS buffer is used;
+                           built for k step 16                               */
 } xpose_sgemm_info;
 
 /* C = alpha * A * B + beta * C with the default kernel. */

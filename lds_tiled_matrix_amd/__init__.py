@@ -95,7 +95,7 @@ class XposeSgemmInfo(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("vector_loads", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("buffer_loads", ctypes.c_int32),
-                ("tiles", ctypes.c_int64)]
+                ("tiles", ctypes.c_int64), ("whole_matrix", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -125,14 +125,22 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   const bool vec = !uses_ab || ((uintptr_t)a % 16 == 0 &&
                                 (uintptr_t)b % 16 == 0 && lda % 4 == 0 &&
                                 ldb % 4 == 0);
+  const bool buf_ok = buffers && vec && uses_ab &&
+                      lda <= max_buffer_lda(tile_m) && ldb <= kMaxBufferLdb;
+  // Every block, k step, load and C tail whole: the kernel without edge
+  // code, where one is built.
+  const bool whole = buf_ok && stages == 1 && m % tile_m == 0 &&
+                     n % kTileN == 0 && k % bk == 0 &&
+                     ldc <= ((int64_t)1 << 29) / tile_m;
   int count = 0;
   const xpose::SgemmKernel *table = xpose::sgemm_kernels(&count);
   const xpose::SgemmKernel *kern = nullptr;
-  for (int i = 0; i < count && !kern; ++i)
-    if (table[i].bk == bk && table[i].layout == layout &&
-        table[i].vec == vec && table[i].stages == stages &&
-        table[i].tile_m == tile_m)
-      kern = &table[i];
+  for (int pass = whole ? 0 : 1; pass < 2 && !kern; ++pass)
+    for (int i = 0; i < count && !kern; ++i)
+      if (table[i].bk == bk && table[i].layout == layout &&
+          table[i].vec == vec && table[i].stages == stages &&
+          table[i].tile_m == tile_m && table[i].whole == (pass == 0))
+        kern = &table[i];
   if (!kern) return XPOSE_ENOTILE;
   if (group_m > tiles_m) group_m = (int)tiles_m;
 
@@ -151,8 +159,7 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   g.group_m = (uint32_t)group_m;
   g.xcd_remap = remap ? 1 : 0;
   // Buffer-load byte offsets within one k step's tiles must fit in 31 bits.
-  g.buf_ok = buffers && vec && uses_ab && lda <= max_buffer_lda(tile_m) &&
-             ldb <= kMaxBufferLdb;
+  g.buf_ok = buf_ok;
   plan.kernel = kern;
   plan.tiles = tiles;
   return XPOSE_OK;
@@ -211,6 +218,7 @@ int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
   info->stages = kern.stages;
   info->buffer_loads = plan.args.buf_ok;
   info->tiles = plan.tiles;
+  info->whole_matrix = kern.whole ? 1 : 0;
   return rc;
 }
 

@@ -29,6 +29,10 @@ struct SgemmKernel {
   int stages;  // LDS buffers: 1 = two barriers per k step, 2 = one
   int tile_m;  // rows of C per workgroup (128 or 256; 128 columns)
   hipError_t (*launch)(const SgemmArgs &, uint32_t grid, hipStream_t);
+  // Built for matrices of whole blocks only: m and n multiples of the
+  // block, k of the k step, buffer loads and the one-descriptor C tail
+  // allowed.  No edge code at all.
+  bool whole = false;
 };
 
 // Every compiled SGEMM kernel; *count receives the table length.

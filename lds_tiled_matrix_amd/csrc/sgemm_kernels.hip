@@ -57,11 +57,16 @@ __device__ inline float *uniform(const float *p) {
 // barrier per step separates the writes of one buffer from the reads of
 // the other.  Either way the next step's global loads are issued before
 // this step's products and land in registers while the matrix cores run.
-template <int BK, int L, bool VEC, int STAGES, int BM = 128>
+//
+// WHOLE kernels serve calls whose every block is whole (the host checks m, n,
+// k, the pitches and alignments): the same loop and tail without the edge
+// code, which measured about 1% faster than keeping it in the kernel.
+template <int BK, int L, bool VEC, int STAGES, int BM = 128, bool WHOLE = false>
 __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(
     SgemmTile<BK, L, BM>::waves_per_simd(STAGES)))) void
 xpose_sgemm_kernel(SgemmArgs a) {
   using T = SgemmTile<BK, L, BM>;
+  static_assert(!WHOLE || (VEC && STAGES == 1), "whole-matrix kernels");
   __shared__ __attribute__((aligned(16))) float As[STAGES * T::AS_FLOATS];
   __shared__ __attribute__((aligned(16))) float Bs[STAGES * T::BS_FLOATS];
 
@@ -190,7 +195,9 @@ xpose_sgemm_kernel(SgemmArgs a) {
     else
       load_checked(k0);
   };
-  if (VEC && a.buf_ok && m0 + T::BM <= a.m && n0 + T::BN <= a.n) {
+  if constexpr (WHOLE) {
+    k_loop(load_whole);
+  } else if (VEC && a.buf_ok && m0 + T::BM <= a.m && n0 + T::BN <= a.n) {
     if (a.k % BK == 0)
       k_loop(load_whole);
     else
@@ -208,8 +215,8 @@ xpose_sgemm_kernel(SgemmArgs a) {
   // each lane's a single register, and all 32 C values of one 32-row half
   // are loaded before the first is used (one memory round trip per half
   // instead of one per element).
-  if (m0 + T::BM <= a.m && n0 + T::BN <= a.n &&
-      a.ldc <= ((int64_t)1 << 29) / T::BM) {
+  if (WHOLE || (m0 + T::BM <= a.m && n0 + T::BN <= a.n &&
+                a.ldc <= ((int64_t)1 << 29) / T::BM)) {
     const float *cb = uniform(a.c + m0 * a.ldc + n0);
     const __amdgpu_buffer_rsrc_t c_d = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(cb), 0,
@@ -242,6 +249,7 @@ xpose_sgemm_kernel(SgemmArgs a) {
     }
     return;
   }
+  if constexpr (!WHOLE) {
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -258,15 +266,16 @@ xpose_sgemm_kernel(SgemmArgs a) {
         *p = v;
       }
     }
+  }
 }
 
-template <int BK, int L, bool VEC, int STAGES, int BM>
+template <int BK, int L, bool VEC, int STAGES, int BM, bool WHOLE = false>
 hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
   SgemmArgs copy = a;
   void *args[] = {&copy};
   return hipLaunchKernel(
       reinterpret_cast<const void *>(
-          &xpose_sgemm_kernel<BK, L, VEC, STAGES, BM>),
+          &xpose_sgemm_kernel<BK, L, VEC, STAGES, BM, WHOLE>),
       dim3(grid), dim3(SgemmTile<BK, L, BM>::NT), args, 0, s);
 }
 
@@ -278,19 +287,29 @@ hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
   }
 #define XPOSE_SGEMM_L(BK, L, ST, BM)                                         \
   XPOSE_SGEMM(BK, L, true, ST, BM), XPOSE_SGEMM(BK, L, false, ST, BM)
+#define XPOSE_SGEMM_WHOLE(BK, L, BM)                                         \
+  SgemmKernel {                                                              \
+    BK, L, SgemmTile<BK, L, BM>::AS_STRIDE, SgemmTile<BK, L, BM>::LDS_BYTES,  \
+        SgemmTile<BK, L, BM>::NT, true, 1, BM,                               \
+        &launch_sgemm<BK, L, true, 1, BM, true>, true                        \
+  }
 #define XPOSE_SGEMM_BK(BK, ST, BM)                                           \
   XPOSE_SGEMM_L(BK, kAsUnpadded, ST, BM), XPOSE_SGEMM_L(BK, kAsPadded, ST, BM), \
       XPOSE_SGEMM_L(BK, kAsSwizzle, ST, BM)
 
 // 128-row blocks for every k step and buffer count; 256-row blocks (8
 // waves) for the k steps whose B tile covers every lane (16 and 32), one
-// LDS buffer.
+// LDS buffer; whole-matrix twins of the k-step-16 kernels.
 const SgemmKernel kSgemmKernels[] = {
     XPOSE_SGEMM_BK(8, 1, 128),  XPOSE_SGEMM_BK(16, 1, 128),
     XPOSE_SGEMM_BK(32, 1, 128), XPOSE_SGEMM_BK(64, 1, 128),
     XPOSE_SGEMM_BK(8, 2, 128),  XPOSE_SGEMM_BK(16, 2, 128),
     XPOSE_SGEMM_BK(32, 2, 128), XPOSE_SGEMM_BK(64, 2, 128),
-    XPOSE_SGEMM_BK(16, 1, 256), XPOSE_SGEMM_BK(32, 1, 256)};
+    XPOSE_SGEMM_BK(16, 1, 256), XPOSE_SGEMM_BK(32, 1, 256),
+    // whole-matrix twins of the k-step-16 kernels, every layout, both heights
+    XPOSE_SGEMM_WHOLE(16, kAsUnpadded, 128), XPOSE_SGEMM_WHOLE(16, kAsPadded, 128),
+    XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 128), XPOSE_SGEMM_WHOLE(16, kAsUnpadded, 256),
+    XPOSE_SGEMM_WHOLE(16, kAsPadded, 256), XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 256)};
 
 }  // namespace
 

@@ -183,3 +183,24 @@ def test_k_zero_needs_only_c():
     rc, info = plan(k=0, a=0, b=0, lda=1)
     assert rc == 0 and info.tiles == 1024
     assert plan(k=0, a=0, b=0, lda=1, c=0)[0] == X.XPOSE_EINVAL
+
+
+@pytest.mark.parametrize("kw, whole", [
+    (dict(), 1),                                   # 4096^3: tall swizzled blocks
+    (dict(m=3072), 1),                             # padded 128-row blocks
+    (dict(k=4100, lda=4100), 0),                   # k not a multiple of the k step
+    (dict(m=4100), 0),                             # ragged block rows
+    (dict(n=4100, ldb=4100, ldc=4100), 0),         # ragged block columns
+    (dict(lda=4097), 0),                           # 4-byte loads
+    (dict(a=A + 4), 0),                            # A not 16-byte aligned
+    (dict(m=256, ldc=(1 << 29) // 128 + 4), 0),    # C pitch past the tail's limit
+    (dict(opts=X.make_sgemm_opts(bk=32)), 0),      # built for k step 16 only
+    (dict(opts=X.make_sgemm_opts(flags=X.SGEMM_DOUBLE_BUFFER)), 0),
+    (dict(opts=X.make_sgemm_opts(flags=X.SGEMM_NO_BUFFER_LOADS)), 0),
+    (dict(opts=X.make_sgemm_opts(layout=X.AS_UNPADDED)), 1),
+    (dict(opts=X.make_sgemm_opts(layout=X.AS_PADDED, tile_m=256)), 1)])
+def test_whole_matrix_kernel_choice(kw, whole):
+    """The kernel without edge code serves a call only when every block, k
+    step, load and C tail is whole."""
+    rc, info = plan(**kw)
+    assert rc == 0 and info.whole_matrix == whole
