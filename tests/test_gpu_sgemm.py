@@ -188,6 +188,26 @@ def test_whole_blocks_with_ragged_k(bk, tile_m):
             check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(pad_a, 0, 3))
 
 
+@pytest.mark.parametrize("tile_m", (128, 256))
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
+def test_whole_matrix_kernels(layout, tile_m):
+    """The kernels without edge code (every block, k step, load and C tail
+    whole), with both beta paths and C pitch padding."""
+    opts = X.make_sgemm_opts(layout, 16, 0, 0, tile_m)
+    for idx, (m, n, k) in enumerate([(2 * tile_m, 384, 512), (tile_m, 128, 16),
+                                     (4 * tile_m, 256, 48)]):
+        rc, info = X.xpose_sgemm_plan(m, n, k, 1 << 40, k, 1 << 41, n, 1 << 42,
+                                      n + 3, opts)
+        assert rc == 0 and info.whole_matrix == 1
+        A = wl.small_int_f32((m, k), 1300 + idx)
+        B = wl.small_int_f32((k, n), 1400 + idx)
+        C = wl.small_int_f32((m, n), 1500 + idx)
+        check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(0, 0, 3))
+        Cn = np.full((m, n), np.nan, np.float32)
+        got = check_exact(A, B, Cn, 1.0, 0.0, opts=opts, pads=(0, 0, 3))
+        assert np.isfinite(got[region_mask(m, n, n + 3, got.size)]).all()
+
+
 def test_scalar_load_path_is_exact():
     """4-byte aligned (not 16-byte) operands and pitches that are not a
     multiple of 4 take the 4-byte loads."""
