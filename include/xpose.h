@@ -217,6 +217,20 @@ typedef struct xpose_copy_opts {
 int xpose_2d(void *out, const void *in, int64_t rows, int64_t cols,
              int64_t ld_in, int64_t ld_out, int32_t dtype, void *stream);
 
+/* xpose_2d with an explicit LDS layout, tile shape and launch knobs (opts
+ * may be NULL, which is exactly xpose_2d).  This is the per-call switch for
+ * the record "Shared memory and the bank conflict" asks for (section "What
+ * to record": the same tile with the 32-word row and with the 33-word row,
+ * the copy and the best naive kernel, timed the same way): opts->layout
+ * selects the unpadded row, the one-word pad, the swizzle or a naive kernel,
+ * opts->tile_rows / tile_cols the tile.  Arguments, layout, ownership and
+ * errors as xpose_2d, plus XPOSE_EINVAL for an invalid opts field and
+ * XPOSE_ENOTILE for a combination no kernel is built for.  Results are
+ * bit-identical for every choice. */
+int xpose_2d_ex(void *out, const void *in, int64_t rows, int64_t cols,
+                int64_t ld_in, int64_t ld_out, int32_t dtype,
+                const xpose_opts *opts, void *stream);
+
 /* Batched transpose: `batch` independent matrices, input matrix b starting
  * stride_in elements after matrix b-1, output matrix b stride_out elements
  * after output b-1.  Output matrices must not overlap each other:

@@ -6,7 +6,8 @@ kernels.  The library must have been built (``python lds_tiled_matrix_amd/build.
 importing this package without it raises ImportError rather than falling
 back to anything else.
 
-Low-level names mirror the C ABI (``xpose_2d``, ``xpose_batched``,
+Low-level names mirror the C ABI (``xpose_2d``, ``xpose_2d_ex``,
+``xpose_batched``,
 ``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``,
 and the tiled SGEMM's ``xpose_sgemm``, ``xpose_sgemm_ex``,
 ``xpose_sgemm_plan`` of ``include/xpose_sgemm.h``) and take raw device
@@ -48,7 +49,8 @@ SGEMM_NO_XCD_REMAP, SGEMM_DOUBLE_BUFFER, SGEMM_NO_BUFFER_LOADS = 1, 2, 4
 
 # Every exported entry point, in header order (include/xpose.h, then
 # include/xpose_sgemm.h).
-EXPORTS = ("xpose_2d", "xpose_batched", "xpose_batched_ex", "xpose_plan",
+EXPORTS = ("xpose_2d", "xpose_2d_ex", "xpose_batched", "xpose_batched_ex",
+           "xpose_plan",
            "xpose_copy", "xpose_copy_ex", "xpose_lds_probe",
            "xpose_last_hip_error", "xpose_strerror",
            "xpose_sgemm", "xpose_sgemm_ex", "xpose_sgemm_plan")
@@ -121,6 +123,7 @@ def _load() -> ctypes.CDLL:
     opts_p, info_p = ctypes.POINTER(XposeOpts), ctypes.POINTER(XposePlanInfo)
     sig = {
         "xpose_2d": [p, p, i64, i64, i64, i64, i32, p],
+        "xpose_2d_ex": [p, p, i64, i64, i64, i64, i32, opts_p, p],
         "xpose_batched": [p, p, i64, i64, i64, i64, i64, i64, i64, i32, p],
         "xpose_batched_ex": [p, p, i64, i64, i64, i64, i64, i64, i64, i32,
                              opts_p, p],
@@ -176,6 +179,13 @@ def make_opts(layout=LAYOUT_AUTO, tile=None, flags=0, cache=CACHE_AUTO,
 def xpose_2d(out: int, inp: int, rows: int, cols: int, ld_in: int,
              ld_out: int, dtype: int, stream: int = 0) -> int:
     return _lib.xpose_2d(out, inp, rows, cols, ld_in, ld_out, dtype, stream)
+
+
+def xpose_2d_ex(out: int, inp: int, rows: int, cols: int, ld_in: int,
+                ld_out: int, dtype: int, opts: XposeOpts | None = None,
+                stream: int = 0) -> int:
+    return _lib.xpose_2d_ex(out, inp, rows, cols, ld_in, ld_out, dtype,
+                            ctypes.byref(opts) if opts else None, stream)
 
 
 def xpose_batched(out: int, inp: int, batch: int, rows: int, cols: int,
@@ -278,6 +288,19 @@ def dtype_code(t) -> int:
     return table[t]
 
 
+def _require_device(*tensors) -> None:
+    """The library dereferences its pointers on the GPU only: every tensor
+    must live in device memory, all on one device.  Checked before anything
+    is launched, so a host tensor is a Python error, not a GPU fault."""
+    devs = set()
+    for t in tensors:
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"expected a CUDA tensor, got one on {t.device}")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
 def _stream_handle(stream) -> int:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -291,6 +314,7 @@ def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
     is contiguous.  Row pitches and the batch stride are taken from the
     tensor's strides.  Returns ``out`` (allocated contiguous if None)."""
     import torch
+    _require_device(x)
     if x.dim() not in (2, 3):
         raise ValueError("expected a 2-D or 3-D tensor")
     if x.stride(-1) != 1:
@@ -300,6 +324,7 @@ def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
     if out is None:
         shape = (cols, rows) if x.dim() == 2 else (batch, cols, rows)
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _require_device(x, out)
     if out.dtype != x.dtype or out.stride(-1) != 1:
         raise ValueError("out must match dtype and have a contiguous last dim")
     if tuple(out.shape[-2:]) != (cols, rows):
@@ -322,6 +347,7 @@ def transpose(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
 def copy(dst, src, stream=None):
     """Byte copy between two contiguous CUDA tensors of equal byte size, by
     the library's 128-bit copy kernel."""
+    _require_device(dst, src)
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("byte sizes differ")
@@ -359,6 +385,7 @@ def sgemm(a, b, c=None, *, alpha: float = 1.0, beta: float = 0.0,
     dimension is contiguous (pitches come from the row strides).  With c
     None, a new tensor is allocated and beta must be 0.  Returns c."""
     import torch
+    _require_device(a, b, *(() if c is None else (c,)))
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("expected 2-D tensors")
     m, k = a.shape

@@ -557,6 +557,13 @@ int xpose_2d(void *out, const void *in, int64_t rows, int64_t cols,
                           nullptr, stream);
 }
 
+int xpose_2d_ex(void *out, const void *in, int64_t rows, int64_t cols,
+                int64_t ld_in, int64_t ld_out, int32_t dtype,
+                const xpose_opts *opts, void *stream) {
+  return xpose_batched_ex(out, in, 1, rows, cols, ld_in, ld_out, 0, 0, dtype,
+                          opts, stream);
+}
+
 int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                int64_t cols, int64_t ld_in, int64_t ld_out, int64_t stride_in,
                int64_t stride_out, int32_t dtype, const xpose_opts *opts,

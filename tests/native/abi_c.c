@@ -63,6 +63,18 @@ int main(void) {
   plan("null", NULL, in, 1, 64, 64, 64, 64, XPOSE_F32, NULL);
   plan("alias", in, in, 1, 64, 64, 64, 64, XPOSE_F32, NULL);
   plan("dtype", out, in, 1, 64, 64, 64, 64, 9, NULL);
+  {
+    /* xpose_2d_ex rejects invalid calls on the host before any launch, and a
+     * zero-sized shape is a no-op; NULL opts is xpose_2d. */
+    xpose_opts bad;
+    memset(&bad, 0, sizeof bad);
+    bad.layout = 9;
+    printf("ex pitch %d\n", xpose_2d_ex(out, in, 64, 64, 63, 64, XPOSE_F32, NULL, NULL));
+    printf("ex alias %d\n", xpose_2d_ex(in, in, 64, 64, 64, 64, XPOSE_F32, &tr, NULL));
+    printf("ex layout %d\n", xpose_2d_ex(out, in, 64, 64, 64, 64, XPOSE_F32, &bad, NULL));
+    printf("ex dtype %d\n", xpose_2d_ex(out, in, 64, 64, 64, 64, 9, NULL, NULL));
+    printf("ex empty %d\n", xpose_2d_ex(NULL, NULL, 0, 64, 64, 0, XPOSE_F16, &tr, NULL));
+  }
   SIZE(xpose_sgemm_opts);
   OFF(xpose_sgemm_opts, bk); OFF(xpose_sgemm_opts, flags);
   OFF(xpose_sgemm_opts, tile_m);

@@ -128,6 +128,42 @@ def test_invalid_calls_rejected_by_entry_points_too():
     assert X.xpose_lds_probe(OUT, [0] * 64, 4, 0, 0) == X.XPOSE_EINVAL
 
 
+def test_2d_ex_validates_like_the_batched_call():
+    # xpose_2d_ex is xpose_batched_ex with batch 1: same host validation,
+    # including every opts field, before anything is launched.
+    assert X.xpose_2d_ex(OUT, IN, 64, 64, 63, 64, X.XPOSE_F32) == X.XPOSE_EINVAL
+    assert X.xpose_2d_ex(IN, IN, 64, 64, 64, 64, X.XPOSE_F32) == X.XPOSE_EALIAS
+    assert X.xpose_2d_ex(OUT, IN + 2, 64, 64, 64, 64, X.XPOSE_F32) == X.XPOSE_EALIGN
+    assert X.xpose_2d_ex(OUT, IN, 64, 64, 64, 64, 11) == X.XPOSE_EDTYPE
+    for bad in (X.make_opts(layout=9), X.make_opts(cache=7),
+                X.make_opts(flags=1 << 20), X.make_opts(order=5),
+                X.make_opts(flags=X.FLAG_ALIGN_OUT | X.FLAG_TR_READ)):
+        assert X.xpose_2d_ex(OUT, IN, 64, 64, 64, 64, X.XPOSE_F32,
+                             bad) == X.XPOSE_EINVAL
+        assert X.xpose_batched_ex(OUT, IN, 1, 64, 64, 64, 64, 0, 0,
+                                  X.XPOSE_F32, bad) == X.XPOSE_EINVAL
+    # An unbuilt tile shape is reported, not launched.
+    assert X.xpose_2d_ex(OUT, IN, 64, 64, 64, 64, X.XPOSE_F32,
+                         X.make_opts(tile=(48, 48))) == X.XPOSE_ENOTILE
+    assert X.xpose_2d_ex(0, 0, 0, 7, 7, 0, X.XPOSE_U8,
+                         X.make_opts(layout=X.LAYOUT_PAD1)) == X.XPOSE_OK
+
+
+def test_binding_rejects_host_tensors():
+    # The torch conveniences check where the tensors live before calling the
+    # library, so a host tensor never reaches a kernel.
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(8, 8)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        X.transpose(a)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        X.copy(torch.zeros(8, 8), a)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        X.sgemm(a, a)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        X.sgemm(a, a, torch.zeros(8, 8))
+
+
 def test_zero_sizes_are_noops_even_with_null_pointers():
     for b, r, c in ((0, 5, 5), (1, 0, 5), (1, 5, 0)):
         assert X.xpose_batched(0, 0, b, r, c, 5, 5, 25, 25, X.XPOSE_F32, 0) == 0

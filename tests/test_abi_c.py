@@ -87,6 +87,19 @@ def test_plans_match_binding(c_output):
     assert plans["c4tr"][1]["tr_read"] == "1"
 
 
+def test_2d_ex_from_c(c_output):
+    ex = dict(_entries(c_output, "ex"))
+    assert int(ex["pitch"]) == X.XPOSE_EINVAL
+    assert int(ex["alias"]) == X.XPOSE_EALIAS
+    assert int(ex["layout"]) == X.XPOSE_EINVAL
+    assert int(ex["dtype"]) == X.XPOSE_EDTYPE
+    assert int(ex["empty"]) == X.XPOSE_OK
+    out, inp = 0x100000000000, 0x200000000000
+    assert X.xpose_2d_ex(out, inp, 64, 64, 63, 64, X.XPOSE_F32) == X.XPOSE_EINVAL
+    assert X.xpose_2d_ex(out, inp, 64, 64, 64, 64, X.XPOSE_F32,
+                         X.make_opts(layout=9)) == X.XPOSE_EINVAL
+
+
 def test_strerror_matches_binding(c_output):
     for code, text in _entries(c_output, "strerror"):
         assert X.strerror(int(code)) == text

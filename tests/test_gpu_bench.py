@@ -18,10 +18,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def record():
-    say("bench.py --steps 3 --warmup 1 --no-cold --no-ablation")
+    say("bench.py --steps 3 --warmup 1 --no-ablation")
     out = subprocess.run(
         [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3",
-         "--warmup", "1", "--no-cold", "--no-ablation"],
+         "--warmup", "1", "--no-ablation"],
         capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert out.returncode == 0, out.stderr[-3000:]
     lines = [ln for ln in out.stdout.splitlines() if ln.strip()]
@@ -50,6 +50,20 @@ def test_roofline(record):
     assert 0 < rf["achieved"] and rf["frac"] == pytest.approx(
         rf["achieved"] / rf["peak"], abs=1e-3)
     assert rf["traffic"] is None or rf["traffic"] > 0
+    # achieved follows the average launch duration of the timed region
+    avg = record["timing"]["region_avg_us"]
+    assert rf["achieved"] == pytest.approx(
+        record["config"]["rw_bytes"] / (avg * 1e-6) / 1e9, rel=2e-3)
+
+
+def test_cold_roofline(record):
+    rc, cold = record["roofline_cold"], record["cold"]
+    assert rc["bound"] == "hbm" and rc["unit"] == "GB/s" and rc["peak"] == 8000.0
+    assert rc["achieved"] == cold["transpose"]["median_GBps"]
+    assert rc["copy"] == cold["copy"]["median_GBps"]
+    assert rc["frac"] == pytest.approx(rc["achieved"] / rc["peak"], abs=1e-3)
+    assert rc["frac_of_copy"] == pytest.approx(rc["achieved"] / rc["copy"],
+                                               abs=1e-3)
 
 
 def test_cpu_baseline_and_parity(record):

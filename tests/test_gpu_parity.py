@@ -162,6 +162,23 @@ def test_2d_entry_matches():
     check_case(2, 1, 300, 200, seed=6, entry="2d", label="2d")
 
 
+@pytest.mark.parametrize("layout", (X.LAYOUT_UNPADDED, X.LAYOUT_PAD1,
+                                    X.LAYOUT_SWIZZLE, X.LAYOUT_NAIVE_READ,
+                                    X.LAYOUT_NAIVE_WRITE))
+def test_2d_ex_entry_per_layout(layout):
+    """xpose_2d_ex: every layout of the pages' record (the 32-word row, the
+    one-word pad, the swizzle, the naive kernels), on a ragged shape with
+    padded pitches and on the pages' 32 x 32 tile, bit-exact."""
+    for s, seed in ((4, 21), (2, 22), (1, 23), (8, 24)):
+        check_case(s, 1, 300, 200, ld_in=203, ld_out=301, seed=seed + layout,
+                   entry="2d_ex", opts=X.make_opts(layout),
+                   label=f"2d_ex layout={layout}")
+    if layout <= X.LAYOUT_SWIZZLE:
+        check_case(4, 1, 256, 192, seed=25, entry="2d_ex",
+                   opts=X.make_opts(layout, (32, 32)),
+                   label=f"2d_ex 32x32 layout={layout}")
+
+
 @pytest.mark.parametrize("s", (2, 4))
 def test_special_float_bits(s):
     """NaN payloads, infinities, -0, subnormals move unchanged."""

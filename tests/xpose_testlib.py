@@ -70,6 +70,10 @@ def gpu_transpose(src_flat, s, batch, rows, cols, ld_in, ld_out, stride_in,
         assert batch == 1
         rc = X.xpose_2d(pout, pin, rows, cols, ld_in, ld_out,
                         DTYPE_OF_SIZE[s], sh)
+    elif entry == "2d_ex":
+        assert batch == 1
+        rc = X.xpose_2d_ex(pout, pin, rows, cols, ld_in, ld_out,
+                           DTYPE_OF_SIZE[s], opts, sh)
     elif opts is None:
         rc = X.xpose_batched(pout, pin, batch, rows, cols, ld_in, ld_out,
                              stride_in, stride_out, DTYPE_OF_SIZE[s], sh)
