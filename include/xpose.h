@@ -175,6 +175,11 @@ typedef struct xpose_opts {
                          walking many tiles with two LDS buffers so the
                          next tile's loads overlap the current tile's
                          stores (swizzled layout only)                      */
+  int32_t occupancy;  /* tile kernels: at most this many workgroups of the
+                         launch share one compute unit (1..64), enforced by
+                         reserving LDS that is never touched; 0 = the
+                         library default for the case; -1 = no cap.  Not
+                         combined with persistent (XPOSE_EINVAL)             */
 } xpose_opts;
 
 /* What xpose_plan reports about the kernel a call would launch. */
@@ -202,6 +207,8 @@ typedef struct xpose_plan_info {
   int32_t packed;      /* packed small-matrix kernel: matrices per workgroup
                           (tile_rows x tile_cols = one matrix, tiles =
                           workgroups); 0 = tile kernels                      */
+  int32_t occupancy;   /* resolved cap on workgroups per compute unit (0 =
+                          none: as many as registers and LDS allow)          */
 } xpose_plan_info;
 
 /* Knobs of the copy yardstick (zero-initialise for defaults). */

@@ -61,7 +61,8 @@ class XposeOpts(ctypes.Structure):
                 ("tile_cols", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("cache", ctypes.c_int32), ("group_rows", ctypes.c_int32),
                 ("group_cols", ctypes.c_int32), ("threads", ctypes.c_int32),
-                ("order", ctypes.c_int32), ("persistent", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("persistent", ctypes.c_int32),
+                ("occupancy", ctypes.c_int32)]
 
 
 class XposeCopyOpts(ctypes.Structure):
@@ -78,7 +79,8 @@ class XposePlanInfo(ctypes.Structure):
                 ("group_cols", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("persistent", ctypes.c_int32),
                 ("direct_lds", ctypes.c_int32), ("aligned_out", ctypes.c_int32),
-                ("tr_read", ctypes.c_int32), ("packed", ctypes.c_int32)]
+                ("tr_read", ctypes.c_int32), ("packed", ctypes.c_int32),
+                ("occupancy", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -168,10 +170,10 @@ def _check(code: int, what: str) -> int:
 
 def make_opts(layout=LAYOUT_AUTO, tile=None, flags=0, cache=CACHE_AUTO,
               group_rows=0, group_cols=0, threads=0, order=ORDER_AUTO,
-              persistent=0) -> XposeOpts:
+              persistent=0, occupancy=0) -> XposeOpts:
     tr, tc = tile if tile else (0, 0)
     return XposeOpts(layout, tr, tc, flags, cache, group_rows, group_cols,
-                     threads, order, persistent)
+                     threads, order, persistent, occupancy)
 
 
 # ----- C ABI, one to one -----------------------------------------------------

@@ -59,17 +59,29 @@ int elem_bytes_of(int32_t dtype) {
 //     elementwise or direct loads, persistent workgroups, a tile shape,
 //     workgroup size or cache policy without such a kernel) select the
 //     ordinary tiles with their own defaults instead.
-//   big: the call moves more than kBigCallBytes (read + write).  Then the
-//     256 MB memory-side cache cannot hold a useful part of the data across
-//     calls, every access goes to HBM, and the diagonal order (resident
-//     tiles spread over all row and column offsets) is fastest.  Below it,
-//     repeated calls partly hit that cache and small 32 x 32 tiles in compact
-//     super-tiles are fastest.
-// cache is an xpose_cache value; group_cols 0 means all tile columns.
+//   big: the call moves at least kBigCallBytes (read + write), twice the
+//     256 MB memory-side cache.  The diagonal order (resident tiles spread
+//     over all row and column offsets) is then the one that holds up when
+//     the bytes come from HBM: 8192^2 fp32 runs 5.9 TB/s cache-cold with
+//     it, 0.97 of the cold copy, against 5.0-5.1 TB/s (0.82) for compact
+//     32 x 32 super-tiles, which win only in back-to-back repeats of the
+//     same call (7.3 against 6.8 TB/s) because the memory-side cache then
+//     serves part of the bytes.  The diagonal order also runs best with few
+//     workgroups per compute unit: every resident workgroup streams its own
+//     set of rows on both sides, and HBM serves fewer, longer streams
+//     better.  Measured caps: 8192^2 fp32 with 128 x 128 tiles 0.97 of the
+//     cold copy at 1 workgroup per compute unit, 0.94 at 2 (no cap: LDS
+//     allows 2); 16384^2 fp16 with 128 x 64 tiles 0.89 at 3, 0.86 uncapped
+//     (8); 1-byte 0.84 at 4, 0.81-0.83 uncapped; 8-byte 32 x 32 0.86 at 4,
+//     0.84 uncapped.  Below 512 MiB, compact super-tiles hold up cold as
+//     well on most shapes (6144^2 fp32: 0.92 against 0.85).
+// cache is an xpose_cache value; group_cols 0 means all tile columns;
+// occupancy caps the workgroups per compute unit (0 = no cap).
 struct Default {
   int tile_rows, tile_cols, threads, layout, cache, group_rows, group_cols,
       xcd_remap, order;
   bool align_out = false;
+  int occupancy = 0;
 };
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
 constexpr int64_t kShortAlignRows = 256;
@@ -85,7 +97,10 @@ Default default_for(int s, bool out_row128, bool small, bool big,
       case 2:
         if (big) return {128, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
         return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
-      case 4: return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
+      // Tall super-tiles: the tile above each tile (whose last rows are its
+      // halo) ran just before on the same XCD, except at the top of a
+      // super-tile, 1 tile in 128 (1 in 16 with 16 x 16 super-tiles).
+      case 4: return {64, 64, 256, kSwz, kNT, 128, 4, 1, kSup, true};
       case 8: return {32, 32, 256, kSwz, kNT, 16, 16, 1, kSup, true};
       default: break;  // no line-aligned tiles for 1-byte elements
     }
@@ -101,14 +116,16 @@ Default default_for(int s, bool out_row128, bool small, bool big,
   switch (s) {
     case 4:
       if (small) return {128, 64, 256, kSwz, kNT, 8, 8, 0, kSup};
-      if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      if (big) return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 1};
       return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
     case 2:
-      if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 3};
       return {128, 64, 256, kSwz, kNT, 32, 8, 0, kSup};
-    case 1: return {128, 128, 256, kSwz, kNT, 16, 16, 1, kSup};
+    case 1:
+      if (big) return {128, 64, 128, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
+      return {128, 128, 256, kSwz, kNT, 16, 16, 1, kSup};
     default:
-      if (big) return {64, 64, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      if (big) return {32, 32, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
       return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
   }
 }
@@ -142,6 +159,7 @@ struct Plan {
   xpose::PackedArgs pk;
   const xpose::TileKernel *kernel;  // null for the naive kernels
   int persistent;                   // persistent workgroups per CU, 0 = none
+  int occupancy;                    // cap on workgroups per CU, 0 = none
   int naive;                        // 0, xpose::kNaiveRead or kNaiveWrite
   int elem_bytes;
   xpose::TileArgs args;
@@ -170,7 +188,8 @@ int plan_packed(const void *out, const void *in, int64_t batch, int64_t rows,
   const bool want = flags & XPOSE_FLAG_PACKED;
   const bool knobs =
       opts && (opts->layout || opts->tile_rows || opts->tile_cols ||
-               opts->threads || opts->persistent || opts->order ||
+               opts->threads || opts->persistent || opts->occupancy ||
+               opts->order ||
                opts->group_rows || opts->group_cols ||
                (flags & ~(XPOSE_FLAG_XCD_REMAP | XPOSE_FLAG_NO_XCD_REMAP |
                           XPOSE_FLAG_PACKED)));
@@ -265,7 +284,9 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                opts->cache > XPOSE_CACHE_NT_ALL || opts->group_rows < 0 ||
                opts->group_cols < 0 || opts->threads < 0 ||
                opts->order < XPOSE_ORDER_AUTO || opts->persistent < 0 ||
-               opts->persistent > 64 ||
+               opts->persistent > 64 || opts->occupancy < -1 ||
+               opts->occupancy > 64 ||
+               (opts->occupancy && opts->persistent) ||
                opts->order > XPOSE_ORDER_DIAGONAL ||
                opts->tile_rows < 0 || opts->tile_cols < 0))
     return XPOSE_EINVAL;
@@ -310,7 +331,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   const bool small = batch > 1 && rows * cols * s <= kSmallMatrixBytes;
   int64_t call_bytes;
   const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
-                   call_bytes > kBigCallBytes;
+                   call_bytes >= kBigCallBytes;
   const bool direct = opts && (opts->flags & XPOSE_FLAG_DIRECT_LDS);
   const bool tr_read = opts && (opts->flags & XPOSE_FLAG_TR_READ);
   // Line-aligned output tiles are the default where they apply, unless a
@@ -425,8 +446,15 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (opts && (opts->flags & XPOSE_FLAG_XCD_REMAP)) xcd = 1;
   if (opts && (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) xcd = 0;
 
+  // The default cap belongs to the default tile: it applies when the
+  // resolved kernel has the default shape and workgroup size.
+  int occupancy = (opts && opts->occupancy) ? opts->occupancy : 0;
+  if (!occupancy && !persistent && tr == d.tile_rows && tc == d.tile_cols &&
+      k->threads == d.threads)
+    occupancy = d.occupancy;
   plan->kernel = k;
   plan->persistent = persistent;
+  plan->occupancy = occupancy > 0 ? occupancy : 0;
   plan->batch = batch;
   plan->tiles_per_matrix = tiles;
   plan->batch_per_launch = 0x7fffffff / tiles;
@@ -472,6 +500,52 @@ hipError_t compute_units(int *out) {
   return hipSuccess;
 }
 
+// LDS bytes per compute unit and per workgroup of the current device,
+// looked up once per device.
+hipError_t device_lds(int *per_cu, int *per_block) {
+  static std::atomic<int> cache_cu[64], cache_block[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache_cu[dev].load(std::memory_order_relaxed);
+    const int b = cache_block[dev].load(std::memory_order_relaxed);
+    if (c > 0 && b > 0) {
+      *per_cu = c;
+      *per_block = b;
+      return hipSuccess;
+    }
+  }
+  int c = 0, b = 0;
+  e = hipDeviceGetAttribute(
+      &c, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  if (c <= 0 || b <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64) {
+    cache_cu[dev].store(c, std::memory_order_relaxed);
+    cache_block[dev].store(b, std::memory_order_relaxed);
+  }
+  *per_cu = c;
+  *per_block = b;
+  return hipSuccess;
+}
+
+// Dynamic LDS to reserve so that at most `occupancy` workgroups of a kernel
+// with `static_lds` bytes of its own share one compute unit: each workgroup
+// then holds floor(per_cu / occupancy) bytes, rounded down to 1 KiB (so
+// `occupancy` of them fit and one more does not, for occupancy <= 64), but
+// never more than a workgroup may hold.  0 where the kernel's own LDS
+// already caps it that low.
+uint32_t reserve_lds(int occupancy, int static_lds, int per_cu,
+                     int per_block) {
+  if (occupancy <= 0) return 0;
+  int64_t total = (int64_t)per_cu / occupancy / 1024 * 1024;
+  if (total > per_block) total = per_block;
+  return total > static_lds ? (uint32_t)(total - static_lds) : 0;
+}
+
 int run_plan(Plan &plan, void *stream) {
   if (plan.empty) return XPOSE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -496,6 +570,14 @@ int run_plan(Plan &plan, void *stream) {
                             plan.naive == XPOSE_LAYOUT_NAIVE_READ, st);
     return e == hipSuccess ? XPOSE_OK : hip_fail(e);
   }
+  uint32_t lds_extra = 0;
+  if (plan.occupancy) {
+    int per_cu = 0, per_block = 0;
+    const hipError_t e = device_lds(&per_cu, &per_block);
+    if (e != hipSuccess) return hip_fail(e);
+    lds_extra = reserve_lds(plan.occupancy, plan.kernel->lds_bytes, per_cu,
+                            per_block);
+  }
   for (int64_t b0 = 0; b0 < plan.batch; b0 += plan.batch_per_launch) {
     int64_t nb = plan.batch - b0;
     if (nb > plan.batch_per_launch) nb = plan.batch_per_launch;
@@ -519,7 +601,7 @@ int run_plan(Plan &plan, void *stream) {
       grid = (grid + 7) / 8 * 8;
       e = plan.kernel->launch_persistent(a, ntiles, (uint32_t)grid, st);
     } else {
-      e = plan.kernel->launch(a, ntiles, st);
+      e = plan.kernel->launch(a, ntiles, lds_extra, st);
     }
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -613,6 +695,7 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->aligned_out = plan.kernel->aligned_out ? 1 : 0;
       info->tr_read = plan.kernel->tr_read ? 1 : 0;
       info->xcd_remap = plan.args.xcd_remap;
+      info->occupancy = plan.occupancy;
     }
   }
   return rc;

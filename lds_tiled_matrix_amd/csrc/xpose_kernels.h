@@ -83,8 +83,11 @@ __host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
 // One compiled tile kernel.
 struct TileKernel {
   int elem_bytes, tile_rows, tile_cols, threads, layout, cache, lds_bytes;
-  // One workgroup per tile: grid = tiles.
-  hipError_t (*launch)(const TileArgs &, uint32_t grid, hipStream_t);
+  // One workgroup per tile: grid = tiles.  lds_extra bytes of dynamic LDS
+  // are reserved per workgroup (never touched): a cap on the workgroups that
+  // share one compute unit.
+  hipError_t (*launch)(const TileArgs &, uint32_t grid, uint32_t lds_extra,
+                       hipStream_t);
   // Persistent, double-buffered variant (null if not built): `grid`
   // workgroups (a multiple of 8) walk `ntiles` tiles; LDS use is twice
   // lds_bytes.

@@ -429,8 +429,12 @@ __global__ __launch_bounds__(NT) void xpose_tile_persistent_kernel(
   }
 }
 
+// lds_extra: bytes of dynamic LDS reserved per workgroup and never touched.
+// It only raises the workgroup's LDS footprint, which caps how many
+// workgroups of the launch share one compute unit.
 template <int S, int TR, int TC, int NT, int L, int CP, bool DIRECT = false>
-hipError_t launch_tile(const TileArgs &a, uint32_t grid, hipStream_t stream) {
+hipError_t launch_tile(const TileArgs &a, uint32_t grid, uint32_t lds_extra,
+                       hipStream_t stream) {
   TileArgs copy = a;
   void *args[] = {&copy};
   // hipLaunchKernel reports this launch's own status; the sticky
@@ -438,7 +442,7 @@ hipError_t launch_tile(const TileArgs &a, uint32_t grid, hipStream_t stream) {
   return hipLaunchKernel(
       reinterpret_cast<const void *>(
           &xpose_tile_kernel<S, TR, TC, NT, L, CP, DIRECT>),
-      dim3(grid), dim3(NT), args, 0, stream);
+      dim3(grid), dim3(NT), args, lds_extra, stream);
 }
 
 template <int S, int TR, int TC, int NT, int L, int CP>
@@ -565,12 +569,13 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
 }
 
 template <int S, int TR, int TC, int NT, int CP>
-hipError_t launch_shift(const TileArgs &a, uint32_t grid, hipStream_t stream) {
+hipError_t launch_shift(const TileArgs &a, uint32_t grid, uint32_t lds_extra,
+                        hipStream_t stream) {
   TileArgs copy = a;
   void *args[] = {&copy};
   return hipLaunchKernel(
       reinterpret_cast<const void *>(&xpose_shift_kernel<S, TR, TC, NT, CP>),
-      dim3(grid), dim3(NT), args, 0, stream);
+      dim3(grid), dim3(NT), args, lds_extra, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -724,12 +729,13 @@ __global__ __launch_bounds__(NT) void xpose_tr_kernel(TileArgs a) {
 }
 
 template <int S, int TR, int TC, int NT, int CP, bool DIRECT>
-hipError_t launch_tr(const TileArgs &a, uint32_t grid, hipStream_t stream) {
+hipError_t launch_tr(const TileArgs &a, uint32_t grid, uint32_t lds_extra,
+                     hipStream_t stream) {
   TileArgs copy = a;
   void *args[] = {&copy};
   return hipLaunchKernel(
       reinterpret_cast<const void *>(&xpose_tr_kernel<S, TR, TC, NT, CP, DIRECT>),
-      dim3(grid), dim3(NT), args, 0, stream);
+      dim3(grid), dim3(NT), args, lds_extra, stream);
 }
 
 #define XPOSE_TR(S, TR, TC, NT, CP, D)                                      \

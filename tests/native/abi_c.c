@@ -29,20 +29,22 @@ static void plan(const char *tag, void *out, const void *in, int64_t batch,
   if (rc == XPOSE_OK)
     printf(" layout=%d tile_rows=%d tile_cols=%d threads=%d lds_bytes=%d "
            "vector_path=%d tiles=%lld launches=%d cache=%d aligned_out=%d "
-           "tr_read=%d",
+           "tr_read=%d occupancy=%d",
            info.layout, info.tile_rows, info.tile_cols, info.threads,
            info.lds_bytes, info.vector_path, (long long)info.tiles,
-           info.launches, info.cache, info.aligned_out, info.tr_read);
+           info.launches, info.cache, info.aligned_out, info.tr_read,
+           info.occupancy);
   printf("\n");
 }
 
 int main(void) {
   SIZE(xpose_opts);
   OFF(xpose_opts, layout); OFF(xpose_opts, flags); OFF(xpose_opts, threads);
-  OFF(xpose_opts, persistent);
+  OFF(xpose_opts, persistent); OFF(xpose_opts, occupancy);
   SIZE(xpose_plan_info);
   OFF(xpose_plan_info, vector_path); OFF(xpose_plan_info, tiles);
   OFF(xpose_plan_info, launches); OFF(xpose_plan_info, tr_read);
+  OFF(xpose_plan_info, occupancy);
   SIZE(xpose_copy_opts);
   OFF(xpose_copy_opts, cache);
   CONST(XPOSE_F32); CONST(XPOSE_F16); CONST(XPOSE_BF16); CONST(XPOSE_U8);

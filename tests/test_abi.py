@@ -56,15 +56,42 @@ def plan(out=OUT, inp=IN, batch=1, rows=64, cols=64, ld_in=None, ld_out=None,
 
 
 def test_valid_plan_defaults():
+    # 8192^2 fp32 (512 MiB read + write): 128 x 128 tiles in diagonal order,
+    # one workgroup per compute unit
     rc, info = plan(rows=8192, cols=8192)
     assert rc == X.XPOSE_OK
+    assert (info.tile_rows, info.tile_cols) == (128, 128)
+    assert info.layout == X.LAYOUT_SWIZZLE and info.order == X.ORDER_DIAGONAL
+    assert info.cache == X.CACHE_NT_STORE and info.xcd_remap == 0
+    assert info.occupancy == 1
+    assert info.vector_path == 1 and info.tiles == 64 * 64
+    assert info.launches == 1 and info.threads == 256
+    assert info.lds_bytes == 128 * 128 * 4
+    # 4096^2 fp32: 32 x 32 tiles in 8 x 32 super-tiles, per-XCD ranges
+    rc, info = plan(rows=4096, cols=4096)
+    assert rc == X.XPOSE_OK
     assert (info.tile_rows, info.tile_cols) == (32, 32)
-    assert info.layout == X.LAYOUT_SWIZZLE
     assert info.cache == X.CACHE_NT_STORE and info.xcd_remap == 1
     assert (info.group_rows, info.group_cols) == (8, 32)
-    assert info.vector_path == 1 and info.tiles == 256 * 256
-    assert info.launches == 1 and info.threads == 256
+    assert info.tiles == 128 * 128 and info.occupancy == 0
     assert info.lds_bytes == 32 * 32 * 4
+
+
+def test_occupancy_option():
+    rc, info = plan(rows=4096, cols=4096, opts=X.make_opts(occupancy=3))
+    assert rc == 0 and info.occupancy == 3
+    # -1: no cap, even where the default has one
+    rc, info = plan(rows=8192, cols=8192, opts=X.make_opts(occupancy=-1))
+    assert rc == 0 and info.occupancy == 0 and info.tile_rows == 128
+    # the default cap belongs to the default tile
+    rc, info = plan(rows=8192, cols=8192, opts=X.make_opts(tile=(64, 64)))
+    assert rc == 0 and info.occupancy == 0
+    for bad in (-2, 65):
+        assert plan(opts=X.make_opts(occupancy=bad))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.make_opts(occupancy=2, persistent=2))[0] == X.XPOSE_EINVAL
+    # naive kernels have no LDS to reserve: the cap is not reported
+    rc, info = plan(opts=X.make_opts(layout=X.LAYOUT_NAIVE_READ, occupancy=2))
+    assert rc == 0 and info.occupancy == 0
 
 
 def test_ragged_and_batched_tile_counts():
@@ -78,7 +105,7 @@ def test_ragged_and_batched_tile_counts():
     rc, info = plan(rows=12288, cols=6789, ld_out=12289)
     assert rc == 0 and info.aligned_out == 1 and info.tiles == 193 * 107
     rc, info = plan(rows=12288, cols=6789)
-    assert rc == 0 and info.aligned_out == 0 and info.tiles == 96 * 107
+    assert rc == 0 and info.aligned_out == 0 and info.tiles == 96 * 54
     # A batch of small matrices: taller tiles, small super-tiles.
     rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
                     stride_out=1024 * 2048)
@@ -240,15 +267,25 @@ def test_one_hip_runtime_per_process():
 
 
 def test_footprint_rules():
-    # Over 512 MiB moved per call: the diagonal tile order.
+    # At least 512 MiB moved per call: the diagonal tile order with a cap on
+    # the workgroups per compute unit.
     rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F16)
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
     assert (info.tile_rows, info.tile_cols) == (128, 64) and info.xcd_remap == 0
+    assert info.occupancy == 3
     rc, info = plan(rows=16384, cols=8192)
-    assert rc == 0 and info.order == X.ORDER_DIAGONAL
-    # 8192^2 fp32 moves exactly 512 MiB: compact super-tiles.
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 1
+    # 8192^2 fp32 moves exactly 512 MiB: big.
     rc, info = plan(rows=8192, cols=8192)
-    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert (info.tile_rows, info.tile_cols) == (128, 128)
+    # 1-byte elements: 128 x 64 tiles of 128 threads, at most 4 per CU.
+    rc, info = plan(rows=32768, cols=16384, dtype=X.XPOSE_U8)
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 4
+    assert (info.tile_rows, info.tile_cols, info.threads) == (128, 64, 128)
+    # Just under 512 MiB: compact super-tiles, no cap.
+    rc, info = plan(rows=8192, cols=8191, ld_in=8191)
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES and info.occupancy == 0
     # A batch of small matrices keeps super-tiles even when the call is big.
     rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
                     stride_out=1024 * 2048)
@@ -379,10 +416,12 @@ def test_auto_cache_takes_a_built_policy():
 
 
 def test_big_f64_default_is_diagonal():
-    # more than 512 MiB read + write: 64 x 64 tiles in diagonal order
+    # at least 512 MiB read + write: 32 x 32 tiles in diagonal order, at most
+    # 4 workgroups per compute unit
     rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F64)
-    assert rc == 0 and (info.tile_rows, info.tile_cols) == (64, 64)
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.order == X.ORDER_DIAGONAL and info.cache == X.CACHE_NT_STORE
+    assert info.occupancy == 4
     rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)
     assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.order == X.ORDER_SUPER_TILES

@@ -30,8 +30,9 @@ def random_opts(rng, s):
         order = rng.choice((0, 1, 2))
         gr, gc = rng.choice(((0, 0), (1, 0), (3, 5), (8, 32), (1000, 2)))
         persistent = rng.choice((0, 0, 0, 1, 2))
+        occupancy = 0 if persistent else rng.choice((0, 0, 0, 1, 2, 3, -1))
         opts = X.make_opts(layout, tile, flags, cache, gr, gc, 0, order,
-                           persistent)
+                           persistent, occupancy)
         rc, _ = X.xpose_plan(0x100000, 0x40000000, 1, 64, 64, 64, 64, 0, 0,
                              DTYPE_OF_SIZE[s], opts)
         if rc == 0:
@@ -129,8 +130,10 @@ def campaign_opts(rng, s):
             cands.append(X.make_opts(X.LAYOUT_SWIZZLE, rng.choice(SHIFT_TILES[s] + (None,)),
                                      X.FLAG_ALIGN_OUT | rng.choice((0, 2, 4)),
                                      rng.choice((0, 1, 2)),
-                                     *rng.choice(((0, 0), (1, 0), (3, 5), (16, 16))), 0,
-                                     rng.choice((0, 1, 2))))
+                                     *rng.choice(((0, 0), (1, 0), (3, 5), (16, 16),
+                                                  (128, 4))), 0,
+                                     rng.choice((0, 1, 2)), 0,
+                                     rng.choice((0, 0, 2, 4))))
     for o in cands:
         if X.xpose_plan(0x100000, 0x40000000, 1, 64, 64, 64, 64, 0, 0,
                         DTYPE_OF_SIZE[s], o)[0] == 0:

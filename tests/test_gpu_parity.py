@@ -179,6 +179,27 @@ def test_2d_ex_entry_per_layout(layout):
                    label=f"2d_ex 32x32 layout={layout}")
 
 
+@pytest.mark.parametrize("s", (1, 2, 4, 8))
+def test_occupancy_caps(s):
+    """Reserved LDS caps the workgroups per compute unit; results are the
+    same for every cap, on the ordinary, line-aligned and transpose-read
+    tiles, with diagonal and super-tile orders."""
+    fam = [(None, 0), (None, X.FLAG_NO_ALIGN_OUT)]
+    if s in (2, 4, 8):
+        fam.append((None, X.FLAG_ALIGN_OUT))
+    if s in (1, 2):
+        fam.append((None, X.FLAG_TR_READ))
+    for occ in (1, 2, 3, -1):
+        for tile, fl in fam:
+            for order in (X.ORDER_DIAGONAL, X.ORDER_SUPER_TILES):
+                o = X.make_opts(X.LAYOUT_SWIZZLE, tile, fl, X.CACHE_AUTO, 0, 0,
+                                0, order, 0, occ)
+                check_case(s, 1, 515, 333, ld_out=517, seed=40 + occ,
+                           opts=o, label=f"occupancy {occ} flags {fl}")
+                check_case(s, 2, 256, 384, seed=50 + occ, opts=o,
+                           label=f"occupancy {occ} flags {fl} batch")
+
+
 @pytest.mark.parametrize("s", (2, 4))
 def test_special_float_bits(s):
     """NaN payloads, infinities, -0, subnormals move unchanged."""
