@@ -102,8 +102,11 @@ typedef enum xpose_cache {
 typedef enum xpose_order {
   XPOSE_ORDER_AUTO = 0,        /* library default                          */
   XPOSE_ORDER_SUPER_TILES = 1, /* group_rows x group_cols super-tiles      */
-  XPOSE_ORDER_DIAGONAL = 2     /* consecutive workgroups step diagonally:
+  XPOSE_ORDER_DIAGONAL = 2,    /* consecutive workgroups step diagonally:
                                   tile row g mod R, column (g/R + row) mod C */
+  XPOSE_ORDER_COLUMN_BANDS = 3 /* bands of group_cols tile columns, left to
+                                  right; inside a band tile rows top to
+                                  bottom, each row's tiles left to right    */
 } xpose_order;
 
 /* Option flags for xpose_batched_ex. */

@@ -124,9 +124,10 @@ typedef struct xpose_sgemm_opts {
                       block-column by block-column; 0 = default (8)          */
   int32_t flags;   /* XPOSE_SGEMM_*                                           */
   int32_t tile_m;  /* rows of C per workgroup: 0 = default (128, or 256
-                      under the rule of XPOSE_AS_AUTO), 128 (4 waves) or
-                      256 (8 waves; k steps 16 and 32, one LDS buffer);
-                      blocks are 128 columns wide                           */
+                      or 64 under the rule of XPOSE_AS_AUTO), 64 (2 waves;
+                      k step 16, one LDS buffer), 128 (4 waves) or 256 (8
+                      waves; k steps 16 and 32, one LDS buffer); blocks are
+                      128 columns wide                                       */
 } xpose_sgemm_opts;
 
 /* What xpose_sgemm_plan reports about the kernel a call would launch. */
@@ -149,6 +150,11 @@ typedef struct xpose_sgemm_info {
                            block, k of the k step, buffer loads are allowed,
                            ldc <= 2^29 / tile_m and one LDS buffer is used;
                            built for k step 16                               */
+  int32_t edge_buffer_loads; /* 1: edge blocks and a ragged last k step read
+                           with buffer loads too, their descriptors clipped
+                           to the matrix (buffer loads allowed, k and n
+                           multiples of 4); 0: those take bounds-checked
+                           global loads                                      */
 } xpose_sgemm_info;
 
 /* C = alpha * A * B + beta * C with the default kernel. */

@@ -38,7 +38,7 @@ FLAG_DIRECT_LDS, FLAG_ALIGN_OUT, FLAG_NO_ALIGN_OUT = 8, 16, 32
 FLAG_TR_READ = 64
 FLAG_PACKED, FLAG_NO_PACKED = 128, 256
 CACHE_AUTO, CACHE_DEFAULT, CACHE_NT_STORE, CACHE_NT_ALL = 0, 1, 2, 3
-ORDER_AUTO, ORDER_SUPER_TILES, ORDER_DIAGONAL = 0, 1, 2
+ORDER_AUTO, ORDER_SUPER_TILES, ORDER_DIAGONAL, ORDER_COLUMN_BANDS = 0, 1, 2, 3
 CACHE_NAMES = {CACHE_DEFAULT: "default", CACHE_NT_STORE: "nt_store",
                CACHE_NT_ALL: "nt_all"}
 
@@ -99,7 +99,8 @@ class XposeSgemmInfo(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("vector_loads", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("buffer_loads", ctypes.c_int32),
-                ("tiles", ctypes.c_int64), ("whole_matrix", ctypes.c_int32)]
+                ("tiles", ctypes.c_int64), ("whole_matrix", ctypes.c_int32),
+                ("edge_buffer_loads", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -74,7 +74,8 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
         opts->bk != 64)
       return XPOSE_EINVAL;
     if (opts->group_m < 0) return XPOSE_EINVAL;
-    if (opts->tile_m != 0 && opts->tile_m != 128 && opts->tile_m != 256)
+    if (opts->tile_m != 0 && opts->tile_m != 64 && opts->tile_m != 128 &&
+        opts->tile_m != 256)
       return XPOSE_EINVAL;
     if (opts->flags & ~(XPOSE_SGEMM_NO_XCD_REMAP | XPOSE_SGEMM_DOUBLE_BUFFER |
                         XPOSE_SGEMM_NO_BUFFER_LOADS))
@@ -160,6 +161,7 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   g.xcd_remap = remap ? 1 : 0;
   // Buffer-load byte offsets within one k step's tiles must fit in 31 bits.
   g.buf_ok = buf_ok;
+  g.edge_buf = buf_ok && k % 4 == 0 && n % 4 == 0;
   plan.kernel = kern;
   plan.tiles = tiles;
   return XPOSE_OK;
@@ -219,6 +221,7 @@ int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
   info->buffer_loads = plan.args.buf_ok;
   info->tiles = plan.tiles;
   info->whole_matrix = kern.whole ? 1 : 0;
+  info->edge_buffer_loads = kern.vec && plan.args.edge_buf ? 1 : 0;
   return rc;
 }
 

@@ -21,6 +21,10 @@ struct SgemmArgs {
   // and 32-bit lane offsets); needs 16-byte tile loads and 128 * lda and
   // 32 * ldb floats to fit in a 31-bit byte offset
   int32_t buf_ok;
+  // 1: edge blocks and ragged last k steps also use buffer loads, with
+  // descriptor extents clipped to the matrix (needs buf_ok, and k and n
+  // multiples of 4 so no 16-byte vector straddles an extent's end)
+  int32_t edge_buf;
 };
 
 struct SgemmKernel {

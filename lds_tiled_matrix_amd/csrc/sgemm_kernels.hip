@@ -187,6 +187,49 @@ xpose_sgemm_kernel(SgemmArgs a) {
       }
     }
   };
+  // Every block, whole or at an edge, where the host set edge_buf (buffer
+  // loads allowed, k and n multiples of 4): the same buffer loads with each
+  // descriptor's extent clipped to the matrix (for whole blocks and steps
+  // the clip is the tile itself).  A
+  // load past the extent returns zero without touching memory: A's rows at
+  // or past m and the last valid row's columns at or past k, B's rows at or
+  // past k and the last valid row's columns at or past n.  With k and n
+  // multiples of 4 no 16-byte vector straddles an extent's end.  A's columns
+  // at or past k in the other rows read the next row or pitch padding
+  // (inside A), and are zeroed after the load, since padding may hold NaN
+  // and B's zero rows would not cancel it.  B's columns at or past n and
+  // A's rows past m only reach C entries that are never stored.
+  const int rows_a = a.m - m0 < T::BM ? (int)(a.m - m0) : T::BM;
+  const int cols_b = a.n - n0 < T::BN ? (int)(a.n - n0) : T::BN;
+  auto load_clipped = [&](int64_t k0) __attribute__((always_inline)) {
+    const int kk = a.k - k0 < BK ? (int)(a.k - k0) : BK;
+    const float *ab = uniform(a.a + m0 * a.lda + k0);
+    const float *bb = uniform(a.b + k0 * a.ldb + n0);
+    const __amdgpu_buffer_rsrc_t ra_d = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(ab), 0, (int)(((rows_a - 1) * a.lda + kk) * 4),
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb_d = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(bb), 0, (int)(((kk - 1) * a.ldb + cols_b) * 4),
+        kBufferWord3);
+#pragma unroll
+    for (int p = 0; p < T::A_PASSES; ++p) {
+      ra[p] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     ra_d, (int)((T::a_row(t, p) * a.lda + T::a_col(t, p)) * 4),
+                     0, 0));
+      if (kk < BK) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (T::a_col(t, p) + e >= kk) ra[p][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < T::B_PASSES; ++p)
+      rb[p] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rb_d, (int)((T::b_row(t, p) * a.ldb + T::b_col(t)) * 4),
+                     0, 0));
+  };
   // Whole blocks with a ragged k take buffer loads for every whole k step
   // and checked loads for the last, partial one.
   auto load_ragged_k = [&](int64_t k0) __attribute__((always_inline)) {
@@ -197,6 +240,8 @@ xpose_sgemm_kernel(SgemmArgs a) {
   };
   if constexpr (WHOLE) {
     k_loop(load_whole);
+  } else if (VEC && a.edge_buf) {
+    k_loop(load_clipped);
   } else if (VEC && a.buf_ok && m0 + T::BM <= a.m && n0 + T::BN <= a.n) {
     if (a.k % BK == 0)
       k_loop(load_whole);
@@ -299,17 +344,22 @@ hipError_t launch_sgemm(const SgemmArgs &a, uint32_t grid, hipStream_t s) {
 
 // 128-row blocks for every k step and buffer count; 256-row blocks (8
 // waves) for the k steps whose B tile covers every lane (16 and 32), one
-// LDS buffer; whole-matrix twins of the k-step-16 kernels.
+// LDS buffer; 64-row blocks (2 waves: finer grids where 128-row blocks
+// leave compute units idle) for k step 16, one LDS buffer; whole-matrix
+// twins of the k-step-16 kernels.
 const SgemmKernel kSgemmKernels[] = {
     XPOSE_SGEMM_BK(8, 1, 128),  XPOSE_SGEMM_BK(16, 1, 128),
     XPOSE_SGEMM_BK(32, 1, 128), XPOSE_SGEMM_BK(64, 1, 128),
     XPOSE_SGEMM_BK(8, 2, 128),  XPOSE_SGEMM_BK(16, 2, 128),
     XPOSE_SGEMM_BK(32, 2, 128), XPOSE_SGEMM_BK(64, 2, 128),
     XPOSE_SGEMM_BK(16, 1, 256), XPOSE_SGEMM_BK(32, 1, 256),
-    // whole-matrix twins of the k-step-16 kernels, every layout, both heights
+    XPOSE_SGEMM_BK(16, 1, 64),
+    // whole-matrix twins of the k-step-16 kernels, every layout and height
     XPOSE_SGEMM_WHOLE(16, kAsUnpadded, 128), XPOSE_SGEMM_WHOLE(16, kAsPadded, 128),
     XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 128), XPOSE_SGEMM_WHOLE(16, kAsUnpadded, 256),
-    XPOSE_SGEMM_WHOLE(16, kAsPadded, 256), XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 256)};
+    XPOSE_SGEMM_WHOLE(16, kAsPadded, 256), XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 256),
+    XPOSE_SGEMM_WHOLE(16, kAsUnpadded, 64), XPOSE_SGEMM_WHOLE(16, kAsPadded, 64),
+    XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 64)};
 
 }  // namespace
 

@@ -28,7 +28,7 @@ namespace xpose {
 enum AsLayout : int { kAsUnpadded = 1, kAsPadded = 2, kAsSwizzle = 3 };
 
 // Compile-time geometry of one SGEMM kernel: BK is the k step, L the As
-// layout, BM_ the rows of C per workgroup (128 or 256).  A workgroup of
+// layout, BM_ the rows of C per workgroup (64, 128 or 256).  A workgroup of
 // BM_ / 32 waves computes a BM_ x 128 block of C; wave w computes the
 // 64 x 64 block at (64 * (w / 2), 64 * (w % 2)) as 2 x 2 matrix-core tiles
 // of 32 x 32.
@@ -37,7 +37,7 @@ struct SgemmTile {
   static constexpr int BM = BM_, BN = 128, NT = 2 * BM_;
   static constexpr int WM = 64, WN = 64;  // C block of one wave
 
-  // A's 128 x BK tile is read in strips of LK = min(BK, 32) columns: each
+  // A's BM x BK tile is read in strips of LK = min(BK, 32) columns: each
   // lane reads one 16-byte vector (4 consecutive l) of one row i of a
   // strip, LPR lanes per strip row.
   static constexpr int LK = BK < 32 ? BK : 32;
@@ -54,12 +54,12 @@ struct SgemmTile {
   // As[s LK + 4c + e][i] for the strip s, the lane's chunk c < LPR and row i.
   // One half-wave (the 32 lanes one pass serves) holds HG = 32 / LPR
   // consecutive rows i (starting at a multiple of HG) times LPR chunks of
-  // one strip.  With row stride 128 + p the lane lands on bank
-  // (s LK p + 4 c p + e p + i) mod 32, the first term the same for the whole
-  // half-wave, so
+  // one strip.  With row stride BM + p (BM a multiple of 32) the lane lands
+  // on bank (s LK p + 4 c p + e p + i) mod 32, the first term the same for
+  // the whole half-wave, so
   //   p = 0:      the bank is i mod 32 alone: LPR lanes per bank, LPR-way;
   //   4 p = HG:   the chunks fall HG banks apart, covering all 32 once;
-  // hence the padded stride 128 + HG / 4 = 128 + 32 / LK.
+  // hence the padded stride BM + HG / 4 = BM + 32 / LK.
   static constexpr int HG = 32 / LPR;
   static constexpr int PAD = L == kAsPadded ? HG / 4 : 0;
   static constexpr int AS_STRIDE = BM + PAD;
@@ -68,25 +68,37 @@ struct SgemmTile {
   static constexpr int LDS_BYTES = 4 * (AS_FLOATS + BS_FLOATS);
   static constexpr int LAYOUT = L;
   static constexpr int KSTEP = BK;
-  // Waves per SIMD the register budget is set for (one wave per SIMD per
-  // 256-thread workgroup): as many workgroups as the LDS of `stages`
-  // buffers lets share a compute unit's 160 KiB, at most four (128
-  // registers per lane) where the k step's prefetch registers fit beside
-  // the 64 accumulators, else three.
+  // Waves per SIMD the register budget is set for.  A workgroup has
+  // NT / 64 waves spread over the compute unit's 4 SIMDs; as many
+  // workgroups as the LDS of `stages` buffers lets share the compute unit's
+  // 160 KiB give LDS_WGS * NT / 256 waves per SIMD (rounded up: a
+  // 128-thread workgroup puts one wave on two of the four SIMDs).  The
+  // budget is at most four waves (128 registers per lane) where the k
+  // step's prefetch registers (one 16-byte vector per A and B pass) fit
+  // beside the 64 accumulators, at most four vectors, else three waves;
+  // and for workgroups of more than one wave per SIMD it is a whole number
+  // of workgroups, since a partial one never fits (256-row blocks, two
+  // waves per SIMD: 4, i.e. two workgroups, or 2).
   SGEMM_HD static constexpr int waves_per_simd(int stages) {
-    return (160 * 1024) / (stages * LDS_BYTES) < (BK <= 16 ? 4 : 3)
-               ? (160 * 1024) / (stages * LDS_BYTES)
-               : (BK <= 16 ? 4 : 3);
+    return whole_workgroups(
+        min_int((A_PASSES + B_PASSES <= 4 ? 4 : 3),
+                ((160 * 1024) / (stages * LDS_BYTES) * NT + 255) / 256));
+  }
+  SGEMM_HD static constexpr int min_int(int a, int b) { return a < b ? a : b; }
+  SGEMM_HD static constexpr int whole_workgroups(int w) {
+    return NT <= 256 ? (w > 0 ? w : 1)
+                     : (w / (NT / 256) > 0 ? w / (NT / 256) * (NT / 256)
+                                           : NT / 256);
   }
 
   static_assert(BK == 8 || BK == 16 || BK == 32 || BK == 64, "built k steps");
-  static_assert(BM == 128 || BM == 256, "built block heights");
+  static_assert(BM == 64 || BM == 128 || BM == 256, "built block heights");
   static_assert(B_PASSES >= 1, "every lane loads part of B's tile");
   static_assert(A_ROW_PASSES * A_ROWS_PER_PASS == BM, "whole A tile");
   static_assert(B_PASSES * B_ROWS_PER_PASS == BK, "whole B tile");
   static_assert(L != kAsPadded || 4 * PAD == HG, "pad spreads the chunks");
 
-  // Swizzle: row l of As keeps stride 128 and holds element i at column
+  // Swizzle: row l of As keeps stride BM and holds element i at column
   // i ^ x(l), x(l) = ((l / 4) mod LPR) * HG.  In one half-wave's store
   // (l / 4) mod LPR is the chunk c and i runs over HG consecutive rows from
   // a multiple of HG, so the banks (i ^ c HG) mod 32 are all distinct;

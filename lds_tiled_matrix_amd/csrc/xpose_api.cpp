@@ -86,8 +86,19 @@ struct Default {
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
 constexpr int64_t kShortAlignRows = 256;
 constexpr int64_t kBigCallBytes = 512ll << 20;
+// 4-byte elements in big calls: the diagonal order only where output rows
+// lie within kPitchSlack bytes of a multiple of kPitchPeriod apart.  There
+// the column walk of a compact super-tile keeps writing the same few
+// address offsets and stalls on the memory channels they map to (8192^2:
+// 0.82 of the cold copy with 32 x 32 super-tiles, 0.97 diagonal; output
+// pitch 8224 elements, 128 bytes off the period: 0.74 against 0.84-0.86).
+// At other pitches the super-tiles win both ways: 12288^2 0.88 against
+// 0.78 diagonal, 10240^2 0.89 against 0.76, 9216^2 0.87 against 0.81,
+// 12288 x 6784 0.88 against 0.79 (fractions of the copy, cold).
+constexpr int64_t kPitchPeriod = 32768, kPitchSlack = 512;
 constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
-              kDiag = XPOSE_ORDER_DIAGONAL, kWB = XPOSE_CACHE_DEFAULT,
+              kDiag = XPOSE_ORDER_DIAGONAL, kBands = XPOSE_ORDER_COLUMN_BANDS,
+              kWB = XPOSE_CACHE_DEFAULT,
               kNT = XPOSE_CACHE_NT_STORE;
 
 Default default_for(int s, bool out_row128, bool small, bool big,
@@ -97,10 +108,15 @@ Default default_for(int s, bool out_row128, bool small, bool big,
       case 2:
         if (big) return {128, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
         return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
-      // Tall super-tiles: the tile above each tile (whose last rows are its
-      // halo) ran just before on the same XCD, except at the top of a
-      // super-tile, 1 tile in 128 (1 in 16 with 16 x 16 super-tiles).
-      case 4: return {64, 64, 256, kSwz, kNT, 128, 4, 1, kSup, true};
+      // Bands of 64 tile columns, per-XCD ranges: the tile above (whose last
+      // rows are the halo) and the tile to the left (which shares the input
+      // lines that straddle the tile's column edge when input rows are not
+      // line-aligned) ran shortly before on the same XCD, so both re-reads
+      // hit L2.  12345 x 6789: 1.019 x the algorithmic read bytes beyond L2
+      // and 0.84 of the copy, against 1.067 x with 16 x 16 super-tiles (the
+      // tile above missed at each super-tile's top) and 1.25 x with 128 x 4
+      // super-tiles (the tile to the left ran 128 tiles earlier).
+      case 4: return {64, 64, 256, kSwz, kNT, 1, 64, 1, kBands, true};
       case 8: return {32, 32, 256, kSwz, kNT, 16, 16, 1, kSup, true};
       default: break;  // no line-aligned tiles for 1-byte elements
     }
@@ -287,7 +303,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                opts->persistent > 64 || opts->occupancy < -1 ||
                opts->occupancy > 64 ||
                (opts->occupancy && opts->persistent) ||
-               opts->order > XPOSE_ORDER_DIAGONAL ||
+               opts->order > XPOSE_ORDER_COLUMN_BANDS ||
                opts->tile_rows < 0 || opts->tile_cols < 0))
     return XPOSE_EINVAL;
   if (batch == 0 || rows == 0 || cols == 0) {
@@ -347,7 +363,12 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                  (opts->layout && opts->layout != XPOSE_LAYOUT_SWIZZLE) ||
                  opts->persistent));
   const bool short_rows = s == 2 && rows < kShortAlignRows;
-  Default d = default_for(s, out_row128, small, big,
+  bool big_order = big;
+  if (s == 4 && big) {
+    const int64_t off = (ld_out * 4) % kPitchPeriod;
+    big_order = off <= kPitchSlack || kPitchPeriod - off <= kPitchSlack;
+  }
+  Default d = default_for(s, out_row128, small, big_order,
                           want_align || (align_ok && !out_row128 && !short_rows));
   const int layout = (opts && opts->layout) ? opts->layout : d.layout;
   plan->elem_bytes = s;
@@ -440,17 +461,26 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
 
   int64_t group_r = (opts && opts->group_rows) ? opts->group_rows : d.group_rows;
   int64_t group_c = (opts && opts->group_cols) ? opts->group_cols : d.group_cols;
+  const int order = (opts && opts->order) ? opts->order : d.order;
+  if (order == XPOSE_ORDER_COLUMN_BANDS && !(opts && opts->group_cols) &&
+      group_c > 0 && group_c < tiles_c) {
+    // Default bands: equal widths of at most d.group_cols tile columns
+    // (12345 x 6789 fp32: two bands of 54 and 53, 2-3% faster than 64 + 43).
+    const int64_t nb = (tiles_c + group_c - 1) / group_c;
+    group_c = (tiles_c + nb - 1) / nb;
+  }
   if (group_r > tiles_r) group_r = tiles_r;
   if (group_c > tiles_c || group_c == 0) group_c = tiles_c;
   int xcd = d.xcd_remap;
   if (opts && (opts->flags & XPOSE_FLAG_XCD_REMAP)) xcd = 1;
   if (opts && (opts->flags & XPOSE_FLAG_NO_XCD_REMAP)) xcd = 0;
 
-  // The default cap belongs to the default tile: it applies when the
-  // resolved kernel has the default shape and workgroup size.
+  // The default cap belongs to the default tile and order: it applies when
+  // the resolved kernel has the default shape and workgroup size and the
+  // tile order is the default one.
   int occupancy = (opts && opts->occupancy) ? opts->occupancy : 0;
   if (!occupancy && !persistent && tr == d.tile_rows && tc == d.tile_cols &&
-      k->threads == d.threads)
+      k->threads == d.threads && (!opts || !opts->order || opts->order == d.order))
     occupancy = d.occupancy;
   plan->kernel = k;
   plan->persistent = persistent;
@@ -471,7 +501,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   a.tiles_c = (uint32_t)tiles_c;
   a.batch_first = 0;
   a.vec_ok = vec ? 1 : 0;
-  a.order = (opts && opts->order) ? opts->order : d.order;
+  a.order = order;
   a.group_rows = (uint32_t)group_r;
   a.group_cols = (uint32_t)group_c;
   a.xcd_remap = xcd;

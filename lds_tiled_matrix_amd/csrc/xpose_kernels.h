@@ -29,11 +29,15 @@ struct TileArgs {
   uint32_t group_rows; // tile order: super-tile height in tiles (>= 1)
   uint32_t group_cols; // tile order: super-tile width in tiles (>= 1)
   int32_t xcd_remap;   // 1: one contiguous tile range per XCD
-  int32_t order;       // kOrderSuperTiles or kOrderDiagonal
+  int32_t order;       // kOrderSuperTiles, kOrderDiagonal or kOrderColumnBands
 };
 
 // Tile orders (values match xpose_order in include/xpose.h).
-enum TileOrder : int { kOrderSuperTiles = 1, kOrderDiagonal = 2 };
+enum TileOrder : int {
+  kOrderSuperTiles = 1,
+  kOrderDiagonal = 2,
+  kOrderColumnBands = 3
+};
 
 // Workgroup index -> (batch entry, tile row, tile column), for `block` of a
 // grid of `nblocks` workgroups.  A bijection from [0, nblocks) onto
@@ -53,6 +57,13 @@ enum TileOrder : int { kOrderSuperTiles = 1, kOrderDiagonal = 2 };
 //     resident tiles then spread over all address offsets on both the read
 //     and the write side, instead of camping on the few memory channels one
 //     narrow offset range maps to.
+//   column bands: bands of group_cols tile columns, left to right; inside a
+//     band, tile rows top to bottom, the band's tile columns left to right
+//     inside each tile row (the last band may be narrower).  Each tile's
+//     left and upper neighbours then ran shortly before it, except in a
+//     band's first column: what a tile shares with them (input lines that
+//     straddle the tile's column edge, the halo rows of line-aligned output
+//     tiles) is still in L2.
 __host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
                                             uint32_t nblocks, uint32_t &tr,
                                             uint32_t &tc, int64_t &b) {
@@ -67,6 +78,15 @@ __host__ __device__ inline void tile_coords(const TileArgs &a, uint32_t block,
   if (a.order == kOrderDiagonal) {
     tr = g % a.tiles_r;
     tc = (g / a.tiles_r + tr) % a.tiles_c;
+    return;
+  }
+  if (a.order == kOrderColumnBands) {
+    const uint32_t GC = a.group_cols;
+    const uint32_t band = g / (GC * a.tiles_r), rem = g % (GC * a.tiles_r);
+    const uint32_t cols_here =
+        (band + 1) * GC <= a.tiles_c ? GC : a.tiles_c - band * GC;
+    tr = rem / cols_here;
+    tc = band * GC + rem % cols_here;
     return;
   }
   const uint32_t GR = a.group_rows, GC = a.group_cols;

@@ -83,6 +83,7 @@ int main(void) {
   SIZE(xpose_sgemm_info);
   OFF(xpose_sgemm_info, as_stride); OFF(xpose_sgemm_info, xcd_remap);
   OFF(xpose_sgemm_info, tiles); OFF(xpose_sgemm_info, whole_matrix);
+  OFF(xpose_sgemm_info, edge_buffer_loads);
   CONST(XPOSE_AS_UNPADDED); CONST(XPOSE_AS_PADDED); CONST(XPOSE_AS_SWIZZLE);
   CONST(XPOSE_SGEMM_NO_XCD_REMAP); CONST(XPOSE_SGEMM_DOUBLE_BUFFER); CONST(XPOSE_SGEMM_NO_BUFFER_LOADS);
   {

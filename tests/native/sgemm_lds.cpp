@@ -160,6 +160,8 @@ int main() {
   kernel<16, kAsUnpadded, 256>(); kernel<16, kAsPadded, 256>();
   kernel<16, kAsSwizzle, 256>(); kernel<32, kAsUnpadded, 256>();
   kernel<32, kAsPadded, 256>(); kernel<32, kAsSwizzle, 256>();
+  kernel<16, kAsUnpadded, 64>(); kernel<16, kAsPadded, 64>();
+  kernel<16, kAsSwizzle, 64>();
   const uint32_t dims[] = {1, 2, 3, 7, 8, 9, 32, 33};
   for (uint32_t tm : dims)
     for (uint32_t tn : dims)

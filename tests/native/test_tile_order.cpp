@@ -18,9 +18,11 @@ int main() {
       for (uint32_t batch : {1u, 3u})
         for (uint32_t gr : {1u, 2u, 3u, 8u, 16u, 1000u})
           for (uint32_t gc : {1u, 3u, 8u, 32u, 1000u})
-            for (int xcd = 0; xcd < 4; ++xcd) {
+            for (int xcd = 0; xcd < 6; ++xcd) {
               xpose::TileArgs a = {};
-              a.order = xcd < 2 ? xpose::kOrderSuperTiles : xpose::kOrderDiagonal;
+              a.order = xcd < 2   ? xpose::kOrderSuperTiles
+                        : xcd < 4 ? xpose::kOrderDiagonal
+                                  : xpose::kOrderColumnBands;
               a.tiles_r = tr_n;
               a.tiles_c = tc_n;
               a.group_rows = gr < tr_n ? gr : tr_n;

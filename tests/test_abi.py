@@ -105,7 +105,7 @@ def test_ragged_and_batched_tile_counts():
     rc, info = plan(rows=12288, cols=6789, ld_out=12289)
     assert rc == 0 and info.aligned_out == 1 and info.tiles == 193 * 107
     rc, info = plan(rows=12288, cols=6789)
-    assert rc == 0 and info.aligned_out == 0 and info.tiles == 96 * 54
+    assert rc == 0 and info.aligned_out == 0 and info.tiles == 384 * 213
     # A batch of small matrices: taller tiles, small super-tiles.
     rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
                     stride_out=1024 * 2048)
@@ -286,6 +286,21 @@ def test_footprint_rules():
     # Just under 512 MiB: compact super-tiles, no cap.
     rc, info = plan(rows=8192, cols=8191, ld_in=8191)
     assert rc == 0 and info.order == X.ORDER_SUPER_TILES and info.occupancy == 0
+    # 4-byte elements: the diagonal order only where output rows lie (nearly)
+    # a multiple of 32 KiB apart
+    rc, info = plan(rows=12288, cols=12288)
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    assert (info.tile_rows, info.tile_cols) == (32, 32) and info.occupancy == 0
+    rc, info = plan(rows=8192, cols=8192, ld_in=8224, ld_out=8224)
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 1
+    rc, info = plan(rows=12288, cols=8192, ld_out=16384 + 32)  # 128 B off 64 KiB
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    rc, info = plan(rows=12288, cols=8192, ld_out=16384 + 256)  # 1 KiB off
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    # an explicit order drops the default cap
+    rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F16,
+                    opts=X.make_opts(order=X.ORDER_SUPER_TILES))
+    assert rc == 0 and info.occupancy == 0 and info.tile_rows == 128
     # A batch of small matrices keeps super-tiles even when the call is big.
     rc, info = plan(batch=64, rows=2048, cols=1024, stride_in=2048 * 1024,
                     stride_out=1024 * 2048)
@@ -293,7 +308,10 @@ def test_footprint_rules():
     # Explicit order wins.
     rc, info = plan(opts=X.make_opts(order=X.ORDER_DIAGONAL))
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
-    assert plan(opts=X.make_opts(order=3))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.make_opts(order=4))[0] == X.XPOSE_EINVAL
+    rc, info = plan(rows=1024, cols=1024,
+                    opts=X.make_opts(order=X.ORDER_COLUMN_BANDS, group_cols=16))
+    assert rc == 0 and info.order == X.ORDER_COLUMN_BANDS and info.group_cols == 16
 
 
 def test_naive_plans():

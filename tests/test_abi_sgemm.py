@@ -90,7 +90,11 @@ def test_tall_blocks():
     assert rc == 0 and info.tiles == 2 * 2
     assert plan(opts=X.make_sgemm_opts(bk=8, tile_m=256))[0] == X.XPOSE_ENOTILE
     assert plan(opts=X.make_sgemm_opts(tile_m=256, flags=X.SGEMM_DOUBLE_BUFFER))[0] == X.XPOSE_ENOTILE
-    assert plan(opts=X.make_sgemm_opts(tile_m=64))[0] == X.XPOSE_EINVAL
+    assert plan(opts=X.make_sgemm_opts(tile_m=96))[0] == X.XPOSE_EINVAL
+    # 64-row blocks: 2 waves, k step 16, one LDS buffer
+    rc, info = plan(opts=X.make_sgemm_opts(tile_m=64))
+    assert rc == 0 and (info.tile_m, info.threads) == (64, 128)
+    assert plan(opts=X.make_sgemm_opts(bk=32, tile_m=64))[0] == X.XPOSE_ENOTILE
     # buffer loads: half the lda limit of 128-row blocks
     big = (1 << 31) // (4 * 257)
     assert plan(m=512, lda=big - big % 4, opts=X.make_sgemm_opts(tile_m=256))[1].buffer_loads == 1

@@ -155,12 +155,13 @@ def test_exact_on_integer_inputs(layout, bk, flags):
         assert np.isfinite(got[region_mask(m, n, max(n, 1), got.size)]).all()
 
 
-@pytest.mark.parametrize("bk", (16, 32))
+@pytest.mark.parametrize("bk, tile_m", [(16, 256), (32, 256), (16, 64)])
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
-def test_exact_tall_blocks(layout, bk):
-    """256 x 128 blocks (8 waves), buffer and global loads."""
+def test_exact_tall_and_short_blocks(layout, bk, tile_m):
+    """256 x 128 blocks (8 waves) and 64 x 128 blocks (2 waves), buffer and
+    global loads."""
     for flags in (0, X.SGEMM_NO_BUFFER_LOADS):
-        opts = X.make_sgemm_opts(layout, bk, 0, flags, 256)
+        opts = X.make_sgemm_opts(layout, bk, 0, flags, tile_m)
         for idx, (m, n, k) in enumerate(EXACT_SHAPES + [(512, 256, 96), (257, 300, 65)]):
             A = wl.small_int_f32((m, k), 700 + idx)
             B = wl.small_int_f32((k, n), 800 + idx)
@@ -169,7 +170,7 @@ def test_exact_tall_blocks(layout, bk):
 
 
 @pytest.mark.parametrize("bk, tile_m", [(8, 128), (16, 128), (32, 128), (64, 128),
-                                         (16, 256), (32, 256)])
+                                         (16, 256), (32, 256), (16, 64)])
 def test_whole_blocks_with_ragged_k(bk, tile_m):
     """Blocks wholly inside C with k not a multiple of the k step: buffer
     loads for every whole k step, checked loads for the last one.  A's
@@ -188,24 +189,57 @@ def test_whole_blocks_with_ragged_k(bk, tile_m):
             check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(pad_a, 0, 3))
 
 
-@pytest.mark.parametrize("tile_m", (128, 256))
+@pytest.mark.parametrize("tile_m", (64, 128, 256))
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda v: X.AS_NAMES[v])
 def test_whole_matrix_kernels(layout, tile_m):
     """The kernels without edge code (every block, k step, load and C tail
-    whole), with both beta paths and C pitch padding."""
+    whole), with both beta paths, C pitch padding, and A and B pitches
+    padded by 4 floats (still 16-byte multiples, so the plan keeps the
+    whole-matrix kernel; the descriptors and lane offsets then scale with
+    lda and ldb, and NaN in the padding would show)."""
     opts = X.make_sgemm_opts(layout, 16, 0, 0, tile_m)
     for idx, (m, n, k) in enumerate([(2 * tile_m, 384, 512), (tile_m, 128, 16),
                                      (4 * tile_m, 256, 48)]):
-        rc, info = X.xpose_sgemm_plan(m, n, k, 1 << 40, k, 1 << 41, n, 1 << 42,
-                                      n + 3, opts)
-        assert rc == 0 and info.whole_matrix == 1
-        A = wl.small_int_f32((m, k), 1300 + idx)
-        B = wl.small_int_f32((k, n), 1400 + idx)
-        C = wl.small_int_f32((m, n), 1500 + idx)
-        check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(0, 0, 3))
-        Cn = np.full((m, n), np.nan, np.float32)
-        got = check_exact(A, B, Cn, 1.0, 0.0, opts=opts, pads=(0, 0, 3))
-        assert np.isfinite(got[region_mask(m, n, n + 3, got.size)]).all()
+        for pad_a, pad_b in ((0, 0), (4, 4), (8, 0), (0, 12)):
+            rc, info = X.xpose_sgemm_plan(m, n, k, 1 << 40, k + pad_a, 1 << 41,
+                                          n + pad_b, 1 << 42, n + 3, opts)
+            assert rc == 0 and info.whole_matrix == 1, (pad_a, pad_b)
+            A = wl.small_int_f32((m, k), 1300 + idx)
+            B = wl.small_int_f32((k, n), 1400 + idx)
+            C = wl.small_int_f32((m, n), 1500 + idx)
+            check_exact(A, B, C, 2.0, -1.0, opts=opts, pads=(pad_a, pad_b, 3))
+            Cn = np.full((m, n), np.nan, np.float32)
+            got = check_exact(A, B, Cn, 1.0, 0.0, opts=opts,
+                              pads=(pad_a, pad_b, 3))
+            assert np.isfinite(got[region_mask(m, n, n + 3, got.size)]).all()
+
+
+def test_edge_blocks_with_buffer_loads():
+    """Edge blocks (m or n not a multiple of the block) and ragged last k
+    steps read with buffer loads whose descriptors are clipped to the
+    matrix, where k and n are multiples of 4.  A's and B's pitch padding
+    holds NaN, so a column of A past k that was not zeroed, or a read past
+    the matrix, would show; guard sentinels around C must stay unchanged."""
+    shapes = [(200, 136, 72), (130, 260, 100), (1000, 132, 44), (129, 4, 4),
+              (1, 128, 16), (257, 388, 36), (64, 1028, 8), (300, 300, 300)]
+    for tile_m in (64, 128, 256):
+        for layout in LAYOUTS:
+            opts = X.make_sgemm_opts(layout, 16, 0, 0, tile_m)
+            for idx, (m, n, k) in enumerate(shapes):
+                for pad_a, pad_b in ((0, 0), (4, 8)):
+                    rc, info = X.xpose_sgemm_plan(m, n, k, 1 << 40, k + pad_a,
+                                                  1 << 41, n + pad_b, 1 << 42,
+                                                  n, opts)
+                    assert rc == 0 and info.edge_buffer_loads == 1, (m, n, k)
+                    A = wl.small_int_f32((m, k), 1600 + idx)
+                    B = wl.small_int_f32((k, n), 1700 + idx)
+                    C = wl.small_int_f32((m, n), 1800 + idx)
+                    check_exact(A, B, C, 2.0, -1.0, opts=opts,
+                                pads=(pad_a, pad_b, 1))
+    # k or n not a multiple of 4: the bounds-checked loads
+    rc, info = X.xpose_sgemm_plan(200, 130, 72, 1 << 40, 72, 1 << 41, 132,
+                                  1 << 42, 130)
+    assert rc == 0 and info.edge_buffer_loads == 0
 
 
 def test_scalar_load_path_is_exact():
@@ -242,8 +276,10 @@ def test_all_kernels_agree_bit_for_bit():
     for layout in LAYOUTS:
         for bk in BKS:
             for flags in FLAG_SETS.values():
-                for tile_m in (128, 256):
+                for tile_m in (64, 128, 256):
                     if tile_m == 256 and (bk not in (16, 32) or flags == X.SGEMM_DOUBLE_BUFFER):
+                        continue
+                    if tile_m == 64 and (bk != 16 or flags == X.SGEMM_DOUBLE_BUFFER):
                         continue
                     for shifts in ((0, 0, 0), (1, 1, 0)):
                         got, _, _ = run_case(A, B, C, 1.5, 0.5, shifts=shifts,
@@ -332,7 +368,9 @@ def test_random_campaign():
         flags = int(rng.choice([0, 0, X.SGEMM_DOUBLE_BUFFER, X.SGEMM_NO_BUFFER_LOADS,
                                 X.SGEMM_NO_XCD_REMAP]))
         bk = int(rng.choice(BKS))
-        tile_m = int(rng.choice([128, 256])) if bk in (16, 32) and flags != X.SGEMM_DOUBLE_BUFFER else 128
+        tile_m = 128
+        if flags != X.SGEMM_DOUBLE_BUFFER and bk in (16, 32):
+            tile_m = int(rng.choice([64, 128, 256] if bk == 16 else [128, 256]))
         opts = X.make_sgemm_opts(int(rng.choice(LAYOUTS)), bk,
                                  int(rng.choice([0, 1, 3, 8])), flags, tile_m)
         A = wl.small_int_f32((m, k), 10_000 + case)

@@ -58,7 +58,7 @@ def test_self_checks_pass(listing):
 
 
 @pytest.mark.parametrize("bk, m", [(8, ""), (16, ""), (32, ""), (64, ""),
-                                   (16, "/m256"), (32, "/m256")])
+                                   (16, "/m256"), (32, "/m256"), (16, "/m64")])
 def test_transposed_store(worst, bk, m):
     assert worst[(f"sgemm/bk{bk}/unpadded{m}", "a_store")] == min(bk, 32) // 4
     assert worst[(f"sgemm/bk{bk}/padded{m}", "a_store")] == 1
@@ -75,4 +75,5 @@ def test_every_built_kernel_listed(worst):
     names = {n for n, _ in worst}
     layouts = ("unpadded", "padded", "swizzle")
     assert names == ({f"sgemm/bk{bk}/{l}" for bk in (8, 16, 32, 64) for l in layouts} |
-                     {f"sgemm/bk{bk}/{l}/m256" for bk in (16, 32) for l in layouts})
+                     {f"sgemm/bk{bk}/{l}/m256" for bk in (16, 32) for l in layouts} |
+                     {f"sgemm/bk16/{l}/m64" for l in layouts})

@@ -8,7 +8,10 @@ import workloads as wl
 def test_workload_table():
     assert set(wl.WORKLOADS) == {
         "c1_index_1024_f32", "c2_8192_f32", "c3_ragged_12345x6789_f32",
-        "c4_16384_f16", "c5_batched_64x2048x1024_f32"}
+        "c4_16384_f16", "c5_batched_64x2048x1024_f32",
+        "shard_1024x8192_f32", "shard_batched_8x2048x1024_f32"}
+    assert wl.WORKLOADS["shard_1024x8192_f32"].rw_bytes * 8 == 536_870_912
+    assert wl.WORKLOADS["shard_batched_8x2048x1024_f32"].rw_bytes * 8 == 1_073_741_824
     c2 = wl.WORKLOADS[wl.HEADLINE]
     assert (c2.rows, c2.cols, c2.dtype) == (8192, 8192, "f32")
     assert c2.rw_bytes == 536_870_912

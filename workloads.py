@@ -72,6 +72,18 @@ WORKLOADS = {
     "c5_batched_64x2048x1024_f32": Workload(
         "c5_batched_64x2048x1024_f32", 64, 2048, 1024, "f32", "uniform", 5,
         "batched transpose, 64 matrices of 2048x1024 fp32, uniform [-1,1)"),
+    # One GPU's share of the two workloads above when they are spread over 8
+    # GPUs (rows of the input and of the output in contiguous blocks, or the
+    # batch split 8 ways): the local kernel each GPU would run, measured at
+    # its real shape.
+    "shard_1024x8192_f32": Workload(
+        "shard_1024x8192_f32", 1, 1024, 8192, "f32", "uniform", 6,
+        "2-D transpose 1024x8192 fp32 (one GPU's row block of 8192x8192 "
+        "on 8 GPUs), uniform [-1,1)"),
+    "shard_batched_8x2048x1024_f32": Workload(
+        "shard_batched_8x2048x1024_f32", 8, 2048, 1024, "f32", "uniform", 7,
+        "batched transpose, 8 matrices of 2048x1024 fp32 (one GPU's share "
+        "of the 64-matrix batch on 8 GPUs), uniform [-1,1)"),
 }
 
 # The workload the headline throughput is quoted on.
