@@ -423,6 +423,78 @@ def bench_sgemm(X, steps, warmup, stream, with_cpu=True):
     return res
 
 
+SGEMM_SHAPES = ((1024, 1024, 1024), (1536, 1536, 1536), (2048, 2048, 2048),
+                (3000, 3000, 3000), (4100, 4100, 4100), (5000, 5000, 5000),
+                (1024, 1024, 8192))
+
+
+def bench_sgemm_shapes(X, shapes, steps, warmup, stream):
+    """The SGEMM off the page's size, where the grid of 128 x 128 blocks
+    is too small to fill 256 compute units: per shape, the library's
+    default with a workspace (xpose_sgemm_ws: its split of k, product and
+    sum kernels, timed together), the same without a workspace (no split),
+    and torch's fp32 addmm; C += A B on uniform [-1, 1) inputs, medians of
+    per-call events."""
+    import torch
+    dev = torch.device("cuda", 0)
+    sh = int(stream.cuda_stream)
+    out = []
+    n = max(10, min(steps, 50))
+    for idx, (m, nn, k) in enumerate(shapes):
+        g = torch.Generator(device="cpu").manual_seed(100 + idx)
+        dA = (torch.rand(m, k, generator=g) * 2 - 1).to(dev)
+        dB = (torch.rand(k, nn, generator=g) * 2 - 1).to(dev)
+        dC = (torch.rand(m, nn, generator=g) * 2 - 1).to(dev)
+        args = (m, nn, k, dA.data_ptr(), k, dB.data_ptr(), nn, dC.data_ptr(),
+                nn)
+        rc, info = X.xpose_sgemm_plan_ws(*args, None, 0, 0)
+        if rc:
+            raise RuntimeError(X.strerror(rc))
+        ws = torch.empty(max(info.workspace_wanted // 4, 1),
+                         dtype=torch.float32, device=dev)
+        rc, info = X.xpose_sgemm_plan_ws(*args, None, ws.data_ptr(),
+                                         info.workspace_wanted)
+
+        def split_call():
+            rc = X.xpose_sgemm_ws(m, nn, k, 1.0, dA.data_ptr(), k,
+                                  dB.data_ptr(), nn, 1.0, dC.data_ptr(), nn,
+                                  None, ws.data_ptr(), info.workspace_wanted,
+                                  sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+
+        def plain_call():
+            rc = X.xpose_sgemm_ex(m, nn, k, 1.0, dA.data_ptr(), k,
+                                  dB.data_ptr(), nn, 1.0, dC.data_ptr(), nn,
+                                  None, sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+
+        c2 = torch.empty_like(dC)
+        flops = 2 * m * nn * k
+        row = {"m": m, "n": nn, "k": k, "splits": info.splits,
+               "split_len": info.split_len,
+               "workspace_MiB": round(info.workspace_bytes / 2 ** 20, 1),
+               "workgroups": info.tiles}
+        variants = (("split", split_call), ("no_split", plain_call),
+                    ("torch_addmm", lambda: torch.addmm(dC, dA, dB, out=c2)))
+        with torch.cuda.stream(stream):
+            # one untimed pass over all three first: the first calls after
+            # the inputs are made run while clocks and caches settle
+            for _, fn in variants:
+                time_launches(fn, stream, n, min(warmup, 5))
+            for name, fn in variants:
+                _, _, d = time_launches(fn, stream, n, min(warmup, 5))
+                row[name + "_TFLOPs"] = round(
+                    flops / statistics.median(d) / 1e12, 2)
+        torch.cuda.synchronize()
+        row["split_vs_torch"] = round(row["split_TFLOPs"] /
+                                      row["torch_addmm_TFLOPs"], 3)
+        out.append(row)
+        del dA, dB, dC, c2, ws
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -440,7 +512,23 @@ def main(argv=None):
                     help="skip the tiled SGEMM (padded transposed As store)")
     ap.add_argument("--sgemm-only", action="store_true",
                     help="measure only the tiled SGEMM; print its JSON line")
+    ap.add_argument("--sgemm-shapes", default=None,
+                    help="comma-separated MxNxK list for the SGEMM's small-grid "
+                         "table (split of k against none and torch); 'none' "
+                         "skips it; default: " +
+                         ",".join("x".join(map(str, t)) for t in SGEMM_SHAPES))
     args = ap.parse_args(argv)
+    if args.sgemm_shapes is None:
+        shapes = SGEMM_SHAPES
+    elif args.sgemm_shapes == "none":
+        shapes = ()
+    else:
+        try:
+            shapes = tuple(tuple(int(v) for v in t.split("x"))
+                           for t in args.sgemm_shapes.split(","))
+            assert all(len(t) == 3 and min(t) > 0 for t in shapes)
+        except (ValueError, AssertionError):
+            ap.error("--sgemm-shapes takes MxNxK[,MxNxK...] of positive sizes")
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for "
@@ -459,9 +547,13 @@ def main(argv=None):
     stream = torch.cuda.Stream()
     if args.sgemm_only:
         log("bench: tiled SGEMM only")
-        print(json.dumps({"sgemm": bench_sgemm(X, args.steps, args.warmup, stream,
-                                               with_cpu=not args.no_cpu)}),
-              flush=True)
+        sg = bench_sgemm(X, args.steps, args.warmup, stream,
+                         with_cpu=not args.no_cpu)
+        if shapes:
+            log("bench: SGEMM small grids")
+            sg["shapes"] = bench_sgemm_shapes(X, shapes, args.steps,
+                                              args.warmup, stream)
+        print(json.dumps({"sgemm": sg}), flush=True)
         return 0
     w = wl.WORKLOADS[args.workload]
     log(f"bench: {w.description}; steps={args.steps} warmup={args.warmup}")
@@ -496,6 +588,10 @@ def main(argv=None):
         torch.cuda.empty_cache()
         sgemm = bench_sgemm(X, args.steps, args.warmup, stream,
                             with_cpu=not args.no_cpu)
+        if shapes:
+            log("bench: SGEMM small grids")
+            sgemm["shapes"] = bench_sgemm_shapes(X, shapes, args.steps,
+                                                 args.warmup, stream)
 
     plan = res["plan"]
     line = {
@@ -519,9 +615,14 @@ def main(argv=None):
             "tile": f"{plan['tile_rows']}x{plan['tile_cols']}",
             "threads": plan["threads"], "workgroups": plan["tiles"],
             "cache": X.CACHE_NAMES[plan["cache"]],
-            "tile_order": (f"super-tiles {plan['group_rows']}x{plan['group_cols']}"
-                           if plan["order"] == X.ORDER_SUPER_TILES else "diagonal")
+            "tile_order": {
+                X.ORDER_SUPER_TILES:
+                    f"super-tiles {plan['group_rows']}x{plan['group_cols']}",
+                X.ORDER_DIAGONAL: "diagonal",
+                X.ORDER_COLUMN_BANDS: f"column bands {plan['group_cols']}",
+            }[plan["order"]]
                           + (", per-XCD ranges" if plan["xcd_remap"] else ""),
+            "occupancy": plan["occupancy"],
         },
         "system": system_info(),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

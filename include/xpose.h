@@ -64,9 +64,11 @@ enum {
   XPOSE_EDTYPE = -3, /* unknown dtype                                       */
   XPOSE_EHIP = -4,   /* a HIP call failed; see xpose_last_hip_error()       */
   XPOSE_EALIGN = -5, /* a pointer is not aligned to the element size        */
-  XPOSE_ENOTILE = -6 /* no kernel is built for the combination xpose_opts
+  XPOSE_ENOTILE = -6, /* no kernel is built for the combination xpose_opts
                         asks for (tile shape, layout, flags, workgroup size,
                         cache policy)                                       */
+  XPOSE_EWORKSPACE = -7 /* the split of k an SGEMM call asks for needs more
+                        workspace than the call has (include/xpose_sgemm.h) */
 };
 
 /* LDS tile layouts (the row stride of the on-chip tile).  A padded or a

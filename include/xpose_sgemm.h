@@ -42,6 +42,21 @@
  * C's byte range must not overlap A's or B's (XPOSE_EALIAS); A and B may
  * overlap each other.
  *
+ * Split of k.  A product with few blocks of C (1024 x 1024 is 64 blocks of
+ * 128 x 128, for 256 compute units) leaves most of the chip idle.  Given a
+ * WORKSPACE (xpose_sgemm_ws), the call may split k into S slices of whole k
+ * steps: S copies of the block grid run at once, copy z storing its slice's
+ * raw sums sum_{l in slice z} A[i][l] B[l][j] into the z-th m x n partial
+ * matrix of the workspace (pitch n), and a second kernel on the same stream
+ * writes C = alpha * (P_0 + P_1 + ... + P_{S-1}) + beta * C, adding the
+ * partials in the order z = 0, 1, ... (so results are deterministic and
+ * repeat bit for bit).  The error bound above holds unchanged (a split only
+ * regroups the same sum).  The workspace holds S * m * n floats; it is
+ * written and read by the call's kernels only, so it may be reused as soon
+ * as the call's work on the stream has finished, and two calls that share a
+ * workspace must not overlap in time.  xpose_sgemm and xpose_sgemm_ex have
+ * no workspace and never split.
+ *
  * Errors (validated on the host before anything is launched):
  *   XPOSE_EINVAL  negative m, n or k; lda < max(k, 1), ldb < max(n, 1) or
  *                 ldc < max(n, 1); a NULL pointer that the call would use;
@@ -49,7 +64,12 @@
  *   XPOSE_EALIGN  a pointer not 4-byte aligned
  *   XPOSE_EALIAS  C overlaps A or B
  *   XPOSE_ENOTILE no kernel built for the requested options
+ *   XPOSE_EWORKSPACE  an explicit split (split_k >= 2) with a workspace
+ *                 smaller than the split needs (or none: xpose_sgemm_ex)
  *   XPOSE_EHIP    the launch failed (xpose_last_hip_error())
+ * A workspace that the call uses must be 4-byte aligned (XPOSE_EALIGN; 16
+ * bytes lets the final sum use 16-byte accesses) and must not overlap A, B
+ * or C (XPOSE_EALIAS); workspace_bytes < 0 is XPOSE_EINVAL.
  * m == 0 or n == 0 is a successful no-op (pointers may then be NULL);
  * k == 0 sets C = beta * C (a and b are not used and may be NULL).
  */
@@ -128,6 +148,13 @@ typedef struct xpose_sgemm_opts {
                       k step 16, one LDS buffer), 128 (4 waves) or 256 (8
                       waves; k steps 16 and 32, one LDS buffer); blocks are
                       128 columns wide                                       */
+  int32_t split_k; /* k slices: 0 = the library's choice (with a workspace,
+                      a split where the grid of blocks is too small to fill
+                      the chip, as many slices as the workspace holds at
+                      most; without one, none), 1 = no split, 2..64 = k
+                      split into slices of ceil(k / split_k) rounded up to
+                      whole k steps (so at most split_k slices; fewer when k
+                      is short, none when one slice covers k)              */
 } xpose_sgemm_opts;
 
 /* What xpose_sgemm_plan reports about the kernel a call would launch. */
@@ -155,6 +182,14 @@ typedef struct xpose_sgemm_info {
                            to the matrix (buffer loads allowed, k and n
                            multiples of 4); 0: those take bounds-checked
                            global loads                                      */
+  int32_t splits;       /* k slices the call takes (1: no split)             */
+  int64_t split_len;    /* k per slice (the last may be shorter); k if none  */
+  int64_t workspace_bytes;  /* workspace the call uses: splits * m * n * 4,
+                           0 without a split                                */
+  int64_t workspace_wanted; /* workspace the library's split choice for this
+                           shape and these options would use given enough
+                           (an explicit split_k: that split's); 0 if it
+                           would not split                                  */
 } xpose_sgemm_info;
 
 /* C = alpha * A * B + beta * C with the default kernel. */
@@ -169,14 +204,40 @@ int xpose_sgemm_ex(int64_t m, int64_t n, int64_t k, float alpha,
                    float beta, float *c, int64_t ldc,
                    const xpose_sgemm_opts *opts, void *stream);
 
-/* Host-only: validate a call and report the kernel it would launch, without
- * touching the GPU (pointers are compared and checked for alignment, never
- * dereferenced).  Returns the status the call would return; `info` may be
- * NULL. */
+/* Host-only: validate an xpose_sgemm_ex call and report the kernel it
+ * would launch, without touching the GPU (pointers are compared and checked
+ * for alignment, never dereferenced).  Returns the status the call would
+ * return; `info` may be NULL. */
 int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
                      int64_t lda, const float *b, int64_t ldb, const float *c,
                      int64_t ldc, const xpose_sgemm_opts *opts,
                      xpose_sgemm_info *info);
+
+/* xpose_sgemm_ex with a caller-owned DEVICE workspace of workspace_bytes
+ * (on the current device) for the partial sums of a split of k (see "Split
+ * of k" above; `workspace` may be NULL when workspace_bytes is 0).  With
+ * opts->split_k == 0 the library splits where the block grid is small, into
+ * as many slices as its rule picks and the workspace holds; the workspace
+ * is only touched when the call splits.  Two kernels are enqueued on
+ * `stream` when it does (the split product, then the sum), one otherwise.
+ * The split is for grids of blocks too small to occupy MI355X's 256
+ * compute units. */
+int xpose_sgemm_ws(int64_t m, int64_t n, int64_t k, float alpha,
+                   const float *a, int64_t lda, const float *b, int64_t ldb,
+                   float beta, float *c, int64_t ldc,
+                   const xpose_sgemm_opts *opts, void *workspace,
+                   int64_t workspace_bytes, void *stream);
+
+/* Host-only counterpart of xpose_sgemm_ws, as xpose_sgemm_plan is of
+ * xpose_sgemm_ex (the workspace too is compared, never dereferenced).
+ * With workspace NULL and workspace_bytes 0 it serves as the size query:
+ * info->workspace_wanted is what to allocate.  On XPOSE_EWORKSPACE (from
+ * either plan call) `info` is zeroed except for workspace_wanted. */
+int xpose_sgemm_plan_ws(int64_t m, int64_t n, int64_t k, const float *a,
+                        int64_t lda, const float *b, int64_t ldb,
+                        const float *c, int64_t ldc,
+                        const xpose_sgemm_opts *opts, const void *workspace,
+                        int64_t workspace_bytes, xpose_sgemm_info *info);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,8 @@ Low-level names mirror the C ABI (``xpose_2d``, ``xpose_2d_ex``,
 ``xpose_batched``,
 ``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``,
 and the tiled SGEMM's ``xpose_sgemm``, ``xpose_sgemm_ex``,
-``xpose_sgemm_plan`` of ``include/xpose_sgemm.h``) and take raw device
+``xpose_sgemm_plan``, ``xpose_sgemm_ws``, ``xpose_sgemm_plan_ws`` of
+``include/xpose_sgemm.h``) and take raw device
 addresses as integers.  ``transpose``, ``copy`` and ``sgemm`` are
 conveniences over torch tensors: torch supplies the device memory and the
 stream, nothing else.
@@ -27,6 +28,7 @@ XPOSE_F32, XPOSE_F16, XPOSE_BF16, XPOSE_U8, XPOSE_F64 = 0, 1, 2, 3, 4
 XPOSE_OK = 0
 XPOSE_EINVAL, XPOSE_EALIAS, XPOSE_EDTYPE = -1, -2, -3
 XPOSE_EHIP, XPOSE_EALIGN, XPOSE_ENOTILE = -4, -5, -6
+XPOSE_EWORKSPACE = -7
 LAYOUT_AUTO, LAYOUT_UNPADDED, LAYOUT_PAD1, LAYOUT_SWIZZLE = 0, 1, 2, 3
 LAYOUT_NAIVE_READ, LAYOUT_NAIVE_WRITE = 4, 5
 LAYOUT_NAMES = {LAYOUT_UNPADDED: "unpadded", LAYOUT_PAD1: "pad1",
@@ -53,7 +55,8 @@ EXPORTS = ("xpose_2d", "xpose_2d_ex", "xpose_batched", "xpose_batched_ex",
            "xpose_plan",
            "xpose_copy", "xpose_copy_ex", "xpose_lds_probe",
            "xpose_last_hip_error", "xpose_strerror",
-           "xpose_sgemm", "xpose_sgemm_ex", "xpose_sgemm_plan")
+           "xpose_sgemm", "xpose_sgemm_ex", "xpose_sgemm_plan",
+           "xpose_sgemm_ws", "xpose_sgemm_plan_ws")
 
 
 class XposeOpts(ctypes.Structure):
@@ -89,7 +92,7 @@ class XposePlanInfo(ctypes.Structure):
 class XposeSgemmOpts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("bk", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("tile_m", ctypes.c_int32)]
+                ("tile_m", ctypes.c_int32), ("split_k", ctypes.c_int32)]
 
 
 class XposeSgemmInfo(ctypes.Structure):
@@ -100,7 +103,10 @@ class XposeSgemmInfo(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("buffer_loads", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("whole_matrix", ctypes.c_int32),
-                ("edge_buffer_loads", ctypes.c_int32)]
+                ("edge_buffer_loads", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("split_len", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64),
+                ("workspace_wanted", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -143,6 +149,11 @@ def _load() -> ctypes.CDLL:
         "xpose_sgemm_plan": [i64, i64, i64, p, i64, p, i64, p, i64,
                              ctypes.POINTER(XposeSgemmOpts),
                              ctypes.POINTER(XposeSgemmInfo)],
+        "xpose_sgemm_ws": [i64, i64, i64, f32, p, i64, p, i64, f32, p, i64,
+                           ctypes.POINTER(XposeSgemmOpts), p, i64, p],
+        "xpose_sgemm_plan_ws": [i64, i64, i64, p, i64, p, i64, p, i64,
+                                ctypes.POINTER(XposeSgemmOpts), p, i64,
+                                ctypes.POINTER(XposeSgemmInfo)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -237,8 +248,8 @@ def xpose_lds_probe(cycles_out: int, lane_bytes, width: int, is_write: int,
 
 
 def make_sgemm_opts(layout=AS_AUTO, bk=0, group_m=0, flags=0,
-                    tile_m=0) -> XposeSgemmOpts:
-    return XposeSgemmOpts(layout, bk, group_m, flags, tile_m)
+                    tile_m=0, split_k=0) -> XposeSgemmOpts:
+    return XposeSgemmOpts(layout, bk, group_m, flags, tile_m, split_k)
 
 
 def xpose_sgemm(m: int, n: int, k: int, alpha: float, a: int, lda: int,
@@ -264,6 +275,28 @@ def xpose_sgemm_plan(m: int, n: int, k: int, a: int, lda: int, b: int,
     rc = _lib.xpose_sgemm_plan(m, n, k, a, lda, b, ldb, c, ldc,
                                ctypes.byref(opts) if opts else None,
                                ctypes.byref(info))
+    return rc, info
+
+
+def xpose_sgemm_ws(m: int, n: int, k: int, alpha: float, a: int, lda: int,
+                   b: int, ldb: int, beta: float, c: int, ldc: int,
+                   opts: XposeSgemmOpts | None = None, workspace: int = 0,
+                   workspace_bytes: int = 0, stream: int = 0) -> int:
+    return _lib.xpose_sgemm_ws(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc,
+                               ctypes.byref(opts) if opts else None,
+                               workspace, workspace_bytes, stream)
+
+
+def xpose_sgemm_plan_ws(m: int, n: int, k: int, a: int, lda: int, b: int,
+                        ldb: int, c: int, ldc: int,
+                        opts: XposeSgemmOpts | None = None,
+                        workspace: int = 0, workspace_bytes: int = 0):
+    """Returns (status, XposeSgemmInfo)."""
+    info = XposeSgemmInfo()
+    rc = _lib.xpose_sgemm_plan_ws(m, n, k, a, lda, b, ldb, c, ldc,
+                                  ctypes.byref(opts) if opts else None,
+                                  workspace, workspace_bytes,
+                                  ctypes.byref(info))
     return rc, info
 
 
@@ -383,10 +416,12 @@ def plan_for(x, out=None, *, layout: int = LAYOUT_AUTO, tile=None,
 
 
 def sgemm(a, b, c=None, *, alpha: float = 1.0, beta: float = 0.0,
-          layout: int = AS_AUTO, bk: int = 0, stream=None):
+          layout: int = AS_AUTO, bk: int = 0, split_k: int = 0, stream=None):
     """c = alpha * a @ b + beta * c for 2-D float32 CUDA tensors whose last
     dimension is contiguous (pitches come from the row strides).  With c
-    None, a new tensor is allocated and beta must be 0.  Returns c."""
+    None, a new tensor is allocated and beta must be 0.  Where the library
+    splits k (split_k 0: its own rule; >= 2: that split), torch allocates
+    the workspace for the partial sums.  Returns c."""
     import torch
     _require_device(a, b, *(() if c is None else (c,)))
     if a.dim() != 2 or b.dim() != 2:
@@ -407,8 +442,22 @@ def sgemm(a, b, c=None, *, alpha: float = 1.0, beta: float = 0.0,
     lda = a.stride(0) if m > 1 else max(k, 1)
     ldb = b.stride(0) if k > 1 else max(n, 1)
     ldc = c.stride(0) if m > 1 else max(n, 1)
-    opts = make_sgemm_opts(layout, bk) if (layout or bk) else None
-    _check(xpose_sgemm_ex(m, n, k, alpha, a.data_ptr(), lda, b.data_ptr(), ldb,
-                          beta, c.data_ptr(), ldc, opts,
-                          _stream_handle(stream)), "xpose_sgemm_ex")
+    opts = make_sgemm_opts(layout, bk, split_k=split_k)
+    args = (m, n, k, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), ldc)
+    rc, info = xpose_sgemm_plan_ws(*args, opts)   # the size query
+    if rc != XPOSE_EWORKSPACE:
+        _check(rc, "xpose_sgemm_plan_ws")
+    ws = None
+    if info.workspace_wanted:
+        ws = torch.empty(info.workspace_wanted // 4, dtype=torch.float32,
+                         device=a.device)
+    _check(xpose_sgemm_ws(m, n, k, alpha, a.data_ptr(), lda, b.data_ptr(),
+                          ldb, beta, c.data_ptr(), ldc, opts,
+                          ws.data_ptr() if ws is not None else 0,
+                          info.workspace_wanted, _stream_handle(stream)),
+           "xpose_sgemm_ws")
+    if ws is not None and stream is not None:
+        # allocated on the current stream, used on `stream`: keep it from
+        # being reused before the call's kernels have run there
+        ws.record_stream(stream)
     return c

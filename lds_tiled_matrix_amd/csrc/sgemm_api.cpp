@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "sgemm_kernels.h"
 
 namespace {
@@ -31,11 +33,15 @@ constexpr int64_t max_buffer_lda(int tile_m) {
 }
 constexpr int64_t kMaxBufferLdb = ((int64_t)1 << 31) / (4 * 129) * 2;
 
+// Split of k: at most this many slices.
+constexpr int kMaxSplits = 64;
+
 struct SgemmPlan {
   bool empty = false;
   const xpose::SgemmKernel *kernel = nullptr;
   xpose::SgemmArgs args{};
   int64_t tiles = 0;
+  int64_t workspace_wanted = 0;
 };
 
 // a * b + c without overflow, all >= 0; false if it does not fit.
@@ -60,14 +66,74 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
   return a0 < b1 && b0 < a1;
 }
 
+// Slice length for at most `want` slices of k, in whole k steps.
+int64_t split_len(int64_t k, int64_t want, int bk) {
+  const int64_t per = (k + want - 1) / want;
+  return (per + bk - 1) / bk * bk;
+}
+
+// Slices of k taken for at most `want` of length `len`.
+int64_t slice_count(int64_t k, int64_t want, int64_t len) {
+  return want < 2 || len >= k ? 1 : (k + len - 1) / len;
+}
+
+// Estimated busy time of the compute unit holding `w` workgroups of
+// `len` k elements each: they run four at a time (the register budget of
+// the 128-row kernels), and w of them together go at kShare[w] times one
+// alone (one workgroup leaves the matrix cores idle while it waits on
+// memory and barriers).
+double cu_time(int64_t w, double len) {
+  static const double kShare[5] = {0, 1.0, 1.2, 1.3, 1.4};
+  const int64_t full = w / 4, rem = w % 4;
+  double t = (double)full * 4 * len / kShare[4];
+  if (rem) t += rem * len / kShare[rem];
+  return t;
+}
+
+// The library's split: the slice count (1 = none) whose estimated time is
+// least.  Blocks count as units of 128 rows (tiles * tile_m / 128); the
+// units * slices workgroups spread over 256 compute units, so the busiest
+// holds w = ceil(units * slices / 256) and the product takes cu_time(w,
+// slice length); a split adds its partial sums, written once and read
+// once, 6 (slices + 1) m n / (256 * 1024) in the same units.  The
+// constants are fitted to measured times of 1 to 32 slices over 23 shapes
+// from 512^3 to 8192 x 8192 x 2048 on MI355X: the choice lands within 0.96
+// of the fastest measured split everywhere, 0.997 on average.
+int64_t auto_splits(int64_t tiles, int tile_m, int64_t m, int64_t n,
+                    int64_t k, int bk) {
+  const double units = (double)tiles * tile_m / 128;
+  double best_cost = 0;
+  int64_t best = 1, last = 0;
+  for (int64_t want = 1; want <= kMaxSplits; ++want) {
+    const int64_t len = split_len(k, want, bk);
+    const int64_t slices = slice_count(k, want, len);
+    if (slices == last) continue;
+    last = slices;
+    const int64_t w = (int64_t)std::ceil(units * slices / 256);
+    double cost = cu_time(w, (double)(slices > 1 ? len : k));
+    if (slices > 1) cost += 6.0 * (slices + 1) * ((double)m * n) / (256 * 1024);
+    if (want == 1 || cost < best_cost) {
+      best_cost = cost;
+      best = want;
+    }
+  }
+  return best;
+}
+
+// Validates a call and fills `plan`.  has_ws: the entry point takes a
+// workspace (`ws`, ws_bytes), so it may split k.
 int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
               const float *b, int64_t ldb, const float *c, int64_t ldc,
-              const xpose_sgemm_opts *opts, SgemmPlan &plan) {
+              const xpose_sgemm_opts *opts, bool has_ws, const void *ws,
+              int64_t ws_bytes, SgemmPlan &plan) {
   int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM,
-      tile_m = kDefaultTileM;
+      tile_m = kDefaultTileM, split = 0;
   bool remap = true, buffers = true;
   int stages = 1;
+  if (has_ws && ws_bytes < 0) return XPOSE_EINVAL;
   if (opts) {
+    if (opts->split_k < 0 || opts->split_k > kMaxSplits) return XPOSE_EINVAL;
+    split = opts->split_k;
     if (opts->layout < XPOSE_AS_AUTO || opts->layout > XPOSE_AS_SWIZZLE)
       return XPOSE_EINVAL;
     if (opts->bk != 0 && opts->bk != 8 && opts->bk != 16 && opts->bk != 32 &&
@@ -162,47 +228,98 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
   // Buffer-load byte offsets within one k step's tiles must fit in 31 bits.
   g.buf_ok = buf_ok;
   g.edge_buf = buf_ok && k % 4 == 0 && n % 4 == 0;
+  g.splits = 1;
+  g.split_k = k;
   plan.kernel = kern;
   plan.tiles = tiles;
+
+  // Split of k.  Slices are whole k steps, so every slice but the last is
+  // whole, and the last is whole exactly when k is: the kernel chosen above
+  // (whole-matrix or not) serves every slice, and its partials' pitch n is
+  // at most ldc.
+  const int64_t plane = m * n;  // fits: C's byte range did
+  auto slices_of = [&](int64_t want, int64_t *len) {
+    *len = split_len(k, want, bk);
+    return slice_count(k, want, *len);
+  };
+  int64_t want = split == 1   ? 1
+                 : split >= 2 ? split
+                 : k > 0      ? auto_splits(tiles, tile_m, m, n, k, bk)
+                              : 1;
+  int64_t len, slices = k > 0 ? slices_of(want, &len) : 1;
+  if (slices > 1) {
+    int64_t floats, bytes;
+    if (__builtin_mul_overflow(slices, plane, &floats) ||
+        __builtin_mul_overflow(floats, (int64_t)4, &bytes) ||
+        tiles * slices > INT32_MAX)
+      return XPOSE_EINVAL;
+    plan.workspace_wanted = bytes;
+  }
+  if (slices > 1 && split == 0) {
+    // The library's choice shrinks to what the workspace holds.
+    const int64_t fit = has_ws ? ws_bytes / 4 / plane : 0;
+    if (fit < slices) slices = fit < 2 ? 1 : slices_of(fit, &len);
+  } else if (slices > 1 && (!has_ws || ws_bytes / 4 / plane < slices)) {
+    return XPOSE_EWORKSPACE;
+  }
+  if (slices > 1) {
+    uintptr_t w0 = (uintptr_t)ws, w1;
+    if (!ws) return XPOSE_EINVAL;
+    if (w0 % 4) return XPOSE_EALIGN;
+    if (__builtin_add_overflow(w0, (uintptr_t)(slices * plane * 4), &w1))
+      return XPOSE_EINVAL;
+    uintptr_t a0, a1, b0, b1;
+    byte_range(a, m, k, lda, &a0, &a1);
+    byte_range(b, k, n, ldb, &b0, &b1);
+    if (overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1) ||
+        overlaps(w0, w1, c0, c1))
+      return XPOSE_EALIAS;
+    g.splits = (int32_t)slices;
+    g.split_k = len;
+    g.partial = static_cast<float *>(const_cast<void *>(ws));
+    plan.tiles = tiles * slices;
+  }
   return XPOSE_OK;
 }
 
 int run(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
         int64_t lda, const float *b, int64_t ldb, float beta, float *c,
-        int64_t ldc, const xpose_sgemm_opts *opts, void *stream) {
+        int64_t ldc, const xpose_sgemm_opts *opts, bool has_ws, void *ws,
+        int64_t ws_bytes, void *stream) {
   SgemmPlan plan;
-  const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, plan);
+  const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, has_ws, ws,
+                           ws_bytes, plan);
   if (rc != XPOSE_OK || plan.empty) return rc;
   plan.args.alpha = alpha;
   plan.args.beta = beta;
-  const hipError_t e = plan.kernel->launch(plan.args, (uint32_t)plan.tiles,
-                                           static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = plan.kernel->launch(plan.args, (uint32_t)plan.tiles, s);
+  if (e == hipSuccess && plan.args.splits > 1) {
+    xpose::SgemmReduceArgs r{};
+    r.partial = plan.args.partial;
+    r.c = c;
+    r.m = m;
+    r.n = n;
+    r.ldc = ldc;
+    r.splits = plan.args.splits;
+    r.alpha = alpha;
+    r.beta = beta;
+    e = xpose::launch_sgemm_reduce(r, s);
+  }
   return e == hipSuccess ? XPOSE_OK : xpose::record_hip_error(e);
 }
 
-}  // namespace
-
-extern "C" {
-
-int xpose_sgemm(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
-                int64_t lda, const float *b, int64_t ldb, float beta,
-                float *c, int64_t ldc, void *stream) {
-  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, nullptr, stream);
-}
-
-int xpose_sgemm_ex(int64_t m, int64_t n, int64_t k, float alpha,
-                   const float *a, int64_t lda, const float *b, int64_t ldb,
-                   float beta, float *c, int64_t ldc,
-                   const xpose_sgemm_opts *opts, void *stream) {
-  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, opts, stream);
-}
-
-int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
-                     int64_t lda, const float *b, int64_t ldb, const float *c,
-                     int64_t ldc, const xpose_sgemm_opts *opts,
-                     xpose_sgemm_info *info) {
+int plan_info(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
+              const float *b, int64_t ldb, const float *c, int64_t ldc,
+              const xpose_sgemm_opts *opts, bool has_ws, const void *ws,
+              int64_t ws_bytes, xpose_sgemm_info *info) {
   SgemmPlan plan;
-  const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, plan);
+  const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, has_ws, ws,
+                           ws_bytes, plan);
+  if (rc == XPOSE_EWORKSPACE && info) {
+    *info = xpose_sgemm_info{};
+    info->workspace_wanted = plan.workspace_wanted;
+  }
   if (rc != XPOSE_OK || !info) return rc;
   *info = xpose_sgemm_info{};
   if (plan.empty) return rc;
@@ -222,7 +339,57 @@ int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
   info->tiles = plan.tiles;
   info->whole_matrix = kern.whole ? 1 : 0;
   info->edge_buffer_loads = kern.vec && plan.args.edge_buf ? 1 : 0;
+  info->splits = plan.args.splits;
+  info->split_len = plan.args.split_k;
+  info->workspace_bytes =
+      plan.args.splits > 1 ? (int64_t)plan.args.splits * m * n * 4 : 0;
+  info->workspace_wanted = plan.workspace_wanted;
   return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int xpose_sgemm(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
+                int64_t lda, const float *b, int64_t ldb, float beta,
+                float *c, int64_t ldc, void *stream) {
+  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, nullptr, false,
+             nullptr, 0, stream);
+}
+
+int xpose_sgemm_ex(int64_t m, int64_t n, int64_t k, float alpha,
+                   const float *a, int64_t lda, const float *b, int64_t ldb,
+                   float beta, float *c, int64_t ldc,
+                   const xpose_sgemm_opts *opts, void *stream) {
+  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, opts, false,
+             nullptr, 0, stream);
+}
+
+int xpose_sgemm_plan(int64_t m, int64_t n, int64_t k, const float *a,
+                     int64_t lda, const float *b, int64_t ldb, const float *c,
+                     int64_t ldc, const xpose_sgemm_opts *opts,
+                     xpose_sgemm_info *info) {
+  return plan_info(m, n, k, a, lda, b, ldb, c, ldc, opts, false, nullptr, 0,
+                   info);
+}
+
+int xpose_sgemm_ws(int64_t m, int64_t n, int64_t k, float alpha,
+                   const float *a, int64_t lda, const float *b, int64_t ldb,
+                   float beta, float *c, int64_t ldc,
+                   const xpose_sgemm_opts *opts, void *workspace,
+                   int64_t workspace_bytes, void *stream) {
+  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, opts, true,
+             workspace, workspace_bytes, stream);
+}
+
+int xpose_sgemm_plan_ws(int64_t m, int64_t n, int64_t k, const float *a,
+                        int64_t lda, const float *b, int64_t ldb,
+                        const float *c, int64_t ldc,
+                        const xpose_sgemm_opts *opts, const void *workspace,
+                        int64_t workspace_bytes, xpose_sgemm_info *info) {
+  return plan_info(m, n, k, a, lda, b, ldb, c, ldc, opts, true, workspace,
+                   workspace_bytes, info);
 }
 
 }  // extern "C"

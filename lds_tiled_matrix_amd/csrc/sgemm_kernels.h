@@ -25,13 +25,33 @@ struct SgemmArgs {
   // descriptor extents clipped to the matrix (needs buf_ok, and k and n
   // multiples of 4 so no 16-byte vector straddles an extent's end)
   int32_t edge_buf;
+  // Split of the k range: with splits > 1 the grid is splits copies of the
+  // tiles_m * tiles_n blocks; copy z sums k in [z * split_k, min(k, (z + 1)
+  // * split_k)) and stores the raw sums (no alpha, beta or C) into the m x n
+  // partial matrix at partial + z * m * n (pitch n).  split_k is a multiple
+  // of the k step.
+  int32_t splits;
+  int64_t split_k;
+  float *partial;
 };
+
+// C = alpha * (sum over z < splits of partial z) + beta * C, the partial
+// matrices m x n with pitch n, summed in the order z = 0, 1, ...; with beta
+// == 0 C is not read.
+struct SgemmReduceArgs {
+  const float *partial;
+  float *c;
+  int64_t m, n, ldc;
+  int32_t splits;
+  float alpha, beta;
+};
+hipError_t launch_sgemm_reduce(const SgemmReduceArgs &r, hipStream_t s);
 
 struct SgemmKernel {
   int bk, layout, as_stride, lds_bytes, threads;
   bool vec;    // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)
   int stages;  // LDS buffers: 1 = two barriers per k step, 2 = one
-  int tile_m;  // rows of C per workgroup (128 or 256; 128 columns)
+  int tile_m;  // rows of C per workgroup (64, 128 or 256; 128 columns)
   hipError_t (*launch)(const SgemmArgs &, uint32_t grid, hipStream_t);
   // Built for matrices of whole blocks only: m and n multiples of the
   // block, k of the k step, buffer loads and the one-descriptor C tail

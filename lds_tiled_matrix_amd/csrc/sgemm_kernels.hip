@@ -64,16 +64,34 @@ __device__ inline float *uniform(const float *p) {
 template <int BK, int L, bool VEC, int STAGES, int BM = 128, bool WHOLE = false>
 __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(
     SgemmTile<BK, L, BM>::waves_per_simd(STAGES)))) void
-xpose_sgemm_kernel(SgemmArgs a) {
+xpose_sgemm_kernel(SgemmArgs args) {
   using T = SgemmTile<BK, L, BM>;
   static_assert(!WHOLE || (VEC && STAGES == 1), "whole-matrix kernels");
   __shared__ __attribute__((aligned(16))) float As[STAGES * T::AS_FLOATS];
   __shared__ __attribute__((aligned(16))) float Bs[STAGES * T::BS_FLOATS];
 
+  // A split of k is the same product over a slice of k, stored raw into
+  // its own partial matrix: shift A and B to the slice, shorten k, and
+  // point the epilogue at the partial with alpha = 1, beta = 0.
+  SgemmArgs a = args;
+  uint32_t block = blockIdx.x;
+  if (a.splits > 1) {
+    const uint32_t tiles = a.tiles_m * a.tiles_n;
+    const uint32_t z = block / tiles;
+    block -= z * tiles;
+    const int64_t k0 = (int64_t)z * a.split_k;
+    a.a += k0;
+    a.b += k0 * a.ldb;
+    a.k = a.k - k0 < a.split_k ? a.k - k0 : a.split_k;
+    a.c = a.partial + (int64_t)z * a.m * a.n;
+    a.ldc = a.n;
+    a.alpha = 1.f;
+    a.beta = 0.f;
+  }
+
   const int t = threadIdx.x, q = t & 63, w = t >> 6;
   uint32_t bm, bn;
-  sgemm_block(blockIdx.x, a.tiles_m, a.tiles_n, a.group_m, a.xcd_remap, bm,
-              bn);
+  sgemm_block(block, a.tiles_m, a.tiles_n, a.group_m, a.xcd_remap, bm, bn);
   const int64_t m0 = (int64_t)bm * T::BM, n0 = (int64_t)bn * T::BN;
   f32x4 ra[T::A_PASSES], rb[T::B_PASSES];
   // Buffer loads of one whole k step's tiles: the A and B tiles each get a
@@ -361,11 +379,64 @@ const SgemmKernel kSgemmKernels[] = {
     XPOSE_SGEMM_WHOLE(16, kAsUnpadded, 64), XPOSE_SGEMM_WHOLE(16, kAsPadded, 64),
     XPOSE_SGEMM_WHOLE(16, kAsSwizzle, 64)};
 
+// The sum of the split partials, 4 consecutive elements of a row per lane
+// where n is a multiple of 4 and C's rows are 16-byte aligned, else one.
+// A grid-stride loop over the m x n elements; the partials are read once
+// and C read (beta != 0) and written once.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void xpose_sgemm_reduce_kernel(
+    SgemmReduceArgs r) {
+  const int64_t per_row = VEC4 ? r.n / 4 : r.n;
+  const int64_t total = r.m * per_row, plane = r.m * r.n;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+       v += step) {
+    const int64_t i = v / per_row, j = (v - i * per_row) * (VEC4 ? 4 : 1);
+    const float *p = r.partial + i * r.n + j;
+    float *c = r.c + i * r.ldc + j;
+    if constexpr (VEC4) {
+      f32x4 s = *reinterpret_cast<const f32x4 *>(p);
+      for (int z = 1; z < r.splits; ++z)
+        s += *reinterpret_cast<const f32x4 *>(p + z * plane);
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = r.alpha * s[e];
+      if (r.beta != 0.f) {
+        const f32x4 old = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(r.beta, old[e], o[e]);
+      }
+      *reinterpret_cast<f32x4 *>(c) = o;
+    } else {
+      float s = p[0];
+      for (int z = 1; z < r.splits; ++z) s += p[z * plane];
+      float o = r.alpha * s;
+      if (r.beta != 0.f) o = fmaf(r.beta, *c, o);
+      *c = o;
+    }
+  }
+}
+
 }  // namespace
 
 const SgemmKernel *sgemm_kernels(int *count) {
   *count = (int)(sizeof kSgemmKernels / sizeof kSgemmKernels[0]);
   return kSgemmKernels;
+}
+
+hipError_t launch_sgemm_reduce(const SgemmReduceArgs &r, hipStream_t s) {
+  SgemmReduceArgs copy = r;
+  void *args[] = {&copy};
+  const bool vec4 = r.n % 4 == 0 && r.ldc % 4 == 0 &&
+                    (uintptr_t)r.c % 16 == 0 && (uintptr_t)r.partial % 16 == 0;
+  const int64_t work = vec4 ? r.m * (r.n / 4) : r.m * r.n;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  return hipLaunchKernel(
+      vec4 ? reinterpret_cast<const void *>(&xpose_sgemm_reduce_kernel<true>)
+           : reinterpret_cast<const void *>(&xpose_sgemm_reduce_kernel<false>),
+      dim3((uint32_t)blocks), dim3(256), args, 0, s);
 }
 
 }  // namespace xpose

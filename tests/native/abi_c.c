@@ -79,11 +79,14 @@ int main(void) {
   }
   SIZE(xpose_sgemm_opts);
   OFF(xpose_sgemm_opts, bk); OFF(xpose_sgemm_opts, flags);
-  OFF(xpose_sgemm_opts, tile_m);
+  OFF(xpose_sgemm_opts, tile_m); OFF(xpose_sgemm_opts, split_k);
   SIZE(xpose_sgemm_info);
   OFF(xpose_sgemm_info, as_stride); OFF(xpose_sgemm_info, xcd_remap);
   OFF(xpose_sgemm_info, tiles); OFF(xpose_sgemm_info, whole_matrix);
-  OFF(xpose_sgemm_info, edge_buffer_loads);
+  OFF(xpose_sgemm_info, edge_buffer_loads); OFF(xpose_sgemm_info, splits);
+  OFF(xpose_sgemm_info, split_len); OFF(xpose_sgemm_info, workspace_bytes);
+  OFF(xpose_sgemm_info, workspace_wanted);
+  CONST(XPOSE_EWORKSPACE);
   CONST(XPOSE_AS_UNPADDED); CONST(XPOSE_AS_PADDED); CONST(XPOSE_AS_SWIZZLE);
   CONST(XPOSE_SGEMM_NO_XCD_REMAP); CONST(XPOSE_SGEMM_DOUBLE_BUFFER); CONST(XPOSE_SGEMM_NO_BUFFER_LOADS);
   {
@@ -97,8 +100,18 @@ int main(void) {
     printf("sgemm %d layout=%d bk=%d as_stride=%d lds_bytes=%d tiles=%lld\n",
            rc, gi.layout, gi.bk, gi.as_stride, gi.lds_bytes,
            (long long)gi.tiles);
+    /* a small grid with a workspace: the library's split */
+    const void *ws = (const void *)0x330000000000ull;
+    memset(&gi, 0xff, sizeof gi);
+    const int rs = xpose_sgemm_plan_ws(1024, 1024, 1024, a, 1024, b, 1024, c,
+                                       1024, NULL, ws, (int64_t)1 << 30, &gi);
+    printf("sgemmws %d splits=%d split_len=%lld workspace_bytes=%lld "
+           "workspace_wanted=%lld tiles=%lld\n",
+           rs, gi.splits, (long long)gi.split_len,
+           (long long)gi.workspace_bytes, (long long)gi.workspace_wanted,
+           (long long)gi.tiles);
   }
-  for (int code = 0; code >= -6; --code)
+  for (int code = 0; code >= -7; --code)
     printf("strerror %d %s\n", code, xpose_strerror(code));
   return 0;
 }

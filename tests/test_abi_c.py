@@ -54,7 +54,7 @@ def test_struct_layouts_match_ctypes(c_output):
 
 def test_constants_match_binding(c_output):
     consts = dict(_entries(c_output, "const"))
-    assert len(consts) == 20
+    assert len(consts) == 21
     for name, value in consts.items():
         short = name.replace("XPOSE_FLAG_", "FLAG_").replace("XPOSE_AS_", "AS_")
         short = short.replace("XPOSE_SGEMM_", "SGEMM_")
@@ -113,5 +113,19 @@ def test_sgemm_plan_matches_binding(c_output):
     rc, info = X.xpose_sgemm_plan(4096, 4096, 4096, 0x300000000000, 4096,
                                   0x310000000000, 4096, 0x320000000000, 4096)
     assert int(f[1]) == rc == 0
+    for k, v in fields.items():
+        assert getattr(info, k) == int(v), k
+
+
+def test_sgemm_plan_ws_matches_binding(c_output):
+    line = [ln for ln in c_output if ln.startswith("sgemmws ")]
+    assert len(line) == 1
+    f = line[0].split()
+    fields = dict(kv.split("=") for kv in f[2:])
+    rc, info = X.xpose_sgemm_plan_ws(1024, 1024, 1024, 0x300000000000, 1024,
+                                     0x310000000000, 1024, 0x320000000000,
+                                     1024, None, 0x330000000000, 1 << 30)
+    assert int(f[1]) == rc == 0
+    assert info.splits > 1
     for k, v in fields.items():
         assert getattr(info, k) == int(v), k

@@ -208,3 +208,115 @@ def test_whole_matrix_kernel_choice(kw, whole):
     step, load and C tail is whole."""
     rc, info = plan(**kw)
     assert rc == 0 and info.whole_matrix == whole
+
+
+WS = 0x7f3000000000
+
+
+def plan_ws(m=1024, n=1024, k=1024, ws=WS, ws_bytes=1 << 40, opts=None,
+            a=A, b=B, c=C, ldc=None):
+    ldc = max(n, 1) if ldc is None else ldc
+    return X.xpose_sgemm_plan_ws(m, n, k, a, max(k, 1), b, max(n, 1), c, ldc,
+                                 opts, ws, ws_bytes)
+
+
+def test_no_split_without_a_workspace():
+    """xpose_sgemm and xpose_sgemm_ex never split; the plan still reports
+    what the workspace entry point would want."""
+    rc, info = plan(m=1024, n=1024, k=1024)
+    assert rc == 0 and info.splits == 1 and info.split_len == 1024
+    assert info.workspace_bytes == 0 and info.tiles == 64
+    assert info.workspace_wanted == 4 * 1024 * 1024 * 4
+    rc, info = plan(opts=X.make_sgemm_opts(split_k=4), m=1024, n=1024, k=1024)
+    assert rc == X.XPOSE_EWORKSPACE
+    # the call returns the same before launching anything
+    assert X.xpose_sgemm_ex(1024, 1024, 1024, 1.0, A, 1024, B, 1024, 0.0, C,
+                            1024, X.make_sgemm_opts(split_k=4)) == X.XPOSE_EWORKSPACE
+    assert X.strerror(X.XPOSE_EWORKSPACE).startswith("workspace")
+
+
+@pytest.mark.parametrize("m, n, k, splits, split_len", [
+    # each within 0.96 of the fastest split measured on MI355X (1 to 32
+    # slices), most of them the fastest
+    (1024, 1024, 1024, 4, 256),     # 64 blocks: one per compute unit
+    (1024, 1024, 4096, 8, 512),
+    (2048, 2048, 2048, 4, 512),     # 256 blocks
+    (1536, 1536, 1536, 5, 320),     # 144 blocks: 4 slices unbalance
+    (768, 768, 768, 7, 112),        # 36 blocks: short slices still pay
+    (512, 512, 512, 8, 64),
+    (2560, 2560, 2560, 5, 512),
+    (3072, 3072, 3072, 3, 1024),    # 576 blocks
+    (4100, 4100, 4100, 3, 1376),    # 1089 blocks: 65 in a second round
+    (4096, 4096, 4096, 1, 4096),    # 512 blocks of 256 rows: full rounds
+    (3072, 4096, 4096, 1, 4096),    # 768 blocks
+    (6144, 6144, 6144, 1, 6144),
+    (8192, 8192, 2048, 1, 2048),
+    (100, 100, 100000, 64, 1568)])  # one block: at most 64 slices
+def test_library_split_rule(m, n, k, splits, split_len):
+    rc, info = plan_ws(m, n, k)
+    assert rc == 0
+    assert (info.splits, info.split_len) == (splits, split_len)
+    tiles = -(-m // info.tile_m) * -(-n // 128)
+    assert info.tiles == tiles * splits
+    assert info.workspace_bytes == (4 * splits * m * n if splits > 1 else 0)
+    assert info.workspace_wanted == info.workspace_bytes
+    assert (splits - 1) * split_len < k <= splits * split_len
+
+
+def test_library_split_shrinks_to_the_workspace():
+    plane = 1024 * 1024 * 4
+    for ws_bytes, splits in ((4 * plane, 4), (4 * plane - 4, 3),
+                             (2 * plane + 7, 2), (2 * plane - 1, 1), (0, 1)):
+        rc, info = plan_ws(ws_bytes=ws_bytes)
+        assert rc == 0 and info.splits == splits, ws_bytes
+        assert info.workspace_bytes <= ws_bytes
+        assert info.workspace_wanted == 4 * plane
+    # no split: the workspace is not used and may be NULL
+    rc, info = plan_ws(ws=0, ws_bytes=0)
+    assert rc == 0 and info.splits == 1
+
+
+@pytest.mark.parametrize("k, split_k, splits, split_len", [
+    (1000, 3, 3, 336), (1000, 4, 4, 256), (450, 64, 57, 8 * 1),
+    (16, 4, 1, 16), (17, 2, 2, 16), (0, 8, 1, 0), (4096, 1, 1, 4096),
+    (4096, 2, 2, 2048)])
+def test_explicit_split(k, split_k, splits, split_len):
+    """split_k slices of ceil(k / split_k) rounded up to whole k steps."""
+    bk = 8 if split_k == 64 else 16
+    opts = X.make_sgemm_opts(bk=bk, split_k=split_k)
+    rc, info = plan_ws(m=300, n=200, k=k, opts=opts)
+    assert rc == 0
+    assert (info.splits, info.split_len) == (splits, split_len)
+    assert info.split_len % info.bk == 0 or splits == 1
+
+
+def test_split_validation():
+    plane = 1024 * 1024 * 4
+    four = X.make_sgemm_opts(split_k=4)
+    rc, info = plan_ws(opts=four, ws_bytes=4 * plane - 1)
+    assert rc == X.XPOSE_EWORKSPACE
+    assert info.workspace_wanted == 4 * plane and info.splits == 0
+    rc, info = plan_ws(opts=four, ws=0, ws_bytes=0)     # the size query
+    assert rc == X.XPOSE_EWORKSPACE and info.workspace_wanted == 4 * plane
+    assert plan_ws(opts=four, ws_bytes=4 * plane)[0] == 0
+    assert plan_ws(opts=X.make_sgemm_opts(split_k=65))[0] == X.XPOSE_EINVAL
+    assert plan_ws(opts=X.make_sgemm_opts(split_k=-1))[0] == X.XPOSE_EINVAL
+    assert plan_ws(ws_bytes=-1)[0] == X.XPOSE_EINVAL
+    assert plan_ws(ws=0)[0] == X.XPOSE_EINVAL          # a split needs it
+    assert plan_ws(ws=WS + 2)[0] == X.XPOSE_EALIGN
+    assert plan_ws(ws=WS + 4)[0] == 0
+    # the workspace may not overlap A, B or C (over the bytes it uses)
+    assert plan_ws(ws=C + 4 * 1024 * 1024 - 4)[0] == X.XPOSE_EALIAS
+    assert plan_ws(ws=A - 4 * plane + 4)[0] == X.XPOSE_EALIAS
+    assert plan_ws(ws=A - 4 * plane)[0] == 0
+    assert plan_ws(ws=B)[0] == X.XPOSE_EALIAS
+    # a workspace larger than the split uses may overlap C beyond those bytes
+    assert plan_ws(ws=C - 4 * plane, ws_bytes=1 << 40)[0] == 0
+    # split_k 1: never, whatever the workspace
+    rc, info = plan_ws(opts=X.make_sgemm_opts(split_k=1))
+    assert rc == 0 and info.splits == 1 and info.workspace_wanted == 0
+    # the xpose_sgemm_ws call validates the same way before launching
+    assert X.xpose_sgemm_ws(1024, 1024, 1024, 1.0, A, 1024, B, 1024, 0.0, C,
+                            1024, four, WS, 4 * plane - 1) == X.XPOSE_EWORKSPACE
+    assert X.xpose_sgemm_ws(1024, 1024, 1024, 1.0, A, 1024, B, 1024, 0.0, C,
+                            1024, None, B, 1 << 40) == X.XPOSE_EALIAS

@@ -28,6 +28,13 @@ def test_bad_step_counts_are_rejected():
     assert out.returncode != 0 and not out.stdout.strip()
 
 
+def test_bad_sgemm_shapes_are_rejected():
+    for bad in ("1024x1024", "0x5x5", "axbxc"):
+        out = run("--sgemm-shapes", bad)
+        assert out.returncode == 2 and "--sgemm-shapes" in out.stderr
+        assert not out.stdout.strip()
+
+
 def test_no_gpu_is_reported():
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():

@@ -82,3 +82,11 @@ def test_sgemm_record(record):
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 157.3
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], abs=1e-3)
     assert sg["cpu_baseline"]["kind"] == "oracle"
+    # the small-grid table: the library's split of k where 128 x 128 blocks
+    # leave compute units idle, against no split and torch
+    rows = {(r["m"], r["n"], r["k"]): r for r in sg["shapes"]}
+    assert (1024, 1024, 1024) in rows and rows[(1024, 1024, 1024)]["splits"] > 1
+    for r in rows.values():
+        assert r["split_TFLOPs"] > 0 and r["no_split_TFLOPs"] > 0
+        assert r["torch_addmm_TFLOPs"] > 0 and r["splits"] >= 1
+        assert (r["workspace_MiB"] > 0) == (r["splits"] > 1)

@@ -49,9 +49,14 @@ def _upload(buf, shift):
 
 
 def run_case(A, B, C, alpha, beta, pads=(0, 0, 0), shifts=(0, 0, 0),
-             opts=None, stream=None, entry="ex"):
+             opts=None, stream=None, entry="ex", ws_bytes=None, ws_shift=0,
+             want_splits=None):
     """Run the library; return (C buffer as read back, flat C buffer before,
-    ldc).  Both buffers include GUARD sentinels on each side."""
+    ldc).  Both buffers include GUARD sentinels on each side.  entry "ws":
+    xpose_sgemm_ws with a workspace of ws_bytes (None: what the plan wants)
+    starting ws_shift floats into an allocation, NaN-filled (a partial sum
+    the split failed to write would reach C as NaN) and followed by GUARD
+    sentinels that must stay unchanged."""
     m, k = A.shape
     n = B.shape[1]
     lda, ldb, ldc = max(k, 1) + pads[0], max(n, 1) + pads[1], max(n, 1) + pads[2]
@@ -69,6 +74,31 @@ def run_case(A, B, C, alpha, beta, pads=(0, 0, 0), shifts=(0, 0, 0),
         f"opts={None if opts is None else (opts.layout, opts.bk, opts.flags, opts.tile_m)}")
     if entry == "plain":
         rc = X.xpose_sgemm(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, sh)
+    elif entry == "ws":
+        if ws_bytes is None:
+            prc, info = X.xpose_sgemm_plan_ws(m, n, k, pa, lda, pb, ldb, pc,
+                                              ldc, opts, 1 << 40, 1 << 50)
+            assert prc == 0, X.strerror(prc)
+            ws_bytes = info.workspace_wanted
+        nws = ws_bytes // 4
+        dw = torch.full((ws_shift + nws + GUARD,), float("nan"),
+                        dtype=torch.float32, device=_dev())
+        dw[ws_shift + nws:] = float(SENTINEL)
+        pw = dw.data_ptr() + 4 * ws_shift
+        prc, info = X.xpose_sgemm_plan_ws(m, n, k, pa, lda, pb, ldb, pc, ldc,
+                                          opts, pw, ws_bytes)
+        assert prc == 0, X.strerror(prc)
+        if want_splits is not None:
+            assert info.splits == want_splits, (info.splits, want_splits)
+        assert info.workspace_bytes <= ws_bytes
+        say(f"  ws splits={info.splits} split_len={info.split_len} "
+            f"bytes={info.workspace_bytes} shift={ws_shift}")
+        rc = X.xpose_sgemm_ws(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
+                              opts, pw, ws_bytes, sh)
+        torch.cuda.synchronize()
+        tail = dw[ws_shift + nws:].cpu().numpy()
+        assert np.array_equal(tail.view(np.uint32),
+                              np.full(GUARD, SENTINEL).view(np.uint32))
     else:
         rc = X.xpose_sgemm_ex(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
                               opts, sh)
@@ -380,14 +410,113 @@ def test_random_campaign():
         check_exact(A, B, C, alpha, beta, pads=pads, shifts=shifts, opts=opts)
 
 
+SPLIT_SHAPES = [(128, 128, 512), (130, 67, 450), (300, 257, 1000),
+                (256, 384, 768), (1, 129, 333), (64, 200, 48), (257, 4, 36)]
+
+
+@pytest.mark.parametrize("splits", (2, 3, 4, 7, 64))
+def test_split_k_exact_on_integer_inputs(splits):
+    """k split into slices whose partial sums land in the workspace and are
+    added by the second kernel: exact on integer inputs, with both beta
+    paths (NaN in C with beta == 0 must not leak), ragged shapes, slices
+    that end inside a k step, every load path and A/B pitch padding."""
+    for idx, (m, n, k) in enumerate(SPLIT_SHAPES):
+        for layout, bk, tile_m, flags in ((X.AS_PADDED, 16, 128, 0),
+                                          (X.AS_SWIZZLE, 16, 256, 0),
+                                          (X.AS_UNPADDED, 32, 128,
+                                           X.SGEMM_NO_BUFFER_LOADS),
+                                          (X.AS_PADDED, 8, 128,
+                                           X.SGEMM_DOUBLE_BUFFER),
+                                          (X.AS_SWIZZLE, 16, 64, 0)):
+            opts = X.make_sgemm_opts(layout, bk, 0, flags, tile_m, splits)
+            A = wl.small_int_f32((m, k), 3100 + idx)
+            B = wl.small_int_f32((k, n), 3200 + idx)
+            C = wl.small_int_f32((m, n), 3300 + idx)
+            check_exact(A, B, C, 2.0, -1.0, opts=opts, entry="ws",
+                        pads=(idx % 3, 4 * (idx % 2), 5))
+            Cn = np.full((m, n), np.nan, np.float32)
+            got = check_exact(A, B, Cn, 1.0, 0.0, opts=opts, entry="ws")
+            assert np.isfinite(got[region_mask(m, n, max(n, 1), got.size)]).all()
+
+
+def test_split_k_plans_and_small_workspaces():
+    """The library's split at a small grid (1024 x 1024: 64 blocks), with
+    the workspace it wants, one that holds only two slices, and one that
+    holds none (then it does not split); a 4-byte aligned workspace and an
+    odd n take the one-element sum."""
+    m, n, k = 1024, 1024, 1024
+    A = wl.small_int_f32((m, k), 41)
+    B = wl.small_int_f32((k, n), 42)
+    C = wl.small_int_f32((m, n), 43)
+    rc, info = X.xpose_sgemm_plan_ws(m, n, k, 1 << 40, k, 1 << 41, n, 1 << 42,
+                                     n, None, 1 << 43, 1 << 40)
+    assert rc == 0 and info.splits > 1
+    check_exact(A, B, C, 1.0, 1.0, entry="ws", want_splits=info.splits)
+    check_exact(A, B, C, 1.0, 1.0, entry="ws", ws_bytes=2 * m * n * 4 + 100,
+                want_splits=2)
+    check_exact(A, B, C, 1.0, 1.0, entry="ws", ws_bytes=m * n * 4,
+                want_splits=1)
+    opts = X.make_sgemm_opts(split_k=3)
+    m, n, k = 200, 131, 500
+    A = wl.small_int_f32((m, k), 44)
+    B = wl.small_int_f32((k, n), 45)
+    C = wl.small_int_f32((m, n), 46)
+    check_exact(A, B, C, -1.0, 0.5, entry="ws", opts=opts, ws_shift=1,
+                want_splits=3)
+    check_exact(A, B, C, -1.0, 0.5, entry="ws", opts=opts, ws_shift=3,
+                pads=(1, 0, 2), shifts=(1, 1, 1), want_splits=3)
+
+
+def test_split_k_uniform_bound_and_repeatable():
+    """Uniform inputs: within the fp32 bound at the library's split, and
+    the same call twice gives the same bits (the partials are added in a
+    fixed order, no atomics)."""
+    for idx, (m, n, k) in enumerate(((1024, 1024, 1024), (640, 384, 3000),
+                                     (100, 1000, 2048))):
+        A = wl.uniform_f32((m, k), 4100 + idx)
+        B = wl.uniform_f32((k, n), 4200 + idx)
+        C = wl.uniform_f32((m, n), 4300 + idx)
+        got = check_bound(A, B, C, 1.0, 1.0, entry="ws")
+        again, _, _ = run_case(A, B, C, 1.0, 1.0, entry="ws")
+        assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+def test_sgemm_convenience_splits_small_grids():
+    """X.sgemm takes the library's split where the grid is small, with a
+    torch-allocated workspace; integer inputs, exact."""
+    dev = _dev()
+    m, n, k = 768, 640, 1536
+    rc, info = X.xpose_sgemm_plan_ws(m, n, k, 1 << 40, k, 1 << 41, n, 1 << 42,
+                                     n, None, 1 << 43, 1 << 40)
+    assert rc == 0 and info.splits > 1
+    A = wl.small_int_f32((m, k), 51)
+    B = wl.small_int_f32((k, n), 52)
+    C = wl.small_int_f32((m, n), 53)
+    dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+    say("sgemm convenience split")
+    X.sgemm(dA, dB, dC, alpha=2.0, beta=-1.0)
+    torch.cuda.synchronize()
+    want = og.sgemm(m, n, k, 2.0, A.reshape(-1), k, B.reshape(-1), n, -1.0,
+                    C.reshape(-1), n).astype(np.float32).reshape(m, n)
+    assert np.array_equal(dC.cpu().numpy(), want)
+    # an explicit split, and no split, through the same convenience
+    for split_k in (5, 1):
+        dC = torch.from_numpy(C).to(dev)
+        X.sgemm(dA, dB, dC, alpha=2.0, beta=-1.0, split_k=split_k)
+        torch.cuda.synchronize()
+        assert np.array_equal(dC.cpu().numpy(), want), split_k
+
+
 def test_hip_graph_capture_and_replay():
-    """The SGEMM only enqueues its kernel (no allocation, memset or
-    synchronisation), so it can be captured into a HIP graph.  C is reset
-    eagerly between replays, and every replay must match the oracle."""
+    """The SGEMM only enqueues its kernels (no allocation, memset or
+    synchronisation), so it can be captured into a HIP graph, a split of k
+    (product and sum kernels, workspace given) included.  C is reset eagerly
+    between replays, and every replay must match the oracle."""
     dev = _dev()
     cases = [((300, 257, 100), 2.0, -1.0, None),
              ((512, 384, 64), 1.0, 0.0, X.make_sgemm_opts(X.AS_SWIZZLE, 32)),
-             ((256, 256, 48), 1.0, 1.0, X.make_sgemm_opts(X.AS_PADDED, 16, 0, 0, 256))]
+             ((256, 256, 48), 1.0, 1.0, X.make_sgemm_opts(X.AS_PADDED, 16, 0, 0, 256)),
+             ((256, 130, 1000), 1.0, 1.0, X.make_sgemm_opts(split_k=4))]
     bufs = []
     for idx, ((m, n, k), alpha, beta, opts) in enumerate(cases):
         A = wl.small_int_f32((m, k), 60 + idx)
@@ -395,17 +524,27 @@ def test_hip_graph_capture_and_replay():
         C = wl.small_int_f32((m, n), 80 + idx)
         want = og.sgemm(m, n, k, alpha, A.reshape(-1), k, B.reshape(-1), n, beta,
                         C.reshape(-1), n).astype(np.float32)
+        ws = None
+        if opts is not None and opts.split_k:
+            ws = torch.empty(4 * m * n, dtype=torch.float32, device=dev)
         bufs.append((torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
                      torch.from_numpy(C).to(dev), torch.from_numpy(C).to(dev),
-                     alpha, beta, opts, want))
+                     alpha, beta, opts, want, ws))
 
     def enqueue():
         sh = int(torch.cuda.current_stream().cuda_stream)
-        for dA, dB, dC, _, alpha, beta, opts, _ in bufs:
+        for dA, dB, dC, _, alpha, beta, opts, _, ws in bufs:
             m, k = dA.shape
             n = dB.shape[1]
-            assert X.xpose_sgemm_ex(m, n, k, alpha, dA.data_ptr(), k, dB.data_ptr(), n,
-                                    beta, dC.data_ptr(), n, opts, sh) == 0
+            if ws is None:
+                assert X.xpose_sgemm_ex(m, n, k, alpha, dA.data_ptr(), k,
+                                        dB.data_ptr(), n, beta, dC.data_ptr(),
+                                        n, opts, sh) == 0
+            else:
+                assert X.xpose_sgemm_ws(m, n, k, alpha, dA.data_ptr(), k,
+                                        dB.data_ptr(), n, beta, dC.data_ptr(),
+                                        n, opts, ws.data_ptr(),
+                                        4 * ws.numel(), sh) == 0
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -424,5 +563,5 @@ def test_hip_graph_capture_and_replay():
         say(f"sgemm graph replay {rep}")
         g.replay()
         torch.cuda.synchronize()
-        for i, (_, _, dC, _, _, _, _, want) in enumerate(bufs):
+        for i, (_, _, dC, _, _, _, _, want, _) in enumerate(bufs):
             assert np.array_equal(dC.cpu().numpy(), want), f"replay {rep}, case {i}"
