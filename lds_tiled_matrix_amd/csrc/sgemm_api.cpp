@@ -33,8 +33,10 @@ constexpr int64_t max_buffer_lda(int tile_m) {
 }
 constexpr int64_t kMaxBufferLdb = ((int64_t)1 << 31) / (4 * 129) * 2;
 
-// Split of k: at most this many slices.
+// Split of k: at most this many slices; the library's own choice keeps
+// slices at least kMinAutoSplitLen long (the shortest measured to pay).
 constexpr int kMaxSplits = 64;
+constexpr int64_t kMinAutoSplitLen = 64;
 
 struct SgemmPlan {
   bool empty = false;
@@ -91,14 +93,17 @@ double cu_time(int64_t w, double len) {
 }
 
 // The library's split: the slice count (1 = none) whose estimated time is
-// least.  Blocks count as units of 128 rows (tiles * tile_m / 128); the
-// units * slices workgroups spread over 256 compute units, so the busiest
-// holds w = ceil(units * slices / 256) and the product takes cu_time(w,
-// slice length); a split adds its partial sums, written once and read
-// once, 6 (slices + 1) m n / (256 * 1024) in the same units.  The
-// constants are fitted to measured times of 1 to 32 slices over 23 shapes
-// from 512^3 to 8192 x 8192 x 2048 on MI355X: the choice lands within 0.96
-// of the fastest measured split everywhere, 0.997 on average.
+// least, among slices of at least kMinAutoSplitLen.  Blocks count as units
+// of 128 rows (tiles * tile_m / 128).  The units * slices workgroups spread
+// over 256 compute units, so the busiest holds w = ceil(units * slices /
+// 256), and the product takes cu_time(w, slice length).  A split adds its
+// partial sums, written once and read once, 6 (slices + 1) m n / (256 *
+// 1024) in the same units, and 40 for the second kernel's launch (about
+// 3 us; a unit is one k element of a lone workgroup, 1024 of which take
+// 73 us).  The constants are fitted to measured times of 1 to 32 slices
+// over 23 shapes from 512^3 to 8192 x 8192 x 2048 on MI355X: the choice
+// lands within 0.96 of the fastest measured split everywhere, 0.997 on
+// average.
 int64_t auto_splits(int64_t tiles, int tile_m, int64_t m, int64_t n,
                     int64_t k, int bk) {
   const double units = (double)tiles * tile_m / 128;
@@ -108,10 +113,12 @@ int64_t auto_splits(int64_t tiles, int tile_m, int64_t m, int64_t n,
     const int64_t len = split_len(k, want, bk);
     const int64_t slices = slice_count(k, want, len);
     if (slices == last) continue;
+    if (slices > 1 && len < kMinAutoSplitLen) break;
     last = slices;
     const int64_t w = (int64_t)std::ceil(units * slices / 256);
     double cost = cu_time(w, (double)(slices > 1 ? len : k));
-    if (slices > 1) cost += 6.0 * (slices + 1) * ((double)m * n) / (256 * 1024);
+    if (slices > 1)
+      cost += 6.0 * (slices + 1) * ((double)m * n) / (256 * 1024) + 40;
     if (want == 1 || cost < best_cost) {
       best_cost = cost;
       best = want;
