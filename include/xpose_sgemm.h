@@ -228,6 +228,34 @@ int xpose_sgemm_ws(int64_t m, int64_t n, int64_t k, float alpha,
                    const xpose_sgemm_opts *opts, void *workspace,
                    int64_t workspace_bytes, void *stream);
 
+/* Size of the device scratch array of xpose_sgemm_noalloc, per GPU. */
+#define XPOSE_SGEMM_SCRATCH_BYTES ((int64_t)64 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * as xpose_sgemm_ws, with the workspace replaced by the library's own
+ * device array of XPOSE_SGEMM_SCRATCH_BYTES (64 MiB), a file-scope device
+ * array of the library that each GPU it runs on holds until the process
+ * ends; the call allocates nothing, and neither does any library routine it
+ * calls.  A split of k the library chooses (opts->split_k == 0) is shrunk
+ * to what the scratch holds (none when one m x n plane does not fit, as
+ * for m n > 16 Mi); an explicit split_k >= 2 whose partials (splits * m * n
+ * * 4 bytes) exceed it is rejected with XPOSE_EWORKSPACE before anything is
+ * launched.  xpose_sgemm_plan_ws with workspace_bytes =
+ * XPOSE_SGEMM_SCRATCH_BYTES reports the split it takes.
+ *
+ * Every call on one GPU shares that GPU's array, and it keeps the last
+ * call's contents (nothing in it needs to start at zero: each split writes
+ * all of its partials before summing them).  Calls that overlap in time on
+ * one GPU -- on different streams, or from different threads -- race on the
+ * array and give wrong results; serialise them (one stream, or events).  On
+ * a device's first call the array's device address is looked up (a HIP
+ * symbol query, XPOSE_EHIP if it fails) and kept. */
+int xpose_sgemm_noalloc(int64_t m, int64_t n, int64_t k, float alpha,
+                        const float *a, int64_t lda, const float *b,
+                        int64_t ldb, float beta, float *c, int64_t ldc,
+                        const xpose_sgemm_opts *opts, void *stream);
+
 /* Host-only counterpart of xpose_sgemm_ws, as xpose_sgemm_plan is of
  * xpose_sgemm_ex (the workspace too is compared, never dereferenced).
  * With workspace NULL and workspace_bytes 0 it serves as the size query:

@@ -10,7 +10,8 @@ Low-level names mirror the C ABI (``xpose_2d``, ``xpose_2d_ex``,
 ``xpose_batched``,
 ``xpose_batched_ex``, ``xpose_copy``, ``xpose_plan``, ``xpose_lds_probe``,
 and the tiled SGEMM's ``xpose_sgemm``, ``xpose_sgemm_ex``,
-``xpose_sgemm_plan``, ``xpose_sgemm_ws``, ``xpose_sgemm_plan_ws`` of
+``xpose_sgemm_plan``, ``xpose_sgemm_ws``, ``xpose_sgemm_noalloc``,
+``xpose_sgemm_plan_ws`` of
 ``include/xpose_sgemm.h``) and take raw device
 addresses as integers.  ``transpose``, ``copy`` and ``sgemm`` are
 conveniences over torch tensors: torch supplies the device memory and the
@@ -29,6 +30,7 @@ XPOSE_OK = 0
 XPOSE_EINVAL, XPOSE_EALIAS, XPOSE_EDTYPE = -1, -2, -3
 XPOSE_EHIP, XPOSE_EALIGN, XPOSE_ENOTILE = -4, -5, -6
 XPOSE_EWORKSPACE = -7
+SGEMM_SCRATCH_BYTES = 64 << 20   # xpose_sgemm_noalloc's device array, per GPU
 LAYOUT_AUTO, LAYOUT_UNPADDED, LAYOUT_PAD1, LAYOUT_SWIZZLE = 0, 1, 2, 3
 LAYOUT_NAIVE_READ, LAYOUT_NAIVE_WRITE = 4, 5
 LAYOUT_NAMES = {LAYOUT_UNPADDED: "unpadded", LAYOUT_PAD1: "pad1",
@@ -56,7 +58,7 @@ EXPORTS = ("xpose_2d", "xpose_2d_ex", "xpose_batched", "xpose_batched_ex",
            "xpose_copy", "xpose_copy_ex", "xpose_lds_probe",
            "xpose_last_hip_error", "xpose_strerror",
            "xpose_sgemm", "xpose_sgemm_ex", "xpose_sgemm_plan",
-           "xpose_sgemm_ws", "xpose_sgemm_plan_ws")
+           "xpose_sgemm_ws", "xpose_sgemm_noalloc", "xpose_sgemm_plan_ws")
 
 
 class XposeOpts(ctypes.Structure):
@@ -151,6 +153,8 @@ def _load() -> ctypes.CDLL:
                              ctypes.POINTER(XposeSgemmInfo)],
         "xpose_sgemm_ws": [i64, i64, i64, f32, p, i64, p, i64, f32, p, i64,
                            ctypes.POINTER(XposeSgemmOpts), p, i64, p],
+        "xpose_sgemm_noalloc": [i64, i64, i64, f32, p, i64, p, i64, f32, p,
+                                i64, ctypes.POINTER(XposeSgemmOpts), p],
         "xpose_sgemm_plan_ws": [i64, i64, i64, p, i64, p, i64, p, i64,
                                 ctypes.POINTER(XposeSgemmOpts), p, i64,
                                 ctypes.POINTER(XposeSgemmInfo)],
@@ -285,6 +289,15 @@ def xpose_sgemm_ws(m: int, n: int, k: int, alpha: float, a: int, lda: int,
     return _lib.xpose_sgemm_ws(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc,
                                ctypes.byref(opts) if opts else None,
                                workspace, workspace_bytes, stream)
+
+
+def xpose_sgemm_noalloc(m: int, n: int, k: int, alpha: float, a: int,
+                        lda: int, b: int, ldb: int, beta: float, c: int,
+                        ldc: int, opts: XposeSgemmOpts | None = None,
+                        stream: int = 0) -> int:
+    return _lib.xpose_sgemm_noalloc(m, n, k, alpha, a, lda, b, ldb, beta, c,
+                                    ldc, ctypes.byref(opts) if opts else None,
+                                    stream)
 
 
 def xpose_sgemm_plan_ws(m: int, n: int, k: int, a: int, lda: int, b: int,

@@ -128,11 +128,14 @@ int64_t auto_splits(int64_t tiles, int tile_m, int64_t m, int64_t n,
 }
 
 // Validates a call and fills `plan`.  has_ws: the entry point takes a
-// workspace (`ws`, ws_bytes), so it may split k.
+// workspace (`ws`, ws_bytes), so it may split k.  scratch: the workspace is
+// the library's own device array (ws_bytes = kSgemmScratchBytes, `ws`
+// ignored), whose address is only looked up once every argument has been
+// validated and the call does split.
 int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
               const float *b, int64_t ldb, const float *c, int64_t ldc,
               const xpose_sgemm_opts *opts, bool has_ws, const void *ws,
-              int64_t ws_bytes, SgemmPlan &plan) {
+              int64_t ws_bytes, SgemmPlan &plan, bool scratch = false) {
   int layout = kDefaultLayout, bk = kDefaultBk, group_m = kDefaultGroupM,
       tile_m = kDefaultTileM, split = 0;
   bool remap = true, buffers = true;
@@ -270,6 +273,12 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
     return XPOSE_EWORKSPACE;
   }
   if (slices > 1) {
+    if (scratch) {
+      void *p = nullptr;
+      const hipError_t e = xpose::sgemm_scratch(&p);
+      if (e != hipSuccess) return xpose::record_hip_error(e);
+      ws = p;
+    }
     uintptr_t w0 = (uintptr_t)ws, w1;
     if (!ws) return XPOSE_EINVAL;
     if (w0 % 4) return XPOSE_EALIGN;
@@ -292,10 +301,10 @@ int make_plan(int64_t m, int64_t n, int64_t k, const float *a, int64_t lda,
 int run(int64_t m, int64_t n, int64_t k, float alpha, const float *a,
         int64_t lda, const float *b, int64_t ldb, float beta, float *c,
         int64_t ldc, const xpose_sgemm_opts *opts, bool has_ws, void *ws,
-        int64_t ws_bytes, void *stream) {
+        int64_t ws_bytes, void *stream, bool scratch = false) {
   SgemmPlan plan;
   const int rc = make_plan(m, n, k, a, lda, b, ldb, c, ldc, opts, has_ws, ws,
-                           ws_bytes, plan);
+                           ws_bytes, plan, scratch);
   if (rc != XPOSE_OK || plan.empty) return rc;
   plan.args.alpha = alpha;
   plan.args.beta = beta;
@@ -388,6 +397,14 @@ int xpose_sgemm_ws(int64_t m, int64_t n, int64_t k, float alpha,
                    int64_t workspace_bytes, void *stream) {
   return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, opts, true,
              workspace, workspace_bytes, stream);
+}
+
+int xpose_sgemm_noalloc(int64_t m, int64_t n, int64_t k, float alpha,
+                        const float *a, int64_t lda, const float *b,
+                        int64_t ldb, float beta, float *c, int64_t ldc,
+                        const xpose_sgemm_opts *opts, void *stream) {
+  return run(m, n, k, alpha, a, lda, b, ldb, beta, c, ldc, opts, true,
+             nullptr, xpose::kSgemmScratchBytes, stream, true);
 }
 
 int xpose_sgemm_plan_ws(int64_t m, int64_t n, int64_t k, const float *a,

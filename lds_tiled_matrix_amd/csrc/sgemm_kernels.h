@@ -47,6 +47,14 @@ struct SgemmReduceArgs {
 };
 hipError_t launch_sgemm_reduce(const SgemmReduceArgs &r, hipStream_t s);
 
+// The partial sums of xpose_sgemm_noalloc live in a file-scope device array
+// of kSgemmScratchBytes in sgemm_kernels.hip, one per GPU for the life of
+// the process.  sgemm_scratch() gives its address on the current device:
+// looked up with hipGetSymbolAddress on a device's first call (with that
+// device current) and kept per device.  It allocates nothing.
+constexpr int64_t kSgemmScratchBytes = (int64_t)64 << 20;
+hipError_t sgemm_scratch(void **ptr);
+
 struct SgemmKernel {
   int bk, layout, as_stride, lds_bytes, threads;
   bool vec;    // 16-byte tile loads (a, b 16-byte aligned, lda, ldb % 4 == 0)

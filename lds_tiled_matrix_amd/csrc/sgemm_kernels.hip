@@ -12,8 +12,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sgemm_lanes.h"
 #include "sgemm_kernels.h"
+
+// The no-allocation entry point's partial sums: 64 MiB per GPU, held until
+// the process ends.  In host code this name is only a stand-in for the
+// device array, never a device address: host code takes the address from
+// sgemm_scratch() below and passes that to kernels.
+static __device__ __align__(256) float
+    scratch[xpose::kSgemmScratchBytes / sizeof(float)];
 
 namespace xpose {
 namespace {
@@ -437,6 +446,28 @@ hipError_t launch_sgemm_reduce(const SgemmReduceArgs &r, hipStream_t s) {
       vec4 ? reinterpret_cast<const void *>(&xpose_sgemm_reduce_kernel<true>)
            : reinterpret_cast<const void *>(&xpose_sgemm_reduce_kernel<false>),
       dim3((uint32_t)blocks), dim3(256), args, 0, s);
+}
+
+// Once per device, with that device current: the device address of
+// `scratch`, kept per device (each GPU holds its own copy of the array at
+// its own address).  Concurrent first calls may both look it up; they store
+// the same value.
+hipError_t sgemm_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace xpose

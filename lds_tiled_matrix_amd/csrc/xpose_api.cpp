@@ -791,7 +791,8 @@ const char *xpose_strerror(int code) {
     case XPOSE_EALIGN: return "pointer not aligned to the element size";
     case XPOSE_ENOTILE: return "no kernel built for the requested options";
     case XPOSE_EWORKSPACE:
-      return "workspace too small for the requested split of k";
+      return "workspace (or the 64 MiB no-allocation scratch) too small "
+             "for the requested split of k";
     default: return "unknown status code";
   }
 }

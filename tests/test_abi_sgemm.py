@@ -320,3 +320,20 @@ def test_split_validation():
                             1024, four, WS, 4 * plane - 1) == X.XPOSE_EWORKSPACE
     assert X.xpose_sgemm_ws(1024, 1024, 1024, 1.0, A, 1024, B, 1024, 0.0, C,
                             1024, None, B, 1 << 40) == X.XPOSE_EALIAS
+
+
+def test_noalloc_validates_before_touching_the_gpu():
+    """xpose_sgemm_noalloc checks its arguments, and an explicit split
+    against its 64 MiB scratch, before it looks the scratch up or launches
+    anything."""
+    assert X.SGEMM_SCRATCH_BYTES == 64 << 20
+    assert X.xpose_sgemm_noalloc(1024, 1024, 1024, 1.0, A, 1000, B, 1024,
+                                 0.0, C, 1024) == X.XPOSE_EINVAL
+    assert X.xpose_sgemm_noalloc(1024, 1024, 1024, 1.0, A, 1024, B, 1024,
+                                 0.0, A, 1024) == X.XPOSE_EALIAS
+    # 1024 x 1024 planes are 4 MiB: 16 fit, 17 (k = 17 * 256) do not
+    assert X.xpose_sgemm_noalloc(1024, 1024, 4352, 1.0, A, 4352, B, 1024,
+                                 0.0, C, 1024,
+                                 X.make_sgemm_opts(split_k=17)) == X.XPOSE_EWORKSPACE
+    assert X.xpose_sgemm_noalloc(0, 1024, 4096, 1.0, 0, 4096, 0, 1024, 0.0,
+                                 0, 1024) == X.XPOSE_OK
