@@ -78,3 +78,53 @@ def test_noalloc_limits():
     assert rc == X.XPOSE_EWORKSPACE
     assert "scratch" in X.strerror(rc)
     _one_call(256, 256, 32, 1.0, 0.5, None, 520, 1)
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for: captured into a HIP graph (after one eager
+    call, which looks the scratch address up), two split calls in a row
+    share the scratch; C is reset eagerly between replays and every replay
+    must match the oracle exactly."""
+    dev = _dev()
+    cases = [((1024, 1024, 1024), 1.0, 1.0, None),
+             ((256, 130, 1000), 2.0, 0.0, X.make_sgemm_opts(split_k=4))]
+    bufs = []
+    for idx, ((m, n, k), alpha, beta, opts) in enumerate(cases):
+        A = wl.small_int_f32((m, k), 530 + 3 * idx)
+        B = wl.small_int_f32((k, n), 531 + 3 * idx)
+        C = wl.small_int_f32((m, n), 532 + 3 * idx)
+        want = og.sgemm(m, n, k, alpha, A.reshape(-1), k, B.reshape(-1), n,
+                        beta, C.reshape(-1), n).astype(np.float32)
+        bufs.append((torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                     torch.from_numpy(C).to(dev), torch.from_numpy(C).to(dev),
+                     alpha, beta, opts, want.reshape(m, n)))
+
+    def enqueue():
+        sh = int(torch.cuda.current_stream().cuda_stream)
+        for dA, dB, dC, _, alpha, beta, opts, _ in bufs:
+            m, k = dA.shape
+            n = dB.shape[1]
+            rc = X.xpose_sgemm_noalloc(m, n, k, alpha, dA.data_ptr(), k,
+                                       dB.data_ptr(), n, beta, dC.data_ptr(),
+                                       n, opts, sh)
+            assert rc == 0, X.strerror(rc)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        say("noalloc graph warm-up")
+        enqueue()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue()
+    for rep in range(3):
+        for _, _, dC, dC0, *_ in bufs:
+            dC.copy_(dC0)
+        torch.cuda.synchronize()
+        say(f"noalloc graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (_, _, dC, _, _, _, _, want) in enumerate(bufs):
+            assert np.array_equal(dC.cpu().numpy(), want), (rep, i)
