@@ -179,7 +179,15 @@ typedef struct xpose_opts {
                          persistent workgroups per compute unit, each
                          walking many tiles with two LDS buffers so the
                          next tile's loads overlap the current tile's
-                         stores (swizzled layout only)                      */
+                         stores (swizzled layout only).  For line-aligned
+                         output tiles (4- and 8-byte elements; built for
+                         fp32 64x64, 128x64, 128x32 and fp64 32x32, 64x32,
+                         non-temporal stores): column strips instead, each
+                         workgroup walking n (1..64) tile rows of one tile
+                         column top to bottom with its input rows in an
+                         LDS ring of twice the tile height, so the one-line
+                         halo is not read again; order and group_* are
+                         ignored there                                      */
   int32_t occupancy;  /* tile kernels: at most this many workgroups of the
                          launch share one compute unit (1..64), enforced by
                          reserving LDS that is never touched; 0 = the
@@ -205,7 +213,9 @@ typedef struct xpose_plan_info {
   int32_t group_cols;  /* resolved super-tile width in tiles                  */
   int32_t xcd_remap;   /* 1 if tiles are remapped per XCD                    */
   int32_t order;       /* resolved xpose_order                               */
-  int32_t persistent;  /* persistent workgroups per compute unit, 0 = none   */
+  int32_t persistent;  /* persistent workgroups per compute unit (line-
+                          aligned column strips: tile rows per workgroup),
+                          0 = none                                          */
   int32_t direct_lds;  /* 1 if interior tiles load straight into LDS         */
   int32_t aligned_out; /* 1 if output segments are shifted onto lines        */
   int32_t tr_read;     /* 1 if the column walk uses LDS transpose reads      */

@@ -436,8 +436,12 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (!k && !explicit_tile) k = lookup(d, d.align_out || want_align, true);
   if (!k) return XPOSE_ENOTILE;
   const int tr = k->tile_rows, tc = k->tile_cols;
+  // persistent: n workgroups per compute unit walking the tiles; for
+  // line-aligned tiles, column strips of n tile rows per workgroup.
   const int persistent = opts ? opts->persistent : 0;
-  if (persistent && !k->launch_persistent) return XPOSE_ENOTILE;
+  if (persistent && (k->aligned_out ? k->launch_strip == nullptr
+                                     : k->launch_persistent == nullptr))
+    return XPOSE_ENOTILE;
 
   // Line-aligned output tiles shift each segment back by up to 128 / s - 1
   // rows, so one more partial tile row may be needed to reach the last row.
@@ -619,7 +623,12 @@ int run_plan(Plan &plan, void *stream) {
     a.out = static_cast<char *>(a.out) + b0 * a.stride_out * s;
     const uint32_t ntiles = (uint32_t)(nb * plan.tiles_per_matrix);
     hipError_t e;
-    if (plan.persistent) {
+    if (plan.persistent && plan.kernel->aligned_out) {
+      const uint32_t seg = (uint32_t)plan.persistent;
+      const uint32_t nseg = (a.tiles_r + seg - 1) / seg;
+      const int64_t grid = nb * (int64_t)nseg * a.tiles_c;  // <= nb * tiles
+      e = plan.kernel->launch_strip(a, seg, nseg, (uint32_t)grid, st);
+    } else if (plan.persistent) {
       int cus = 0;
       e = compute_units(&cus);
       if (e != hipSuccess) return hip_fail(e);
@@ -711,7 +720,9 @@ int xpose_plan(const void *out, const void *in, int64_t batch, int64_t rows,
       info->tile_rows = plan.kernel->tile_rows;
       info->tile_cols = plan.kernel->tile_cols;
       info->threads = plan.kernel->threads;
-      info->lds_bytes = plan.kernel->lds_bytes;
+      info->lds_bytes = plan.persistent && plan.kernel->aligned_out
+                            ? plan.kernel->strip_lds_bytes
+                            : plan.kernel->lds_bytes;
       info->vector_path = plan.args.vec_ok;
       info->tiles = plan.tiles_per_matrix * plan.batch;
       info->launches = (int32_t)((plan.batch + plan.batch_per_launch - 1) /

@@ -122,6 +122,13 @@ struct TileKernel {
   // Row-major LDS tile of raw elements read back with the LDS transpose
   // reads (ds_read_b64_tr_b16 / _b8; 1- and 2-byte elements only).
   bool tr_read = false;
+  // Line-aligned tiles in column strips (null if not built): `grid` =
+  // batch_count * nseg * tiles_c workgroups, each walking `seg` tile rows
+  // (nseg = ceil(tiles_r / seg) segments per strip) with its input rows in
+  // an LDS ring of strip_lds_bytes.
+  hipError_t (*launch_strip)(const TileArgs &, uint32_t seg, uint32_t nseg,
+                             uint32_t grid, hipStream_t) = nullptr;
+  int strip_lds_bytes = 0;
 };
 
 // Every compiled tile kernel; *count receives the table length.

@@ -579,6 +579,188 @@ hipError_t launch_shift(const TileArgs &a, uint32_t grid, uint32_t lds_extra,
 }
 
 // ---------------------------------------------------------------------------
+// Column strips of line-aligned output tiles (4- and 8-byte elements).  The
+// one-shot line-aligned tile reads its HALO rows again although the tile
+// above it has just read them.  Here workgroup (segment s, tile column tc)
+// walks tile rows [s seg, min((s + 1) seg, tiles_r)) of tile column tc top
+// to bottom and keeps the input rows in a ring of Q = 2 TR rows of LDS
+// (input row r in ring row (r + HALO) mod Q): after the segment's first
+// tile, each tile loads only its own TR rows and finds its halo in the
+// ring.  The next tile's rows are loaded into registers before the current
+// tile is gathered and stored, so those loads are in flight during the
+// stores.  Two barriers per tile: every gather of tile t must be done before
+// tile t + 1's rows overwrite tile t's halo rows in the ring, and those rows
+// must be in the ring before tile t + 1's gathers.  Q is a multiple of the
+// swizzle's period, so each ring row keeps the bank pattern of the same row
+// of the one-shot tile.
+// ---------------------------------------------------------------------------
+template <int S, int TR, int TC, int NT, int CP>
+struct StripTile {
+  using Shift = ShiftTile<S, TR, TC, NT, CP>;
+  static constexpr int HALO = Shift::HALO, Q = 2 * TR;
+  using Ring = Tile<S, Q, TC, NT, kSwizzle, CP>;
+  using U = typename Ring::U;
+  static constexpr int V = Ring::V, NCI = Ring::NCI, NW = NT / 64;
+  static constexpr int LIT_NEW = TR * NCI / NT;     // load tasks, TR rows
+  static constexpr int LIT_HALO = HALO * NCI / NT;  // load tasks, HALO rows
+  static constexpr int PERIOD = Ring::UPV * Ring::NCL / Ring::QSTEP;
+  static constexpr int LDS_BYTES = Ring::LDS_BYTES;
+  static_assert(Ring::K == 1, "one input row per LDS unit (4, 8 bytes)");
+  static_assert(HALO <= TR && Q % PERIOD == 0, "ring keeps the swizzle");
+  static_assert(LIT_NEW >= 1 && LIT_HALO >= 1 && TR * NCI % NT == 0 &&
+                    HALO * NCI % NT == 0,
+                "even load split");
+  XPOSE_HD static inline int ring_row(int64_t r) {
+    return (int)((r + HALO) & (Q - 1));
+  }
+};
+
+// Input rows [first, first + LIT * NT / NCI) of the strip's columns
+// [c0, c0 + TC) into registers; rows outside the matrix and columns past
+// its edge read as zero (never stored).
+template <class ST, int LIT>
+__device__ __forceinline__ void strip_load(u32x4 (&v)[LIT], const char *in,
+                                           int64_t first, int64_t rows,
+                                           int64_t ld_in, int64_t c0,
+                                           int64_t cols_left, int wave,
+                                           int lane) {
+  constexpr int S = (int)sizeof(typename ST::Ring::E);
+  using E = typename Elem<S>::E;
+#pragma unroll
+  for (int it = 0; it < LIT; ++it) {
+    int p, ch;
+    lane_map<ST::NCI, false>(it * ST::NW + wave, lane, p, ch);
+    const int64_t row = first + p;
+    const char *src = in + (row * ld_in + c0 + ch * ST::V) * S;
+    if (row < 0 || row >= rows) {
+      v[it] = u32x4{0, 0, 0, 0};
+    } else if ((ch + 1) * ST::V <= cols_left) {
+      v[it] = load16<ST::Ring::CACHE == kNtLoadStore ? kNtLoadStore
+                                                     : kCacheDefault>(src);
+    } else {
+      E e[ST::V];
+#pragma unroll
+      for (int x = 0; x < ST::V; ++x)
+        e[x] = ch * ST::V + x < cols_left ? reinterpret_cast<const E *>(src)[x]
+                                          : E(0);
+      __builtin_memcpy(&v[it], e, 16);
+    }
+  }
+}
+
+template <class ST, int LIT>
+__device__ __forceinline__ void strip_to_ring(typename ST::U *lds,
+                                              const u32x4 (&v)[LIT],
+                                              int64_t first, int wave,
+                                              int lane) {
+  constexpr int S = (int)sizeof(typename ST::Ring::E);
+#pragma unroll
+  for (int it = 0; it < LIT; ++it) {
+    int p, ch;
+    lane_map<ST::NCI, false>(it * ST::NW + wave, lane, p, ch);
+    typename ST::U u[ST::V];
+    pack_units<S>(&v[it], u);
+    write_units<typename ST::Ring>(lds, ST::ring_row(first + p), ch * ST::V,
+                                   u);
+  }
+}
+
+template <int S, int TR, int TC, int NT, int CP>
+__global__ __launch_bounds__(NT) void xpose_shift_strip_kernel(TileArgs a,
+                                                               uint32_t seg,
+                                                               uint32_t nseg) {
+  using ST = StripTile<S, TR, TC, NT, CP>;
+  using Sh = typename ST::Shift;
+  using E = typename Elem<S>::E;
+  __shared__ __attribute__((aligned(16))) typename ST::U lds[ST::Ring::LDS_UNITS];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t g = blockIdx.x;
+  if (a.xcd_remap) {
+    const uint32_t q = gridDim.x / 8, r = gridDim.x % 8, x = g % 8;
+    g = x * q + (x < r ? x : r) + g / 8;
+  }
+  // Workgroups of one segment row are consecutive: neighbouring strips,
+  // which share the input lines that straddle their column edge, run
+  // together on one XCD.
+  const uint32_t per = nseg * a.tiles_c;
+  const int64_t b = (int64_t)(g / per) + a.batch_first;
+  g %= per;
+  const uint32_t tc = g % a.tiles_c, tr_first = (g / a.tiles_c) * seg;
+  const uint32_t tr_end =
+      tr_first + seg < a.tiles_r ? tr_first + seg : a.tiles_r;
+  const int64_t c0 = (int64_t)tc * TC, cols_left = a.cols - c0;
+  const char *in = static_cast<const char *>(a.in) + b * a.stride_in * S;
+  char *out = static_cast<char *>(a.out) + b * a.stride_out * S;
+
+  {  // the first tile's rows, its halo included
+    const int64_t r0 = (int64_t)tr_first * TR;
+    u32x4 h[ST::LIT_HALO];
+    strip_load<ST>(h, in, r0 - ST::HALO, a.rows, a.ld_in, c0, cols_left, wave,
+                   lane);
+    strip_to_ring<ST>(lds, h, r0 - ST::HALO, wave, lane);
+    u32x4 v[ST::LIT_NEW];
+    strip_load<ST>(v, in, r0, a.rows, a.ld_in, c0, cols_left, wave, lane);
+    strip_to_ring<ST>(lds, v, r0, wave, lane);
+  }
+  __syncthreads();
+  // tr_first and tr_end are uniform per workgroup, so every wave takes the
+  // same trips and reaches the same barriers.
+  for (uint32_t tr = tr_first; tr < tr_end; ++tr) {
+    const int64_t r0 = (int64_t)tr * TR;
+    const bool more = tr + 1 < tr_end;
+    u32x4 v[ST::LIT_NEW];
+    if (more)
+      strip_load<ST>(v, in, r0 + TR, a.rows, a.ld_in, c0, cols_left, wave,
+                     lane);
+    // Output row j = c0 + c, line-aligned segment from input row r0 - d_j
+    // (as the one-shot line-aligned tile), its rows read from the ring.
+#pragma unroll
+    for (int it = 0; it < Sh::SIT; ++it) {
+      int c, q;
+      lane_map<Sh::NCO, true>(it * Sh::NW + wave, lane, c, q);
+      if (c < cols_left) {
+        char *row_out = out + (c0 + c) * a.ld_out * S;
+        const int d = (int)(((uintptr_t)row_out & 127) / S);
+        const int64_t first = r0 - d + ST::V * q;
+        typename ST::U w[ST::V];
+#pragma unroll
+        for (int k = 0; k < ST::V; ++k)
+          w[k] = lds[ST::Ring::lds_index(ST::ring_row(first + k), c)];
+        const u32x4 o = units_to_vec<S>(w);
+        if (first >= 0 && first + ST::V - 1 < a.rows) {
+          store16<CP>(row_out + first * S, o);
+        } else {
+          E e[ST::V];
+          __builtin_memcpy(e, &o, 16);
+#pragma unroll
+          for (int x = 0; x < ST::V; ++x)
+            if (first + x >= 0 && first + x < a.rows)
+              reinterpret_cast<E *>(row_out)[first + x] = e[x];
+        }
+      }
+    }
+    if (more) {
+      __syncthreads();
+      strip_to_ring<ST>(lds, v, r0 + TR, wave, lane);
+      __syncthreads();
+    }
+  }
+}
+
+template <int S, int TR, int TC, int NT, int CP>
+hipError_t launch_strip(const TileArgs &a, uint32_t seg, uint32_t nseg,
+                        uint32_t grid, hipStream_t stream) {
+  TileArgs copy = a;
+  uint32_t sg = seg, ns = nseg;
+  void *args[] = {&copy, &sg, &ns};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(
+          &xpose_shift_strip_kernel<S, TR, TC, NT, CP>),
+      dim3(grid), dim3(NT), args, 0, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Transpose-read tiles (1- and 2-byte elements).  gfx950's LDS transpose
 // reads turn small blocks around on the way out of LDS.  Within each 16-lane
 // group, with HR = 8 / S elements per 8 bytes and NQ = 16 / HR:
@@ -749,6 +931,14 @@ hipError_t launch_tr(const TileArgs &a, uint32_t grid, uint32_t lds_extra,
     S, TR, TC, NT, kSwizzle, CP, ShiftTile<S, TR, TC, NT, CP>::LDS_BYTES,  \
         &launch_shift<S, TR, TC, NT, CP>, nullptr, false, true              \
   }
+// Also built as column strips (4- and 8-byte elements).
+#define XPOSE_SHIFT_S(S, TR, TC, NT, CP)                                    \
+  TileKernel {                                                              \
+    S, TR, TC, NT, kSwizzle, CP, ShiftTile<S, TR, TC, NT, CP>::LDS_BYTES,  \
+        &launch_shift<S, TR, TC, NT, CP>, nullptr, false, true, false,      \
+        &launch_strip<S, TR, TC, NT, CP>,                                   \
+        StripTile<S, TR, TC, NT, CP>::LDS_BYTES                             \
+  }
 
 #define XPOSE_TILE(S, TR, TC, NT, L, CP)                                    \
   TileKernel {                                                              \
@@ -797,13 +987,13 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kNtStore),
     XPOSE_TILE_D(8, 32, 32, 256, kSwizzle, kCacheDefault),
     // Line-aligned output tiles (4-byte elements).
-    XPOSE_SHIFT(4, 64, 64, 256, kNtStore),
+    XPOSE_SHIFT_S(4, 64, 64, 256, kNtStore),
     XPOSE_SHIFT(4, 64, 64, 256, kCacheDefault),
-    XPOSE_SHIFT(4, 128, 64, 256, kNtStore),
+    XPOSE_SHIFT_S(4, 128, 64, 256, kNtStore),
     XPOSE_SHIFT(4, 128, 64, 256, kCacheDefault),
     XPOSE_SHIFT(4, 256, 64, 256, kNtStore),
     XPOSE_SHIFT(4, 256, 64, 256, kCacheDefault),
-    XPOSE_SHIFT(4, 128, 32, 256, kNtStore), XPOSE_SHIFT(4, 64, 32, 128, kNtStore),
+    XPOSE_SHIFT_S(4, 128, 32, 256, kNtStore), XPOSE_SHIFT(4, 64, 32, 128, kNtStore),
     XPOSE_TILE(4, 64, 64, 256, kSwizzle, kNtLoadStore),
     // 2-byte elements
     XPOSE_TILES(2, 32, 32, 64), XPOSE_TILES(2, 32, 64, 128),
@@ -845,9 +1035,9 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILES(8, 32, 32, 128),
     XPOSE_TILES(8, 32, 32, 256), XPOSE_TILES(8, 64, 64, 256),
     // Line-aligned output tiles (8-byte elements).
-    XPOSE_SHIFT(8, 32, 32, 256, kNtStore),
+    XPOSE_SHIFT_S(8, 32, 32, 256, kNtStore),
     XPOSE_SHIFT(8, 32, 32, 256, kCacheDefault),
-    XPOSE_SHIFT(8, 64, 32, 256, kNtStore),
+    XPOSE_SHIFT_S(8, 64, 32, 256, kNtStore),
     XPOSE_SHIFT(8, 64, 64, 256, kNtStore),
     XPOSE_SHIFT(8, 64, 64, 256, kCacheDefault),
 };

@@ -494,6 +494,43 @@ def test_aligned_out_kernels(s):
                    opts=opts, label=tag + " in-shift")
 
 
+STRIP_TILES = {4: ((64, 64), (128, 64), (128, 32)), 8: ((32, 32), (64, 32))}
+
+
+@pytest.mark.parametrize("s", sorted(STRIP_TILES))
+def test_aligned_out_column_strips(s):
+    """Line-aligned output tiles in column strips (persistent = tile rows
+    per workgroup, the halo kept in an LDS ring): segments of 1, 2, 3 and 8
+    tile rows and one segment per strip, ragged in both dimensions, output
+    rows at many offsets within a line, input rows off alignment, batches
+    with odd strides, with and without the per-XCD remap."""
+    line = 128 // s
+    for tile in STRIP_TILES[s]:
+        for seg in (1, 2, 3, 8, 64):
+            for flags in (X.FLAG_XCD_REMAP, X.FLAG_NO_XCD_REMAP):
+                opts = X.make_opts(X.LAYOUT_SWIZZLE, tile,
+                                   X.FLAG_ALIGN_OUT | flags,
+                                   X.CACHE_NT_STORE, persistent=seg)
+                rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8,
+                                        8, 0, 0, DTYPE_OF_SIZE[s], opts)
+                assert rc == 0 and info.aligned_out == 1
+                assert info.persistent == seg
+                tag = f"strip s{s} {tile} seg{seg} f{flags}"
+                for r, c, pad, shift in ((777, 555, 3, 0),
+                                         (5 * tile[0] + line - 1, 130, 0, 5),
+                                         (1000, 3 * tile[1], 13, line - 1),
+                                         (33, 7, 1, 2), (tile[0], tile[1], line, 0)):
+                    check_case(s, 1, r, c, ld_out=r + pad, out_shift=shift,
+                               seed=r + c + seg, opts=opts, label=tag)
+                check_case(s, 3, 301, 257, ld_out=305,
+                           stride_out=257 * 305 + 9, seed=3, opts=opts,
+                           label=tag + " batch")
+                check_case(s, 1, 4 * tile[0] + 3, tile[1] + 5,
+                           ld_in=tile[1] + 6, ld_out=4 * tile[0] + 7,
+                           in_shift=1, out_shift=3, seed=4, opts=opts,
+                           label=tag + " in-shift")
+
+
 TR_TILES = {2: ((64, 64), (128, 64), (64, 128), (128, 128), (64, 32)),
             1: ((128, 128), (64, 128), (128, 64), (128, 256))}
 
