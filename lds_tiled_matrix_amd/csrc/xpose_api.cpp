@@ -86,6 +86,21 @@ struct Default {
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
 constexpr int64_t kShortAlignRows = 256;
 constexpr int64_t kBigCallBytes = 512ll << 20;
+// Single matrices with both sides at least kLargeMinDim take 128 KiB tiles
+// (one workgroup per compute unit) in the diagonal order: 2-byte elements
+// from kLargeCallBytes (read + write) on, 4-byte ones (in the diagonal
+// order's pitches) from kHugeCallBytes, 8-byte ones from kBigCallBytes.
+// Measured against the tiles before them, fraction of the copy hot / cold:
+// fp16 8192^2 1.03 / 0.94 against 0.94 / 0.78, 16384^2 0.94 / 0.92 against
+// 0.89 / 0.88, 32768 x 16384 0.87 / 0.88 against 0.80 / 0.80 (256 x 256);
+// fp32 16384 x 8192 0.93 / 0.93 against 0.90 / 0.90, 16384^2 0.89 / 0.89
+// against 0.82 / 0.82 (256 x 128; at 8192^2 level hot and 0.94 against
+// 0.97 cold, so 128 x 128 stays there); fp64 8192^2 0.92 / 0.93 against
+// 0.86 / 0.88, 6144^2 0.83 / 0.82 against 0.82 / 0.74 (128 x 128).  fp16
+// 6144^2 (144 MiB) loses (0.93 / 0.84 against 1.04 / 0.88), hence the floor.
+constexpr int64_t kLargeCallBytes = 256ll << 20;
+constexpr int64_t kHugeCallBytes = 1024ll << 20;
+constexpr int64_t kLargeMinDim = 1024;
 // 4-byte elements in big calls: the diagonal order only where output rows
 // lie within kPitchSlack bytes of a multiple of kPitchPeriod apart.  There
 // the column walk of a compact super-tile keeps writing the same few
@@ -102,7 +117,7 @@ constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
               kNT = XPOSE_CACHE_NT_STORE;
 
 Default default_for(int s, bool out_row128, bool small, bool big,
-                    bool align) {
+                    bool align, bool huge = false, bool large = false) {
   if (align) {
     switch (s) {
       case 2:
@@ -129,18 +144,24 @@ Default default_for(int s, bool out_row128, bool small, bool big,
       default: return {32, 32, 256, kSwz, kWB, 16, 16, 1, kSup};
     }
   }
+  // Tiles of 128 KiB (one workgroup per compute unit) give 512-byte row
+  // segments on both sides for 2- and 8-byte elements and 1 KiB output
+  // segments for 4-byte ones; HBM serves the longer streams better.
   switch (s) {
     case 4:
       if (small) return {128, 64, 256, kSwz, kNT, 8, 8, 0, kSup};
+      if (big && huge) return {256, 128, 256, kSwz, kNT, 1, 0, 0, kDiag};
       if (big) return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 1};
       return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
     case 2:
+      if (large) return {256, 256, 256, kSwz, kNT, 1, 0, 0, kDiag};
       if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 3};
       return {128, 64, 256, kSwz, kNT, 32, 8, 0, kSup};
     case 1:
       if (big) return {128, 64, 128, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
       return {128, 128, 256, kSwz, kNT, 16, 16, 1, kSup};
     default:
+      if (big && large) return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag};
       if (big) return {32, 32, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
       return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
   }
@@ -368,8 +389,15 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     const int64_t off = (ld_out * 4) % kPitchPeriod;
     big_order = off <= kPitchSlack || kPitchPeriod - off <= kPitchSlack;
   }
+  // One large matrix (not a batch): the 128 KiB tiles.
+  const bool single = batch == 1 && rows >= kLargeMinDim && cols >= kLargeMinDim;
+  const bool huge = single && (!mul_ok(2, rows * cols * s, &call_bytes) ||
+                               call_bytes >= kHugeCallBytes);
+  const bool large = single && (!mul_ok(2, rows * cols * s, &call_bytes) ||
+                                call_bytes >= kLargeCallBytes);
   Default d = default_for(s, out_row128, small, big_order,
-                          want_align || (align_ok && !out_row128 && !short_rows));
+                          want_align || (align_ok && !out_row128 && !short_rows),
+                          huge, large);
   const int layout = (opts && opts->layout) ? opts->layout : d.layout;
   plan->elem_bytes = s;
   if (layout == XPOSE_LAYOUT_NAIVE_READ || layout == XPOSE_LAYOUT_NAIVE_WRITE) {

@@ -968,6 +968,16 @@ hipError_t launch_tr(const TileArgs &a, uint32_t grid, uint32_t lds_extra,
       XPOSE_TILE(S, TR, TC, NT, kPad1, kNtStore),                           \
       XPOSE_TILE(S, TR, TC, NT, kUnpadded, kNtStore)
 
+// Every layout and both cache policies, one LDS buffer only (tiles whose
+// double-buffered persistent kernel would not fit the LDS).
+#define XPOSE_TILES_1(S, TR, TC, NT)                                        \
+  XPOSE_TILE(S, TR, TC, NT, kSwizzle, kCacheDefault),                       \
+      XPOSE_TILE(S, TR, TC, NT, kPad1, kCacheDefault),                      \
+      XPOSE_TILE(S, TR, TC, NT, kUnpadded, kCacheDefault),                  \
+      XPOSE_TILE(S, TR, TC, NT, kSwizzle, kNtStore),                        \
+      XPOSE_TILE(S, TR, TC, NT, kPad1, kNtStore),                           \
+      XPOSE_TILE(S, TR, TC, NT, kUnpadded, kNtStore)
+
 static const TileKernel kTileKernels[] = {
     // 4-byte elements
     XPOSE_TILES(4, 32, 32, 256), XPOSE_TILES(4, 32, 32, 128),
@@ -976,6 +986,7 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILES(4, 64, 128, 256), XPOSE_TILES(4, 128, 64, 256),
     XPOSE_TILES(4, 128, 128, 256), XPOSE_TILES(4, 32, 128, 256),
     XPOSE_TILES(4, 128, 32, 256),
+    XPOSE_TILES_1(4, 256, 128, 256),
     XPOSE_TILE(4, 32, 32, 256, kSwizzle, kNtLoadStore),
     XPOSE_TILE_D(4, 32, 32, 256, kSwizzle, kNtStore),
     XPOSE_TILE_D(4, 32, 32, 256, kSwizzle, kCacheDefault),
@@ -1000,6 +1011,7 @@ static const TileKernel kTileKernels[] = {
     XPOSE_TILES(2, 64, 32, 128), XPOSE_TILES(2, 64, 64, 128),
     XPOSE_TILES(2, 64, 64, 256), XPOSE_TILES(2, 128, 128, 256),
     XPOSE_TILES(2, 64, 128, 256), XPOSE_TILES(2, 128, 64, 256),
+    XPOSE_TILES_1(2, 256, 256, 256), XPOSE_TILES_1(2, 256, 256, 512),
     // Line-aligned output tiles (2-byte elements).
     XPOSE_SHIFT(2, 64, 64, 256, kNtStore),
     XPOSE_SHIFT(2, 64, 64, 256, kCacheDefault),
@@ -1034,6 +1046,7 @@ static const TileKernel kTileKernels[] = {
     // 8-byte elements
     XPOSE_TILES(8, 32, 32, 128),
     XPOSE_TILES(8, 32, 32, 256), XPOSE_TILES(8, 64, 64, 256),
+    XPOSE_TILES_1(8, 128, 128, 256),
     // Line-aligned output tiles (8-byte elements).
     XPOSE_SHIFT_S(8, 32, 32, 256, kNtStore),
     XPOSE_SHIFT(8, 32, 32, 256, kCacheDefault),

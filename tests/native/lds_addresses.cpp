@@ -159,12 +159,13 @@ int main() {
   tiles<4, 32, 64, 128>(); tiles<4, 64, 32, 128>(); tiles<4, 64, 64, 256>();
   tiles<4, 64, 128, 256>(); tiles<4, 128, 64, 256>();
   tiles<4, 128, 128, 256>(); tiles<4, 32, 128, 256>();
-  tiles<4, 128, 32, 256>();
+  tiles<4, 128, 32, 256>(); tiles<4, 256, 128, 256>();
   shift<4, 64, 64, 256>(); shift<4, 128, 64, 256>(); shift<4, 256, 64, 256>();
   shift<4, 128, 32, 256>(); shift<4, 64, 32, 128>();
   // 2-byte elements
   tiles<2, 32, 32, 64>(); tiles<2, 32, 64, 128>(); tiles<2, 64, 32, 128>();
   tiles<2, 64, 64, 128>(); tiles<2, 64, 64, 256>(); tiles<2, 128, 128, 256>();
+  tiles<2, 256, 256, 256>(); tiles<2, 256, 256, 512>();
   tiles<2, 64, 128, 256>(); tiles<2, 128, 64, 256>();
   shift<2, 64, 64, 256>(); shift<2, 128, 64, 256>(); shift<2, 256, 64, 256>();
   tr<2, 64, 64, 256, false>(); tr<2, 128, 64, 256, false>();
@@ -179,7 +180,7 @@ int main() {
   tr<1, 128, 128, 256, true>();
   // 8-byte elements
   tiles<8, 32, 32, 128>(); tiles<8, 32, 32, 256>();
-  tiles<8, 64, 64, 256>();
+  tiles<8, 64, 64, 256>(); tiles<8, 128, 128, 256>();
   shift<8, 32, 32, 256>(); shift<8, 64, 32, 256>(); shift<8, 64, 64, 256>();
   return 0;
 }

@@ -267,14 +267,39 @@ def test_one_hip_runtime_per_process():
 
 
 def test_footprint_rules():
-    # At least 512 MiB moved per call: the diagonal tile order with a cap on
-    # the workgroups per compute unit.
+    # One large fp16 matrix (>= 256 MiB moved, both sides >= 1024): 256 x 256
+    # tiles of 128 KiB (one workgroup per compute unit) in the diagonal order.
     rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F16)
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
-    assert (info.tile_rows, info.tile_cols) == (128, 64) and info.xcd_remap == 0
-    assert info.occupancy == 3
+    assert (info.tile_rows, info.tile_cols, info.threads) == (256, 256, 256)
+    assert info.xcd_remap == 0 and info.occupancy == 0
+    assert info.lds_bytes == 128 * 1024
+    rc, info = plan(rows=8192, cols=8192, dtype=X.XPOSE_F16)  # 256 MiB
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert (info.tile_rows, info.tile_cols) == (256, 256)
+    rc, info = plan(rows=6144, cols=6144, dtype=X.XPOSE_F16)  # 144 MiB
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    assert (info.tile_rows, info.tile_cols) == (128, 64)
+    rc, info = plan(rows=65536, cols=512, dtype=X.XPOSE_F16)  # narrow
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 64)
+    # A batch moving at least 512 MiB: the diagonal order, 128 x 64 tiles,
+    # at most 3 workgroups per compute unit.
+    rc, info = plan(batch=4, rows=8192, cols=8192, stride_in=8192 * 8192,
+                    stride_out=8192 * 8192, dtype=X.XPOSE_F16)
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert (info.tile_rows, info.tile_cols) == (128, 64) and info.occupancy == 3
+    # 4-byte elements from 1 GiB on (in the diagonal order's pitches):
+    # 256 x 128 tiles of 128 KiB.
     rc, info = plan(rows=16384, cols=8192)
-    assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 1
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 0
+    assert (info.tile_rows, info.tile_cols) == (256, 128)
+    # 8-byte elements from 512 MiB on: 128 x 128 tiles of 128 KiB.
+    rc, info = plan(rows=8192, cols=8192, dtype=X.XPOSE_F64)
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert (info.tile_rows, info.tile_cols) == (128, 128) and info.occupancy == 0
+    rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)  # 256 MiB
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    assert (info.tile_rows, info.tile_cols) == (32, 32)
     # 8192^2 fp32 moves exactly 512 MiB: big.
     rc, info = plan(rows=8192, cols=8192)
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
@@ -298,7 +323,8 @@ def test_footprint_rules():
     rc, info = plan(rows=12288, cols=8192, ld_out=16384 + 256)  # 1 KiB off
     assert rc == 0 and info.order == X.ORDER_SUPER_TILES
     # an explicit order drops the default cap
-    rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F16,
+    rc, info = plan(batch=4, rows=8192, cols=8192, stride_in=8192 * 8192,
+                    stride_out=8192 * 8192, dtype=X.XPOSE_F16,
                     opts=X.make_opts(order=X.ORDER_SUPER_TILES))
     assert rc == 0 and info.occupancy == 0 and info.tile_rows == 128
     # A batch of small matrices keeps super-tiles even when the call is big.
@@ -434,12 +460,17 @@ def test_auto_cache_takes_a_built_policy():
 
 
 def test_big_f64_default_is_diagonal():
-    # at least 512 MiB read + write: 32 x 32 tiles in diagonal order, at most
-    # 4 workgroups per compute unit
+    # at least 512 MiB read + write: the diagonal order; one large matrix
+    # takes 128 x 128 tiles (128 KiB, one workgroup per compute unit), a
+    # batch 32 x 32 tiles at most 4 workgroups per compute unit
     rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F64)
-    assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 128)
     assert info.order == X.ORDER_DIAGONAL and info.cache == X.CACHE_NT_STORE
-    assert info.occupancy == 4
+    assert info.occupancy == 0
+    rc, info = plan(batch=2, rows=8192, cols=8192, stride_in=8192 * 8192,
+                    stride_out=8192 * 8192, dtype=X.XPOSE_F64)
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
+    assert info.order == X.ORDER_DIAGONAL and info.occupancy == 4
     rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)
     assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.order == X.ORDER_SUPER_TILES

@@ -106,12 +106,18 @@ def test_primes_and_multi_tile_ragged(s):
 
 
 def _tiles_for(s):
+    """Every built (tile rows, tile cols, workgroup size) for element size s."""
     out = set()
-    for tr, tc in ((32, 32), (64, 64), (64, 128), (128, 64), (128, 128)):
-        rc, _ = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8, 8, 0, 0,
-                             DTYPE_OF_SIZE[s], X.XposeOpts(1, tr, tc, 0))
-        if rc == 0:
-            out.add((tr, tc))
+    for tr, tc in ((32, 32), (32, 64), (64, 32), (64, 64), (64, 128),
+                   (128, 64), (128, 128), (32, 128), (128, 32), (256, 128),
+                   (256, 256)):
+        for nt in (64, 128, 256, 512):
+            opts = X.XposeOpts(1, tr, tc, 0)
+            opts.threads = nt
+            rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, 8, 8, 8, 8, 0,
+                                    0, DTYPE_OF_SIZE[s], opts)
+            if rc == 0:
+                out.add((tr, tc, nt))
     return sorted(out)
 
 
@@ -121,13 +127,15 @@ def _tiles_for(s):
 def test_every_built_kernel(s, layout):
     """Every compiled (element size, tile, layout) kernel on a ragged
     multi-tile shape, on the vector path and forced element-wise."""
-    for tr, tc in _tiles_for(s):
+    for tr, tc, nt in _tiles_for(s):
         for flags in (0, X.FLAG_ELEMENTWISE):
             opts = X.XposeOpts(layout, tr, tc, flags)
+            opts.threads = nt
+            tag = f"{tr}x{tc}/{nt} L{layout} f{flags}"
             check_case(s, 1, 3 * tr + 5, 2 * tc + 3, seed=tr * tc + flags,
-                       opts=opts, label=f"kernel {tr}x{tc} L{layout} f{flags}")
+                       opts=opts, label=f"kernel {tag}")
             check_case(s, 1, 2 * tr, 3 * tc, seed=tr + tc + flags, opts=opts,
-                       label=f"kernel-full {tr}x{tc} L{layout} f{flags}")
+                       label=f"kernel-full {tag}")
 
 
 @pytest.mark.parametrize("s", SIZES)
