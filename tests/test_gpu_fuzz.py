@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 X = pytest.importorskip("lds_tiled_matrix_amd")
 
 TILES = ((32, 32), (64, 64), (128, 64), (64, 128), (128, 128), (32, 64),
-         (64, 32), (16, 16))
+         (64, 32), (16, 16), (256, 128), (256, 256))
 
 
 def random_opts(rng, s):
@@ -127,13 +127,16 @@ def campaign_opts(rng, s):
                                      rng.choice((0, 1, 2))))
     elif r < 0.85 and s in SHIFT_TILES:
         for _ in range(50):
+            # persistent: line-aligned tiles in column strips of that many
+            # tile rows (built for 4- and 8-byte elements)
+            strip = rng.choice((0, 0, 0, 1, 2, 3, 8))
             cands.append(X.make_opts(X.LAYOUT_SWIZZLE, rng.choice(SHIFT_TILES[s] + (None,)),
                                      X.FLAG_ALIGN_OUT | rng.choice((0, 2, 4)),
                                      rng.choice((0, 1, 2)),
                                      *rng.choice(((0, 0), (1, 0), (3, 5), (16, 16),
                                                   (128, 4))), 0,
-                                     rng.choice((0, 1, 2)), 0,
-                                     rng.choice((0, 0, 2, 4))))
+                                     rng.choice((0, 1, 2, 3)), strip,
+                                     0 if strip else rng.choice((0, 0, 2, 4))))
     for o in cands:
         if X.xpose_plan(0x100000, 0x40000000, 1, 64, 64, 64, 64, 0, 0,
                         DTYPE_OF_SIZE[s], o)[0] == 0:

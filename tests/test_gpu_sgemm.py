@@ -507,6 +507,42 @@ def test_sgemm_convenience_splits_small_grids():
         assert np.array_equal(dC.cpu().numpy(), want), split_k
 
 
+def test_split_k_random_campaign():
+    """Seeded random split calls: shapes (ragged, thin, k from 1 to 3000),
+    pitches, pointer and workspace offsets, scalars, kernels and splits (the
+    library's choice with the workspace it wants, with a smaller one, or an
+    explicit 2 to 64); integer inputs, so each is compared bit for bit."""
+    rng = np.random.default_rng(4242)
+    dims = [1, 3, 17, 64, 127, 128, 129, 200, 256, 300, 513, 700]
+    for case in range(40):
+        m, n = int(rng.choice(dims)), int(rng.choice(dims))
+        k = int(rng.choice([1, 5, 16, 100, 255, 256, 512, 777, 1500, 3000]))
+        pads = tuple(int(x) for x in rng.choice([0, 0, 1, 4, 8], 3))
+        shifts = tuple(int(x) for x in rng.choice([0, 0, 1, 3], 3))
+        alpha = float(rng.choice([1.0, 2.0, -1.0, 0.5]))
+        beta = float(rng.choice([0.0, 1.0, -2.0]))
+        flags = int(rng.choice([0, 0, X.SGEMM_NO_BUFFER_LOADS,
+                                X.SGEMM_NO_XCD_REMAP, X.SGEMM_DOUBLE_BUFFER]))
+        bk = int(rng.choice([8, 16, 16, 32]))
+        tile_m = 128
+        if flags != X.SGEMM_DOUBLE_BUFFER and bk in (16, 32):
+            tile_m = int(rng.choice([64, 128, 256] if bk == 16 else [128, 256]))
+        split = int(rng.choice([0, 0, 2, 3, 5, 8, 64]))
+        opts = X.make_sgemm_opts(int(rng.choice(LAYOUTS)), bk, 0, flags,
+                                 tile_m, split)
+        ws_bytes = None
+        if split == 0 and rng.random() < 0.3:
+            ws_bytes = int(rng.integers(0, 3)) * m * n * 4 + 4
+        A = wl.small_int_f32((m, k), 40_000 + case)
+        B = wl.small_int_f32((k, n), 41_000 + case)
+        C = wl.small_int_f32((m, n), 42_000 + case)
+        say(f"split campaign {case}: {m}x{n}x{k} split={split} bk={bk} "
+            f"tile_m={tile_m} flags={flags}")
+        check_exact(A, B, C, alpha, beta, pads=pads, shifts=shifts, opts=opts,
+                    entry="ws", ws_bytes=ws_bytes,
+                    ws_shift=int(rng.choice([0, 1, 4])))
+
+
 def test_hip_graph_capture_and_replay():
     """The SGEMM only enqueues its kernels (no allocation, memset or
     synchronisation), so it can be captured into a HIP graph, a split of k
