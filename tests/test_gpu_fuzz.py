@@ -147,8 +147,9 @@ def campaign_opts(rng, s):
 @pytest.mark.parametrize("chunk", range(4))
 def test_random_campaign(chunk):
     """25 seeds x 25 cases per chunk over every option family, pitches and
-    pointer offsets at every residue (a one-off run of 1,260 seeds of this
-    generator also passed)."""
+    pointer offsets at every residue (one-off runs of 1,260 seeds of the
+    generator before the 128 KiB tiles and column strips joined it, and of
+    seeds 100-699, 15,000 cases, of this one also passed)."""
     for seed in range(chunk * 25, chunk * 25 + 25):
         rng = random.Random(50000 + seed)
         for case in range(25):
