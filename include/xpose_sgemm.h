@@ -238,11 +238,12 @@ int xpose_sgemm_ws(int64_t m, int64_t n, int64_t k, float alpha,
  * array of the library that each GPU it runs on holds until the process
  * ends; the call allocates nothing, and neither does any library routine it
  * calls.  A split of k the library chooses (opts->split_k == 0) is shrunk
- * to what the scratch holds (none when one m x n plane does not fit, as
- * for m n > 16 Mi); an explicit split_k >= 2 whose partials (splits * m * n
- * * 4 bytes) exceed it is rejected with XPOSE_EWORKSPACE before anything is
- * launched.  xpose_sgemm_plan_ws with workspace_bytes =
- * XPOSE_SGEMM_SCRATCH_BYTES reports the split it takes.
+ * to what the scratch holds (none when fewer than two m x n planes fit,
+ * i.e. for m n > 8 Mi); an explicit split_k >= 2 whose partials (splits *
+ * m * n * 4 bytes) exceed it is rejected with XPOSE_EWORKSPACE before
+ * anything is launched.  xpose_sgemm_plan_ws with workspace_bytes =
+ * XPOSE_SGEMM_SCRATCH_BYTES (and any non-NULL, 4-byte aligned workspace
+ * address that overlaps none of A, B and C) reports the split it takes.
  *
  * Every call on one GPU shares that GPU's array, and it keeps the last
  * call's contents (nothing in it needs to start at zero: each split writes
