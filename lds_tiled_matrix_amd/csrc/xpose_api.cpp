@@ -396,7 +396,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
     big_order = off <= kPitchSlack || kPitchPeriod - off <= kPitchSlack;
   }
   // One large matrix (not a batch): the 128 KiB tiles.
-  const bool single = batch == 1 && rows >= kLargeMinDim && cols >= kLargeMinDim;
+  const bool single =
+      batch == 1 && rows >= kLargeMinDim && cols >= kLargeMinDim;
   const bool huge = single && (!mul_ok(2, rows * cols * s, &call_bytes) ||
                                call_bytes >= kHugeCallBytes);
   const bool large = single && (!mul_ok(2, rows * cols * s, &call_bytes) ||
