@@ -578,6 +578,9 @@ def main(argv=None):
         got = y.cpu().numpy()
         parity = bool(np.array_equal(got, want))
         cpu["host_cpu"] = host_cpu_name()
+        # threads this process may run on (the machine's CPU share), for context:
+        # the oracle itself is pinned to one of them
+        cpu["host_threads_available"] = len(os.sched_getaffinity(0))
         if not parity:
             log("bench: PARITY FAILURE against the oracle")
 
