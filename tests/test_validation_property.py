@@ -93,3 +93,42 @@ def test_every_default_plan_has_a_kernel(rows, cols, batch, dtype):
     per = -(-(rows + extra) // info.tile_rows) * -(-cols // info.tile_cols)
     assert info.tiles == batch * per
     assert info.lds_bytes > 0 and info.threads in (64, 128, 256)
+
+
+SG_A, SG_B, SG_C, SG_W = 0x7f0000000000, 0x7f1000000000, 0x7f2000000000, 0x7f3000000000
+
+
+@settings(max_examples=400, deadline=None)
+@given(m=st.integers(1, 5000), n=st.integers(1, 5000), k=st.integers(0, 70000),
+       bk=st.sampled_from([0, 8, 16, 32, 64]), tile_m=st.sampled_from([0, 64, 128, 256]),
+       split=st.integers(0, 64), ws_planes=st.integers(0, 80),
+       ws_extra=st.integers(0, 4096))
+def test_sgemm_split_plan_invariants(m, n, k, bk, tile_m, split, ws_planes,
+                                     ws_extra):
+    """Any xpose_sgemm_plan_ws result: slices of whole k steps covering k
+    exactly once, a workspace use that fits what was given, the grid the
+    slices imply; the library's choice never shorter than 64 per slice and
+    an explicit split never more slices than asked."""
+    X = pytest.importorskip("lds_tiled_matrix_amd")
+    opts = X.make_sgemm_opts(0, bk, 0, 0, tile_m, split)
+    ws_bytes = ws_planes * m * n * 4 + ws_extra
+    rc, info = X.xpose_sgemm_plan_ws(m, n, k, SG_A, max(k, 1), SG_B, n, SG_C,
+                                     n, opts, SG_W, ws_bytes)
+    if rc == X.XPOSE_ENOTILE:      # e.g. bk 64 with 256-row blocks
+        return
+    if rc == X.XPOSE_EWORKSPACE:
+        assert split >= 2 and info.workspace_wanted > ws_bytes
+        return
+    assert rc == 0
+    S, L = info.splits, info.split_len
+    base = -(-m // info.tile_m) * -(-n // 128)
+    assert info.tiles == base * S
+    if S == 1:
+        assert L == k and info.workspace_bytes == 0
+        return
+    assert L % info.bk == 0 and (S - 1) * L < k <= S * L
+    assert info.workspace_bytes == S * m * n * 4 <= ws_bytes
+    if split == 0:
+        assert L >= 64
+    else:
+        assert S <= split
