@@ -495,6 +495,83 @@ def bench_sgemm_shapes(X, shapes, steps, warmup, stream):
     return out
 
 
+# The library's defaults off the five workloads: (element bytes, rows,
+# cols) -- square, wide, tall, odd (line-aligned output) and large shapes of
+# every element size.
+SWEEP_SHAPES = (
+    (4, 2048, 2048), (4, 4096, 4096), (4, 6144, 6144), (4, 8192, 8192),
+    (4, 12288, 12288), (4, 16384, 16384), (4, 1024, 8192), (4, 8192, 1024),
+    (4, 8192, 4096), (4, 16384, 2048), (4, 16384, 8192), (4, 32768, 8192),
+    (4, 12345, 6789), (4, 9999, 9999),
+    (2, 4096, 4096), (2, 8192, 8192), (2, 16384, 16384), (2, 32768, 16384),
+    (2, 12345, 6789), (2, 16383, 16383),
+    (1, 8192, 8192), (1, 16384, 16384), (1, 12345, 6789),
+    (8, 4096, 4096), (8, 6000, 6000), (8, 8192, 8192), (8, 16384, 8192),
+    (8, 8191, 8191))
+
+
+def bench_sweep(X, stream, shapes=SWEEP_SHAPES, steps=20, cold_reps=4):
+    """The default launch on each (element bytes, rows, cols) matrix of
+    ``shapes`` (uninitialised bytes: the path is data-independent), against
+    the library's default copy over the same bytes, back to back (average
+    over the region of ``steps`` launches) and with the caches flushed
+    before each launch (median of ``cold_reps``).  Returns a list of rows."""
+    import torch
+    dev = torch.device("cuda", 0)
+    sh = int(stream.cuda_stream)
+    flush = torch.empty(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+    flush.zero_()
+    rows = []
+    for s, r, c in shapes:
+        nbytes = r * c * s
+        x = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.int32,
+                        device=dev)
+        y = torch.empty_like(x)
+        dt = {1: X.XPOSE_U8, 2: X.XPOSE_F16, 4: X.XPOSE_F32, 8: X.XPOSE_F64}[s]
+        rc, info = X.xpose_plan(y.data_ptr(), x.data_ptr(), 1, r, c, c, r, 0,
+                                0, dt, None)
+        if rc:
+            raise RuntimeError(X.strerror(rc))
+
+        def tr():
+            rc = X.xpose_2d(y.data_ptr(), x.data_ptr(), r, c, c, r, dt, sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+
+        def cp():
+            rc = X.xpose_copy(y.data_ptr(), x.data_ptr(), nbytes, sh)
+            if rc:
+                raise RuntimeError(X.strerror(rc))
+
+        res = {}
+        with torch.cuda.stream(stream):
+            for name, fn in (("transpose", tr), ("copy", cp)):
+                _, region, _ = time_launches(fn, stream, steps, 3)
+                cold = statistics.median(time_cold(fn, stream, cold_reps, flush))
+                res[name] = (2 * nbytes / (region / steps) / 1e9,
+                             2 * nbytes / cold / 1e9)
+        torch.cuda.synchronize()
+        order = {X.ORDER_SUPER_TILES: f"super {info.group_rows}x{info.group_cols}",
+                 X.ORDER_DIAGONAL: "diagonal",
+                 X.ORDER_COLUMN_BANDS: f"bands {info.group_cols}"}.get(
+                     info.order, f"order {info.order}")
+        rows.append({
+            "elem_bytes": s, "rows": r, "cols": c, "rw_bytes": 2 * nbytes,
+            "kernel": f"{info.tile_rows}x{info.tile_cols}"
+                      + (" line-aligned" if info.aligned_out else "")
+                      + f", {order}" + (f", {info.occupancy}/CU" if info.occupancy else ""),
+            "hot_GBps": round(res["transpose"][0], 1),
+            "hot_of_copy": round(res["transpose"][0] / res["copy"][0], 3),
+            "cold_GBps": round(res["transpose"][1], 1),
+            "cold_of_copy": round(res["transpose"][1] / res["copy"][1], 3)})
+        log(f"sweep: s{s} {r}x{c} {rows[-1]['kernel']}: "
+            f"{rows[-1]['hot_GBps']:.0f} ({rows[-1]['hot_of_copy']:.3f}) / "
+            f"{rows[-1]['cold_GBps']:.0f} ({rows[-1]['cold_of_copy']:.3f})")
+        del x, y
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -512,6 +589,10 @@ def main(argv=None):
                     help="skip the tiled SGEMM (padded transposed As store)")
     ap.add_argument("--sgemm-only", action="store_true",
                     help="measure only the tiled SGEMM; print its JSON line")
+    ap.add_argument("--sweep", action="store_true",
+                    help="measure only the library's default over a sweep of "
+                         "shapes and element sizes against the copy, hot and "
+                         "cold; JSON line on stdout, markdown table on stderr")
     ap.add_argument("--sgemm-shapes", default=None,
                     help="comma-separated MxNxK list for the SGEMM's small-grid "
                          "table (split of k against none and torch); 'none' "
@@ -545,6 +626,19 @@ def main(argv=None):
         return 1
 
     stream = torch.cuda.Stream()
+    if args.sweep:
+        log("bench: default kernels over a shape sweep")
+        rows = bench_sweep(X, stream)
+        print(json.dumps({"sweep": rows, "system": system_info()}), flush=True)
+        print("| element bytes | rows x cols | default kernel | hot GB/s | of copy | "
+              "cold GB/s | of copy |", file=sys.stderr)
+        print("|---|---|---|---|---|---|---|", file=sys.stderr)
+        for r in rows:
+            print(f"| {r['elem_bytes']} | {r['rows']} x {r['cols']} | {r['kernel']} | "
+                  f"{r['hot_GBps']:,.0f} | {r['hot_of_copy']:.3f} | "
+                  f"{r['cold_GBps']:,.0f} | {r['cold_of_copy']:.3f} |",
+                  file=sys.stderr)
+        return 0
     if args.sgemm_only:
         log("bench: tiled SGEMM only")
         sg = bench_sgemm(X, args.steps, args.warmup, stream,

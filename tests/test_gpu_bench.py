@@ -90,3 +90,21 @@ def test_sgemm_record(record):
         assert r["split_TFLOPs"] > 0 and r["no_split_TFLOPs"] > 0
         assert r["torch_addmm_TFLOPs"] > 0 and r["splits"] >= 1
         assert (r["workspace_MiB"] > 0) == (r["splits"] > 1)
+
+
+def test_sweep_rows():
+    """The default-kernel sweep: one row per shape, rates positive, the
+    fractions the ratio of the transpose's rate to the copy's."""
+    import torch
+    import bench
+    import lds_tiled_matrix_amd as X
+    shapes = ((4, 1024, 2048), (2, 999, 777), (8, 513, 1000), (1, 2048, 4096))
+    say(f"bench.bench_sweep {shapes}")
+    rows = bench.bench_sweep(X, torch.cuda.Stream(), shapes=shapes, steps=3,
+                             cold_reps=2)
+    assert [(r["elem_bytes"], r["rows"], r["cols"]) for r in rows] == list(shapes)
+    for r in rows:
+        assert r["rw_bytes"] == 2 * r["elem_bytes"] * r["rows"] * r["cols"]
+        assert r["hot_GBps"] > 0 and r["cold_GBps"] > 0
+        assert 0 < r["hot_of_copy"] and 0 < r["cold_of_copy"]
+        assert "x" in r["kernel"]
