@@ -88,37 +88,71 @@ constexpr int64_t kShortAlignRows = 256;
 constexpr int64_t kBigCallBytes = 512ll << 20;
 // Single matrices with both sides at least kLargeMinDim take 128 KiB tiles
 // (one workgroup per compute unit) in the diagonal order: 2-byte elements
-// from kLargeCallBytes (read + write) on, 4-byte ones (in the diagonal
-// order's pitches) from kHugeCallBytes, 8-byte ones from kBigCallBytes.
+// from kLargeCallBytes (read + write) on; 4-byte ones in the pitches below
+// where the diagonal order wins, from kHugeCallBytes on and under
+// kBigCallBytes; 8-byte ones in those pitches from kLargeCallBytes on.
 // Measured against the tiles before them, fraction of the copy hot / cold:
 // fp16 8192^2 1.03 / 0.94 against 0.94 / 0.78, 16384^2 0.94 / 0.92 against
 // 0.89 / 0.88, 32768 x 16384 0.87 / 0.88 against 0.80 / 0.80 (256 x 256);
 // fp32 16384 x 8192 0.93 / 0.93 against 0.90 / 0.90, 16384^2 0.89 / 0.89
 // against 0.82 / 0.82 (256 x 128; at 8192^2 level hot and 0.94 against
 // 0.97 cold, so 128 x 128 stays there); fp64 8192^2 0.92 / 0.93 against
-// 0.86 / 0.88, 6144^2 0.83 / 0.82 against 0.82 / 0.74 (128 x 128).  fp16
-// 6144^2 (144 MiB) loses (0.93 / 0.84 against 1.04 / 0.88), hence the floor.
+// 0.86 / 0.88 (128 x 128).  fp16 6144^2 (144 MiB) loses (0.93 / 0.84
+// against 1.04 / 0.88), hence the floor.
 constexpr int64_t kLargeCallBytes = 256ll << 20;
 constexpr int64_t kHugeCallBytes = 1024ll << 20;
 constexpr int64_t kLargeMinDim = 1024;
-// 4-byte elements in big calls: the diagonal order only where output rows
-// lie within kPitchSlack bytes of a multiple of kPitchPeriod apart.  There
-// the column walk of a compact super-tile keeps writing the same few
-// address offsets and stalls on the memory channels they map to (8192^2:
-// 0.82 of the cold copy with 32 x 32 super-tiles, 0.97 diagonal; output
-// pitch 8224 elements, 128 bytes off the period: 0.74 against 0.84-0.86).
-// At other pitches the super-tiles win both ways: 12288^2 0.88 against
-// 0.78 diagonal, 10240^2 0.89 against 0.76, 9216^2 0.87 against 0.81,
-// 12288 x 6784 0.88 against 0.79 (fractions of the copy, cold).
+// The output pitch decides the tile order of large 4- and 8-byte transposes.
+// Where output rows lie within kPitchSlack bytes of a multiple of
+// kPitchPeriod apart, the column walk of a compact super-tile keeps writing
+// the same few address offsets and stalls on the memory channels they map
+// to (fp32 8192^2: 0.82 of the cold copy with 32 x 32 super-tiles, 0.97
+// diagonal; output pitch 8224 elements, 128 bytes off the period: 0.74
+// against 0.84-0.86); there the diagonal order wins, from 64 MiB on for one
+// fp32 matrix (8192 x 1024 1.10 / 1.07 of the copy hot / cold against 0.90 /
+// 0.94, 8192 x 4096 0.96 / 0.96 against 0.98 / 0.73, 16384 x 2048 0.95 /
+// 0.92 against 0.95 / 0.72, 256 x 128 tiles) and from 256 MiB for one fp64
+// matrix (4096^2 0.92 / 0.92 against 0.97 / 0.77, 128 x 128).  At other
+// pitches the super-tiles win both ways: fp32 12288^2 0.88 against 0.78
+// diagonal, 10240^2 0.89 against 0.76, 20480^2 0.86 against 0.80; fp64
+// 6000^2 0.91 / 0.83 against 0.75 / 0.72, 8000^2 0.78 against 0.74, 10000^2
+// 0.80 against 0.76 (16 x 16 super-tiles).  Output rows 128 KiB apart
+// (kSlowSegmentPitch) with more than kSlowSegmentCols columns are worst for
+// 1 KiB output segments (fp32 256 x 128 and fp64 128 x 128 tiles): fp32
+// 32768 x 4096 0.83 against 0.87 with 128 x 128 tiles (512-byte segments),
+// 32768 x 8192 0.79 against 0.91, 32768 x 12288 0.72 against 0.82; fp64
+// 16384 x 3000 0.78 against 0.90 with 32 x 32 super-tiles, 16384 x 8192
+// 0.77 against 0.84, 16384^2 0.73 against 0.81 (hot and cold alike).  With
+// 2048 columns or fewer, or at 256 or 384 KiB, the long segments keep their
+// lead (fp32 32768 x 2048 0.94 / 0.87 against 0.95 / 0.73, 65536 x 2048
+// 0.87 against 0.74; fp64 16384 x 2048 0.96 / 0.86 against 0.96 / 0.81,
+// 49152 x 4096 0.86 against 0.81).  fp32 8192^2, both pitches 32 KiB, keeps
+// 128 x 128 tiles at one per compute unit: level hot, 0.969 cold against
+// 0.953 (8 interleaved rounds), where every other fp32 shape measured in the
+// diagonal order runs at least as fast with 256 x 128 tiles.
 constexpr int64_t kPitchPeriod = 32768, kPitchSlack = 512;
+constexpr int64_t kSlowSegmentPitch = 131072, kSlowSegmentCols = 2048;
 constexpr int kSwz = xpose::kSwizzle, kSup = XPOSE_ORDER_SUPER_TILES,
               kDiag = XPOSE_ORDER_DIAGONAL, kBands = XPOSE_ORDER_COLUMN_BANDS,
               kWB = XPOSE_CACHE_DEFAULT,
               kNT = XPOSE_CACHE_NT_STORE;
 
-Default default_for(int s, bool out_row128, bool small, bool big,
-                    bool align, bool huge = false, bool large = false) {
-  if (align) {
+// What the default kernel depends on.
+struct CallShape {
+  bool out_row128;   // output rows start on 128-byte lines
+  bool small;        // a batch of matrices of at most kSmallMatrixBytes
+  bool big;          // at least kBigCallBytes read + write
+  bool align;        // line-aligned output tiles
+  bool single;       // one matrix, both sides at least kLargeMinDim
+  bool large, huge;  // single, and at least kLargeCallBytes / kHugeCallBytes
+  bool on_period;    // output pitch near a multiple of kPitchPeriod
+  bool slow_1k;      // output pitch near kSlowSegmentPitch, more columns
+                     // than kSlowSegmentCols
+  bool square_32k;   // both pitches near kPitchPeriod
+};
+
+Default default_for(int s, const CallShape &c) {
+  if (c.align) {
     switch (s) {
       // 2-byte elements in big calls: 128 x 64 tiles in column bands of at
       // most 32 tile columns, for the reason given for 4-byte elements
@@ -127,7 +161,7 @@ Default default_for(int s, bool out_row128, bool small, bool big,
       // Below 512 MiB the bands trade hot for cold (8191^2: 0.86 / 0.85
       // against 0.93 / 0.77), so 64 x 64 super-tiles stay.
       case 2:
-        if (big) return {128, 64, 256, kSwz, kNT, 1, 32, 1, kBands, true};
+        if (c.big) return {128, 64, 256, kSwz, kNT, 1, 32, 1, kBands, true};
         return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
       // Bands of 64 tile columns, per-XCD ranges: the tile above (whose last
       // rows are the halo) and the tile to the left (which shares the input
@@ -142,7 +176,7 @@ Default default_for(int s, bool out_row128, bool small, bool big,
       default: break;  // no line-aligned tiles for 1-byte elements
     }
   }
-  if (!out_row128) {
+  if (!c.out_row128) {
     switch (s) {
       case 4: return {128, 64, 256, kSwz, kWB, 32, 32, 1, kSup};
       case 2: return {64, 64, 256, kSwz, kWB, 16, 16, 1, kSup};
@@ -154,21 +188,27 @@ Default default_for(int s, bool out_row128, bool small, bool big,
   // segments on both sides for 2- and 8-byte elements and 1 KiB output
   // segments for 4-byte ones; HBM serves the longer streams better.
   switch (s) {
-    case 4:
-      if (small) return {128, 64, 256, kSwz, kNT, 8, 8, 0, kSup};
-      if (big && huge) return {256, 128, 256, kSwz, kNT, 1, 0, 0, kDiag};
-      if (big) return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 1};
-      return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
+    case 4: {
+      if (c.small) return {128, 64, 256, kSwz, kNT, 8, 8, 0, kSup};
+      const bool diag = c.big ? c.on_period : c.single && c.on_period;
+      if (!diag) return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
+      if (c.single && !c.slow_1k && !c.square_32k)
+        return {256, 128, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 1};
+    }
     case 2:
-      if (large) return {256, 256, 256, kSwz, kNT, 1, 0, 0, kDiag};
-      if (big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 3};
+      if (c.large) return {256, 256, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      if (c.big) return {128, 64, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 3};
       return {128, 64, 256, kSwz, kNT, 32, 8, 0, kSup};
     case 1:
-      if (big) return {128, 64, 128, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
+      if (c.big) return {128, 64, 128, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
       return {128, 128, 256, kSwz, kNT, 16, 16, 1, kSup};
     default:
-      if (big && large) return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag};
-      if (big) return {32, 32, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
+      if (c.large && c.on_period && !c.slow_1k)
+        return {128, 128, 256, kSwz, kNT, 1, 0, 0, kDiag};
+      if (c.big && !c.single)
+        return {32, 32, 256, kSwz, kNT, 1, 0, 0, kDiag, false, 4};
+      if (c.big) return {32, 32, 256, kSwz, kNT, 16, 16, 1, kSup};
       return {32, 32, 256, kSwz, kNT, 8, 32, 1, kSup};
   }
 }
@@ -390,11 +430,13 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                  (opts->layout && opts->layout != XPOSE_LAYOUT_SWIZZLE) ||
                  opts->persistent));
   const bool short_rows = s == 2 && rows < kShortAlignRows;
-  bool big_order = big;
-  if (s == 4 && big) {
-    const int64_t off = (ld_out * 4) % kPitchPeriod;
-    big_order = off <= kPitchSlack || kPitchPeriod - off <= kPitchSlack;
-  }
+  auto near = [](int64_t pitch, int64_t target) {
+    return pitch >= target - kPitchSlack && pitch <= target + kPitchSlack;
+  };
+  auto near_multiple = [](int64_t pitch, int64_t period) {
+    const int64_t off = pitch % period;
+    return off <= kPitchSlack || period - off <= kPitchSlack;
+  };
   // One large matrix (not a batch): the 128 KiB tiles.
   const bool single =
       batch == 1 && rows >= kLargeMinDim && cols >= kLargeMinDim;
@@ -402,9 +444,20 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
                                call_bytes >= kHugeCallBytes);
   const bool large = single && (!mul_ok(2, rows * cols * s, &call_bytes) ||
                                 call_bytes >= kLargeCallBytes);
-  Default d = default_for(s, out_row128, small, big_order,
-                          want_align || (align_ok && !out_row128 && !short_rows),
-                          huge, large);
+  CallShape shape;
+  shape.out_row128 = out_row128;
+  shape.small = small;
+  shape.big = big;
+  shape.align = want_align || (align_ok && !out_row128 && !short_rows);
+  shape.single = single;
+  shape.large = large;
+  shape.huge = huge;
+  shape.on_period = near_multiple(ld_out * s, kPitchPeriod);
+  shape.slow_1k =
+      near(ld_out * s, kSlowSegmentPitch) && cols > kSlowSegmentCols;
+  shape.square_32k =
+      near(ld_in * s, kPitchPeriod) && near(ld_out * s, kPitchPeriod);
+  Default d = default_for(s, shape);
   const int layout = (opts && opts->layout) ? opts->layout : d.layout;
   plan->elem_bytes = s;
   if (layout == XPOSE_LAYOUT_NAIVE_READ || layout == XPOSE_LAYOUT_NAIVE_WRITE) {
@@ -465,7 +518,8 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   if (!k && d.align_out && !want_align) {
     // The explicit tile, threads or cache exist only as ordinary tiles:
     // fall back to those, with their own defaults for the other knobs.
-    d = default_for(s, out_row128, small, big, false);
+    shape.align = false;
+    d = default_for(s, shape);
     k = lookup(d, false, false);
   }
   if (!k && !explicit_tile) k = lookup(d, d.align_out || want_align, true);

@@ -293,11 +293,15 @@ def test_footprint_rules():
     rc, info = plan(rows=16384, cols=8192)
     assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 0
     assert (info.tile_rows, info.tile_cols) == (256, 128)
-    # 8-byte elements from 512 MiB on: 128 x 128 tiles of 128 KiB.
+    # 8-byte elements from 256 MiB on, output rows a multiple of 32 KiB
+    # apart: 128 x 128 tiles of 128 KiB.
     rc, info = plan(rows=8192, cols=8192, dtype=X.XPOSE_F64)
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
     assert (info.tile_rows, info.tile_cols) == (128, 128) and info.occupancy == 0
     rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)  # 256 MiB
+    assert rc == 0 and info.order == X.ORDER_DIAGONAL
+    assert (info.tile_rows, info.tile_cols) == (128, 128)
+    rc, info = plan(rows=4096, cols=2048, dtype=X.XPOSE_F64)  # 128 MiB
     assert rc == 0 and info.order == X.ORDER_SUPER_TILES
     assert (info.tile_rows, info.tile_cols) == (32, 32)
     # 8192^2 fp32 moves exactly 512 MiB: big.
@@ -308,8 +312,9 @@ def test_footprint_rules():
     rc, info = plan(rows=32768, cols=16384, dtype=X.XPOSE_U8)
     assert rc == 0 and info.order == X.ORDER_DIAGONAL and info.occupancy == 4
     assert (info.tile_rows, info.tile_cols, info.threads) == (128, 64, 128)
-    # Just under 512 MiB: compact super-tiles, no cap.
-    rc, info = plan(rows=8192, cols=8191, ld_in=8191)
+    # Just under 512 MiB, output rows 48 KiB apart: compact super-tiles, no
+    # cap.
+    rc, info = plan(rows=12288, cols=5461)
     assert rc == 0 and info.order == X.ORDER_SUPER_TILES and info.occupancy == 0
     # 4-byte elements: the diagonal order only where output rows lie (nearly)
     # a multiple of 32 KiB apart
@@ -321,6 +326,30 @@ def test_footprint_rules():
     rc, info = plan(rows=12288, cols=8192, ld_out=16384 + 32)  # 128 B off 64 KiB
     assert rc == 0 and info.order == X.ORDER_DIAGONAL
     rc, info = plan(rows=12288, cols=8192, ld_out=16384 + 256)  # 1 KiB off
+    assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+    # ... also under 512 MiB for one matrix of at least 1024 x 1024: 256 x
+    # 128 tiles, except where output rows lie 128 KiB apart with more than
+    # 2048 columns, and at 8192^2 (128 x 128 tiles, one workgroup per
+    # compute unit)
+    for rows, cols in ((8192, 1024), (8192, 4096), (16384, 2048),
+                       (32768, 1024), (32768, 2048), (65536, 4096),
+                       (16384, 4096), (8192, 16384)):
+        rc, info = plan(rows=rows, cols=cols)
+        assert rc == 0 and info.order == X.ORDER_DIAGONAL
+        assert (info.tile_rows, info.tile_cols) == (256, 128)
+    for rows, cols in ((32768, 4096), (32768, 8192), (32768, 16384),
+                       (8192, 8192)):
+        rc, info = plan(rows=rows, cols=cols)
+        assert rc == 0 and info.order == X.ORDER_DIAGONAL
+        assert (info.tile_rows, info.tile_cols) == (128, 128)
+        assert info.occupancy == 1
+    for rows, cols in ((4096, 4096), (1024, 8192), (8192, 512)):
+        rc, info = plan(rows=rows, cols=cols)
+        assert rc == 0 and info.order == X.ORDER_SUPER_TILES
+        assert (info.tile_rows, info.tile_cols) == (32, 32)
+    # a batch under 512 MiB keeps super-tiles
+    rc, info = plan(batch=2, rows=8192, cols=2048, stride_in=8192 * 2048,
+                    stride_out=8192 * 2048)
     assert rc == 0 and info.order == X.ORDER_SUPER_TILES
     # an explicit order drops the default cap
     rc, info = plan(batch=4, rows=8192, cols=8192, stride_in=8192 * 8192,
@@ -459,21 +488,36 @@ def test_auto_cache_takes_a_built_policy():
                 opts=explicit)[0] == X.XPOSE_ENOTILE
 
 
-def test_big_f64_default_is_diagonal():
-    # at least 512 MiB read + write: the diagonal order; one large matrix
-    # takes 128 x 128 tiles (128 KiB, one workgroup per compute unit), a
-    # batch 32 x 32 tiles at most 4 workgroups per compute unit
-    rc, info = plan(rows=16384, cols=16384, dtype=X.XPOSE_F64)
+def test_big_f64_default_follows_the_pitch():
+    # One large matrix: 128 x 128 tiles (128 KiB, one workgroup per compute
+    # unit) in the diagonal order where output rows lie a multiple of 32 KiB
+    # apart but not of 128 KiB; 32 x 32 tiles in 16 x 16 super-tiles
+    # elsewhere from 512 MiB on
+    rc, info = plan(rows=12288, cols=12288, dtype=X.XPOSE_F64)
     assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 128)
     assert info.order == X.ORDER_DIAGONAL and info.cache == X.CACHE_NT_STORE
     assert info.occupancy == 0
+    for rows, cols in ((16384, 16384), (16384, 4096), (16384, 3000), (6000, 6000),
+                       (10000, 8000)):
+        rc, info = plan(rows=rows, cols=cols, dtype=X.XPOSE_F64)
+        assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
+        assert info.order == X.ORDER_SUPER_TILES and info.xcd_remap == 1
+        assert (info.group_rows, info.group_cols) == (16, 16)
+    # 128 KiB apart with 2048 columns, and 384 KiB apart: 128 x 128 tiles
+    for rows, cols in ((16384, 2048), (49152, 4096)):
+        rc, info = plan(rows=rows, cols=cols, dtype=X.XPOSE_F64)
+        assert rc == 0 and (info.tile_rows, info.tile_cols) == (128, 128)
+        assert info.order == X.ORDER_DIAGONAL
+    # a batch: 32 x 32 tiles at most 4 workgroups per compute unit
     rc, info = plan(batch=2, rows=8192, cols=8192, stride_in=8192 * 8192,
                     stride_out=8192 * 8192, dtype=X.XPOSE_F64)
     assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.order == X.ORDER_DIAGONAL and info.occupancy == 4
-    rc, info = plan(rows=4096, cols=4096, dtype=X.XPOSE_F64)
+    # under 512 MiB off the period: 8 x 32 super-tiles
+    rc, info = plan(rows=2048, cols=8192, dtype=X.XPOSE_F64)
     assert rc == 0 and (info.tile_rows, info.tile_cols) == (32, 32)
     assert info.order == X.ORDER_SUPER_TILES
+    assert (info.group_rows, info.group_cols) == (8, 32)
 
 
 def test_store_policy_follows_output_alignment():
