@@ -512,10 +512,15 @@ SWEEP_SHAPES = (
 
 def bench_sweep(X, stream, shapes=SWEEP_SHAPES, steps=20, cold_reps=4):
     """The default launch on each (element bytes, rows, cols) matrix of
-    ``shapes`` (uninitialised bytes: the path is data-independent), against
-    the library's default copy over the same bytes, back to back (average
-    over the region of ``steps`` launches) and with the caches flushed
-    before each launch (median of ``cold_reps``).  Returns a list of rows."""
+    ``shapes``, filled with seeded random bytes, against the library's
+    default copy over the same bytes, back to back (average over the region
+    of ``steps`` launches) and with the caches flushed before each launch
+    (median of ``cold_reps``).  Returns a list of rows.
+
+    The bytes must be random: the kernels never look at them, but on MI355X
+    back-to-back launches over zero-filled buffers (what a fresh, untouched
+    allocation holds) run about 17% faster than over random data, the copy
+    as much as the transpose, while cache-cold launches do not change."""
     import torch
     dev = torch.device("cuda", 0)
     sh = int(stream.cuda_stream)
@@ -526,7 +531,11 @@ def bench_sweep(X, stream, shapes=SWEEP_SHAPES, steps=20, cold_reps=4):
         nbytes = r * c * s
         x = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.int32,
                         device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(s * 1_000_003 + r * 1009 + c)
+        x.view(torch.uint8).random_(0, 256, generator=gen)
         y = torch.empty_like(x)
+        y.view(torch.uint8).random_(0, 256, generator=gen)
         dt = {1: X.XPOSE_U8, 2: X.XPOSE_F16, 4: X.XPOSE_F32, 8: X.XPOSE_F64}[s]
         rc, info = X.xpose_plan(y.data_ptr(), x.data_ptr(), 1, r, c, c, r, 0,
                                 0, dt, None)
