@@ -494,11 +494,98 @@ __device__ __forceinline__ u32x4 shift_gather(const typename T::U *lds,
   }
 }
 
+// Phase 1 of a line-aligned tile: input rows [top, top + PR) x columns
+// [c0, c0 + TC) into the swizzled LDS tile.  INNER (every row and chunk
+// inside the matrix): the loads carry no checks, so each lane issues all of
+// them before it waits for the first.  Otherwise rows outside the matrix
+// read as zero (never stored) and the chunk at the column edge moves element
+// by element; each of those loads sits in its own branch, and the compiler
+// waits for it before the next one is issued.
+template <class T, bool INNER>
+__device__ __forceinline__ void shift_load(typename T::Base::U *lds,
+                                           const char *in, int64_t top,
+                                           int64_t rows, int64_t ld_in,
+                                           int64_t c0, int64_t cols_left,
+                                           int wave, int lane) {
+  using B = typename T::Base;
+  using E = typename B::E;
+  constexpr int S = (int)sizeof(E);
+  constexpr int LCP = B::CACHE == kNtLoadStore ? kNtLoadStore : kCacheDefault;
+  u32x4 v[B::LIT][T::K];
+#pragma unroll
+  for (int it = 0; it < B::LIT; ++it) {
+    int p, ch;
+    lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
+#pragma unroll
+    for (int k = 0; k < T::K; ++k) {
+      const int64_t row = top + p * T::K + k;
+      const char *src = in + (row * ld_in + c0 + ch * T::V) * S;
+      if (INNER) {
+        v[it][k] = load16<LCP>(src);
+      } else if (row < 0 || row >= rows) {
+        v[it][k] = u32x4{0, 0, 0, 0};
+      } else if ((ch + 1) * T::V <= cols_left) {
+        v[it][k] = load16<LCP>(src);
+      } else {
+        E e[T::V];
+#pragma unroll
+        for (int x = 0; x < T::V; ++x)
+          e[x] = ch * T::V + x < cols_left ? reinterpret_cast<const E *>(src)[x]
+                                           : E(0);
+        __builtin_memcpy(&v[it][k], e, 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < B::LIT; ++it) {
+    int p, ch;
+    lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
+    typename B::U u[T::V];
+    pack_units<S>(v[it], u);
+    write_units<B>(lds, p, ch * T::V, u);
+  }
+}
+
+// Phase 2: output row j = c0 + c, line-aligned segment starting at input
+// row r0 - d_j; chunk q holds input rows r0 - d_j + V q .. + V - 1, LDS
+// input rows HALO - d_j + V q .. (always inside [1, PR)).  INNER: the whole
+// segment lies inside the matrix (r0 >= HALO and r0 + TR <= rows) and every
+// tile column is a matrix column, so every store is one 16-byte store.
+template <class T, int CP, bool INNER>
+__device__ __forceinline__ void shift_store(const typename T::Base::U *lds,
+                                            char *out, int64_t r0,
+                                            int64_t rows, int64_t ld_out,
+                                            int64_t c0, int64_t cols_left,
+                                            int wave, int lane) {
+  using E = typename T::Base::E;
+  constexpr int S = (int)sizeof(E);
+#pragma unroll
+  for (int it = 0; it < T::SIT; ++it) {
+    int c, q;
+    lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
+    if (INNER || c < cols_left) {
+      char *row_out = out + (c0 + c) * ld_out * S;
+      const int d = (int)(((uintptr_t)row_out & 127) / S);
+      const int64_t first = r0 - d + T::V * q;  // input row of element 0
+      const u32x4 o = shift_gather<T>(lds, T::HALO - d + T::V * q, c);
+      if (INNER || (first >= 0 && first + T::V - 1 < rows)) {
+        store16<CP>(row_out + first * S, o);
+      } else {
+        E e[T::V];
+        __builtin_memcpy(e, &o, 16);
+#pragma unroll
+        for (int x = 0; x < T::V; ++x)
+          if (first + x >= 0 && first + x < rows)
+            reinterpret_cast<E *>(row_out)[first + x] = e[x];
+      }
+    }
+  }
+}
+
 template <int S, int TR, int TC, int NT, int CP>
 __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
   using T = ShiftTile<S, TR, TC, NT, CP>;
   using B = typename T::Base;
-  using E = typename Elem<S>::E;
   __shared__ __attribute__((aligned(16))) typename B::U lds[T::LDS_UNITS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -510,61 +597,20 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
   const char *in = static_cast<const char *>(a.in) + b * a.stride_in * S;
   char *out = static_cast<char *>(a.out) + b * a.stride_out * S;
   const int64_t cols_left = a.cols - c0;
-
-  // Phase 1: rows [top, top + PR) x columns [c0, c0 + TC) as an ordinary
-  // swizzled tile; rows outside the matrix read as zero (never stored).
-#pragma unroll
-  for (int it = 0; it < B::LIT; ++it) {
-    int p, ch;
-    lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
-    u32x4 v[T::K];
-#pragma unroll
-    for (int k = 0; k < T::K; ++k) {
-      const int64_t row = top + p * T::K + k;
-      const bool in_rows = row >= 0 && row < a.rows;
-      const char *src = in + (row * a.ld_in + c0 + ch * T::V) * S;
-      if (!in_rows) {
-        v[k] = u32x4{0, 0, 0, 0};
-      } else if ((ch + 1) * T::V <= cols_left) {
-        v[k] = load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src);
-      } else {
-        E e[T::V];
-#pragma unroll
-        for (int x = 0; x < T::V; ++x)
-          e[x] = ch * T::V + x < cols_left ? reinterpret_cast<const E *>(src)[x]
-                                           : E(0);
-        __builtin_memcpy(&v[k], e, 16);
-      }
-    }
-    typename B::U u[T::V];
-    pack_units<S>(v, u);
-    write_units<B>(lds, p, ch * T::V, u);
-  }
-  __syncthreads();
-
-  // Phase 2: output row j = c0 + c, line-aligned segment starting at input
-  // row r0 - d_j; chunk q holds input rows r0 - d_j + V q .. + V - 1, LDS
-  // input rows HALO - d_j + V q .. (always inside [1, PR)).
-#pragma unroll
-  for (int it = 0; it < T::SIT; ++it) {
-    int c, q;
-    lane_map<T::NCO, true>(it * T::NW + wave, lane, c, q);
-    if (c < cols_left) {
-      char *row_out = out + (c0 + c) * a.ld_out * S;
-      const int d = (int)(((uintptr_t)row_out & 127) / S);
-      const int64_t first = r0 - d + T::V * q;  // input row of element 0
-      const u32x4 o = shift_gather<T>(lds, T::HALO - d + T::V * q, c);
-      if (first >= 0 && first + T::V - 1 < a.rows) {
-        store16<CP>(row_out + first * S, o);
-      } else {
-        E e[T::V];
-        __builtin_memcpy(e, &o, 16);
-#pragma unroll
-        for (int x = 0; x < T::V; ++x)
-          if (first + x >= 0 && first + x < a.rows)
-            reinterpret_cast<E *>(row_out)[first + x] = e[x];
-      }
-    }
+  // Uniform per workgroup, so every wave takes the same branch and reaches
+  // the barrier inside it.
+  if (top >= 0 && r0 + TR <= a.rows && cols_left >= TC) {
+    shift_load<T, true>(lds, in, top, a.rows, a.ld_in, c0, cols_left, wave,
+                        lane);
+    __syncthreads();
+    shift_store<T, CP, true>(lds, out, r0, a.rows, a.ld_out, c0, cols_left,
+                             wave, lane);
+  } else {
+    shift_load<T, false>(lds, in, top, a.rows, a.ld_in, c0, cols_left, wave,
+                         lane);
+    __syncthreads();
+    shift_store<T, CP, false>(lds, out, r0, a.rows, a.ld_out, c0, cols_left,
+                              wave, lane);
   }
 }
 
@@ -617,8 +663,10 @@ struct StripTile {
 
 // Input rows [first, first + LIT * NT / NCI) of the strip's columns
 // [c0, c0 + TC) into registers; rows outside the matrix and columns past
-// its edge read as zero (never stored).
-template <class ST, int LIT>
+// its edge read as zero (never stored).  INNER (all of those rows and
+// columns inside the matrix): no checks, so the loads go out back to back
+// (as in shift_load).
+template <class ST, int LIT, bool INNER>
 __device__ __forceinline__ void strip_load(u32x4 (&v)[LIT], const char *in,
                                            int64_t first, int64_t rows,
                                            int64_t ld_in, int64_t c0,
@@ -626,17 +674,20 @@ __device__ __forceinline__ void strip_load(u32x4 (&v)[LIT], const char *in,
                                            int lane) {
   constexpr int S = (int)sizeof(typename ST::Ring::E);
   using E = typename Elem<S>::E;
+  constexpr int LCP =
+      ST::Ring::CACHE == kNtLoadStore ? kNtLoadStore : kCacheDefault;
 #pragma unroll
   for (int it = 0; it < LIT; ++it) {
     int p, ch;
     lane_map<ST::NCI, false>(it * ST::NW + wave, lane, p, ch);
     const int64_t row = first + p;
     const char *src = in + (row * ld_in + c0 + ch * ST::V) * S;
-    if (row < 0 || row >= rows) {
+    if (INNER) {
+      v[it] = load16<LCP>(src);
+    } else if (row < 0 || row >= rows) {
       v[it] = u32x4{0, 0, 0, 0};
     } else if ((ch + 1) * ST::V <= cols_left) {
-      v[it] = load16<ST::Ring::CACHE == kNtLoadStore ? kNtLoadStore
-                                                     : kCacheDefault>(src);
+      v[it] = load16<LCP>(src);
     } else {
       E e[ST::V];
 #pragma unroll
@@ -646,6 +697,23 @@ __device__ __forceinline__ void strip_load(u32x4 (&v)[LIT], const char *in,
       __builtin_memcpy(&v[it], e, 16);
     }
   }
+}
+
+// strip_load with the checks only where the rows or columns reach past the
+// matrix (uniform per workgroup).
+template <class ST, int LIT>
+__device__ __forceinline__ void strip_load_any(u32x4 (&v)[LIT],
+                                               const char *in, int64_t first,
+                                               int64_t rows, int64_t ld_in,
+                                               int64_t c0, int64_t cols_left,
+                                               int wave, int lane) {
+  constexpr int64_t N = (int64_t)LIT * ST::Ring::NW * 64 / ST::NCI;
+  if (first >= 0 && first + N <= rows && cols_left >= ST::Ring::TCOLS)
+    strip_load<ST, LIT, true>(v, in, first, rows, ld_in, c0, cols_left, wave,
+                              lane);
+  else
+    strip_load<ST, LIT, false>(v, in, first, rows, ld_in, c0, cols_left, wave,
+                               lane);
 }
 
 template <class ST, int LIT>
@@ -665,13 +733,49 @@ __device__ __forceinline__ void strip_to_ring(typename ST::U *lds,
   }
 }
 
+// One tile of a strip, gathered from the ring and stored: as shift_store,
+// with the unit rows read through the ring.
+template <class ST, int CP, bool INNER>
+__device__ __forceinline__ void strip_store(const typename ST::U *lds,
+                                            char *out, int64_t r0,
+                                            int64_t rows, int64_t ld_out,
+                                            int64_t c0, int64_t cols_left,
+                                            int wave, int lane) {
+  using Sh = typename ST::Shift;
+  constexpr int S = (int)sizeof(typename ST::Ring::E);
+  using E = typename Elem<S>::E;
+#pragma unroll
+  for (int it = 0; it < Sh::SIT; ++it) {
+    int c, q;
+    lane_map<Sh::NCO, true>(it * Sh::NW + wave, lane, c, q);
+    if (INNER || c < cols_left) {
+      char *row_out = out + (c0 + c) * ld_out * S;
+      const int d = (int)(((uintptr_t)row_out & 127) / S);
+      const int64_t first = r0 - d + ST::V * q;
+      typename ST::U w[ST::V];
+#pragma unroll
+      for (int k = 0; k < ST::V; ++k)
+        w[k] = lds[ST::Ring::lds_index(ST::ring_row(first + k), c)];
+      const u32x4 o = units_to_vec<S>(w);
+      if (INNER || (first >= 0 && first + ST::V - 1 < rows)) {
+        store16<CP>(row_out + first * S, o);
+      } else {
+        E e[ST::V];
+        __builtin_memcpy(e, &o, 16);
+#pragma unroll
+        for (int x = 0; x < ST::V; ++x)
+          if (first + x >= 0 && first + x < rows)
+            reinterpret_cast<E *>(row_out)[first + x] = e[x];
+      }
+    }
+  }
+}
+
 template <int S, int TR, int TC, int NT, int CP>
 __global__ __launch_bounds__(NT) void xpose_shift_strip_kernel(TileArgs a,
                                                                uint32_t seg,
                                                                uint32_t nseg) {
   using ST = StripTile<S, TR, TC, NT, CP>;
-  using Sh = typename ST::Shift;
-  using E = typename Elem<S>::E;
   __shared__ __attribute__((aligned(16))) typename ST::U lds[ST::Ring::LDS_UNITS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -696,11 +800,11 @@ __global__ __launch_bounds__(NT) void xpose_shift_strip_kernel(TileArgs a,
   {  // the first tile's rows, its halo included
     const int64_t r0 = (int64_t)tr_first * TR;
     u32x4 h[ST::LIT_HALO];
-    strip_load<ST>(h, in, r0 - ST::HALO, a.rows, a.ld_in, c0, cols_left, wave,
-                   lane);
+    strip_load_any<ST>(h, in, r0 - ST::HALO, a.rows, a.ld_in, c0, cols_left,
+                       wave, lane);
     strip_to_ring<ST>(lds, h, r0 - ST::HALO, wave, lane);
     u32x4 v[ST::LIT_NEW];
-    strip_load<ST>(v, in, r0, a.rows, a.ld_in, c0, cols_left, wave, lane);
+    strip_load_any<ST>(v, in, r0, a.rows, a.ld_in, c0, cols_left, wave, lane);
     strip_to_ring<ST>(lds, v, r0, wave, lane);
   }
   __syncthreads();
@@ -711,35 +815,16 @@ __global__ __launch_bounds__(NT) void xpose_shift_strip_kernel(TileArgs a,
     const bool more = tr + 1 < tr_end;
     u32x4 v[ST::LIT_NEW];
     if (more)
-      strip_load<ST>(v, in, r0 + TR, a.rows, a.ld_in, c0, cols_left, wave,
-                     lane);
+      strip_load_any<ST>(v, in, r0 + TR, a.rows, a.ld_in, c0, cols_left,
+                         wave, lane);
     // Output row j = c0 + c, line-aligned segment from input row r0 - d_j
     // (as the one-shot line-aligned tile), its rows read from the ring.
-#pragma unroll
-    for (int it = 0; it < Sh::SIT; ++it) {
-      int c, q;
-      lane_map<Sh::NCO, true>(it * Sh::NW + wave, lane, c, q);
-      if (c < cols_left) {
-        char *row_out = out + (c0 + c) * a.ld_out * S;
-        const int d = (int)(((uintptr_t)row_out & 127) / S);
-        const int64_t first = r0 - d + ST::V * q;
-        typename ST::U w[ST::V];
-#pragma unroll
-        for (int k = 0; k < ST::V; ++k)
-          w[k] = lds[ST::Ring::lds_index(ST::ring_row(first + k), c)];
-        const u32x4 o = units_to_vec<S>(w);
-        if (first >= 0 && first + ST::V - 1 < a.rows) {
-          store16<CP>(row_out + first * S, o);
-        } else {
-          E e[ST::V];
-          __builtin_memcpy(e, &o, 16);
-#pragma unroll
-          for (int x = 0; x < ST::V; ++x)
-            if (first + x >= 0 && first + x < a.rows)
-              reinterpret_cast<E *>(row_out)[first + x] = e[x];
-        }
-      }
-    }
+    if (r0 >= ST::HALO && r0 + TR <= a.rows && cols_left >= TC)
+      strip_store<ST, CP, true>(lds, out, r0, a.rows, a.ld_out, c0, cols_left,
+                                wave, lane);
+    else
+      strip_store<ST, CP, false>(lds, out, r0, a.rows, a.ld_out, c0,
+                                 cols_left, wave, lane);
     if (more) {
       __syncthreads();
       strip_to_ring<ST>(lds, v, r0 + TR, wave, lane);
@@ -1005,6 +1090,9 @@ static const TileKernel kTileKernels[] = {
     XPOSE_SHIFT(4, 256, 64, 256, kNtStore),
     XPOSE_SHIFT(4, 256, 64, 256, kCacheDefault),
     XPOSE_SHIFT_S(4, 128, 32, 256, kNtStore), XPOSE_SHIFT(4, 64, 32, 128, kNtStore),
+    XPOSE_SHIFT(4, 64, 128, 256, kNtStore),
+    XPOSE_SHIFT(4, 128, 128, 256, kNtStore),
+    XPOSE_SHIFT(4, 256, 128, 256, kNtStore),
     XPOSE_TILE(4, 64, 64, 256, kSwizzle, kNtLoadStore),
     // 2-byte elements
     XPOSE_TILES(2, 32, 32, 64), XPOSE_TILES(2, 32, 64, 128),

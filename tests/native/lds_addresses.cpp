@@ -162,6 +162,7 @@ int main() {
   tiles<4, 128, 32, 256>(); tiles<4, 256, 128, 256>();
   shift<4, 64, 64, 256>(); shift<4, 128, 64, 256>(); shift<4, 256, 64, 256>();
   shift<4, 128, 32, 256>(); shift<4, 64, 32, 128>();
+  shift<4, 64, 128, 256>(); shift<4, 128, 128, 256>(); shift<4, 256, 128, 256>();
   // 2-byte elements
   tiles<2, 32, 32, 64>(); tiles<2, 32, 64, 128>(); tiles<2, 64, 32, 128>();
   tiles<2, 64, 64, 128>(); tiles<2, 64, 64, 256>(); tiles<2, 128, 128, 256>();

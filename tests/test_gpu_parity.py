@@ -465,7 +465,8 @@ def test_direct_lds_kernels(s):
                    label=tag + " batch")
 
 
-SHIFT_TILES = {4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32)),
+SHIFT_TILES = {4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32),
+                   (64, 128), (128, 128), (256, 128)),
                2: ((64, 64), (128, 64), (256, 64)),
                8: ((32, 32), (64, 32), (64, 64))}
 

@@ -71,7 +71,7 @@ def test_pad_and_unpadded_ablation(worst):
 
 def test_line_aligned_tiles_every_pitch(worst):
     shift = [k for k in kernels(worst) if k.startswith("shift/")]
-    assert len(shift) == 11
+    assert len(shift) == 14
     for k in shift:
         assert worst[(k, "read")] == 1 and worst[(k, "write")] == 1
 
