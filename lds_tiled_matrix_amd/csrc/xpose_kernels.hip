@@ -1180,26 +1180,41 @@ __global__ __launch_bounds__(NT) void xpose_packed_kernel(PackedArgs a) {
   char *dst = static_cast<char *>(a.out) + m0 * m * S;
   const uint32_t nv = n / V;  // whole 16-byte vectors
 
-  // Phase 1: the block's input bytes, in order, into LDS.
-  if (pad == 0) {
-    for (uint32_t v = threadIdx.x; v < nv; v += NT)
-      *reinterpret_cast<u32x4 *>(lds + v * V) =
-          load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src + v * 16);
-    for (uint32_t e = nv * V + threadIdx.x; e < n; e += NT)
-      lds[e] = reinterpret_cast<const E *>(src)[e];
-  } else {
-    // Rows are whole 16-byte vectors here (cols * S is a multiple of 64).
-    for (uint32_t v = threadIdx.x; v < nv; v += NT) {
+  // Phase 1: the block's input bytes, in order, into LDS.  Every lane
+  // issues its NIT loads before the first LDS write: lanes past the block's
+  // last vector reload that vector (in bounds, same line) instead of
+  // branching around the load, which would make the compiler wait for each
+  // load before issuing the next.
+  constexpr int NIT = (BB / 16 + NT - 1) / NT;
+  constexpr int LCP = CP == kNtLoadStore ? kNtLoadStore : kCacheDefault;
+  if (nv > 0) {  // uniform per workgroup
+    u32x4 w[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const uint32_t v = threadIdx.x + k * NT;
+      w[k] = load16<LCP>(src + (v < nv ? v : nv - 1) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const uint32_t v = threadIdx.x + k * NT;
+      if (v >= nv) continue;
       const uint32_t e = v * V;
-      const u32x4 w =
-          load16<CP == kNtLoadStore ? kNtLoadStore : kCacheDefault>(src + v * 16);
-      uint32_t *d = reinterpret_cast<uint32_t *>(lds + e + e / cols * pad);
-      d[0] = w.x;
-      d[1] = w.y;
-      d[2] = w.z;
-      d[3] = w.w;
+      if (pad == 0) {
+        *reinterpret_cast<u32x4 *>(lds + e) = w[k];
+      } else {
+        // Rows are whole 16-byte vectors here (cols * S is a multiple of
+        // 64), so a vector never crosses a padded row end.
+        uint32_t *d = reinterpret_cast<uint32_t *>(lds + e + e / cols * pad);
+        d[0] = w[k].x;
+        d[1] = w[k].y;
+        d[2] = w[k].z;
+        d[3] = w[k].w;
+      }
     }
   }
+  if (pad == 0)
+    for (uint32_t e = nv * V + threadIdx.x; e < n; e += NT)
+      lds[e] = reinterpret_cast<const E *>(src)[e];
   __syncthreads();
 
   // Phase 2: output element o of the block is element (j, i) of output
