@@ -86,6 +86,7 @@ struct Default {
 constexpr int64_t kSmallMatrixBytes = 64ll << 20;
 constexpr int64_t kShortAlignRows = 256;
 constexpr int64_t kBigCallBytes = 512ll << 20;
+constexpr int64_t kMidCallBytes = 128ll << 20;
 // Single matrices with both sides at least kLargeMinDim take 128 KiB tiles
 // (one workgroup per compute unit) in the diagonal order: 2-byte elements
 // from kLargeCallBytes (read + write) on; 4-byte ones in the pitches below
@@ -142,6 +143,7 @@ struct CallShape {
   bool out_row128;   // output rows start on 128-byte lines
   bool small;        // a batch of matrices of at most kSmallMatrixBytes
   bool big;          // at least kBigCallBytes read + write
+  bool mid;          // at least kMidCallBytes read + write
   bool align;        // line-aligned output tiles
   bool single;       // one matrix, both sides at least kLargeMinDim
   bool large, huge;  // single, and at least kLargeCallBytes / kHugeCallBytes
@@ -154,14 +156,20 @@ struct CallShape {
 Default default_for(int s, const CallShape &c) {
   if (c.align) {
     switch (s) {
-      // 2-byte elements in big calls: 128 x 64 tiles in column bands of at
-      // most 32 tile columns, for the reason given for 4-byte elements
-      // below: 16383^2 0.85 of the copy hot and cold against 0.80 with
-      // 16 x 16 super-tiles, 20001 x 12345 0.75 / 0.74 against 0.73.
-      // Below 512 MiB the bands trade hot for cold (8191^2: 0.86 / 0.85
-      // against 0.93 / 0.77), so 64 x 64 super-tiles stay.
+      // 2-byte elements from kMidCallBytes on: 128 x 64 tiles in column
+      // bands of at most 32 tile columns, for the reason given for 4-byte
+      // elements below: 16383^2 0.85 of the copy hot and cold against 0.80
+      // with 16 x 16 super-tiles, 20001 x 12345 0.75 / 0.74 against 0.73.
+      // Between 128 and 512 MiB they trade a little hot for more cold
+      // against 64 x 64 super-tiles (fraction of the copy hot / cold:
+      // 12345 x 6789 0.95 / 0.76 against 0.92 / 0.67, 9999^2 0.91 / 0.75
+      // against 0.90 / 0.65, 8191^2 0.90 / 0.86 against 0.93 / 0.77, 6001^2
+      // 0.87 / 0.76 against 0.91 / 0.71, 4 x 4097^2 0.93 / 0.78 against
+      // 0.94 / 0.68).  Below 128 MiB the two are level (4097^2 0.94 /
+      // 0.85 against 0.94 / 0.84) or the wider tile wastes rows (2049^2,
+      // 1000^2), so 64 x 64 super-tiles stay there.
       case 2:
-        if (c.big) return {128, 64, 256, kSwz, kNT, 1, 32, 1, kBands, true};
+        if (c.mid) return {128, 64, 256, kSwz, kNT, 1, 32, 1, kBands, true};
         return {64, 64, 256, kSwz, kNT, 16, 16, 1, kSup, true};
       // Bands of 64 tile columns, per-XCD ranges: the tile above (whose last
       // rows are the halo) and the tile to the left (which shares the input
@@ -415,6 +423,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   int64_t call_bytes;
   const bool big = !mul_ok(2 * batch, rows * cols * s, &call_bytes) ||
                    call_bytes >= kBigCallBytes;
+  const bool mid = big || call_bytes >= kMidCallBytes;
   const bool direct = opts && (opts->flags & XPOSE_FLAG_DIRECT_LDS);
   const bool tr_read = opts && (opts->flags & XPOSE_FLAG_TR_READ);
   // Line-aligned output tiles are the default where they apply, unless a
@@ -448,6 +457,7 @@ int make_plan(const void *out, const void *in, int64_t batch, int64_t rows,
   shape.out_row128 = out_row128;
   shape.small = small;
   shape.big = big;
+  shape.mid = mid;
   shape.align = want_align || (align_ok && !out_row128 && !short_rows);
   shape.single = single;
   shape.large = large;

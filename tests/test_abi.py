@@ -437,11 +437,18 @@ def test_align_out_option():
     assert plan(rows=150, ld_out=150, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT), **kw)[1].aligned_out == 1
     assert plan(rows=150, ld_out=150, dtype=X.XPOSE_F32, batch=40, cols=600,
                 stride_in=600 * 150, stride_out=600 * 150)[1].aligned_out == 1
-    # big 2-byte calls take 128 x 64 line-aligned tiles, smaller ones 64 x 64
-    rc, info = plan(rows=16383, cols=16383, ld_out=16383, dtype=X.XPOSE_F16)
-    assert rc == 0 and info.aligned_out == 1 and (info.tile_rows, info.tile_cols) == (128, 64)
-    rc, info = plan(rows=9999, cols=9999, ld_out=9999, dtype=X.XPOSE_F16)
-    assert rc == 0 and info.aligned_out == 1 and (info.tile_rows, info.tile_cols) == (64, 64)
+    # 2-byte calls of 128 MiB (read + write) or more take 128 x 64
+    # line-aligned tiles in column bands, smaller ones 64 x 64 super-tiles
+    for r, c in ((16383, 16383), (9999, 9999), (5793, 5793)):
+        rc, info = plan(rows=r, cols=c, ld_out=r, dtype=X.XPOSE_F16)
+        assert rc == 0 and info.aligned_out == 1
+        assert (info.tile_rows, info.tile_cols) == (128, 64), (r, c)
+        assert info.order == X.ORDER_COLUMN_BANDS
+    for r, c in ((5791, 5791), (4097, 4097)):
+        rc, info = plan(rows=r, cols=c, ld_out=r, dtype=X.XPOSE_F16)
+        assert rc == 0 and info.aligned_out == 1
+        assert (info.tile_rows, info.tile_cols) == (64, 64), (r, c)
+        assert info.order == X.ORDER_SUPER_TILES
     # asked for on line-aligned rows: the aligned-out default tile
     rc, info = plan(rows=8192, cols=8192, opts=X.make_opts(flags=X.FLAG_ALIGN_OUT))
     assert rc == 0 and info.aligned_out == 1 and info.tiles == -(-(8192 + 31) // info.tile_rows) * (8192 // info.tile_cols)

@@ -471,6 +471,21 @@ SHIFT_TILES = {4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32),
                8: ((32, 32), (64, 32), (64, 64))}
 
 
+def test_aligned_out_defaults_by_call_size():
+    """The default line-aligned tile changes with the call size: fp16 from
+    128 MiB on takes 128 x 64 tiles in column bands, below it 64 x 64
+    super-tiles; fp32 and fp64 keep one tile.  Each default at an odd pitch,
+    every element against the oracle."""
+    for s, r, c, want in ((2, 5793, 5793, (128, 64)), (2, 5791, 5791, (64, 64)),
+                          (2, 12345, 3001, (128, 64)), (4, 4001, 3333, (64, 64)),
+                          (8, 3001, 2999, (32, 32))):
+        rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, r, c, c, r, 0, 0,
+                                DTYPE_OF_SIZE[s], None)
+        assert rc == 0 and info.aligned_out == 1
+        assert (info.tile_rows, info.tile_cols) == want, (s, r, c)
+        check_case(s, 1, r, c, seed=r + c + s, label=f"align-out default s{s}")
+
+
 @pytest.mark.parametrize("s", sorted(SHIFT_TILES))
 def test_aligned_out_kernels(s):
     """Line-aligned output tiles: every built shape and cache policy, output
