@@ -105,7 +105,8 @@ def test_random_tr_cases(seed):
 
 
 SHIFT_TILES = {2: ((64, 64), (128, 64), (256, 64)),
-               4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32)),
+               4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32),
+                   (64, 128), (128, 128), (256, 128)),
                8: ((32, 32), (64, 32), (64, 64))}
 
 
@@ -148,8 +149,9 @@ def campaign_opts(rng, s):
 def test_random_campaign(chunk):
     """25 seeds x 25 cases per chunk over every option family, pitches and
     pointer offsets at every residue (one-off runs of 1,260 seeds of the
-    generator before the 128 KiB tiles and column strips joined it, and of
-    seeds 100-699, 15,000 cases, of this one also passed)."""
+    generator before the 128 KiB tiles and column strips joined it, of
+    seeds 100-699, 15,000 cases, before the wider line-aligned tiles joined
+    it, and of seeds 100-6599, 162,500 cases, of this one also passed)."""
     for seed in range(chunk * 25, chunk * 25 + 25):
         rng = random.Random(50000 + seed)
         for case in range(25):
