@@ -256,6 +256,75 @@ __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
 // the edge go element by element; without it (the element-wise path asked
 // for explicitly, or rows a direct-load kernel cannot take) every access is
 // one element.
+// Phase 1 of an edge tile on the 16-byte path, every load issued before the
+// first wait: each chunk is one unconditional 16-byte load from an address
+// chosen without a branch (a branch around each load makes the compiler
+// wait for every load before it issues the next).
+//  * whole chunk inside the matrix: the chunk itself;
+//  * chunk across the row's end (partial): the 16 bytes that END at the
+//    row's last element, then shifted down so the chunk's elements come
+//    first and the bytes past the row's end are zero.  Those 16 bytes lie in
+//    the row because the tile holds at least V columns (cols_left >= V);
+//  * chunk past the row's end, or row past the matrix: the tile's first
+//    chunk (whole, by the same condition), then zeroed.
+template <class T>
+__device__ __forceinline__ void edge_load_batched(typename T::U *lds,
+                                                  const char *src,
+                                                  int64_t ld_in,
+                                                  int64_t rows_left,
+                                                  int64_t cols_left, int wave,
+                                                  int lane) {
+  constexpr int S = (int)sizeof(typename T::E);
+  constexpr bool LSPLIT = !T::WIDE_WRITE;
+  u32x4 v[T::LIT][T::K];
+#pragma unroll
+  for (int it = 0; it < T::LIT; ++it) {
+    int p, ch;
+    lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
+    const int64_t have = cols_left - (int64_t)ch * T::V;  // elements left
+#pragma unroll
+    for (int k = 0; k < T::K; ++k) {
+      const int row = p * T::K + k;
+      const char *rs = src + ((int64_t)row * ld_in + ch * T::V) * S;
+      const char *at = src;
+      if (row < rows_left && have > 0)
+        at = have >= T::V ? rs : rs + have * S - 16;
+      v[it][k] = load16<T::CACHE>(at);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < T::LIT; ++it) {
+    int p, ch;
+    lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
+    const int64_t have = cols_left - (int64_t)ch * T::V;
+#pragma unroll
+    for (int k = 0; k < T::K; ++k) {
+      const int row = p * T::K + k;
+      if (row >= rows_left || have <= 0) {
+        v[it][k] = u32x4{0, 0, 0, 0};
+      } else if (have < T::V) {
+        // bytes [16 - have * S, 16) of the load are the chunk's first
+        // have * S bytes: shift the 128-bit value down by that offset.
+        const int sh = (int)(16 - have * S) * 8;  // 8 .. 120 bits
+        uint64_t lo = (uint64_t)v[it][k].x | ((uint64_t)v[it][k].y << 32);
+        uint64_t hi = (uint64_t)v[it][k].z | ((uint64_t)v[it][k].w << 32);
+        if (sh >= 64) {
+          lo = hi >> (sh - 64);
+          hi = 0;
+        } else {
+          lo = (lo >> sh) | (hi << (64 - sh));
+          hi >>= sh;
+        }
+        v[it][k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                         (uint32_t)(hi >> 32)};
+      }
+    }
+    typename T::U u[T::V];
+    pack_units<S>(v[it], u);
+    write_units<T>(lds, p, ch * T::V, u);
+  }
+}
+
 template <class T, bool VEC>
 __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
                                                  const char *src, char *dst,
@@ -266,38 +335,42 @@ __device__ __forceinline__ void tile_elementwise(typename T::U *lds,
   using E = typename T::E;
   constexpr int S = (int)sizeof(E);
   constexpr bool LSPLIT = !T::WIDE_WRITE;
+  if (VEC && cols_left >= T::V) {  // uniform per workgroup
+    edge_load_batched<T>(lds, src, ld_in, rows_left, cols_left, wave, lane);
+  } else {
 #pragma unroll
-  for (int it = 0; it < T::LIT; ++it) {
-    int p, ch;
-    lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
-    u32x4 v[T::K];
+    for (int it = 0; it < T::LIT; ++it) {
+      int p, ch;
+      lane_map<T::NCI, LSPLIT>(it * T::NW + wave, lane, p, ch);
+      u32x4 v[T::K];
 #pragma unroll
-    for (int k = 0; k < T::K; ++k) {
-      const int row = p * T::K + k;
-      const char *rs = src + ((int64_t)row * ld_in + ch * T::V) * S;
-      if (VEC && row < rows_left && (ch + 1) * T::V <= cols_left) {
-        v[k] = load16<T::CACHE>(rs);
-      } else if (VEC && S <= 2) {
-        // 1- and 2-byte elements: the chunk's elements inside the matrix
-        // in at most four pieces instead of up to 16 element loads.
-        const int64_t have = row < rows_left ? cols_left - ch * T::V : 0;
-        uint64_t lo, hi;
-        load_head(rs, have > 0 ? (int)(have * S) : 0, lo, hi);
-        v[k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
-                     (uint32_t)(hi >> 32)};
-      } else {
-        E e[T::V];
+      for (int k = 0; k < T::K; ++k) {
+        const int row = p * T::K + k;
+        const char *rs = src + ((int64_t)row * ld_in + ch * T::V) * S;
+        if (VEC && row < rows_left && (ch + 1) * T::V <= cols_left) {
+          v[k] = load16<T::CACHE>(rs);
+        } else if (VEC && S <= 2) {
+          // 1- and 2-byte elements: the chunk's elements inside the matrix
+          // in at most four pieces instead of up to 16 element loads.
+          const int64_t have = row < rows_left ? cols_left - ch * T::V : 0;
+          uint64_t lo, hi;
+          load_head(rs, have > 0 ? (int)(have * S) : 0, lo, hi);
+          v[k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                       (uint32_t)(hi >> 32)};
+        } else {
+          E e[T::V];
 #pragma unroll
-        for (int x = 0; x < T::V; ++x)
-          e[x] = (row < rows_left && ch * T::V + x < cols_left)
-                     ? reinterpret_cast<const E *>(rs)[x]
-                     : E(0);
-        __builtin_memcpy(&v[k], e, 16);
+          for (int x = 0; x < T::V; ++x)
+            e[x] = (row < rows_left && ch * T::V + x < cols_left)
+                       ? reinterpret_cast<const E *>(rs)[x]
+                       : E(0);
+          __builtin_memcpy(&v[k], e, 16);
+        }
       }
+      typename T::U u[T::V];
+      pack_units<S>(v, u);
+      write_units<T>(lds, p, ch * T::V, u);
     }
-    typename T::U u[T::V];
-    pack_units<S>(v, u);
-    write_units<T>(lds, p, ch * T::V, u);
   }
   __syncthreads();
 #pragma unroll
