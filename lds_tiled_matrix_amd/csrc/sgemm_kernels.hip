@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "sgemm_lanes.h"
 #include "sgemm_kernels.h"
@@ -391,10 +392,15 @@ const SgemmKernel kSgemmKernels[] = {
 // The sum of the split partials, 4 consecutive elements of a row per lane
 // where n is a multiple of 4 and C's rows are 16-byte aligned, else one.
 // A grid-stride loop over the m x n elements; the partials are read once
-// and C read (beta != 0) and written once.
+// and C read (beta != 0) and written once.  The planes are read kGroup at a
+// time, every load of a group issued before the first add (lanes past the
+// last plane reread plane z0, in bounds, and do not add it), and added in
+// plane order z = 0, 1, ..., so the sum is the same as a plain loop's.
+constexpr int kReduceGroup = 8;
 template <bool VEC4>
 __global__ __launch_bounds__(256) void xpose_sgemm_reduce_kernel(
     SgemmReduceArgs r) {
+  using V = typename std::conditional<VEC4, f32x4, float>::type;
   const int64_t per_row = VEC4 ? r.n / 4 : r.n;
   const int64_t total = r.m * per_row, plane = r.m * r.n;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
@@ -403,10 +409,19 @@ __global__ __launch_bounds__(256) void xpose_sgemm_reduce_kernel(
     const int64_t i = v / per_row, j = (v - i * per_row) * (VEC4 ? 4 : 1);
     const float *p = r.partial + i * r.n + j;
     float *c = r.c + i * r.ldc + j;
+    V s = *reinterpret_cast<const V *>(p);
+    for (int z0 = 1; z0 < r.splits; z0 += kReduceGroup) {
+      V t[kReduceGroup];
+#pragma unroll
+      for (int u = 0; u < kReduceGroup; ++u) {
+        const int z = z0 + u < r.splits ? z0 + u : z0;
+        t[u] = *reinterpret_cast<const V *>(p + z * plane);
+      }
+#pragma unroll
+      for (int u = 0; u < kReduceGroup; ++u)
+        if (z0 + u < r.splits) s += t[u];
+    }
     if constexpr (VEC4) {
-      f32x4 s = *reinterpret_cast<const f32x4 *>(p);
-      for (int z = 1; z < r.splits; ++z)
-        s += *reinterpret_cast<const f32x4 *>(p + z * plane);
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = r.alpha * s[e];
@@ -417,8 +432,6 @@ __global__ __launch_bounds__(256) void xpose_sgemm_reduce_kernel(
       }
       *reinterpret_cast<f32x4 *>(c) = o;
     } else {
-      float s = p[0];
-      for (int z = 1; z < r.splits; ++z) s += p[z * plane];
       float o = r.alpha * s;
       if (r.beta != 0.f) o = fmaf(r.beta, *c, o);
       *c = o;
