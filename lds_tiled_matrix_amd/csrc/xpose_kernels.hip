@@ -259,7 +259,9 @@ __device__ __forceinline__ void tile_vector(typename T::U *lds, const char *src,
 // Phase 1 of an edge tile on the 16-byte path, every load issued before the
 // first wait: each chunk is one unconditional 16-byte load from an address
 // chosen without a branch (a branch around each load makes the compiler
-// wait for every load before it issues the next).
+// wait for every load before it issues the next).  edge_chunk_src and
+// edge_chunk_fix in xpose_lanes.h state the same address choice and fix-up
+// as host functions, which a host test checks against a guard page.
 //  * whole chunk inside the matrix: the chunk itself;
 //  * chunk across the row's end (partial): the 16 bytes that END at the
 //    row's last element, then shifted down so the chunk's elements come

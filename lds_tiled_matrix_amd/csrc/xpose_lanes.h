@@ -69,6 +69,42 @@ XPOSE_HD inline void store_head(char *p, int n, uint64_t lo, uint64_t hi) {
   if (n & 1) p[off] = (char)get_piece(lo, hi, off);
 }
 
+// Edge tiles on the 16-byte path load every chunk with one unconditional
+// 16-byte access (no branch, so all of a lane's loads go out before the
+// first wait), which needs an in-bounds address for every chunk.  The tile
+// holds at least one whole chunk of each of its rows (16 bytes from the
+// tile's first element on), and `have` is the number of row elements from
+// the chunk's first to the row's end (<= 0 past the end).
+//  * have >= V (whole chunk): the chunk itself;
+//  * 0 < have < V (the chunk crosses the row's end): the 16 bytes that end
+//    at the row's last element, which lie in the row;
+//  * have <= 0 or a row past the matrix: the tile's first chunk (whole).
+XPOSE_HD inline const char *edge_chunk_src(const char *tile0,
+                                           const char *chunk, int64_t have,
+                                           int V, int S, bool in_row) {
+  if (!in_row || have <= 0) return tile0;
+  return have >= V ? chunk : chunk + have * S - 16;
+}
+// The loaded bytes (lo = bytes 0-7, hi = 8-15) made into the chunk: the
+// partial chunk's have * S bytes sit at the top of the load and move down
+// to the start, zero above; chunks past the row's end or rows past the
+// matrix become zero.
+XPOSE_HD inline void edge_chunk_fix(uint64_t &lo, uint64_t &hi, int64_t have,
+                                    int V, int S, bool in_row) {
+  if (!in_row || have <= 0) {
+    lo = hi = 0;
+  } else if (have < V) {
+    const int sh = (int)(16 - have * S) * 8;  // S * 8 .. 120 bits
+    if (sh >= 64) {
+      lo = hi >> (sh - 64);
+      hi = 0;
+    } else {
+      lo = (lo >> sh) | (hi << (64 - sh));
+      hi >>= sh;
+    }
+  }
+}
+
 // Cache policy of the global accesses: plain, non-temporal stores, or
 // non-temporal loads and stores (the data is touched exactly once).
 enum CachePolicy : int { kCacheDefault = 0, kNtStore = 1, kNtLoadStore = 2 };
