@@ -570,13 +570,22 @@ __device__ __forceinline__ u32x4 shift_gather(const typename T::U *lds,
 }
 
 // Phase 1 of a line-aligned tile: input rows [top, top + PR) x columns
-// [c0, c0 + TC) into the swizzled LDS tile.  INNER (every row and chunk
-// inside the matrix): the loads carry no checks, so each lane issues all of
-// them before it waits for the first.  Otherwise rows outside the matrix
-// read as zero (never stored) and the chunk at the column edge moves element
-// by element; each of those loads sits in its own branch, and the compiler
-// waits for it before the next one is issued.
-template <class T, bool INNER>
+// [c0, c0 + TC) into the swizzled LDS tile, rows outside the matrix and
+// columns past its edge as zero (never stored).  Three load paths, chosen
+// per workgroup:
+//  * kShiftInner (every row and chunk inside the matrix): no checks, so
+//    each lane issues all its loads before it waits for the first;
+//  * kShiftEdge (some row or chunk outside, but the tile holds at least V
+//    columns): as the edge tiles' edge_load_batched, every chunk is one
+//    unconditional 16-byte load from an address picked without a branch --
+//    the chunk; the 16 bytes ending at the row's last element, shifted
+//    down; or the tile's first chunk of its first row inside the matrix
+//    (row max(top, 0), which the halo keeps below `rows`), zeroed;
+//  * kShiftChecked (fewer than V columns): element by element.  There each
+//    load sits in its own branch, and the compiler waits for it before the
+//    next one is issued.
+enum ShiftLoad : int { kShiftInner = 0, kShiftEdge = 1, kShiftChecked = 2 };
+template <class T, int MODE>
 __device__ __forceinline__ void shift_load(typename T::Base::U *lds,
                                            const char *in, int64_t top,
                                            int64_t rows, int64_t ld_in,
@@ -586,17 +595,24 @@ __device__ __forceinline__ void shift_load(typename T::Base::U *lds,
   using E = typename B::E;
   constexpr int S = (int)sizeof(E);
   constexpr int LCP = B::CACHE == kNtLoadStore ? kNtLoadStore : kCacheDefault;
+  const char *first = in + ((top > 0 ? top : 0) * ld_in + c0) * S;
   u32x4 v[B::LIT][T::K];
 #pragma unroll
   for (int it = 0; it < B::LIT; ++it) {
     int p, ch;
     lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
+    const int64_t have = cols_left - (int64_t)ch * T::V;  // elements left
 #pragma unroll
     for (int k = 0; k < T::K; ++k) {
       const int64_t row = top + p * T::K + k;
       const char *src = in + (row * ld_in + c0 + ch * T::V) * S;
-      if (INNER) {
+      if (MODE == kShiftInner) {
         v[it][k] = load16<LCP>(src);
+      } else if (MODE == kShiftEdge) {
+        const char *at = first;
+        if (row >= 0 && row < rows && have > 0)
+          at = have >= T::V ? src : src + have * S - 16;
+        v[it][k] = load16<LCP>(at);
       } else if (row < 0 || row >= rows) {
         v[it][k] = u32x4{0, 0, 0, 0};
       } else if ((ch + 1) * T::V <= cols_left) {
@@ -615,6 +631,31 @@ __device__ __forceinline__ void shift_load(typename T::Base::U *lds,
   for (int it = 0; it < B::LIT; ++it) {
     int p, ch;
     lane_map<B::NCI, false>(it * B::NW + wave, lane, p, ch);
+    if (MODE == kShiftEdge) {
+      const int64_t have = cols_left - (int64_t)ch * T::V;
+#pragma unroll
+      for (int k = 0; k < T::K; ++k) {
+        const int64_t row = top + p * T::K + k;
+        if (row < 0 || row >= rows || have <= 0) {
+          v[it][k] = u32x4{0, 0, 0, 0};
+        } else if (have < T::V) {
+          // bytes [16 - have * S, 16) of the load are the chunk's first
+          // have * S bytes: shift the 128-bit value down by that offset.
+          const int sh = (int)(16 - have * S) * 8;  // 8 .. 120 bits
+          uint64_t lo = (uint64_t)v[it][k].x | ((uint64_t)v[it][k].y << 32);
+          uint64_t hi = (uint64_t)v[it][k].z | ((uint64_t)v[it][k].w << 32);
+          if (sh >= 64) {
+            lo = hi >> (sh - 64);
+            hi = 0;
+          } else {
+            lo = (lo >> sh) | (hi << (64 - sh));
+            hi >>= sh;
+          }
+          v[it][k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                           (uint32_t)(hi >> 32)};
+        }
+      }
+    }
     typename B::U u[T::V];
     pack_units<S>(v[it], u);
     write_units<B>(lds, p, ch * T::V, u);
@@ -675,14 +716,18 @@ __global__ __launch_bounds__(NT) void xpose_shift_kernel(TileArgs a) {
   // Uniform per workgroup, so every wave takes the same branch and reaches
   // the barrier inside it.
   if (top >= 0 && r0 + TR <= a.rows && cols_left >= TC) {
-    shift_load<T, true>(lds, in, top, a.rows, a.ld_in, c0, cols_left, wave,
-                        lane);
+    shift_load<T, kShiftInner>(lds, in, top, a.rows, a.ld_in, c0, cols_left,
+                               wave, lane);
     __syncthreads();
     shift_store<T, CP, true>(lds, out, r0, a.rows, a.ld_out, c0, cols_left,
                              wave, lane);
   } else {
-    shift_load<T, false>(lds, in, top, a.rows, a.ld_in, c0, cols_left, wave,
-                         lane);
+    if (cols_left >= T::V)
+      shift_load<T, kShiftEdge>(lds, in, top, a.rows, a.ld_in, c0, cols_left,
+                                wave, lane);
+    else
+      shift_load<T, kShiftChecked>(lds, in, top, a.rows, a.ld_in, c0,
+                                   cols_left, wave, lane);
     __syncthreads();
     shift_store<T, CP, false>(lds, out, r0, a.rows, a.ld_out, c0, cols_left,
                               wave, lane);
