@@ -151,7 +151,8 @@ def test_random_campaign(chunk):
     pointer offsets at every residue (one-off runs of 1,260 seeds of the
     generator before the 128 KiB tiles and column strips joined it, of
     seeds 100-699, 15,000 cases, before the wider line-aligned tiles joined
-    it, and of seeds 100-6599, 162,500 cases, of this one also passed)."""
+    it, and of seeds 100-6599 and 10600-30599, 662,500 cases, of this one
+    also passed)."""
     for seed in range(chunk * 25, chunk * 25 + 25):
         rng = random.Random(50000 + seed)
         for case in range(25):
