@@ -179,7 +179,17 @@ Default default_for(int s, const CallShape &c) {
       // and 0.84 of the copy, against 1.067 x with 16 x 16 super-tiles (the
       // tile above missed at each super-tile's top) and 1.25 x with 128 x 4
       // super-tiles (the tile to the left ran 128 tiles earlier).
-      case 4: return {64, 64, 256, kSwz, kNT, 1, 64, 1, kBands, true};
+      // From kBigCallBytes on, 64 x 128 tiles (512-byte input segments, half
+      // the halo rows per output byte) in the same bands: fraction of the
+      // copy hot / cold 12345 x 6789 0.82-0.83 / 0.83 against 0.81-0.82 /
+      // 0.82, 6789 x 12345 0.84 / 0.84 against 0.81 / 0.82, 20001 x 12345
+      // 0.81 / 0.81 against 0.79 / 0.79, 9999^2, 12345^2 and 16383^2 level
+      // or slightly ahead.  Below it they are mixed (8193 x 8191 hot 0.91
+      // against 0.84, cold 0.89 against 0.91; 4097 x 3001 0.81 / 0.76
+      // against 0.92 / 0.81).
+      case 4:
+        if (c.big) return {64, 128, 256, kSwz, kNT, 1, 64, 1, kBands, true};
+        return {64, 64, 256, kSwz, kNT, 1, 64, 1, kBands, true};
       case 8: return {32, 32, 256, kSwz, kNT, 16, 16, 1, kSup, true};
       default: break;  // no line-aligned tiles for 1-byte elements
     }

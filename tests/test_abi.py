@@ -97,13 +97,19 @@ def test_occupancy_option():
 def test_ragged_and_batched_tile_counts():
     # Odd pitches: output rows are not line-aligned, so line-aligned output
     # tiles are chosen, with one extra tile row for the shifted segments.
+    # From 512 MiB moved on, 64 x 128 tiles; below, 64 x 64.
     rc, info = plan(rows=12345, cols=6789)
-    assert rc == 0 and (info.tile_rows, info.tile_cols) == (64, 64)
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (64, 128)
     assert info.aligned_out == 1 and info.cache == X.CACHE_NT_STORE
-    assert info.tiles == 194 * 107 and info.vector_path == 1
+    assert info.tiles == 194 * 54 and info.vector_path == 1
+    assert (info.group_rows, info.group_cols) == (1, 54)
+    rc, info = plan(rows=8193, cols=8191)   # 4 bytes short of 512 MiB moved
+    assert rc == 0 and (info.tile_rows, info.tile_cols) == (64, 64)
+    assert info.aligned_out == 1 and info.tiles == 129 * 128
+    assert (info.group_rows, info.group_cols) == (1, 64)
     # 12288 rows fill 192 tile rows; shifted segments need a 193rd.
     rc, info = plan(rows=12288, cols=6789, ld_out=12289)
-    assert rc == 0 and info.aligned_out == 1 and info.tiles == 193 * 107
+    assert rc == 0 and info.aligned_out == 1 and info.tiles == 193 * 54
     rc, info = plan(rows=12288, cols=6789)
     assert rc == 0 and info.aligned_out == 0 and info.tiles == 384 * 213
     # A batch of small matrices: taller tiles, small super-tiles.

@@ -474,13 +474,15 @@ SHIFT_TILES = {4: ((64, 64), (128, 64), (256, 64), (128, 32), (64, 32),
 def test_aligned_out_defaults_by_call_size():
     """The default line-aligned tile changes with the call size: fp16 from
     128 MiB on takes 128 x 64 tiles in column bands, below it 64 x 64
-    super-tiles; fp32 and fp64 keep one tile.  Each default at an odd pitch,
-    every element against the oracle."""
+    super-tiles; fp32 from 512 MiB on 64 x 128 tiles, below it 64 x 64;
+    fp64 keeps one tile.  Each default at an odd pitch, every element against
+    the oracle."""
     for s, r, c, want in ((2, 5793, 5793, (128, 64)), (2, 5791, 5791, (64, 64)),
                           (2, 12345, 3001, (128, 64)), (4, 4001, 3333, (64, 64)),
+                          (4, 8193, 8193, (64, 128)), (4, 8193, 8191, (64, 64)),
                           (8, 3001, 2999, (32, 32))):
-        rc, info = X.xpose_plan(0x10000000, 0x20000000, 1, r, c, c, r, 0, 0,
-                                DTYPE_OF_SIZE[s], None)
+        rc, info = X.xpose_plan(0x100000000000, 0x200000000000, 1, r, c, c,
+                                r, 0, 0, DTYPE_OF_SIZE[s], None)
         assert rc == 0 and info.aligned_out == 1
         assert (info.tile_rows, info.tile_cols) == want, (s, r, c)
         check_case(s, 1, r, c, seed=r + c + s, label=f"align-out default s{s}")
