@@ -63,9 +63,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def plan_signature(config: dict) -> str:
+    """The launch a bench line's config describes: layout, tile, workgroup
+    size, cache policy, tile order, workgroups per compute unit and grid."""
+    return (f"{config['layout']} {config['tile']} t{config['threads']} "
+            f"{config['cache']} {config['tile_order']} occupancy "
+            f"{config['occupancy']} workgroups {config['workgroups']}")
+
+
+def read_traffic(config: dict | None = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source (else None)."""
+    if it was taken on the current kernel source and, given the bench
+    line's config, on the launch that config describes (else None): the
+    default's rules live outside the kernel source, so the hash alone does
+    not pin the kernel."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
@@ -75,6 +86,8 @@ def read_traffic():
                 k, v = ln[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
     if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if config is not None and fields.get("plan") != plan_signature(config):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -700,6 +713,23 @@ def main(argv=None):
                                                  args.warmup, stream)
 
     plan = res["plan"]
+    config = {
+        "workload": w.description, "batch": w.batch, "rows": w.rows,
+        "cols": w.cols, "ld_in": w.cols, "ld_out": w.rows,
+        "rw_bytes": nbytes,
+        "layout": X.LAYOUT_NAMES[plan["layout"]],
+        "tile": f"{plan['tile_rows']}x{plan['tile_cols']}",
+        "threads": plan["threads"], "workgroups": plan["tiles"],
+        "cache": X.CACHE_NAMES[plan["cache"]],
+        "tile_order": {
+            X.ORDER_SUPER_TILES:
+                f"super-tiles {plan['group_rows']}x{plan['group_cols']}",
+            X.ORDER_DIAGONAL: "diagonal",
+            X.ORDER_COLUMN_BANDS: f"column bands {plan['group_cols']}",
+        }[plan["order"]]
+                      + (", per-XCD ranges" if plan["xcd_remap"] else ""),
+        "occupancy": plan["occupancy"],
+    }
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -713,23 +743,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": w.description, "batch": w.batch, "rows": w.rows,
-            "cols": w.cols, "ld_in": w.cols, "ld_out": w.rows,
-            "rw_bytes": nbytes,
-            "layout": X.LAYOUT_NAMES[plan["layout"]],
-            "tile": f"{plan['tile_rows']}x{plan['tile_cols']}",
-            "threads": plan["threads"], "workgroups": plan["tiles"],
-            "cache": X.CACHE_NAMES[plan["cache"]],
-            "tile_order": {
-                X.ORDER_SUPER_TILES:
-                    f"super-tiles {plan['group_rows']}x{plan['group_cols']}",
-                X.ORDER_DIAGONAL: "diagonal",
-                X.ORDER_COLUMN_BANDS: f"column bands {plan['group_cols']}",
-            }[plan["order"]]
-                          + (", per-XCD ranges" if plan["xcd_remap"] else ""),
-            "occupancy": plan["occupancy"],
-        },
+        "config": config,
         "system": system_info(),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "frac_of_copy": round(d["median_GBps"] / copy_gbps, 4),
@@ -745,7 +759,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic() if w.key == wl.HEADLINE else None,
+            "traffic": read_traffic(config) if w.key == wl.HEADLINE else None,
         },
         # HBM-served figures: every cache (L2 and the 256 MB memory-side
         # cache) is emptied before each launch, so the bytes come from HBM.

@@ -51,3 +51,22 @@ def test_traffic_summary_parses():
     if t is not None:
         # HBM bytes of one 8192 x 8192 fp32 transpose: close to 2 x 256 MiB
         assert abs(t / (2 * 8192 * 8192 * 4) - 1) < 0.05
+
+
+def test_traffic_needs_the_profiled_launch():
+    """The summary counts only for the launch it was taken on: a config
+    naming another tile, order or grid gets no traffic figure."""
+    cfg = {"layout": "swizzle", "tile": "128x128", "threads": 256,
+           "cache": "nt_store", "tile_order": "diagonal", "occupancy": 1,
+           "workgroups": 4096}
+    fields = {}
+    with open(bench.TRAFFIC_FILE) as f:
+        for ln in f:
+            if ln.startswith("- ") and ":" in ln:
+                k, v = ln[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    assert fields["plan"] == bench.plan_signature(cfg)
+    assert bench.read_traffic(cfg) == bench.read_traffic()
+    for key, other in (("tile", "256x128"), ("tile_order", "super-tiles 8x32"),
+                       ("occupancy", 0), ("workgroups", 2048)):
+        assert bench.read_traffic(dict(cfg, **{key: other})) is None, key
